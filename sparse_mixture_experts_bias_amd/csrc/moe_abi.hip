@@ -1,0 +1,789 @@
+// moe_abi.hip - the C ABI of include/moe.h: argument validation, workspace
+// layout and launch sequencing.  No entry point allocates device memory; every
+// argument is checked before the first launch and errors come back as status
+// codes (the load-time validation of mlxcel PR #1044 "Other guards" and of
+// mlxcel issue #974 "Acceptance Criteria": zero checks before divisibility
+// checks, top-k in 1..num_experts, full expert stacks, quantisation parameters
+// bounded before use, nothing that can abort the process later).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "moe_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+#define CHECK(cond, st, ...) \
+  do {                       \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+#define TRY(expr)                      \
+  do {                                 \
+    moe_status _s = (expr);            \
+    if (_s != MOE_OK) return _s;       \
+  } while (0)
+#define HIPCHK(expr)                                                                  \
+  do {                                                                                \
+    hipError_t _e = (expr);                                                           \
+    if (_e != hipSuccess) return fail(MOE_ERR_DEVICE, "%s: %s", #expr, hipGetErrorString(_e)); \
+  } while (0)
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int dt_size(int dt) { return dt == MOE_F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------------------
+// validation
+// ---------------------------------------------------------------------------
+
+// act_dt: dtype of the activations this linear is applied to
+moe_status check_linear(const moe_linear *L, const char *name, int n, int rows, int cols, int act_dt) {
+  CHECK(L != nullptr, MOE_ERR_ARG, "%s: descriptor is NULL", name);
+  CHECK(L->n > 0 && L->rows > 0 && L->cols > 0, MOE_ERR_SHAPE, "%s: zero or negative dimension (n=%d rows=%d cols=%d)",
+        name, L->n, L->rows, L->cols);
+  CHECK(L->n == n, MOE_ERR_SHAPE, "%s: stack holds %d matrices, expected %d", name, L->n, n);
+  CHECK(L->rows == rows && L->cols == cols, MOE_ERR_SHAPE, "%s: shape [%d, %d], expected [%d, %d]", name, L->rows,
+        L->cols, rows, cols);
+  CHECK(L->w != nullptr, MOE_ERR_ARG, "%s: weight pointer is NULL", name);
+  CHECK(aligned(L->w, 16), MOE_ERR_ARG, "%s: weight pointer not 16-byte aligned", name);
+  CHECK(L->bias == nullptr || aligned(L->bias, 4), MOE_ERR_ARG, "%s: bias pointer misaligned", name);
+  switch (L->fmt) {
+    case MOE_W_DENSE:
+      CHECK(L->dense_dtype == MOE_F32 || L->dense_dtype == MOE_BF16, MOE_ERR_ARG, "%s: dense dtype %d not F32/BF16",
+            name, L->dense_dtype);
+      if (L->dense_dtype == MOE_F32) {
+        CHECK(act_dt == MOE_F32, MOE_ERR_UNSUPPORTED, "%s: F32 weights need F32 activations", name);
+      } else {
+        CHECK(act_dt != MOE_F32, MOE_ERR_UNSUPPORTED, "%s: BF16 weights need BF16/F16 activations", name);
+      }
+      break;
+    case MOE_W_AFFINE4:
+      CHECK(L->bits == 4, MOE_ERR_QUANT, "%s: affine bits %d (only 4 is supported)", name, L->bits);
+      CHECK(L->group_size == 32 || L->group_size == 64 || L->group_size == 128, MOE_ERR_QUANT,
+            "%s: affine group_size %d (32, 64 or 128)", name, L->group_size);
+      CHECK(cols % L->group_size == 0, MOE_ERR_SHAPE, "%s: cols %d not a multiple of group_size %d", name, cols,
+            L->group_size);
+      CHECK(L->scales != nullptr && L->qbias != nullptr, MOE_ERR_ARG, "%s: affine scales/qbias missing", name);
+      CHECK(aligned(L->scales, 2) && aligned(L->qbias, 2), MOE_ERR_ARG, "%s: scales/qbias misaligned", name);
+      CHECK(act_dt != MOE_F32, MOE_ERR_UNSUPPORTED, "%s: quantized weights need BF16/F16 activations", name);
+      break;
+    case MOE_W_MXFP4:
+      CHECK(L->bits == 4, MOE_ERR_QUANT, "%s: mxfp4 bits %d (must be 4)", name, L->bits);
+      CHECK(L->group_size == 32, MOE_ERR_QUANT, "%s: mxfp4 group_size %d (must be 32)", name, L->group_size);
+      CHECK(cols % 64 == 0, MOE_ERR_SHAPE, "%s: mxfp4 cols %d not a multiple of 64", name, cols);
+      CHECK(L->scales != nullptr, MOE_ERR_ARG, "%s: mxfp4 scales missing", name);
+      CHECK(act_dt != MOE_F32, MOE_ERR_UNSUPPORTED, "%s: quantized weights need BF16/F16 activations", name);
+      break;
+    default:
+      return fail(MOE_ERR_ARG, "%s: weight format %d out of range", name, L->fmt);
+  }
+  if (act_dt != MOE_F32) {
+    CHECK(rows % 16 == 0, MOE_ERR_SHAPE, "%s: rows %d not a multiple of 16", name, rows);
+    CHECK(cols % 32 == 0, MOE_ERR_SHAPE, "%s: cols %d not a multiple of 32", name, cols);
+  }
+  return MOE_OK;
+}
+
+moe_status check_mlp(const moe_mlp *m, const char *name, int n, int I, int D, int act_in, int act_mid) {
+  char nm[64];
+  snprintf(nm, sizeof nm, "%s.gate", name);
+  TRY(check_linear(&m->gate, nm, n, I, D, act_in));
+  snprintf(nm, sizeof nm, "%s.up", name);
+  TRY(check_linear(&m->up, nm, n, I, D, act_in));
+  snprintf(nm, sizeof nm, "%s.down", name);
+  TRY(check_linear(&m->down, nm, n, D, I, act_mid));
+  CHECK(std::isfinite(m->swiglu_limit), MOE_ERR_ARG, "%s: swiglu_limit not finite", name);
+  return MOE_OK;
+}
+
+moe_status check_router(const moe_router *r, int H, int x_dt) {
+  CHECK(r != nullptr, MOE_ERR_ARG, "router descriptor is NULL");
+  CHECK(r->num_experts > 0, MOE_ERR_SHAPE, "num_experts %d must be positive", r->num_experts);
+  CHECK(r->num_experts <= MOE_MAX_EXPERTS, MOE_ERR_SHAPE, "num_experts %d above %d", r->num_experts,
+        MOE_MAX_EXPERTS);
+  CHECK(r->top_k >= 1 && r->top_k <= r->num_experts, MOE_ERR_SHAPE, "top_k %d outside 1..num_experts (%d)", r->top_k,
+        r->num_experts);
+  CHECK(r->top_k <= MOE_MAX_TOPK, MOE_ERR_SHAPE, "top_k %d above %d", r->top_k, MOE_MAX_TOPK);
+  CHECK(r->scoring == MOE_SIGMOID || r->scoring == MOE_SOFTMAX, MOE_ERR_ARG, "scoring %d out of range", r->scoring);
+  CHECK(r->norm_topk == 0 || r->norm_topk == 1, MOE_ERR_ARG, "norm_topk %d must be 0 or 1", r->norm_topk);
+  CHECK(std::isfinite(r->routed_scale), MOE_ERR_ARG, "routed_scale not finite");
+  CHECK(r->w != nullptr, MOE_ERR_ARG, "router weight is NULL");
+  CHECK(aligned(r->w, 16), MOE_ERR_ARG, "router weight not 16-byte aligned");
+  CHECK(x_dt == MOE_F32 || H % 32 == 0, MOE_ERR_SHAPE, "hidden %d not a multiple of 32", H);
+  return MOE_OK;
+}
+
+moe_status check_tokens(int64_t T, int K) {
+  CHECK(T >= 0, MOE_ERR_SHAPE, "token count %lld negative", (long long)T);
+  CHECK(T <= (int64_t)(INT32_MAX / 2) / (K > 0 ? K : 1), MOE_ERR_SHAPE, "T*K overflows (T=%lld, K=%d)", (long long)T,
+        K);
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// workspace layout
+// ---------------------------------------------------------------------------
+struct Plan {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  }
+};
+
+moe_status check_ws(void *ws, size_t *ws_bytes, size_t need, bool *query) {
+  CHECK(ws_bytes != nullptr, MOE_ERR_ARG, "ws_bytes is NULL");
+  if (ws == nullptr) {
+    *ws_bytes = need;
+    *query = true;
+    return MOE_OK;
+  }
+  *query = false;
+  CHECK(*ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", *ws_bytes, need);
+  CHECK(need == 0 || aligned(ws, 256), MOE_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  return MOE_OK;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+  return (T *)((char *)ws + off);
+}
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+WMat wmat(const moe_linear &L) {
+  WMat m;
+  m.w = L.w;
+  m.scales = L.scales;
+  m.qbias = L.qbias;
+  m.bias = L.bias;
+  m.rows = L.rows;
+  m.cols = L.cols;
+  int64_t ldw;
+  if (L.fmt == MOE_W_DENSE)
+    ldw = (int64_t)L.cols * (L.dense_dtype == MOE_F32 ? 4 : 2);
+  else
+    ldw = L.cols / 2;
+  m.ldw = ldw;
+  m.w_stride = ldw * L.rows;
+  m.lds = (L.fmt == MOE_W_AFFINE4) ? L.cols / L.group_size : (L.fmt == MOE_W_MXFP4 ? L.cols / 32 : 0);
+  m.s_stride = (int64_t)m.lds * L.rows;
+  return m;
+}
+
+int wf_of(const moe_linear &L) { return L.fmt == MOE_W_DENSE ? WF_DENSE : (L.fmt == MOE_W_AFFINE4 ? WF_AFFINE4 : WF_MXFP4); }
+
+// ---------------------------------------------------------------------------
+// optional live timing of one kernel class (moe_timing_enable / moe_timing_read)
+// ---------------------------------------------------------------------------
+enum { TK_OFF = 0, TK_GATEUP = 1, TK_DOWN = 2, TK_ROUTER = 3, TK_TOPK = 4, TK_PERM = 5, TK_COMBINE = 6, TK_PLAIN = 7 };
+constexpr int kTimingPairs = 8192;
+struct Timing {
+  int kind = TK_OFF;
+  hipEvent_t ev[2 * kTimingPairs];
+  bool created = false;
+  int used = 0;
+} g_timing;
+
+struct Timed {  // brackets one launch with events when its class is being timed
+  int slot = -1;
+  hipStream_t s;
+  Timed(int kind, hipStream_t st) : s(st) {
+    if (g_timing.kind == kind && g_timing.used < kTimingPairs) {
+      slot = g_timing.used++;
+      (void)hipEventRecord(g_timing.ev[2 * slot], s);
+    }
+  }
+  ~Timed() {
+    if (slot >= 0) (void)hipEventRecord(g_timing.ev[2 * slot + 1], s);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// launch helpers
+// ---------------------------------------------------------------------------
+moe_status launch_router(const void *x, int x_dt, int T, int H, const moe_router *r, float *logits, hipStream_t s) {
+  const int E = r->num_experts;
+  Timed tm(TK_ROUTER, s);
+  if (x_dt == MOE_BF16) {
+    hipLaunchKernelGGL(router_logits_bf16, dim3((T + 15) / 16, (E + 15) / 16), dim3(512), 0, s, (const uint16_t *)x,
+                       (const uint16_t *)r->w, r->logit_bias, logits, T, H, E);
+  } else {
+    const int64_t n = (int64_t)T * E;
+    hipLaunchKernelGGL(router_logits_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float *)x,
+                       (const float *)r->w, r->logit_bias, logits, T, H, E);
+  }
+  HIPCHK(hipGetLastError());
+  return MOE_OK;
+}
+
+moe_status launch_topk(const void *x, int x_dt, int T, int H, const moe_router *r, const float *logits, int32_t *idx,
+                       float *w, const void *coef_w, const float *coef_b, float *coef, hipStream_t s) {
+  TopkArgs a;
+  a.logits = logits;
+  a.T = T;
+  a.E = r->num_experts;
+  a.K = r->top_k;
+  a.scoring = r->scoring;
+  a.norm = r->norm_topk;
+  a.rscale = r->routed_scale;
+  a.sbias = r->select_bias;
+  a.idx = idx;
+  a.w = w;
+  a.x = x;
+  a.H = H;
+  a.coef_w = coef_w;
+  a.coef_b = coef_b;
+  a.coef = coef;
+  Timed tm(TK_TOPK, s);
+  if (x_dt == MOE_BF16)
+    hipLaunchKernelGGL(topk_kernel<DT_BF16>, dim3((T + 3) / 4), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(topk_kernel<DT_F32>, dim3((T + 3) / 4), dim3(256), 0, s, a);
+  HIPCHK(hipGetLastError());
+  return MOE_OK;
+}
+
+size_t perm_ws_bytes(int64_t T, int E) { return T <= 256 ? 0 : (size_t)((T + 255) / 256) * E * 4; }
+
+moe_status launch_permute(const int32_t *idx, int T, int K, int E, int32_t *counts, int32_t *offsets, int32_t *ss,
+                          int32_t *sp, int32_t *chunk_ws, int4 *tiles, int *tile_count, int Tsh, hipStream_t s) {
+  Timed tm(TK_PERM, s);
+  if (T <= 256) {
+    hipLaunchKernelGGL(perm_small, dim3(1), dim3(256), 0, s, idx, T, K, E, counts, offsets, ss, sp, tiles, tile_count,
+                       Tsh);
+    HIPCHK(hipGetLastError());
+    return MOE_OK;
+  }
+  const int nch = (T + 255) / 256;
+  hipLaunchKernelGGL(perm_count, dim3(nch), dim3(256), 0, s, idx, T, K, E, chunk_ws);
+  HIPCHK(hipGetLastError());
+  hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, s, chunk_ws, nch, E, T * K, counts, offsets, tiles,
+                     tile_count, Tsh);
+  HIPCHK(hipGetLastError());
+  hipLaunchKernelGGL(perm_scatter, dim3(nch), dim3(256), 0, s, idx, T, K, E, chunk_ws, ss, sp);
+  HIPCHK(hipGetLastError());
+  return MOE_OK;
+}
+
+int max_tiles(int TK, int E, int Tsh) { return TK / MOE_MC + (E < TK ? E : TK) + (Tsh + MOE_MC - 1) / MOE_MC + 1; }
+
+int gemm_grid(int units_ub) {
+  const int cap = 4 * device_cus();
+  return units_ub < cap ? units_ub : cap;
+}
+
+AOp aop(const void *a, int64_t lda, const int32_t *gather, int gdiv, int row_sub) {
+  AOp o;
+  o.a = a;
+  o.lda = lda;
+  o.gather = gather;
+  o.gdiv = gdiv;
+  o.row_sub = row_sub;
+  return o;
+}
+
+SegSet segset(AOp A, const moe_linear &w0, const moe_linear *w1, float limit, bool gateup) {
+  SegSet s;
+  s.A = A;
+  s.w0 = wmat(w0);
+  s.w1 = w1 ? wmat(*w1) : s.w0;
+  s.limit = limit;
+  s.K = w0.cols;
+  s.nblk = gateup ? (w0.rows + 63) / 64 : (w0.rows + 127) / 128;
+  return s;
+}
+
+// routed experts (+ optional shared segment in the same launch)
+moe_status run_gemm(int adt, const moe_linear &fmt_of, bool gateup, int odt, const SegSet &routed,
+                    const SegSet *shared, const int4 *tiles, const int *tile_count, int E, int units_ub, void *out,
+                    int64_t ldo, const float *resid, int64_t ldr, int plain_rows, hipStream_t s) {
+  GemmParams p;
+  memset(&p, 0, sizeof p);
+  p.seg[0] = routed;
+  p.seg[1] = shared ? *shared : routed;
+  if (!shared) p.seg[1].nblk = 0;
+  p.tiles = tiles;
+  p.tile_count = tile_count;
+  p.plain_rows = plain_rows;
+  p.E = E;
+  p.out = out;
+  p.ldo = ldo;
+  p.resid = resid;
+  p.ldr = ldr;
+  const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
+  const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
+  Timed tm(gateup ? TK_GATEUP : TK_DOWN, s);
+  HIPCHK(launch_expert_gemm(adt_k, wf_of(fmt_of), fmt_of.group_size, gateup, odt_k, p, gemm_grid(units_ub), s));
+  return MOE_OK;
+}
+
+// a plain GEMM over `rows` rows (no routing): out[r] = W a[r] (+ resid)
+moe_status run_plain(int adt, const moe_linear &W, const moe_linear *W1, float limit, bool gateup, int odt,
+                     const void *a, int64_t lda, int rows, void *out, int64_t ldo, const float *resid, int64_t ldr,
+                     hipStream_t s) {
+  SegSet sg = segset(aop(a, lda, nullptr, 1, 0), W, W1, limit, gateup);
+  const int units = ((rows + MOE_MC - 1) / MOE_MC) * sg.nblk;
+  SegSet none = sg;
+  none.nblk = 0;
+  // plain mode: every tile is a "shared" tile; the routed set has no units
+  GemmParams p;
+  memset(&p, 0, sizeof p);
+  p.seg[0] = none;
+  p.seg[1] = sg;
+  p.tiles = nullptr;
+  p.tile_count = nullptr;
+  p.plain_rows = rows;
+  p.E = 0;
+  p.out = out;
+  p.ldo = ldo;
+  p.resid = resid;
+  p.ldr = ldr;
+  const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
+  const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
+  Timed tm(TK_PLAIN, s);
+  HIPCHK(launch_expert_gemm(adt_k, wf_of(W), W.group_size, gateup, odt_k, p, gemm_grid(units), s));
+  return MOE_OK;
+}
+
+moe_status combine(int odt, int ydt, const void *o, int64_t ldo, const int32_t *slot_pos, const float *topk_w, int K,
+                   int TK, int T, int D, void *y, int64_t ldy, const float *coef, const float *norm_w, float eps,
+                   int mode, hipStream_t s) {
+  CombineArgs a;
+  a.o = o;
+  a.ldo = ldo;
+  a.slot_pos = slot_pos;
+  a.topk_w = topk_w;
+  a.K = K;
+  a.TK = TK;
+  a.T = T;
+  a.D = D;
+  a.y = y;
+  a.ldy = ldy;
+  a.coef = coef;
+  a.norm_w = norm_w;
+  a.eps = eps;
+  a.mode = mode;
+  auto k = [](int dt) { return dt == MOE_F32 ? DT_F32 : (dt == MOE_BF16 ? DT_BF16 : DT_F16); };
+  Timed tm(TK_COMBINE, s);
+  HIPCHK(launch_combine(k(odt), k(ydt), a, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// entry points
+// ===========================================================================
+extern "C" {
+
+const char *moe_status_str(int32_t st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_ARG: return "MOE_ERR_ARG";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+    case MOE_ERR_QUANT: return "MOE_ERR_QUANT";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+int32_t moe_abi_version(void) { return (1 << 16) | 0; }
+
+moe_status moe_timing_enable(int32_t kind) {
+  g_err[0] = 0;
+  CHECK(kind >= TK_OFF && kind <= TK_PLAIN, MOE_ERR_ARG, "timing kind %d out of range", kind);
+  if (kind != TK_OFF && !g_timing.created) {
+    for (int i = 0; i < 2 * kTimingPairs; ++i) HIPCHK(hipEventCreate(&g_timing.ev[i]));
+    g_timing.created = true;
+  }
+  g_timing.kind = kind;
+  return MOE_OK;
+}
+
+moe_status moe_timing_read(int32_t *launches, double *total_ms) {
+  g_err[0] = 0;
+  CHECK(launches != nullptr && total_ms != nullptr, MOE_ERR_ARG, "output pointers must be non-NULL");
+  double tot = 0.0;
+  for (int i = 0; i < g_timing.used; ++i) {
+    HIPCHK(hipEventSynchronize(g_timing.ev[2 * i + 1]));
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]));
+    tot += ms;
+  }
+  *launches = g_timing.used;
+  *total_ms = tot;
+  g_timing.used = 0;
+  return MOE_OK;
+}
+
+moe_status moe_route(const void *x, int32_t x_dtype, int64_t T, int32_t H, const moe_router *r, int32_t *topk_idx,
+                     float *topk_w, float *logits, void *ws, size_t *ws_bytes, void *stream) {
+  g_err[0] = 0;
+  CHECK(x_dtype == MOE_F32 || x_dtype == MOE_BF16, MOE_ERR_ARG, "x dtype %d not F32/BF16", x_dtype);
+  CHECK(H > 0, MOE_ERR_SHAPE, "hidden %d must be positive", H);
+  TRY(check_router(r, H, x_dtype));
+  TRY(check_tokens(T, r->top_k));
+  Plan pl;
+  const size_t o_logits = logits ? 0 : pl.take((size_t)T * r->num_experts * 4);
+  bool query;
+  TRY(check_ws(ws, ws_bytes, pl.off, &query));
+  if (query || T == 0) return MOE_OK;
+  CHECK(x && topk_idx && topk_w, MOE_ERR_ARG, "x, topk_idx and topk_w must be non-NULL");
+  CHECK(aligned(x, 16), MOE_ERR_ARG, "x not 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  float *lg = logits ? logits : at<float>(ws, o_logits);
+  TRY(launch_router(x, x_dtype, (int)T, H, r, lg, s));
+  TRY(launch_topk(x, x_dtype, (int)T, H, r, lg, topk_idx, topk_w, nullptr, nullptr, nullptr, s));
+  return MOE_OK;
+}
+
+moe_status moe_permute(const int32_t *topk_idx, int64_t T, int32_t K, int32_t E, int32_t *counts, int32_t *offsets,
+                       int32_t *sorted_slot, int32_t *slot_pos, void *ws, size_t *ws_bytes, void *stream) {
+  g_err[0] = 0;
+  CHECK(E > 0 && E <= MOE_MAX_EXPERTS, MOE_ERR_SHAPE, "num_experts %d outside 1..%d", E, MOE_MAX_EXPERTS);
+  CHECK(K >= 1 && K <= E && K <= MOE_MAX_TOPK, MOE_ERR_SHAPE, "top_k %d outside 1..min(E, %d)", K, MOE_MAX_TOPK);
+  TRY(check_tokens(T, K));
+  Plan pl;
+  const size_t o_chunk = pl.take(perm_ws_bytes(T, E));
+  bool query;
+  TRY(check_ws(ws, ws_bytes, pl.off, &query));
+  if (query || T == 0) return MOE_OK;
+  CHECK(topk_idx && counts && offsets && sorted_slot && slot_pos, MOE_ERR_ARG,
+        "topk_idx, counts, offsets, sorted_slot and slot_pos must be non-NULL");
+  TRY(launch_permute(topk_idx, (int)T, K, E, counts, offsets, sorted_slot, slot_pos, at<int32_t>(ws, o_chunk), nullptr,
+                     nullptr, 0, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status moe_experts_forward(const void *z, int32_t z_dtype, int64_t T, int32_t D, const moe_mlp *ex, int32_t E,
+                               int32_t K, const int32_t *topk_idx, const float *topk_w, const int32_t *offsets,
+                               const int32_t *sorted_slot, const int32_t *slot_pos, int32_t inter_dtype,
+                               float *y_routed, void *ws, size_t *ws_bytes, void *stream) {
+  g_err[0] = 0;
+  CHECK(z_dtype == MOE_F32 || z_dtype == MOE_BF16 || z_dtype == MOE_F16, MOE_ERR_ARG, "z dtype %d out of range",
+        z_dtype);
+  CHECK(D > 0, MOE_ERR_SHAPE, "expert_dim %d must be positive", D);
+  CHECK(E > 0 && E <= MOE_MAX_EXPERTS, MOE_ERR_SHAPE, "num_experts %d outside 1..%d", E, MOE_MAX_EXPERTS);
+  CHECK(K >= 1 && K <= E && K <= MOE_MAX_TOPK, MOE_ERR_SHAPE, "top_k %d outside 1..min(E, %d)", K, MOE_MAX_TOPK);
+  TRY(check_tokens(T, K));
+  CHECK(ex != nullptr, MOE_ERR_ARG, "expert descriptor is NULL");
+  if (z_dtype == MOE_F32) {
+    CHECK(inter_dtype == MOE_F32, MOE_ERR_UNSUPPORTED, "f32 activations need inter_dtype F32");
+  } else {
+    CHECK(inter_dtype == MOE_BF16 || inter_dtype == MOE_F16, MOE_ERR_ARG, "inter_dtype %d not BF16/F16", inter_dtype);
+  }
+  const int I = ex->gate.rows;
+  CHECK(I > 0, MOE_ERR_SHAPE, "expert intermediate %d must be positive", I);
+  TRY(check_mlp(ex, "experts", E, I, D, z_dtype, inter_dtype));
+  CHECK(z_dtype != MOE_F32 || D % 8 == 0, MOE_ERR_SHAPE, "expert_dim %d not a multiple of 8", D);
+  const int TK = (int)(T * K);
+  const int isz = dt_size(inter_dtype);
+  Plan pl;
+  const bool mf = z_dtype != MOE_F32;
+  const int ntile = max_tiles(TK, E, 0);
+  const size_t o_tiles = mf ? pl.take((size_t)ntile * 16) : 0;
+  const size_t o_tcount = mf ? pl.take(16) : 0;
+  const size_t o_h = pl.take((size_t)TK * I * isz);
+  const size_t o_o = pl.take((size_t)TK * D * isz);
+  bool query;
+  TRY(check_ws(ws, ws_bytes, pl.off, &query));
+  if (query || T == 0) return MOE_OK;
+  CHECK(z && topk_idx && topk_w && offsets && sorted_slot && slot_pos && y_routed, MOE_ERR_ARG,
+        "a required pointer is NULL");
+  CHECK(aligned(z, 16) && aligned(y_routed, 16), MOE_ERR_ARG, "z / y_routed not 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  void *h = at<char>(ws, o_h);
+  void *o = at<char>(ws, o_o);
+  if (mf) {
+    int4 *tiles = at<int4>(ws, o_tiles);
+    int *tc = at<int>(ws, o_tcount);
+    hipLaunchKernelGGL(build_tiles, dim3(1), dim3(256), 0, s, offsets, E, TK, tiles, tc, 0);
+    HIPCHK(hipGetLastError());
+    const int ub_mc = TK / MOE_MC + (E < TK ? E : TK);
+    SegSet gu = segset(aop(z, D, sorted_slot, K, 0), ex->gate, &ex->up, ex->swiglu_limit, true);
+    TRY(run_gemm(z_dtype, ex->gate, true, inter_dtype, gu, nullptr, tiles, tc, E, ub_mc * gu.nblk, h, I, nullptr, 0,
+                 0, s));
+    SegSet dn = segset(aop(h, I, nullptr, 1, 0), ex->down, nullptr, 0.f, false);
+    TRY(run_gemm(inter_dtype, ex->down, false, inter_dtype, dn, nullptr, tiles, tc, E, ub_mc * dn.nblk, o, D, nullptr,
+                 0, 0, s));
+  } else {
+    F32GemmParams p;
+    memset(&p, 0, sizeof p);
+    p.a_routed = (const float *)z;
+    p.lda_r = D;
+    p.sorted_slot = sorted_slot;
+    p.topk_idx = topk_idx;
+    p.K = K;
+    p.TK = TK;
+    p.Tsh = 0;
+    p.r0 = wmat(ex->gate);
+    p.r1 = wmat(ex->up);
+    p.limit = ex->swiglu_limit;
+    p.out = (float *)h;
+    p.ldo = I;
+    p.ncols_r = I;
+    p.gateup = 1;
+    {
+      Timed tm(TK_GATEUP, s);
+      HIPCHK(launch_f32_gemm(p, TK, s));
+    }
+    p.a_routed = (const float *)h;
+    p.lda_r = I;
+    p.r0 = wmat(ex->down);
+    p.out = (float *)o;
+    p.ldo = D;
+    p.ncols_r = D;
+    p.gateup = 0;
+    {
+      Timed tm(TK_DOWN, s);
+      HIPCHK(launch_f32_gemm(p, TK, s));
+    }
+  }
+  TRY(combine(inter_dtype, MOE_F32, o, D, slot_pos, topk_w, K, TK, (int)T, D, y_routed, D, nullptr, nullptr, 0.f, 0,
+              s));
+  return MOE_OK;
+}
+
+moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const moe_block *b, void *y, int32_t y_dtype,
+                             int32_t *topk_idx, float *topk_w, void *ws, size_t *ws_bytes, void *stream) {
+  g_err[0] = 0;
+  CHECK(b != nullptr, MOE_ERR_ARG, "block descriptor is NULL");
+  CHECK(x_dtype == MOE_F32 || x_dtype == MOE_BF16, MOE_ERR_ARG, "x dtype %d not F32/BF16", x_dtype);
+  CHECK(y_dtype == MOE_F32 || y_dtype == MOE_BF16, MOE_ERR_ARG, "y dtype %d not F32/BF16", y_dtype);
+  CHECK(x_dtype == MOE_BF16 || y_dtype == MOE_F32, MOE_ERR_UNSUPPORTED, "f32 input needs f32 output");
+  const int H = b->hidden;
+  CHECK(H > 0 && b->expert_dim > 0, MOE_ERR_SHAPE, "hidden %d / expert_dim %d must be positive", H, b->expert_dim);
+  TRY(check_router(&b->router, H, x_dtype));
+  const int E = b->router.num_experts, K = b->router.top_k;
+  TRY(check_tokens(T, K));
+  const bool latent = b->latent_down.w != nullptr;
+  const int D = b->expert_dim;
+  CHECK(latent || D == H, MOE_ERR_SHAPE, "expert_dim %d != hidden %d without a latent projection", D, H);
+  const int inter = b->inter_dtype;
+  if (x_dtype == MOE_F32) {
+    CHECK(inter == MOE_F32, MOE_ERR_UNSUPPORTED, "f32 input needs inter_dtype F32");
+    CHECK(!latent, MOE_ERR_UNSUPPORTED, "the latent projection needs BF16 input");
+  } else {
+    CHECK(inter == MOE_BF16 || inter == MOE_F16, MOE_ERR_ARG, "inter_dtype %d not BF16/F16", inter);
+  }
+  const int zdt = latent ? inter : x_dtype;
+  const int I = b->experts.gate.rows;
+  CHECK(I > 0, MOE_ERR_SHAPE, "expert intermediate %d must be positive", I);
+  TRY(check_mlp(&b->experts, "experts", E, I, D, zdt, inter));
+  CHECK(b->shared_mode >= MOE_SHARED_NONE && b->shared_mode <= MOE_SHARED_BLEND, MOE_ERR_ARG,
+        "shared_mode %d out of range", b->shared_mode);
+  const bool has_shared = b->shared_mode != MOE_SHARED_NONE;
+  int Is = 0;
+  if (has_shared) {
+    Is = b->shared.gate.rows;
+    CHECK(Is > 0, MOE_ERR_SHAPE, "shared intermediate %d must be positive", Is);
+    TRY(check_mlp(&b->shared, "shared", 1, Is, H, x_dtype, inter));
+  }
+  if (b->shared_mode == MOE_SHARED_BLEND) {
+    CHECK(b->coef_w != nullptr && b->coef_b != nullptr, MOE_ERR_ARG,
+          "blend needs the coefficient head (coef_w [2, H] and coef_b [2])");
+    CHECK(!latent, MOE_ERR_UNSUPPORTED, "blend with the latent projection is not supported");
+    CHECK(aligned(b->coef_w, 16), MOE_ERR_ARG, "coef_w not 16-byte aligned");
+  }
+  if (latent) {
+    TRY(check_linear(&b->latent_down, "latent_down", 1, D, H, x_dtype));
+    TRY(check_linear(&b->latent_up, "latent_up", 1, H, D, inter));
+    CHECK(b->latent_down.fmt == MOE_W_DENSE && b->latent_up.fmt == MOE_W_DENSE, MOE_ERR_UNSUPPORTED,
+          "latent projections must be DENSE BF16");
+    if (b->latent_norm_w) {
+      CHECK(std::isfinite(b->norm_eps) && b->norm_eps > 0.f, MOE_ERR_ARG, "norm_eps must be finite and > 0");
+      CHECK(D <= 8192, MOE_ERR_SHAPE, "latent width %d above 8192 with the norm", D);
+    }
+  }
+  CHECK(H % 8 == 0 && D % 8 == 0, MOE_ERR_SHAPE, "hidden/expert_dim must be multiples of 8");
+
+  // ---- workspace
+  const int TK = (int)(T * K);
+  const int isz = dt_size(inter);
+  const bool mf = x_dtype != MOE_F32;
+  // shared expert inside the routed launches when it shares the routed format and input
+  const bool fuse_shared = has_shared && !latent && mf && b->shared.gate.fmt == b->experts.gate.fmt &&
+                           b->shared.gate.group_size == b->experts.gate.group_size &&
+                           b->shared.down.fmt == b->experts.down.fmt &&
+                           b->shared.down.group_size == b->experts.down.group_size;
+  const int Tsh = (has_shared && !latent) ? (int)T : 0;  // shared rows appended to h / o
+  const int ldh = I > Is ? I : Is;
+  Plan pl;
+  const size_t o_logits = pl.take((size_t)T * E * 4);
+  const size_t o_coef = pl.take((size_t)T * 2 * 4);
+  const size_t o_idx = topk_idx ? 0 : pl.take((size_t)TK * 4);
+  const size_t o_w = topk_w ? 0 : pl.take((size_t)TK * 4);
+  const size_t o_counts = pl.take((size_t)E * 4);
+  const size_t o_offsets = pl.take((size_t)(E + 1) * 4);
+  const size_t o_ss = pl.take((size_t)TK * 4);
+  const size_t o_sp = pl.take((size_t)TK * 4);
+  const size_t o_chunk = pl.take(perm_ws_bytes(T, E));
+  const int ntile = max_tiles(TK, E, fuse_shared ? Tsh : 0);
+  const size_t o_tiles = pl.take((size_t)ntile * 16);
+  const size_t o_tc = pl.take(16);
+  const size_t o_z = latent ? pl.take((size_t)T * D * isz) : 0;
+  const size_t o_h = pl.take((size_t)(TK + Tsh) * ldh * isz);
+  const size_t o_o = pl.take((size_t)(TK + Tsh) * D * isz);
+  const size_t o_yn = latent ? pl.take((size_t)T * D * isz) : 0;
+  const size_t o_hs = (latent && has_shared) ? pl.take((size_t)T * Is * isz) : 0;
+  const size_t o_s = (latent && has_shared) ? pl.take((size_t)T * H * 4) : 0;
+  bool query;
+  TRY(check_ws(ws, ws_bytes, pl.off, &query));
+  if (query || T == 0) return MOE_OK;
+  CHECK(x && y, MOE_ERR_ARG, "x and y must be non-NULL");
+  CHECK(aligned(x, 16) && aligned(y, 16), MOE_ERR_ARG, "x / y not 16-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  float *logits = at<float>(ws, o_logits);
+  float *coef = at<float>(ws, o_coef);
+  int32_t *idx = topk_idx ? topk_idx : at<int32_t>(ws, o_idx);
+  float *wts = topk_w ? topk_w : at<float>(ws, o_w);
+  int32_t *counts = at<int32_t>(ws, o_counts);
+  int32_t *offsets = at<int32_t>(ws, o_offsets);
+  int32_t *ss = at<int32_t>(ws, o_ss);
+  int32_t *sp = at<int32_t>(ws, o_sp);
+  int4 *tiles = at<int4>(ws, o_tiles);
+  int *tc = at<int>(ws, o_tc);
+  void *h = at<char>(ws, o_h);
+  void *o = at<char>(ws, o_o);
+  const int Ti = (int)T;
+
+  // 1. router + selection (+ blend coefficients)
+  TRY(launch_router(x, x_dtype, Ti, H, &b->router, logits, s));
+  const bool blend = b->shared_mode == MOE_SHARED_BLEND;
+  TRY(launch_topk(x, x_dtype, Ti, H, &b->router, logits, idx, wts, blend ? b->coef_w : nullptr,
+                  blend ? b->coef_b : nullptr, coef, s));
+  // 2. permutation + tile list
+  TRY(launch_permute(idx, Ti, K, E, counts, offsets, ss, sp, at<int32_t>(ws, o_chunk), mf ? tiles : nullptr,
+                     mf ? tc : nullptr, fuse_shared ? Tsh : 0, s));
+
+  if (!mf) {
+    // ---- f32 path
+    F32GemmParams p;
+    memset(&p, 0, sizeof p);
+    p.a_routed = (const float *)x;
+    p.lda_r = H;
+    p.a_shared = (const float *)x;
+    p.lda_s = H;
+    p.sorted_slot = ss;
+    p.topk_idx = idx;
+    p.K = K;
+    p.TK = TK;
+    p.Tsh = Tsh;
+    p.r0 = wmat(b->experts.gate);
+    p.r1 = wmat(b->experts.up);
+    if (has_shared) {
+      p.s0 = wmat(b->shared.gate);
+      p.s1 = wmat(b->shared.up);
+    }
+    p.limit = b->experts.swiglu_limit;
+    p.out = (float *)h;
+    p.ldo = ldh;
+    p.ncols_r = I;
+    p.ncols_s = Is;
+    p.gateup = 1;
+    {
+      Timed tm(TK_GATEUP, s);
+      HIPCHK(launch_f32_gemm(p, TK + Tsh, s));
+    }
+    p.a_routed = (const float *)h;
+    p.lda_r = ldh;
+    p.a_shared = (const float *)h;
+    p.lda_s = ldh;
+    p.r0 = wmat(b->experts.down);
+    if (has_shared) p.s0 = wmat(b->shared.down);
+    p.out = (float *)o;
+    p.ldo = D;
+    p.ncols_r = D;
+    p.ncols_s = has_shared ? D : 0;
+    p.gateup = 0;
+    {
+      Timed tm(TK_DOWN, s);
+      HIPCHK(launch_f32_gemm(p, TK + Tsh, s));
+    }
+    const int mode = !has_shared ? 0 : (blend ? 3 : 2);
+    TRY(combine(MOE_F32, y_dtype, o, D, sp, wts, K, TK, Ti, D, y, H, coef, nullptr, 0.f, mode, s));
+    return MOE_OK;
+  }
+
+  const int ub_mc = TK / MOE_MC + (E < TK ? E : TK);
+  const int sh_mc = (Ti + MOE_MC - 1) / MOE_MC;
+  if (!latent) {
+    // 3. gate/up (+ SwiGLU) for every slot, shared rows appended
+    SegSet gu = segset(aop(x, H, ss, K, 0), b->experts.gate, &b->experts.up, b->experts.swiglu_limit, true);
+    SegSet gus;
+    if (has_shared) gus = segset(aop(x, H, nullptr, 1, TK), b->shared.gate, &b->shared.up, b->shared.swiglu_limit, true);
+    TRY(run_gemm(x_dtype, b->experts.gate, true, inter, gu, fuse_shared ? &gus : nullptr, tiles, tc, E,
+                 ub_mc * gu.nblk + (fuse_shared ? sh_mc * gus.nblk : 0), h, ldh, nullptr, 0, 0, s));
+    if (has_shared && !fuse_shared)
+      TRY(run_plain(x_dtype, b->shared.gate, &b->shared.up, b->shared.swiglu_limit, true, inter, x, H, Ti,
+                    (char *)h + (size_t)TK * ldh * isz, ldh, nullptr, 0, s));
+    // 4. down
+    SegSet dn = segset(aop(h, ldh, nullptr, 1, 0), b->experts.down, nullptr, 0.f, false);
+    SegSet dns;
+    if (has_shared) dns = segset(aop(h, ldh, nullptr, 1, 0), b->shared.down, nullptr, 0.f, false);
+    TRY(run_gemm(inter, b->experts.down, false, inter, dn, fuse_shared ? &dns : nullptr, tiles, tc, E,
+                 ub_mc * dn.nblk + (fuse_shared ? sh_mc * dns.nblk : 0), o, D, nullptr, 0, 0, s));
+    if (has_shared && !fuse_shared)
+      TRY(run_plain(inter, b->shared.down, nullptr, 0.f, false, inter, (char *)h + (size_t)TK * ldh * isz, ldh, Ti,
+                    (char *)o + (size_t)TK * D * isz, D, nullptr, 0, s));
+    // 5. weighted combine + shared add/blend
+    const int mode = !has_shared ? 0 : (blend ? 3 : 2);
+    TRY(combine(inter, y_dtype, o, D, sp, wts, K, TK, Ti, H, y, H, coef, nullptr, 0.f, mode, s));
+    return MOE_OK;
+  }
+
+  // ---- latent flow: z = down_proj(x); experts in latent space; rms_norm; up_proj; + shared(x)
+  void *z = at<char>(ws, o_z);
+  void *yn = at<char>(ws, o_yn);
+  TRY(run_plain(x_dtype, b->latent_down, nullptr, 0.f, false, inter, x, H, Ti, z, D, nullptr, 0, s));
+  SegSet gu = segset(aop(z, D, ss, K, 0), b->experts.gate, &b->experts.up, b->experts.swiglu_limit, true);
+  TRY(run_gemm(inter, b->experts.gate, true, inter, gu, nullptr, tiles, tc, E, ub_mc * gu.nblk, h, ldh, nullptr, 0, 0,
+               s));
+  SegSet dn = segset(aop(h, ldh, nullptr, 1, 0), b->experts.down, nullptr, 0.f, false);
+  TRY(run_gemm(inter, b->experts.down, false, inter, dn, nullptr, tiles, tc, E, ub_mc * dn.nblk, o, D, nullptr, 0, 0,
+               s));
+  TRY(combine(inter, inter, o, D, sp, wts, K, TK, Ti, D, yn, D, nullptr, b->latent_norm_w, b->norm_eps,
+              b->latent_norm_w ? 1 : 0, s));
+  const float *resid = nullptr;
+  if (has_shared) {
+    void *hs = at<char>(ws, o_hs);
+    float *sv = at<float>(ws, o_s);
+    TRY(run_plain(x_dtype, b->shared.gate, &b->shared.up, b->shared.swiglu_limit, true, inter, x, H, Ti, hs, Is,
+                  nullptr, 0, s));
+    TRY(run_plain(inter, b->shared.down, nullptr, 0.f, false, MOE_F32, hs, Is, Ti, sv, H, nullptr, 0, s));
+    resid = sv;
+  }
+  TRY(run_plain(inter, b->latent_up, nullptr, 0.f, false, y_dtype, yn, D, Ti, y, H, resid, H, s));
+  return MOE_OK;
+}
+
+}  // extern "C"

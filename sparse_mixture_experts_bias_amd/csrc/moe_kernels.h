@@ -1,0 +1,112 @@
+// moe_kernels.h - kernel argument structs and kernel declarations (device + host side).
+#pragma once
+
+#include "moe_device.h"
+
+#define MOE_MAX_EXPERTS 512  // router top-k keeps 8 experts per lane of a wave64
+#define MOE_MAX_TOPK 32      // chosen experts live one per lane (K <= 32)
+#define MOE_MC 64            // rows (slots or tokens) per m-chunk of the grouped GEMM
+#define MOE_KC 256           // reduction elements staged per LDS chunk
+#define MOE_GEMM_THREADS 256 // 4 waves
+
+struct TopkArgs {
+  const float *logits;
+  int T, E, K, scoring, norm;
+  float rscale;
+  const float *sbias;
+  int32_t *idx;
+  float *w;
+  const void *x;  // blend head input [T, H] (XDT)
+  int H;
+  const void *coef_w;  // [2, H] or nullptr
+  const float *coef_b;
+  float *coef;         // [T, 2]
+};
+
+// one stacked weight operand [n][rows][cols] (see moe_linear)
+struct WMat {
+  const void *w;
+  const void *scales;
+  const void *qbias;
+  const void *bias;     // output bias [n][rows], bf16 (or nullptr)
+  int64_t w_stride;     // bytes between matrices
+  int64_t s_stride;     // elements between matrices of scales/qbias
+  int64_t ldw;          // bytes per row of w
+  int lds;              // elements per row of scales/qbias
+  int rows, cols;
+};
+
+// activation rows feeding a segment set: sorted row r reads A row
+// gather ? gather[r] / gdiv : r - row_sub
+struct AOp {
+  const void *a;
+  int64_t lda;          // elements
+  const int32_t *gather;
+  int gdiv;
+  int row_sub;
+};
+
+struct SegSet {
+  AOp A;
+  WMat w0, w1;          // GATEUP: gate, up;  LINEAR: w0 only
+  float limit;          // GATEUP clamp (<= 0: none)
+  int K;                // reduction length
+  int nblk;             // column blocks of the output
+};
+
+struct GemmParams {
+  SegSet seg[2];        // [0] routed experts (tile.x < E), [1] shared / plain (tile.x == E)
+  const int4 *tiles;    // m-chunk list, or nullptr for a plain GEMM over plain_rows rows
+  const int *tile_count;// [2]: routed chunks, shared chunks
+  int plain_rows;
+  int E;
+  void *out;
+  int64_t ldo;
+  const float *resid;   // LINEAR: optional f32 [rows][ldr] added before the store
+  int64_t ldr;
+};
+
+struct F32GemmParams {   // f32 activations with DENSE F32 weights (one thread per output)
+  const float *a_routed; int64_t lda_r;   // rows gathered through sorted_slot / K
+  const float *a_shared; int64_t lda_s;   // rows r - TK
+  const int32_t *sorted_slot;
+  const int32_t *topk_idx;
+  int K, TK, Tsh;
+  WMat r0, r1, s0, s1;
+  float limit;
+  float *out; int64_t ldo;
+  int ncols_r, ncols_s;
+  int gateup;
+};
+
+struct CombineArgs {
+  const void *o; int64_t ldo;        // per-slot expert outputs (sorted rows), ODT
+  const int32_t *slot_pos;
+  const float *topk_w;
+  int K, TK, T, D;
+  void *y; int64_t ldy;              // YDT
+  const float *coef;                 // blend coefficients [T][2]
+  const float *norm_w; float eps;    // rms norm
+  int mode;                          // 0 routed sum, 1 rms-norm, 2 + shared, 3 blend with shared
+};
+
+// ---- kernels ----
+__global__ void router_logits_bf16(const uint16_t *x, const uint16_t *W, const float *lbias, float *logits,
+                                   int T, int H, int E);
+__global__ void router_logits_f32(const float *x, const float *W, const float *lbias, float *logits, int T,
+                                  int H, int E);
+template <int XDT> __global__ void topk_kernel(TopkArgs a);
+__global__ void perm_count(const int32_t *idx, int T, int K, int E, int32_t *chunk_counts);
+__global__ void perm_scan(int32_t *chunk_counts, int nchunks, int E, int TK, int32_t *counts, int32_t *offsets,
+                          int4 *tiles, int *tile_count, int Tsh);
+__global__ void perm_scatter(const int32_t *idx, int T, int K, int E, const int32_t *chunk_base,
+                             int32_t *sorted_slot, int32_t *slot_pos);
+__global__ void perm_small(const int32_t *idx, int T, int K, int E, int32_t *counts, int32_t *offsets,
+                           int32_t *sorted_slot, int32_t *slot_pos, int4 *tiles, int *tile_count, int Tsh);
+__global__ void build_tiles(const int32_t *offsets, int E, int TK, int4 *tiles, int *tile_count, int Tsh);
+
+// host-side launchers (moe_gemm.hip, moe_combine.hip)
+hipError_t launch_expert_gemm(int adt, int wfmt, int group, bool gateup, int odt, const GemmParams &p, int grid,
+                              hipStream_t s);
+hipError_t launch_f32_gemm(const F32GemmParams &p, int rows, hipStream_t s);
+hipError_t launch_combine(int odt, int ydt, const CombineArgs &a, hipStream_t s);

@@ -346,3 +346,18 @@ def raw(t: Optional[torch.Tensor]):
     if t.dtype == torch.int32:
         return t.numpy().view("uint32")
     return t.numpy()
+
+
+def clone_weights(b: Block) -> Block:
+    """A copy of the layer whose weight tensors live in fresh memory (x is shared)."""
+    cl = lambda t: None if t is None else t.clone()
+
+    def lin(l: Optional[Linear]):
+        return None if l is None else replace(l, w=cl(l.w), scales=cl(l.scales), qbias=cl(l.qbias), bias=cl(l.bias))
+
+    def mlp(m: Optional[MLP]):
+        return None if m is None else replace(m, gate=lin(m.gate), up=lin(m.up), down=lin(m.down))
+
+    return replace(b, router_w=cl(b.router_w), experts=mlp(b.experts), logit_bias=cl(b.logit_bias),
+                   select_bias=cl(b.select_bias), shared=mlp(b.shared), coef_w=cl(b.coef_w), coef_b=cl(b.coef_b),
+                   latent_down=lin(b.latent_down), latent_up=lin(b.latent_up), latent_norm_w=cl(b.latent_norm_w))

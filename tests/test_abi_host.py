@@ -1,0 +1,207 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point include/moe.h declares, and
+reject every hostile argument with the right status before anything would be
+launched (mlxcel issue #974: bounds checks assert on the returned status and
+never run a forward pass; each hostile case has a positive control).  All
+calls below are workspace queries or fail validation, so no HIP call is made.
+"""
+import copy
+import ctypes
+import math
+import os
+import re
+
+import pytest
+import torch
+
+import synth
+import sparse_mixture_experts_bias_amd as moe
+from synth.descs import block_desc
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe.h")
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    return re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", txt)
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert set(names) == {"moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward", "moe_status_str",
+                          "moe_last_error", "moe_abi_version", "moe_timing_enable", "moe_timing_read"}
+    L = moe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(moe.EXPORTS) == set(names)
+
+
+def test_status_strings_and_version():
+    L = moe.lib()
+    for code, name in enumerate(["MOE_OK", "MOE_ERR_ARG", "MOE_ERR_SHAPE", "MOE_ERR_QUANT", "MOE_ERR_WORKSPACE",
+                                 "MOE_ERR_DEVICE", "MOE_ERR_UNSUPPORTED"]):
+        assert L.moe_status_str(code).decode() == name
+    assert L.moe_status_str(99).decode() == "MOE_ERR_UNKNOWN"
+    assert moe.abi_version() >> 16 == 1
+    assert L.moe_timing_enable(42) == moe.MOE_ERR_ARG
+    assert L.moe_timing_enable(0) == moe.MOE_OK
+    assert moe.moe_timing_read() == (0, 0.0)
+
+
+def test_struct_layouts_match_c():
+    """ctypes mirrors of the C structs have the C sizes (x86-64 SysV alignment)."""
+    assert ctypes.sizeof(moe.MoeLinear) == 7 * 4 + 4 + 4 * 8
+    assert ctypes.sizeof(moe.MoeMLP) == 3 * ctypes.sizeof(moe.MoeLinear) + 8
+    assert ctypes.sizeof(moe.MoeRouter) == 5 * 4 + 4 + 3 * 8
+
+
+# ----------------------------------------------------------------------------
+# hostile arguments (block descriptor), each with its positive control
+# ----------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def layers():
+    out = {}
+    for cfg in ("c1", "c2", "c5"):
+        b = synth.make_block(synth.SMALL_SPECS[cfg], "cpu")
+        out[cfg] = b
+    return out
+
+
+def query_block(b, desc, T=None, x_dtype=None, y_dtype=None):
+    n = ctypes.c_size_t(0)
+    T = b.T if T is None else T
+    xd = moe.dtype_code(b.x.dtype) if x_dtype is None else x_dtype
+    yd = moe.MOE_F32 if y_dtype is None else y_dtype
+    st = moe.lib().moe_block_forward(None, xd, T, ctypes.byref(desc.c), None, yd, None, None, None, ctypes.byref(n),
+                                     None)
+    return st, n.value
+
+
+def _set(path):
+    def f(c, v):
+        obj = c
+        parts = path.split(".")
+        for p in parts[:-1]:
+            obj = getattr(obj, p)
+        setattr(obj, parts[-1], v)
+    return f
+
+
+# (layer, field path, hostile value, expected status)
+HOSTILE = [
+    ("c2", "router.top_k", 0, moe.MOE_ERR_SHAPE),
+    ("c2", "router.top_k", 33, moe.MOE_ERR_SHAPE),                 # > num_experts (32)
+    ("c2", "router.num_experts", 0, moe.MOE_ERR_SHAPE),
+    ("c2", "router.num_experts", 513, moe.MOE_ERR_SHAPE),
+    ("c2", "router.scoring", 7, moe.MOE_ERR_ARG),
+    ("c2", "router.norm_topk", 2, moe.MOE_ERR_ARG),
+    ("c2", "router.routed_scale", float("nan"), moe.MOE_ERR_ARG),
+    ("c2", "router.w", None, moe.MOE_ERR_ARG),
+    ("c2", "hidden", 0, moe.MOE_ERR_SHAPE),
+    ("c2", "experts.gate.bits", 0, moe.MOE_ERR_QUANT),
+    ("c2", "experts.gate.bits", 8, moe.MOE_ERR_QUANT),
+    ("c2", "experts.gate.group_size", 0, moe.MOE_ERR_QUANT),
+    ("c2", "experts.down.group_size", 48, moe.MOE_ERR_QUANT),
+    ("c2", "experts.up.n", 31, moe.MOE_ERR_SHAPE),                  # fewer planes than num_experts
+    ("c2", "experts.up.rows", 0, moe.MOE_ERR_SHAPE),                # zero checked before divisibility
+    ("c2", "experts.down.cols", 100, moe.MOE_ERR_SHAPE),
+    ("c2", "experts.gate.fmt", 9, moe.MOE_ERR_ARG),
+    ("c2", "experts.gate.scales", None, moe.MOE_ERR_ARG),
+    ("c2", "experts.swiglu_limit", float("inf"), moe.MOE_ERR_ARG),
+    ("c2", "shared_mode", 5, moe.MOE_ERR_ARG),
+    ("c2", "coef_w", None, moe.MOE_ERR_ARG),                        # blend without its coefficient head
+    ("c2", "inter_dtype", 7, moe.MOE_ERR_ARG),
+    ("c2", "shared.down.rows", 64, moe.MOE_ERR_SHAPE),
+    ("c5", "experts.gate.group_size", 64, moe.MOE_ERR_QUANT),     # MXFP4 blocks are 32
+    ("c5", "experts.gate.bits", 0, moe.MOE_ERR_QUANT),
+    ("c5", "norm_eps", 0.0, moe.MOE_ERR_ARG),
+    ("c5", "norm_eps", float("nan"), moe.MOE_ERR_ARG),
+    ("c5", "latent_up.cols", 64, moe.MOE_ERR_SHAPE),
+    ("c5", "latent_down.fmt", moe.MOE_W_AFFINE4, moe.MOE_ERR_QUANT),
+    ("c5", "shared_mode", moe.MOE_SHARED_BLEND, moe.MOE_ERR_ARG),  # blend needs coef_w (none on c5)
+    ("c1", "inter_dtype", moe.MOE_BF16, moe.MOE_ERR_UNSUPPORTED),  # f32 layer keeps f32 intermediates
+    ("c1", "experts.gate.dense_dtype", 5, moe.MOE_ERR_ARG),
+]
+
+
+@pytest.mark.parametrize("case", range(len(HOSTILE)), ids=[f"{h[0]}:{h[1]}={h[2]}" for h in HOSTILE])
+def test_hostile_block_argument(case, layers):
+    cfg, path, val, want = HOSTILE[case]
+    b = layers[cfg]
+    desc = block_desc(b)
+    st, need = query_block(b, desc)
+    assert st == moe.MOE_OK and need > 0, "positive control must validate"
+    bad = block_desc(b)
+    _set(path)(bad.c, val)
+    st, _ = query_block(b, bad)
+    assert st == want, (path, val, moe.lib().moe_status_str(st), moe.lib().moe_last_error())
+    assert moe.lib().moe_last_error().decode() != ""
+
+
+def test_token_count_guards(layers):
+    b = layers["c2"]
+    d = block_desc(b)
+    assert query_block(b, d, T=-1)[0] == moe.MOE_ERR_SHAPE
+    assert query_block(b, d, T=2 ** 40)[0] == moe.MOE_ERR_SHAPE     # T*K would overflow int32 slot ids
+    st, n0 = query_block(b, d, T=0)
+    assert st == moe.MOE_OK
+    assert query_block(b, d, x_dtype=moe.MOE_F16)[0] == moe.MOE_ERR_ARG
+    assert query_block(b, d, y_dtype=moe.MOE_F16)[0] == moe.MOE_ERR_ARG
+    assert query_block(layers["c1"], block_desc(layers["c1"]), y_dtype=moe.MOE_BF16)[0] == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_grows_with_tokens(layers):
+    b = layers["c2"]
+    d = block_desc(b)
+    sizes = [query_block(b, d, T=t)[1] for t in (1, 64, 1024)]
+    assert sizes[0] < sizes[1] < sizes[2]
+
+
+def test_workspace_too_small_or_misaligned(layers):
+    b = layers["c2"]
+    d = block_desc(b)
+    st, need = query_block(b, d)
+    buf = (ctypes.c_uint8 * (need + 512))()
+    base = ctypes.addressof(buf)
+    aligned = base + ((-base) % 256)
+    L = moe.lib()
+    n = ctypes.c_size_t(need - 1)
+    st = L.moe_block_forward(None, moe.MOE_BF16, b.T, ctypes.byref(d.c), None, moe.MOE_F32, None, None, aligned,
+                             ctypes.byref(n), None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    n = ctypes.c_size_t(need)
+    st = L.moe_block_forward(None, moe.MOE_BF16, b.T, ctypes.byref(d.c), None, moe.MOE_F32, None, None, aligned + 8,
+                             ctypes.byref(n), None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    # right size and alignment, but no input pointers: rejected before any launch
+    st = L.moe_block_forward(None, moe.MOE_BF16, b.T, ctypes.byref(d.c), None, moe.MOE_F32, None, None, aligned,
+                             ctypes.byref(n), None)
+    assert st == moe.MOE_ERR_ARG
+
+
+def test_route_permute_experts_queries(layers):
+    L = moe.lib()
+    b = layers["c2"]
+    r = synth.descs.router_desc(b)
+    n = ctypes.c_size_t(0)
+    assert L.moe_route(None, moe.MOE_BF16, b.T, b.H, ctypes.byref(r.c), None, None, None, None, ctypes.byref(n),
+                       None) == moe.MOE_OK
+    assert n.value >= b.T * b.E * 4
+    assert L.moe_route(None, moe.MOE_BF16, b.T, 0, ctypes.byref(r.c), None, None, None, None, ctypes.byref(n),
+                       None) == moe.MOE_ERR_SHAPE
+    assert L.moe_route(None, moe.MOE_BF16, b.T, 100, ctypes.byref(r.c), None, None, None, None, ctypes.byref(n),
+                       None) == moe.MOE_ERR_SHAPE
+    assert L.moe_permute(None, 1000, 8, 256, None, None, None, None, None, ctypes.byref(n), None) == moe.MOE_OK
+    assert n.value > 0
+    assert L.moe_permute(None, 10, 0, 256, None, None, None, None, None, ctypes.byref(n), None) == moe.MOE_ERR_SHAPE
+    assert L.moe_permute(None, 10, 9, 8, None, None, None, None, None, ctypes.byref(n), None) == moe.MOE_ERR_SHAPE
+    assert L.moe_permute(None, 10, 2, 8, None, None, None, None, None, None, None) == moe.MOE_ERR_ARG
+    ex = synth.descs.mlp_desc(b.experts)
+    assert L.moe_experts_forward(None, moe.MOE_BF16, b.T, b.H, ctypes.byref(ex.c), b.E, b.K, None, None, None, None,
+                                 None, moe.MOE_BF16, None, None, ctypes.byref(n), None) == moe.MOE_OK
+    assert L.moe_experts_forward(None, moe.MOE_BF16, b.T, b.H, ctypes.byref(ex.c), b.E + 1, b.K, None, None, None,
+                                 None, None, moe.MOE_BF16, None, None, ctypes.byref(n), None) == moe.MOE_ERR_SHAPE
+    assert L.moe_experts_forward(None, moe.MOE_BF16, b.T, b.H, ctypes.byref(ex.c), b.E, b.K, None, None, None, None,
+                                 None, moe.MOE_F32, None, None, ctypes.byref(n), None) == moe.MOE_ERR_ARG
