@@ -256,11 +256,18 @@ def route(x, router_w, scoring, K, norm_topk, routed_scale=1.0, logit_bias=None,
     s = scores_from_logits(logits, scoring)
     sel = s if select_bias is None else s + as_f64(select_bias)[None, :]
     idx = select_topk(sel, K)
-    w = np.take_along_axis(s, idx.astype(np.int64), axis=1)
+    w = weights_for(s, idx, norm_topk, routed_scale)
+    return {"idx": idx, "w": w, "logits": logits, "scores": s, "sel": sel}
+
+
+def weights_for(scores, idx, norm_topk, routed_scale=1.0) -> np.ndarray:
+    """Weights of a given selection: the unbiased scores of the chosen experts,
+    divided by their sum if norm_topk, times routed_scale (mlxcel PR #1044
+    point 3; latent_moe.rs route_top_k_sigmoid_with_bias argument order)."""
+    w = np.take_along_axis(np.asarray(scores, dtype=np.float64), np.asarray(idx, dtype=np.int64), axis=1)
     if norm_topk:
         w = w / np.sum(w, axis=1, keepdims=True)
-    w = w * routed_scale
-    return {"idx": idx, "w": w, "logits": logits, "scores": s, "sel": sel}
+    return w * routed_scale
 
 
 def coef_head(x, coef_w, coef_b) -> np.ndarray:
