@@ -44,6 +44,28 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int dt_size(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
+// dynamic LDS of the grouped GEMM: per wave a 4 KB weight tile plus the scale strips
+// of its 32 rows (AFFINE4: bf16 scales and qbias per group; MXFP4: one e8m0 byte per block)
+constexpr int kMaxWaveLds = 10240;
+void strip_layout(const moe_linear &L, int Kmax, int *wave_lds, int *strip_row) {
+  if (L.fmt == MOE_W_AFFINE4) {
+    *strip_row = ((2 * (Kmax / L.group_size)) + 3) & ~3;
+    *wave_lds = 4096 + 2 * 32 * *strip_row;
+  } else if (L.fmt == MOE_W_MXFP4) {
+    *strip_row = ((Kmax / 32) + 3) & ~3;
+    *wave_lds = 4096 + 32 * *strip_row;
+  } else {
+    *strip_row = 0;
+    *wave_lds = 4096;
+  }
+}
+bool strip_fits(const moe_linear &L) {
+  int wl, sr;
+  strip_layout(L, L.cols, &wl, &sr);
+  return wl <= kMaxWaveLds;
+}
+
+
 // ---------------------------------------------------------------------------
 // validation
 // ---------------------------------------------------------------------------
@@ -92,6 +114,9 @@ moe_status check_linear(const moe_linear *L, const char *name, int n, int rows, 
   if (act_dt != MOE_F32) {
     CHECK(rows % 16 == 0, MOE_ERR_SHAPE, "%s: rows %d not a multiple of 16", name, rows);
     CHECK(cols % 32 == 0, MOE_ERR_SHAPE, "%s: cols %d not a multiple of 32", name, cols);
+    CHECK(strip_fits(*L), MOE_ERR_UNSUPPORTED,
+          "%s: %d scale groups per row exceed this build's per-tile scale staging (affine: 48, mxfp4: 192)", name,
+          L->fmt == MOE_W_AFFINE4 ? cols / L->group_size : cols / 32);
   }
   return MOE_OK;
 }
@@ -292,7 +317,7 @@ moe_status launch_permute(const int32_t *idx, int T, int K, int E, int32_t *coun
 int max_tiles(int TK, int E, int Tsh) { return TK / MOE_MC + (E < TK ? E : TK) + (Tsh + MOE_MC - 1) / MOE_MC + 1; }
 
 int gemm_grid(int units_ub) {
-  const int cap = 4 * device_cus();
+  const int cap = 3 * device_cus();  // resident workgroups of the grouped GEMM (3 per CU)
   return units_ub < cap ? units_ub : cap;
 }
 
@@ -334,6 +359,7 @@ moe_status run_gemm(int adt, const moe_linear &fmt_of, bool gateup, int odt, con
   p.ldo = ldo;
   p.resid = resid;
   p.ldr = ldr;
+  strip_layout(fmt_of, shared && shared->K > routed.K ? shared->K : routed.K, &p.wave_lds, &p.strip_row);
   const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
   const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
   Timed tm(gateup ? TK_GATEUP : TK_DOWN, s);
@@ -362,6 +388,7 @@ moe_status run_plain(int adt, const moe_linear &W, const moe_linear *W1, float l
   p.ldo = ldo;
   p.resid = resid;
   p.ldr = ldr;
+  strip_layout(W, W.cols, &p.wave_lds, &p.strip_row);
   const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
   const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
   Timed tm(TK_PLAIN, s);

@@ -103,28 +103,61 @@ MOE_DEV u32x4_t cvt_dense(u32x4_t w) {
 
 }  // namespace
 
-template <int AT, int WF, int GS, bool GATEUP, int OT>
-__global__ __launch_bounds__(MOE_GEMM_THREADS, 2) void expert_gemm(const GemmParams p) {
+// 32x32x16 MFMA: lane l holds A[m = l%32][k = 8*(l/32) .. +8), B[k = 8*(l/32) .. +8][n = l%32]
+// and D[m = 8*(i/4) + 4*(l/32) + i%4][n = l%32], i = 0..15.
+template <int AT>
+MOE_DEV f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
+  if constexpr (AT == DT_BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+}
+
+// Work unit: (m-chunk of up to 32 rows of one segment, block of output columns).
+// Every wave owns one 32-row weight tile (GATEUP: 16 gate rows and the 16 up rows of
+// the same columns; LINEAR: 32 output rows).  Tokens are the MFMA's A operand and
+// weight rows its B operand, so every lane of a tile holds a single weight row.
+//
+// Weight stream: per chunk each tile row contributes one contiguous 128-byte
+// segment; a wave fetches its 4 KB with 16-byte loads, 8 lanes per row (whole
+// cache lines, no partial requests), two chunks ahead of the MFMAs, and writes them
+// into its own LDS tile with the 16-byte blocks of each row XOR-swizzled so that
+// the MFMA-layout reads (32 rows, same column) spread over the banks.
+// Scales/qbias (AFFINE4) or E8M0 exponents (MXFP4) of the tile's rows are copied
+// to LDS once per unit with contiguous loads.
+//
+// Reduction order inside a weight row: a "unit" of UE elements is split between
+// the two half-waves (UE/2 contiguous elements each); MFMA step s of the unit uses
+// elements [s*8, s*8+8) of each half.  For AFFINE4 a unit is one quantisation
+// group, so each step stays inside one group and the exact fold applies per group.
+template <int AT, int WF, int GQ, bool GATEUP, int OT>
+__global__ __launch_bounds__(MOE_GEMM_THREADS, 3) void expert_gemm(const GemmParams p) {
   constexpr bool AFF = (WF == WF_AFFINE4);
   constexpr bool MX = (WF == WF_MXFP4);
   constexpr bool DENSE = (WF == WF_DENSE);
-  constexpr int KC = DENSE ? 128 : MOE_KC;       // reduction elements per staged chunk
-  constexpr int STEPS = KC / 32;                 // MFMA k-steps per chunk
-  constexpr int NU = STEPS / GS;                 // units (GS steps each) per chunk
-  constexpr int WPS = DENSE ? 4 : 1;             // weight words per lane per step
-  constexpr int NW = STEPS * WPS;                // weight words per lane per subtile per chunk
-  constexpr int BPR = KC / 8;                    // 8-element blocks per chunk row
-  constexpr int RPI = MOE_GEMM_THREADS / BPR;    // rows staged per iteration
-  constexpr int SIT = MOE_MC / RPI;              // staging iterations per chunk
-  constexpr int LDA = KC + 8;                    // padded LDS row (16-bit elements)
+  constexpr int UE = AFF ? GQ : (MX ? 64 : 32);            // elements per unit (both halves)
+  constexpr int SPU = UE / 16;                             // MFMA steps per unit
+  constexpr int LB = DENSE ? UE : UE / 4;                  // bytes per lane per unit
+  constexpr int KC = DENSE ? 64 : MOE_KC;                  // reduction elements per chunk (128 B per row)
+  constexpr int NU = KC / UE;                              // units per chunk
+  constexpr int BPR = KC / 8;                              // 8-element activation blocks per chunk row
+  constexpr int RPI = MOE_GEMM_THREADS / BPR;              // activation rows staged per iteration
+  constexpr int SIT = (MOE_MC + RPI - 1) / RPI;            // activation staging iterations
+  constexpr int LDA = KC + 8;                              // padded LDS activation row (16-bit elements)
   constexpr float MAGIC = (AT == DT_BF16) ? 128.0f : 1024.0f;
+  static_assert(MOE_MC == 32, "one 32-row m-tile per chunk");
+  static_assert((DENSE ? KC * 2 : KC / 2) == 128, "128-byte row segments per chunk");
   __shared__ __attribute__((aligned(16))) uint16_t sA[MOE_MC * LDA];
-  __shared__ __attribute__((aligned(16))) float sX[AFF ? NU : 1][MOE_MC];
   __shared__ int64_t sRow[MOE_MC];
+  extern __shared__ __attribute__((aligned(16))) char dyn[];  // per wave: weight tile + scale strip
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r16 = lane & 15, kb = lane >> 4;
-  const int sblk = tid % BPR, srow0 = tid / BPR;  // this thread's staging block / first row
+  const int r32 = lane & 31, kb = lane >> 5;
+  const int sblk = tid % BPR, srow0 = tid / BPR;
+  char *wlds = dyn + wave * p.wave_lds;                    // 32 x 128 B weight tile
+  char *slds = wlds + 4096;                                // scale strip(s)
 
   int nr_routed, nr_shared;
   if (p.tiles) {
@@ -168,252 +201,248 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, 2) void expert_gemm(const GemmPar
     const WMat W1 = GATEUP ? (sh ? p.seg[1].w1 : p.seg[0].w1) : W0;
 #undef SF
 
-    int rowb[2];
-    bool act[2];
-    if constexpr (GATEUP) {
-      const int c0 = nb * 64 + wave * 16;
-      rowb[0] = rowb[1] = c0;
-      act[0] = act[1] = c0 < W0.rows;
-    } else {
-      const int c0 = nb * 128 + wave * 32;
-      rowb[0] = c0;
-      rowb[1] = c0 + 16;
-      act[0] = c0 < W0.rows;
-      act[1] = c0 + 16 < W0.rows;
-    }
-    const uint32_t *wrow[2];
-    const uint16_t *srow[2];
-    const uint16_t *qrow[2];
-    const uint8_t *erow[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const WMat &M = b ? W1 : W0;
-      const int64_t row = act[b] ? rowb[b] + r16 : 0;
-      wrow[b] = (const uint32_t *)((const char *)M.w + (int64_t)e * M.w_stride + row * M.ldw);
-      srow[b] = AFF ? (const uint16_t *)M.scales + (int64_t)e * M.s_stride + row * M.lds : nullptr;
-      qrow[b] = AFF ? (const uint16_t *)M.qbias + (int64_t)e * M.s_stride + row * M.lds : nullptr;
-      erow[b] = MX ? (const uint8_t *)M.scales + (int64_t)e * M.s_stride + row * M.lds : nullptr;
-    }
-    const int n_mt = (nr + 15) >> 4;
+    // tile row t (0..31) -> weight matrix row; GATEUP: rows 0-15 gate, 16-31 up
+    const int col0 = GATEUP ? nb * 64 + wave * 16 : nb * 128 + wave * 32;
+    const bool act = col0 < W0.rows;
+    auto row_of = [&](int t) { return GATEUP ? col0 + (t & 15) : col0 + t; };
+    auto row_ok = [&](int t) { return row_of(t) < W0.rows; };
+    auto mat_of = [&](int t) -> const WMat & { return (GATEUP && t >= 16) ? W1 : W0; };
     const int nchunks = (Kd + KC - 1) / KC;
+    const int nib = min(4, (nr + 7) >> 3);       // 8-row blocks of the m-tile that hold rows
 
-    // where each of the unit's activation rows starts
-    __syncthreads();  // the previous unit is done with sRow / sA
+    // this lane's loader rows (tile rows 8*i + lane/8) and their segment base pointers
+    const char *lrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 8 * i + (lane >> 3);
+      const WMat &M = mat_of(t);
+      const int64_t rr = row_ok(t) ? row_of(t) : 0;
+      lrow[i] = (const char *)M.w + (int64_t)e * M.w_stride + rr * M.ldw + 16 * (lane & 7);
+    }
+
+    u32x4_t gA[4], gB[4], gC[4];  // weight ring: chunk c, c+1 in flight, c+2 being loaded
+    auto load_w = [&](int kc, u32x4_t (&g)[4]) {
+      const int kcc = min(kc, (nchunks - 1) * KC);
+      const int64_t off = DENSE ? (int64_t)kcc * 2 : kcc / 2;
+      // the last chunk may be shorter than 128 B per row: clamp the piece into the row
+      const int rowbytes = DENSE ? Kd * 2 : Kd / 2;
+      const int64_t o2 = min((int64_t)rowbytes - 16, off + 16 * (lane & 7)) - 16 * (lane & 7);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g[i] = *(const u32x4_t *)(lrow[i] + o2);
+    };
+    load_w(0, gA);  // in flight during the setup below
+    load_w(KC, gB);
+
+    __syncthreads();  // the previous unit is done with sRow / sA / the LDS tiles
     if (tid < nr) {
       const int64_t arow = gat ? (int64_t)(gat[r0 + tid] / gdiv) : (int64_t)(r0 + tid - rsub);
       sRow[tid] = arow * lda;
     }
-    __syncthreads();
 
-    // ---- loaders (raw bits only: nothing here waits for the loads)
-    u32x4_t areg[SIT];
-    auto load_a = [&](int kc) {
-      const int kn = min(KC, Kd - kc);
+    // ---- scale strips -> LDS (once per unit): AFF: [32][G] bf16 scales then [32][G] qbias;
+    //      MX: [32][NB] e8m0 bytes.  Row t of a strip belongs to tile row t.
+    if constexpr (AFF || MX) {
+      const int G = AFF ? Kd / UE : Kd / 32;         // entries per row
+      const int esz = AFF ? 2 : 1;
+      const int rowb = G * esz;                      // bytes per strip row in LDS (unpadded)
+      const int nstrip = AFF ? 2 : 1;
+      // lanes walk the strip rows with 2-byte loads: lane -> (row offset, entry pair)
+      const int EPR = (rowb + 1) / 2;                // 2-byte words per row
+      int epp = 1;
+      while (epp < EPR) epp <<= 1;                   // <= 64 (checked on the host)
+      const int rps = 64 / epp;                      // rows per pass
+      for (int sidx = 0; sidx < nstrip; ++sidx) {
+        for (int t0 = 0; t0 < 32; t0 += 8 * rps) {
+          uint16_t v[8];
 #pragma unroll
-      for (int it = 0; it < SIT; ++it) {
-        const int row = srow0 + RPI * it;
-        areg[it] = u32x4_t{0u, 0u, 0u, 0u};
-        if (row < nr && sblk * 8 < kn) areg[it] = *(const u32x4_t *)(Ab + sRow[row] + kc + sblk * 8);
-      }
-    };
-    uint32_t wcur[2][NW], wnxt[2][NW];
-    uint32_t scur[2][NU], snxt[2][NU];  // AFF: scale bits; MX: e8m0 byte
-    uint32_t qcur[2][NU], qnxt[2][NU];  // AFF: qbias bits
-    auto load_w = [&](int kc, uint32_t (&w)[2][NW], uint32_t (&sr)[2][NU], uint32_t (&qr)[2][NU]) {
-      const int nsteps = min(KC, Kd - kc) >> 5;
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        if (!act[b]) continue;
-#pragma unroll
-        for (int uu = 0; uu < NU; ++uu) {
-          if (uu * GS < nsteps) {
-            if constexpr (DENSE) {
-              const u32x4_t v = *(const u32x4_t *)(wrow[b] + ((kc + 32 * uu + 8 * kb) >> 1));
-#pragma unroll
-              for (int i = 0; i < 4; ++i) w[b][4 * uu + i] = v[i];
-            } else {
-              const int wi = ((kc + 32 * GS * uu) >> 3) + kb * GS;
-              if constexpr (GS == 1) {
-                w[b][uu] = wrow[b][wi];
-              } else if constexpr (GS == 2) {
-                const u32x2_t v = *(const u32x2_t *)(wrow[b] + wi);
-                w[b][2 * uu] = v[0];
-                w[b][2 * uu + 1] = v[1];
-              } else {
-                const u32x4_t v = *(const u32x4_t *)(wrow[b] + wi);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) w[b][4 * uu + i] = v[i];
-              }
-              if constexpr (AFF) {
-                const int g = (kc >> 5) / GS + uu;
-                sr[b][uu] = srow[b][g];
-                qr[b][uu] = qrow[b][g];
-              } else {
-                sr[b][uu] = erow[b][((kc + 64 * uu) >> 5) + (kb >> 1)];
-              }
+          for (int i = 0; i < 8; ++i) {
+            const int t = t0 + i * rps + lane / epp;
+            const int w = lane % epp;
+            v[i] = 0;
+            if (t < 32 && w < EPR) {
+              const WMat &M = mat_of(t);
+              const int64_t rr = row_ok(t) ? row_of(t) : 0;
+              const uint16_t *src = (const uint16_t *)((const char *)(sidx ? M.qbias : M.scales) +
+                                                       ((int64_t)e * M.s_stride + rr * M.lds) * esz);
+              v[i] = (esz == 2 || (rowb & 1) == 0 || w < EPR - 1)
+                         ? src[w]
+                         : (uint16_t)((const uint8_t *)src)[2 * w];
             }
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int t = t0 + i * rps + lane / epp;
+            const int w = lane % epp;
+            if (t < 32 && w < EPR) *(uint16_t *)(slds + sidx * 32 * p.strip_row + t * p.strip_row + 2 * w) = v[i];
           }
         }
       }
+    }
+    __syncthreads();
+
+    // ---- loaders: raw bits only; every call issues the same loads (addresses clamped
+    // into valid memory) so the compiler can count them; out-of-chunk data is masked
+    // when consumed.
+    u32x4_t areg[SIT];
+    uint32_t amask = 0;
+    auto load_a = [&](int kc) {
+      const int kcc = min(kc, (nchunks - 1) * KC);
+      const int kn = min(KC, Kd - kcc);
+      amask = 0;
+#pragma unroll
+      for (int it = 0; it < SIT; ++it) {
+        const int row = srow0 + RPI * it;
+        const bool ok = row < nr && sblk * 8 < kn && kc < Kd;
+        amask |= ok ? (1u << it) : 0u;
+        const int rr = row < nr ? row : 0;
+        const int cc = sblk * 8 < kn ? sblk * 8 : 0;
+        areg[it] = *(const u32x4_t *)(Ab + sRow[rr] + kcc + cc);
+      }
     };
-    // activation chunk: registers -> LDS (affine: group sums + pair order)
-    auto store_a = [&](int kc) {
+    auto put_w = [&](const u32x4_t (&g)[4]) {  // registers -> swizzled LDS tile
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 8 * i + (lane >> 3);
+        const int pos = (lane & 7) ^ ((t >> 1) & 7);
+        *(u32x4_t *)(wlds + t * 128 + 16 * pos) = g[i];
+      }
+    };
+    auto store_a = [&]() {
 #pragma unroll
       for (int it = 0; it < SIT; ++it) {
         const int row = srow0 + RPI * it;
         if (row < nr) {
           u32x4_t v = areg[it];
-          if constexpr (AFF) {
-            float f[8];
-            unpack8<AT>(v, f);
-            float s = ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
-#pragma unroll
-            for (int o = 1; o < 4 * GS; o <<= 1) s += __shfl_xor(s, o, 64);
-            if ((sblk & (4 * GS - 1)) == 0) sX[sblk / (4 * GS)][row] = s;
-            v = pair_i_i4(v);
-          }
+          if (!((amask >> it) & 1u)) v = u32x4_t{0u, 0u, 0u, 0u};
+          if constexpr (AFF) v = pair_i_i4(v);
           *(u32x4_t *)&sA[row * LDA + sblk * 8] = v;
         }
       }
     };
 
-    f32x4_t acc[4][2];
+    f32x16_t acc;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+
+    const char *my_w = wlds + r32 * 128;
+    const int my_sw = (r32 >> 1) & 7;
+    auto compute = [&](int kc) {
+      if (!act) return;
+      const int nunits = min(KC, Kd - kc) / UE;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) acc[mt][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int uu = 0; uu < NU; ++uu) {
+        if (uu >= nunits) break;
+        // this lane's LB bytes of the unit: byte offset (UE*uu + UE/2*kb) * bytes-per-element
+        const int boff = DENSE ? (UE * uu + (UE / 2) * kb) * 2 : (UE * uu + (UE / 2) * kb) / 2;
+        uint32_t wv[LB / 4];
+        if constexpr (LB == 8) {
+          const int blk = boff >> 4;
+          const u32x2_t a = *(const u32x2_t *)(my_w + 16 * (blk ^ my_sw) + (boff & 15));
+          wv[0] = a[0];
+          wv[1] = a[1];
+        } else {
+#pragma unroll
+          for (int h = 0; h < LB / 16; ++h) {
+            const int blk = (boff >> 4) + h;
+            const u32x4_t a = *(const u32x4_t *)(my_w + 16 * (blk ^ my_sw));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wv[4 * h + i] = a[i];
+          }
+        }
+        float sc = 0.f, qb = 0.f;
+        if constexpr (AFF) {
+          const int g = kc / UE + uu;
+          sc = bf16_bits_to_f32(*(const uint16_t *)(slds + r32 * p.strip_row + 2 * g));
+          qb = bf16_bits_to_f32(*(const uint16_t *)(slds + 32 * p.strip_row + r32 * p.strip_row + 2 * g));
+        } else if constexpr (MX) {
+          sc = e8m0_to_f32(*(const uint8_t *)(slds + r32 * p.strip_row + (kc >> 5) + 2 * uu + kb));
+        }
+        f32x16_t accg, accx;  // AFF: sum of (MAGIC+q)*a and of a over the unit (one group)
+#pragma unroll
+        for (int s = 0; s < SPU; ++s) {
+          u32x4_t bfr;
+          if constexpr (AFF)
+            bfr = cvt_affine<AT>(wv[s]);
+          else if constexpr (MX)
+            bfr = cvt_mxfp4<AT>(wv[s], sc);
+          else
+            bfr = cvt_dense<AT>(u32x4_t{wv[4 * s], wv[4 * s + 1], wv[4 * s + 2], wv[4 * s + 3]});
+          const int blk8 = uu * (UE / 8) + kb * (UE / 16) + s;
+          const u32x4_t av = *(const u32x4_t *)&sA[r32 * LDA + blk8 * 8];
+          if constexpr (AFF) {
+            constexpr uint32_t ONE2 = (AT == DT_BF16) ? 0x3F803F80u : 0x3C003C00u;  // (1.0, 1.0)
+            const u32x4_t ones = {ONE2, ONE2, ONE2, ONE2};
+            if (s == 0) {
+              f32x16_t z;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) z[i] = 0.f;
+              accg = mfma32<AT>(av, bfr, z);
+              accx = mfma32<AT>(av, ones, z);
+            } else {
+              accg = mfma32<AT>(av, bfr, accg);
+              accx = mfma32<AT>(av, ones, accx);
+            }
+          } else {
+            acc = mfma32<AT>(av, bfr, acc);
+          }
+        }
+        if constexpr (AFF) {
+          const float c_ = fmaf(-MAGIC, sc, qb);
+#pragma unroll
+          for (int ib = 0; ib < 4; ++ib) {
+            if (ib < nib) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                acc[4 * ib + j] = fmaf(sc, accg[4 * ib + j], fmaf(c_, accx[4 * ib + j], acc[4 * ib + j]));
+            }
+          }
+        }
+      }
+    };
+    // one chunk: stage its activations and weights, launch the loads two chunks ahead, compute
+    auto chunk = [&](int c, const u32x4_t (&gcur)[4], u32x4_t (&gnext2)[4]) {
+      const int kc = c * KC;
+      __syncthreads();  // readers of the previous chunk's activations are done
+      if (c < nchunks) {
+        store_a();
+        put_w(gcur);
+      }
+      load_a(kc + KC);
+      load_w(kc + 2 * KC, gnext2);
+      __syncthreads();
+      if (c < nchunks) compute(kc);
+    };
 
     load_a(0);
-    load_w(0, wcur, scur, qcur);
-    for (int c = 0; c < nchunks; ++c) {
-      const int kc = c * KC;
-      const int nsteps = min(KC, Kd - kc) >> 5;
-      __syncthreads();  // readers of the previous chunk are done
-      store_a(kc);
-      if (c + 1 < nchunks) {  // next chunk in flight while this one computes
-        load_a(kc + KC);
-        load_w(kc + KC, wnxt, snxt, qnxt);
-      }
-      __syncthreads();
-
-      if (act[0] || act[1]) {
-#pragma unroll
-        for (int uu = 0; uu < NU; ++uu) {
-          if (uu * GS >= nsteps) break;
-          float sc[2], qb[2];
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            if constexpr (AFF) {
-              sc[b] = bf16_bits_to_f32(scur[b][uu]);
-              qb[b] = bf16_bits_to_f32(qcur[b][uu]);
-            } else if constexpr (MX) {
-              sc[b] = e8m0_to_f32(scur[b][uu]);
-            }
-          }
-          f32x4_t accg[4][2];
-#pragma unroll
-          for (int s = 0; s < GS; ++s) {
-            const int q = uu * GS + s;
-            u32x4_t bf[2];
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              if constexpr (AFF)
-                bf[b] = cvt_affine<AT>(wcur[b][q]);
-              else if constexpr (MX)
-                bf[b] = cvt_mxfp4<AT>(wcur[b][q], sc[b]);
-              else
-                bf[b] = cvt_dense<AT>(u32x4_t{wcur[b][4 * q], wcur[b][4 * q + 1], wcur[b][4 * q + 2], wcur[b][4 * q + 3]});
-            }
-            const int blk8 = uu * 4 * GS + kb * GS + s;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-              if (mt < n_mt) {
-                const u32x4_t av = *(const u32x4_t *)&sA[(mt * 16 + r16) * LDA + blk8 * 8];
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                  if (act[b]) {
-                    if constexpr (AFF)
-                      accg[mt][b] = mfma16<AT>(av, bf[b], s == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : accg[mt][b]);
-                    else
-                      acc[mt][b] = mfma16<AT>(av, bf[b], acc[mt][b]);
-                  }
-                }
-              }
-            }
-          }
-          if constexpr (AFF) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-              if (mt < n_mt) {
-                const f32x4_t xs = *(const f32x4_t *)&sX[uu][mt * 16 + 4 * kb];
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                  if (act[b]) {
-                    const float c_ = fmaf(-MAGIC, sc[b], qb[b]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                      acc[mt][b][i] = fmaf(sc[b], accg[mt][b][i], fmaf(c_, xs[i], acc[mt][b][i]));
-                  }
-                }
-              }
-            }
-          }
-        }
-      }
-      if (c + 1 < nchunks) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-#pragma unroll
-          for (int i = 0; i < NW; ++i) wcur[b][i] = wnxt[b][i];
-#pragma unroll
-          for (int i = 0; i < NU; ++i) {
-            scur[b][i] = snxt[b][i];
-            qcur[b][i] = qnxt[b][i];
-          }
-        }
-      }
+    for (int c = 0; c < nchunks; c += 3) {
+      chunk(c, gA, gC);
+      chunk(c + 1, gB, gA);
+      chunk(c + 2, gC, gB);
     }
 
-    // ---- epilogue: acc[mt][b][i] is row mt*16 + 4*kb + i, column rowb[b] + r16
-    if constexpr (GATEUP) {
-      if (act[0]) {
-        const int col = rowb[0] + r16;
-        const float bg = W0.bias ? bf16_bits_to_f32(((const uint16_t *)W0.bias)[(int64_t)e * W0.rows + col]) : 0.f;
-        const float bu = W1.bias ? bf16_bits_to_f32(((const uint16_t *)W1.bias)[(int64_t)e * W1.rows + col]) : 0.f;
+    // ---- epilogue: acc[4*ib + j] is row 8*ib + 4*kb + j of the m-chunk, tile row r32
+    if (act) {
+      const bool lane_ok = row_ok(r32);
+      const int wrow_i = row_of(r32);
+      const WMat &M = mat_of(r32);
+      const float bo =
+          (lane_ok && M.bias) ? bf16_bits_to_f32(((const uint16_t *)M.bias)[(int64_t)e * M.rows + wrow_i]) : 0.f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          if (mt < n_mt) {
+      for (int ib = 0; ib < 4; ++ib) {
+        if (ib < nib) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int m = mt * 16 + 4 * kb + i;
-              if (m < nr) {
-                float g = acc[mt][0][i] + bg, v = acc[mt][1][i] + bu;
-                if (limit > 0.f) {
-                  g = fminf(fmaxf(g, -limit), limit);
-                  v = fminf(fmaxf(v, -limit), limit);
-                }
-                store_act<OT>(p.out, (int64_t)(r0 + m) * p.ldo + col, silu_f(g) * v);
-              }
-            }
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        if (!act[b]) continue;
-        const int col = rowb[b] + r16;
-        const float bo = W0.bias ? bf16_bits_to_f32(((const uint16_t *)W0.bias)[(int64_t)e * W0.rows + col]) : 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          if (mt < n_mt) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int m = mt * 16 + 4 * kb + i;
-              if (m < nr) {
-                float v = acc[mt][b][i] + bo;
-                if (p.resid) v += p.resid[(int64_t)(r0 + m) * p.ldr + col];
-                store_act<OT>(p.out, (int64_t)(r0 + m) * p.ldo + col, v);
+          for (int j = 0; j < 4; ++j) {
+            const int m = 8 * ib + 4 * kb + j;
+            float v = acc[4 * ib + j] + bo;
+            if constexpr (GATEUP) {
+              if (limit > 0.f) v = fminf(fmaxf(v, -limit), limit);
+              const float up = __shfl_xor(v, 16, 64);   // lanes r32 >= 16 hold the up rows
+              if (r32 < 16 && m < nr)
+                store_act<OT>(p.out, (int64_t)(r0 + m) * p.ldo + col0 + r32, silu_f(v) * up);
+            } else {
+              if (lane_ok && m < nr) {
+                if (p.resid) v += p.resid[(int64_t)(r0 + m) * p.ldr + wrow_i];
+                store_act<OT>(p.out, (int64_t)(r0 + m) * p.ldo + wrow_i, v);
               }
             }
           }
@@ -468,33 +497,34 @@ __global__ __launch_bounds__(64) void f32_gemm_kernel(const F32GemmParams p) {
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
-template <int AT, int WF, int GS, bool GU, int OT>
+template <int AT, int WF, int GQ, bool GU, int OT>
 static hipError_t launch_t(const GemmParams &p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((expert_gemm<AT, WF, GS, GU, OT>), dim3(grid), dim3(MOE_GEMM_THREADS), 0, s, p);
+  hipLaunchKernelGGL((expert_gemm<AT, WF, GQ, GU, OT>), dim3(grid), dim3(MOE_GEMM_THREADS),
+                     (size_t)p.wave_lds * (MOE_GEMM_THREADS / 64), s, p);
   return hipGetLastError();
 }
 
-template <int AT, int WF, int GS>
+template <int AT, int WF, int GQ>
 static hipError_t launch_o(bool gateup, int odt, const GemmParams &p, int grid, hipStream_t s) {
   if (gateup) {
-    if (odt == DT_BF16) return launch_t<AT, WF, GS, true, DT_BF16>(p, grid, s);
-    if (odt == DT_F16) return launch_t<AT, WF, GS, true, DT_F16>(p, grid, s);
+    if (odt == DT_BF16) return launch_t<AT, WF, GQ, true, DT_BF16>(p, grid, s);
+    if (odt == DT_F16) return launch_t<AT, WF, GQ, true, DT_F16>(p, grid, s);
   } else {
-    if (odt == DT_F32) return launch_t<AT, WF, GS, false, DT_F32>(p, grid, s);
-    if (odt == DT_BF16) return launch_t<AT, WF, GS, false, DT_BF16>(p, grid, s);
-    if (odt == DT_F16) return launch_t<AT, WF, GS, false, DT_F16>(p, grid, s);
+    if (odt == DT_F32) return launch_t<AT, WF, GQ, false, DT_F32>(p, grid, s);
+    if (odt == DT_BF16) return launch_t<AT, WF, GQ, false, DT_BF16>(p, grid, s);
+    if (odt == DT_F16) return launch_t<AT, WF, GQ, false, DT_F16>(p, grid, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <int AT>
 static hipError_t launch_w(int wfmt, int group, bool gateup, int odt, const GemmParams &p, int grid, hipStream_t s) {
-  if (wfmt == WF_DENSE) return launch_o<AT, WF_DENSE, 1>(gateup, odt, p, grid, s);
-  if (wfmt == WF_MXFP4) return launch_o<AT, WF_MXFP4, 2>(gateup, odt, p, grid, s);
+  if (wfmt == WF_DENSE) return launch_o<AT, WF_DENSE, 0>(gateup, odt, p, grid, s);
+  if (wfmt == WF_MXFP4) return launch_o<AT, WF_MXFP4, 0>(gateup, odt, p, grid, s);
   if (wfmt == WF_AFFINE4) {
-    if (group == 32) return launch_o<AT, WF_AFFINE4, 1>(gateup, odt, p, grid, s);
-    if (group == 64) return launch_o<AT, WF_AFFINE4, 2>(gateup, odt, p, grid, s);
-    if (group == 128) return launch_o<AT, WF_AFFINE4, 4>(gateup, odt, p, grid, s);
+    if (group == 32) return launch_o<AT, WF_AFFINE4, 32>(gateup, odt, p, grid, s);
+    if (group == 64) return launch_o<AT, WF_AFFINE4, 64>(gateup, odt, p, grid, s);
+    if (group == 128) return launch_o<AT, WF_AFFINE4, 128>(gateup, odt, p, grid, s);
   }
   return hipErrorInvalidValue;
 }

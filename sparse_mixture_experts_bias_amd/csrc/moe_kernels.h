@@ -5,8 +5,8 @@
 
 #define MOE_MAX_EXPERTS 512  // router top-k keeps 8 experts per lane of a wave64
 #define MOE_MAX_TOPK 32      // chosen experts live one per lane (K <= 32)
-#define MOE_MC 64            // rows (slots or tokens) per m-chunk of the grouped GEMM
-#define MOE_KC 256           // reduction elements staged per LDS chunk
+#define MOE_MC 32            // rows (slots or tokens) per m-chunk of the grouped GEMM
+#define MOE_KC 256           // reduction elements per chunk for 4-bit weights (128 B per row)
 #define MOE_GEMM_THREADS 256 // 4 waves
 
 struct TopkArgs {
@@ -64,6 +64,8 @@ struct GemmParams {
   int64_t ldo;
   const float *resid;   // LINEAR: optional f32 [rows][ldr] added before the store
   int64_t ldr;
+  int wave_lds;         // dynamic LDS bytes per wave: 4 KB weight tile + scale strips
+  int strip_row;        // bytes per scale-strip row in LDS
 };
 
 struct F32GemmParams {   // f32 activations with DENSE F32 weights (one thread per output)
