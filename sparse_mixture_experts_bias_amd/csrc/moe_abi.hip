@@ -44,27 +44,27 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int dt_size(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
-// dynamic LDS of the grouped GEMM: per wave a 4 KB weight tile plus the scale strips
-// of its 32 rows (AFFINE4: bf16 scales and qbias per group; MXFP4: one e8m0 byte per block)
-constexpr int kMaxWaveLds = 10240;
+// dynamic LDS of the grouped GEMM: per wave a 4 KB weight tile plus the scale strip of
+// its 32 rows (AFFINE4: one 4-byte word per group, scale | qbias << 16; MXFP4: one e8m0
+// byte per block).  Rows are padded so that 16 rows read at one column hit 16 banks.
+constexpr int kMaxWaveLds = 16384;
+constexpr int kMaxAffineGroups = (kMaxWaveLds - 4096) / 32 / 4 - 2;  // 94
+constexpr int kMaxMxBlocks = (kMaxWaveLds - 4096) / 32 - 4;           // 380
 void strip_layout(const moe_linear &L, int Kmax, int *wave_lds, int *strip_row) {
   if (L.fmt == MOE_W_AFFINE4) {
-    *strip_row = ((2 * (Kmax / L.group_size)) + 3) & ~3;
-    *wave_lds = 4096 + 2 * 32 * *strip_row;
+    *strip_row = (4 * (Kmax / L.group_size) + 4 + 7) & ~7;
   } else if (L.fmt == MOE_W_MXFP4) {
-    *strip_row = ((Kmax / 32) + 3) & ~3;
-    *wave_lds = 4096 + 32 * *strip_row;
+    *strip_row = (((Kmax / 32) + 3) & ~3) + 4;
   } else {
     *strip_row = 0;
-    *wave_lds = 4096;
   }
+  *wave_lds = 4096 + 32 * *strip_row;
 }
 bool strip_fits(const moe_linear &L) {
   int wl, sr;
   strip_layout(L, L.cols, &wl, &sr);
   return wl <= kMaxWaveLds;
 }
-
 
 // ---------------------------------------------------------------------------
 // validation
@@ -115,8 +115,8 @@ moe_status check_linear(const moe_linear *L, const char *name, int n, int rows, 
     CHECK(rows % 16 == 0, MOE_ERR_SHAPE, "%s: rows %d not a multiple of 16", name, rows);
     CHECK(cols % 32 == 0, MOE_ERR_SHAPE, "%s: cols %d not a multiple of 32", name, cols);
     CHECK(strip_fits(*L), MOE_ERR_UNSUPPORTED,
-          "%s: %d scale groups per row exceed this build's per-tile scale staging (affine: 48, mxfp4: 192)", name,
-          L->fmt == MOE_W_AFFINE4 ? cols / L->group_size : cols / 32);
+          "%s: %d scale groups per row exceed this build's per-tile scale staging (affine: %d, mxfp4: %d)", name,
+          L->fmt == MOE_W_AFFINE4 ? cols / L->group_size : cols / 32, kMaxAffineGroups, kMaxMxBlocks);
   }
   return MOE_OK;
 }
@@ -295,11 +295,11 @@ moe_status launch_topk(const void *x, int x_dt, int T, int H, const moe_router *
 size_t perm_ws_bytes(int64_t T, int E) { return T <= 256 ? 0 : (size_t)((T + 255) / 256) * E * 4; }
 
 moe_status launch_permute(const int32_t *idx, int T, int K, int E, int32_t *counts, int32_t *offsets, int32_t *ss,
-                          int32_t *sp, int32_t *chunk_ws, int4 *tiles, int *tile_count, int Tsh, hipStream_t s) {
+                          int32_t *sp, int32_t *chunk_ws, int4 *tiles, int *tile_count, int mt, hipStream_t s) {
   Timed tm(TK_PERM, s);
   if (T <= 256) {
     hipLaunchKernelGGL(perm_small, dim3(1), dim3(256), 0, s, idx, T, K, E, counts, offsets, ss, sp, tiles, tile_count,
-                       Tsh);
+                       mt);
     HIPCHK(hipGetLastError());
     return MOE_OK;
   }
@@ -307,17 +307,23 @@ moe_status launch_permute(const int32_t *idx, int T, int K, int E, int32_t *coun
   hipLaunchKernelGGL(perm_count, dim3(nch), dim3(256), 0, s, idx, T, K, E, chunk_ws);
   HIPCHK(hipGetLastError());
   hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, s, chunk_ws, nch, E, T * K, counts, offsets, tiles,
-                     tile_count, Tsh);
+                     tile_count, mt);
   HIPCHK(hipGetLastError());
   hipLaunchKernelGGL(perm_scatter, dim3(nch), dim3(256), 0, s, idx, T, K, E, chunk_ws, ss, sp);
   HIPCHK(hipGetLastError());
   return MOE_OK;
 }
 
-int max_tiles(int TK, int E, int Tsh) { return TK / MOE_MC + (E < TK ? E : TK) + (Tsh + MOE_MC - 1) / MOE_MC + 1; }
+// routed m-tiles of at most mt rows: sum over experts of ceil(n_e / mt) <= TK / mt + min(E, TK)
+int routed_tiles_ub(int TK, int E, int mt) { return TK / mt + (E < TK ? E : TK); }
+int max_tiles(int TK, int E) { return routed_tiles_ub(TK, E, MOE_MT_MIN) + 1; }
 
-int gemm_grid(int units_ub) {
-  const int cap = 3 * device_cus();  // resident workgroups of the grouped GEMM (3 per CU)
+// m-blocks (16 rows each) per m-tile: 1 for decode-sized segments, 4 otherwise
+int pick_mb(double avg_rows) { return avg_rows <= 16.0 ? 1 : 4; }
+int mb_for_routing(int TK, int E) { return pick_mb((double)TK / (E < TK ? E : (TK > 0 ? TK : 1))); }
+
+int gemm_grid(int units_ub, int mb) {
+  const int cap = (mb == 1 ? 3 : 2) * device_cus();  // resident workgroups of the grouped GEMM per CU
   return units_ub < cap ? units_ub : cap;
 }
 
@@ -331,6 +337,16 @@ AOp aop(const void *a, int64_t lda, const int32_t *gather, int gdiv, int row_sub
   return o;
 }
 
+// scale entries of L loadable as aligned 4-byte words (AFFINE4: 2 entries, MXFP4: 4)
+bool scales_vec(const moe_linear &L) {
+  if (L.fmt == MOE_W_AFFINE4) {
+    const int G = L.cols / L.group_size;
+    return G % 2 == 0 && aligned(L.scales, 4) && aligned(L.qbias, 4);
+  }
+  if (L.fmt == MOE_W_MXFP4) return (L.cols / 32) % 4 == 0 && aligned(L.scales, 4);
+  return false;
+}
+
 SegSet segset(AOp A, const moe_linear &w0, const moe_linear *w1, float limit, bool gateup) {
   SegSet s;
   s.A = A;
@@ -339,31 +355,42 @@ SegSet segset(AOp A, const moe_linear &w0, const moe_linear *w1, float limit, bo
   s.limit = limit;
   s.K = w0.cols;
   s.nblk = gateup ? (w0.rows + 63) / 64 : (w0.rows + 127) / 128;
+  s.svec = scales_vec(w0) && (!w1 || scales_vec(*w1)) ? 1 : 0;
   return s;
 }
 
-// routed experts (+ optional shared segment in the same launch)
-moe_status run_gemm(int adt, const moe_linear &fmt_of, bool gateup, int odt, const SegSet &routed,
-                    const SegSet *shared, const int4 *tiles, const int *tile_count, int E, int units_ub, void *out,
-                    int64_t ldo, const float *resid, int64_t ldr, int plain_rows, hipStream_t s) {
+// routed experts (m-tiles of 16*mb rows from the tile list) + optional segment-1 rows
+// [sh_row0, sh_row0 + sh_rows) (the shared expert) in the same launch
+moe_status run_gemm(int adt, const moe_linear &fmt_of, bool gateup, int odt, int mb, const SegSet &routed,
+                    const SegSet *shared, int sh_row0, int sh_rows, const int4 *tiles, const int *tile_count,
+                    int ntiles_alloc, int TK, int E, void *out, int64_t ldo, const float *resid, int64_t ldr,
+                    hipStream_t s) {
+  const int mt = 16 * mb;
   GemmParams p;
   memset(&p, 0, sizeof p);
   p.seg[0] = routed;
   p.seg[1] = shared ? *shared : routed;
-  if (!shared) p.seg[1].nblk = 0;
+  if (!shared) {
+    p.seg[1].nblk = 0;
+    sh_rows = 0;
+  }
   p.tiles = tiles;
   p.tile_count = tile_count;
-  p.plain_rows = plain_rows;
+  p.max_tiles = ntiles_alloc;
+  p.sh_row0 = sh_row0;
+  p.sh_rows = sh_rows;
   p.E = E;
   p.out = out;
   p.ldo = ldo;
   p.resid = resid;
   p.ldr = ldr;
   strip_layout(fmt_of, shared && shared->K > routed.K ? shared->K : routed.K, &p.wave_lds, &p.strip_row);
+  const int units_ub = routed_tiles_ub(TK, E, mt) * routed.nblk + ((sh_rows + mt - 1) / mt) * p.seg[1].nblk;
   const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
   const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
   Timed tm(gateup ? TK_GATEUP : TK_DOWN, s);
-  HIPCHK(launch_expert_gemm(adt_k, wf_of(fmt_of), fmt_of.group_size, gateup, odt_k, p, gemm_grid(units_ub), s));
+  HIPCHK(launch_expert_gemm(adt_k, wf_of(fmt_of), fmt_of.group_size, gateup, odt_k, mb, p, gemm_grid(units_ub, mb),
+                            s));
   return MOE_OK;
 }
 
@@ -371,28 +398,32 @@ moe_status run_gemm(int adt, const moe_linear &fmt_of, bool gateup, int odt, con
 moe_status run_plain(int adt, const moe_linear &W, const moe_linear *W1, float limit, bool gateup, int odt,
                      const void *a, int64_t lda, int rows, void *out, int64_t ldo, const float *resid, int64_t ldr,
                      hipStream_t s) {
+  const int mb = pick_mb(rows);
+  const int mt = 16 * mb;
   SegSet sg = segset(aop(a, lda, nullptr, 1, 0), W, W1, limit, gateup);
-  const int units = ((rows + MOE_MC - 1) / MOE_MC) * sg.nblk;
   SegSet none = sg;
   none.nblk = 0;
-  // plain mode: every tile is a "shared" tile; the routed set has no units
+  // plain mode: every m-tile is a segment-1 tile; the routed set has no units
   GemmParams p;
   memset(&p, 0, sizeof p);
   p.seg[0] = none;
   p.seg[1] = sg;
   p.tiles = nullptr;
   p.tile_count = nullptr;
-  p.plain_rows = rows;
+  p.max_tiles = 0;
+  p.sh_row0 = 0;
+  p.sh_rows = rows;
   p.E = 0;
   p.out = out;
   p.ldo = ldo;
   p.resid = resid;
   p.ldr = ldr;
   strip_layout(W, W.cols, &p.wave_lds, &p.strip_row);
+  const int units = ((rows + mt - 1) / mt) * sg.nblk;
   const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
   const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
   Timed tm(TK_PLAIN, s);
-  HIPCHK(launch_expert_gemm(adt_k, wf_of(W), W.group_size, gateup, odt_k, p, gemm_grid(units), s));
+  HIPCHK(launch_expert_gemm(adt_k, wf_of(W), W.group_size, gateup, odt_k, mb, p, gemm_grid(units, mb), s));
   return MOE_OK;
 }
 
@@ -506,7 +537,7 @@ moe_status moe_permute(const int32_t *topk_idx, int64_t T, int32_t K, int32_t E,
   CHECK(topk_idx && counts && offsets && sorted_slot && slot_pos, MOE_ERR_ARG,
         "topk_idx, counts, offsets, sorted_slot and slot_pos must be non-NULL");
   TRY(launch_permute(topk_idx, (int)T, K, E, counts, offsets, sorted_slot, slot_pos, at<int32_t>(ws, o_chunk), nullptr,
-                     nullptr, 0, (hipStream_t)stream));
+                     nullptr, MOE_MT_MIN, (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -535,7 +566,7 @@ moe_status moe_experts_forward(const void *z, int32_t z_dtype, int64_t T, int32_
   const int isz = dt_size(inter_dtype);
   Plan pl;
   const bool mf = z_dtype != MOE_F32;
-  const int ntile = max_tiles(TK, E, 0);
+  const int ntile = max_tiles(TK, E);
   const size_t o_tiles = mf ? pl.take((size_t)ntile * 16) : 0;
   const size_t o_tcount = mf ? pl.take(16) : 0;
   const size_t o_h = pl.take((size_t)TK * I * isz);
@@ -552,15 +583,15 @@ moe_status moe_experts_forward(const void *z, int32_t z_dtype, int64_t T, int32_
   if (mf) {
     int4 *tiles = at<int4>(ws, o_tiles);
     int *tc = at<int>(ws, o_tcount);
-    hipLaunchKernelGGL(build_tiles, dim3(1), dim3(256), 0, s, offsets, E, TK, tiles, tc, 0);
+    const int mb = mb_for_routing(TK, E);
+    hipLaunchKernelGGL(build_tiles, dim3(1), dim3(256), 0, s, offsets, E, tiles, tc, 16 * mb);
     HIPCHK(hipGetLastError());
-    const int ub_mc = TK / MOE_MC + (E < TK ? E : TK);
     SegSet gu = segset(aop(z, D, sorted_slot, K, 0), ex->gate, &ex->up, ex->swiglu_limit, true);
-    TRY(run_gemm(z_dtype, ex->gate, true, inter_dtype, gu, nullptr, tiles, tc, E, ub_mc * gu.nblk, h, I, nullptr, 0,
+    TRY(run_gemm(z_dtype, ex->gate, true, inter_dtype, mb, gu, nullptr, 0, 0, tiles, tc, ntile, TK, E, h, I, nullptr,
                  0, s));
     SegSet dn = segset(aop(h, I, nullptr, 1, 0), ex->down, nullptr, 0.f, false);
-    TRY(run_gemm(inter_dtype, ex->down, false, inter_dtype, dn, nullptr, tiles, tc, E, ub_mc * dn.nblk, o, D, nullptr,
-                 0, 0, s));
+    TRY(run_gemm(inter_dtype, ex->down, false, inter_dtype, mb, dn, nullptr, 0, 0, tiles, tc, ntile, TK, E, o, D,
+                 nullptr, 0, s));
   } else {
     F32GemmParams p;
     memset(&p, 0, sizeof p);
@@ -673,7 +704,8 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   const size_t o_ss = pl.take((size_t)TK * 4);
   const size_t o_sp = pl.take((size_t)TK * 4);
   const size_t o_chunk = pl.take(perm_ws_bytes(T, E));
-  const int ntile = max_tiles(TK, E, fuse_shared ? Tsh : 0);
+  const int ntile = max_tiles(TK, E);
+  const int mb = mb_for_routing(TK, E);
   const size_t o_tiles = pl.take((size_t)ntile * 16);
   const size_t o_tc = pl.take(16);
   const size_t o_z = latent ? pl.take((size_t)T * D * isz) : 0;
@@ -710,7 +742,7 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
                   blend ? b->coef_b : nullptr, coef, s));
   // 2. permutation + tile list
   TRY(launch_permute(idx, Ti, K, E, counts, offsets, ss, sp, at<int32_t>(ws, o_chunk), mf ? tiles : nullptr,
-                     mf ? tc : nullptr, fuse_shared ? Tsh : 0, s));
+                     mf ? tc : nullptr, 16 * mb, s));
 
   if (!mf) {
     // ---- f32 path
@@ -761,15 +793,13 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
     return MOE_OK;
   }
 
-  const int ub_mc = TK / MOE_MC + (E < TK ? E : TK);
-  const int sh_mc = (Ti + MOE_MC - 1) / MOE_MC;
   if (!latent) {
     // 3. gate/up (+ SwiGLU) for every slot, shared rows appended
     SegSet gu = segset(aop(x, H, ss, K, 0), b->experts.gate, &b->experts.up, b->experts.swiglu_limit, true);
     SegSet gus;
     if (has_shared) gus = segset(aop(x, H, nullptr, 1, TK), b->shared.gate, &b->shared.up, b->shared.swiglu_limit, true);
-    TRY(run_gemm(x_dtype, b->experts.gate, true, inter, gu, fuse_shared ? &gus : nullptr, tiles, tc, E,
-                 ub_mc * gu.nblk + (fuse_shared ? sh_mc * gus.nblk : 0), h, ldh, nullptr, 0, 0, s));
+    TRY(run_gemm(x_dtype, b->experts.gate, true, inter, mb, gu, fuse_shared ? &gus : nullptr, TK, Tsh, tiles, tc,
+                 ntile, TK, E, h, ldh, nullptr, 0, s));
     if (has_shared && !fuse_shared)
       TRY(run_plain(x_dtype, b->shared.gate, &b->shared.up, b->shared.swiglu_limit, true, inter, x, H, Ti,
                     (char *)h + (size_t)TK * ldh * isz, ldh, nullptr, 0, s));
@@ -777,8 +807,8 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
     SegSet dn = segset(aop(h, ldh, nullptr, 1, 0), b->experts.down, nullptr, 0.f, false);
     SegSet dns;
     if (has_shared) dns = segset(aop(h, ldh, nullptr, 1, 0), b->shared.down, nullptr, 0.f, false);
-    TRY(run_gemm(inter, b->experts.down, false, inter, dn, fuse_shared ? &dns : nullptr, tiles, tc, E,
-                 ub_mc * dn.nblk + (fuse_shared ? sh_mc * dns.nblk : 0), o, D, nullptr, 0, 0, s));
+    TRY(run_gemm(inter, b->experts.down, false, inter, mb, dn, fuse_shared ? &dns : nullptr, TK, Tsh, tiles, tc,
+                 ntile, TK, E, o, D, nullptr, 0, s));
     if (has_shared && !fuse_shared)
       TRY(run_plain(inter, b->shared.down, nullptr, 0.f, false, inter, (char *)h + (size_t)TK * ldh * isz, ldh, Ti,
                     (char *)o + (size_t)TK * D * isz, D, nullptr, 0, s));
@@ -793,10 +823,10 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   void *yn = at<char>(ws, o_yn);
   TRY(run_plain(x_dtype, b->latent_down, nullptr, 0.f, false, inter, x, H, Ti, z, D, nullptr, 0, s));
   SegSet gu = segset(aop(z, D, ss, K, 0), b->experts.gate, &b->experts.up, b->experts.swiglu_limit, true);
-  TRY(run_gemm(inter, b->experts.gate, true, inter, gu, nullptr, tiles, tc, E, ub_mc * gu.nblk, h, ldh, nullptr, 0, 0,
-               s));
+  TRY(run_gemm(inter, b->experts.gate, true, inter, mb, gu, nullptr, 0, 0, tiles, tc, ntile, TK, E, h, ldh, nullptr,
+               0, s));
   SegSet dn = segset(aop(h, ldh, nullptr, 1, 0), b->experts.down, nullptr, 0.f, false);
-  TRY(run_gemm(inter, b->experts.down, false, inter, dn, nullptr, tiles, tc, E, ub_mc * dn.nblk, o, D, nullptr, 0, 0,
+  TRY(run_gemm(inter, b->experts.down, false, inter, mb, dn, nullptr, 0, 0, tiles, tc, ntile, TK, E, o, D, nullptr, 0,
                s));
   TRY(combine(inter, inter, o, D, sp, wts, K, TK, Ti, D, yn, D, nullptr, b->latent_norm_w, b->norm_eps,
               b->latent_norm_w ? 1 : 0, s));

@@ -8,19 +8,23 @@
 //           libmir-metal's gate/up kernel, read as a clamp of both to [-L, L])
 //   LINEAR: o = W a + b (+ an f32 residual)      (down projections, latent maps)
 //
-// Work unit = (m-chunk of up to 64 rows of one segment, block of output columns).
-// A 256-thread workgroup (4 waves) stages the chunk's activation rows in LDS,
-// 256 reduction elements at a time; every wave streams its own weight rows
-// straight from HBM into registers, dequantises them there, and feeds
-// v_mfma_f32_16x16x32_{bf16,f16} (tokens = A operand, weight rows = B operand).
+// Work unit = (m-tile of up to 16*MB activation rows of one segment, block of
+// output columns).  A 256-thread workgroup (4 waves) stages the m-tile's rows in
+// LDS one reduction chunk at a time; each wave streams its own 32 weight rows from
+// HBM and feeds v_mfma_f32_16x16x32_{bf16,f16} with tokens as the A operand and
+// weight rows as the B operand (two 16-row halves per wave).
 //
 // Weight formats (see moe_linear in include/moe.h):
 //   AFFINE4 (mlxcel issue #974's affine gather_qmm plane): a nibble q becomes the
-//     16-bit value MAGIC+q by OR-ing it into the mantissa of MAGIC (128 in bf16,
-//     1024 in f16); that is exact, so each MFMA over one quantisation group sums
-//     (MAGIC+q)*a exactly-rounded in fp32, and the group is folded in fp32 as
-//       acc += scale * S_g + (qbias - MAGIC*scale) * sum_g(a)
-//     which equals sum (scale*q + qbias)*a without rounding the weights.
+//     16-bit value MAGIC+q by OR-ing it into the mantissa of MAGIC, which is exact.
+//     Decode tiles (MB == 1) keep it that way and fold every quantisation group in
+//     fp32:  acc += scale * sum((MAGIC+q) a) + (qbias - MAGIC*scale) * sum(a),
+//     which equals sum (scale*q + qbias) a with the weights never rounded; the
+//     group sums of a come from one extra MFMA against a vector of ones.
+//     Prefill tiles (MB > 1) dequantise instead: one mixed-precision FMA per weight
+//     gives scale*(1024+q) + (qbias - 1024*scale) in fp32, rounded once to the
+//     MFMA's 16-bit type; the per-group fold would cost VALU in proportion to the
+//     tile height, the dequantisation only per weight.
 //     The nibble pairs come out as (q_i, q_{i+4}), so the activation rows are
 //     staged with the matching element order inside every 8-element block.
 //   MXFP4 (libmir-metal ExpertLayout blocks/scales): gfx950's scaled FP4
@@ -31,6 +35,8 @@
 
 namespace {
 
+// 16x16x32 MFMA: lane l holds A[m = l%16][k = 8*(l/16) .. +8), B[k = 8*(l/16) .. +8][n = l%16]
+// and D[m = 4*(l/16) + i][n = l%16], i = 0..3.
 template <int AT>
 MOE_DEV f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
   if constexpr (AT == DT_BF16)
@@ -41,19 +47,46 @@ MOE_DEV f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                   0, 0, 0);
 }
 
-// 8 nibbles (element i in bits 4i..4i+3) -> 4 words holding (MAGIC+q_i, MAGIC+q_{i+4}), i = 0..3
-template <int AT>
-MOE_DEV u32x4_t cvt_affine(uint32_t w) {
-  constexpr uint32_t M = (AT == DT_BF16) ? 0x43004300u : 0x64006400u;
+// a constant the compiler must keep in a VGPR (so that mask-and-or with two constants is one v_and_or_b32)
+MOE_DEV uint32_t in_vgpr(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// 8 nibbles (element i in bits 4i..4i+3) -> 4 words holding (mag+q_i, mag+q_{i+4}), i = 0..3
+MOE_DEV u32x4_t magic_pairs(uint32_t w, uint32_t msk, uint32_t mag) {
   u32x4_t r;
-  r[0] = (w & 0x000F000Fu) | M;
-  r[1] = ((w >> 4) & 0x000F000Fu) | M;
-  r[2] = ((w >> 8) & 0x000F000Fu) | M;
-  r[3] = ((w >> 12) & 0x000F000Fu) | M;
+  r[0] = (w & msk) | mag;
+  r[1] = ((w >> 4) & msk) | mag;
+  r[2] = ((w >> 8) & msk) | mag;
+  r[3] = ((w >> 12) & msk) | mag;
   return r;
 }
 
-// activation block (e0..e7) -> (e0,e4),(e1,e5),(e2,e6),(e3,e7): the order of cvt_affine
+MOE_DEV float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+MOE_DEV float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// 8 nibbles -> 4 words of dequantised (w_i, w_{i+4}) in the MFMA type; w = sc*(1024+q) + c,
+// c = qbias - 1024*sc (one fp32 FMA from the exact f16 1024+q, one rounding to 16 bits)
+template <int AT>
+MOE_DEV u32x4_t deq_affine(uint32_t w, uint32_t msk, uint32_t mag16, float sc, float c) {
+  const u32x4_t m = magic_pairs(w, msk, mag16);
+  u32x4_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = fmaf(f16lo(m[j]), sc, c), hi = fmaf(f16hi(m[j]), sc, c);
+    if constexpr (AT == DT_BF16) {
+      const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+      r[j] = __builtin_bit_cast(uint32_t, v);
+    } else {
+      r[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+    }
+  }
+  return r;
+}
+
+// activation block (e0..e7) -> (e0,e4),(e1,e5),(e2,e6),(e3,e7): the order of magic_pairs
 MOE_DEV u32x4_t pair_i_i4(u32x4_t v) {
   u32x4_t o;
   o[0] = (v[0] & 0xFFFFu) | (v[2] << 16);
@@ -103,92 +136,78 @@ MOE_DEV u32x4_t cvt_dense(u32x4_t w) {
 
 }  // namespace
 
-// 32x32x16 MFMA: lane l holds A[m = l%32][k = 8*(l/32) .. +8), B[k = 8*(l/32) .. +8][n = l%32]
-// and D[m = 8*(i/4) + 4*(l/32) + i%4][n = l%32], i = 0..15.
-template <int AT>
-MOE_DEV f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
-  if constexpr (AT == DT_BF16)
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                   c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
-                                                  0, 0, 0);
-}
-
-// Work unit: (m-chunk of up to 32 rows of one segment, block of output columns).
-// Every wave owns one 32-row weight tile (GATEUP: 16 gate rows and the 16 up rows of
-// the same columns; LINEAR: 32 output rows).  Tokens are the MFMA's A operand and
-// weight rows its B operand, so every lane of a tile holds a single weight row.
+// Every wave owns one 32-row weight tile: GATEUP: 16 gate rows (half 0) and the 16 up
+// rows of the same columns (half 1); LINEAR: 32 output rows.  Lane l works on tile rows
+// l%16 and 16 + l%16 and on the m-tile's tokens 16*mb + l%16 (A) / 16*mb + 4*(l/16) + i (D).
 //
-// Weight stream: per chunk each tile row contributes one contiguous 128-byte
-// segment; a wave fetches its 4 KB with 16-byte loads, 8 lanes per row (whole
-// cache lines, no partial requests), two chunks ahead of the MFMAs, and writes them
-// into its own LDS tile with the 16-byte blocks of each row XOR-swizzled so that
-// the MFMA-layout reads (32 rows, same column) spread over the banks.
-// Scales/qbias (AFFINE4) or E8M0 exponents (MXFP4) of the tile's rows are copied
-// to LDS once per unit with contiguous loads.
+// Weight stream: per chunk each tile row contributes one contiguous 128-byte segment; a
+// wave fetches its 4 KB with 16-byte loads, 8 lanes per row (whole cache lines), two
+// chunks ahead of the MFMAs, and writes them into its own LDS tile with the 16-byte
+// blocks of each row XOR-swizzled so that the MFMA-layout reads spread over the banks.
+// Scales/qbias (AFFINE4, one word per group: scale | qbias << 16) or E8M0 exponents
+// (MXFP4, one byte per block) of the tile's rows are copied to LDS once per unit.
 //
-// Reduction order inside a weight row: a "unit" of UE elements is split between
-// the two half-waves (UE/2 contiguous elements each); MFMA step s of the unit uses
-// elements [s*8, s*8+8) of each half.  For AFFINE4 a unit is one quantisation
-// group, so each step stays inside one group and the exact fold applies per group.
-template <int AT, int WF, int GQ, bool GATEUP, int OT>
-__global__ __launch_bounds__(MOE_GEMM_THREADS, 3) void expert_gemm(const GemmParams p) {
+// Reduction order: a "unit" of UE elements (AFFINE4: one quantisation group; MXFP4: 64; DENSE: 32)
+// is split into four contiguous quarters, one per lane quarter l/16; MFMA step s of the
+// unit takes elements [8s, 8s+8) of every quarter, so each step stays inside one group.
+template <int AT, int WF, int GQ, bool GATEUP, int OT, int MB>
+__global__ __launch_bounds__(MOE_GEMM_THREADS, MB == 1 ? 3 : 2) void expert_gemm(const GemmParams p) {
   constexpr bool AFF = (WF == WF_AFFINE4);
   constexpr bool MX = (WF == WF_MXFP4);
   constexpr bool DENSE = (WF == WF_DENSE);
-  constexpr int UE = AFF ? GQ : (MX ? 64 : 32);            // elements per unit (both halves)
-  constexpr int SPU = UE / 16;                             // MFMA steps per unit
-  constexpr int LB = DENSE ? UE : UE / 4;                  // bytes per lane per unit
+  constexpr bool FOLD = AFF && MB == 1;                    // exact group fold; else dequantise
+  constexpr int MT = 16 * MB;                              // rows per m-tile
+  constexpr int UE = AFF ? GQ : (MX ? 64 : 32);            // elements per unit
+  constexpr int SPU = UE / 32;                             // MFMA steps per unit
+  constexpr int QE = UE / 4;                               // elements per lane quarter per unit
+  constexpr int LB = DENSE ? 2 * QE : QE / 2;              // weight bytes per lane, unit and half
   constexpr int KC = DENSE ? 64 : MOE_KC;                  // reduction elements per chunk (128 B per row)
   constexpr int NU = KC / UE;                              // units per chunk
   constexpr int BPR = KC / 8;                              // 8-element activation blocks per chunk row
   constexpr int RPI = MOE_GEMM_THREADS / BPR;              // activation rows staged per iteration
-  constexpr int SIT = (MOE_MC + RPI - 1) / RPI;            // activation staging iterations
+  constexpr int SIT = (MT + RPI - 1) / RPI;                // activation staging iterations
   constexpr int LDA = KC + 8;                              // padded LDS activation row (16-bit elements)
-  constexpr float MAGIC = (AT == DT_BF16) ? 128.0f : 1024.0f;
-  static_assert(MOE_MC == 32, "one 32-row m-tile per chunk");
+  constexpr float MAGIC = (FOLD && AT == DT_BF16) ? 128.0f : 1024.0f;
   static_assert((DENSE ? KC * 2 : KC / 2) == 128, "128-byte row segments per chunk");
-  __shared__ __attribute__((aligned(16))) uint16_t sA[MOE_MC * LDA];
-  __shared__ int64_t sRow[MOE_MC];
+  static_assert(KC % UE == 0 && UE % 32 == 0, "units of whole MFMA steps");
+  __shared__ __attribute__((aligned(16))) uint16_t sA[MT * LDA];
+  __shared__ int64_t sRow[MT];
   extern __shared__ __attribute__((aligned(16))) char dyn[];  // per wave: weight tile + scale strip
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r32 = lane & 31, kb = lane >> 5;
+  const int n16 = lane & 15, kq = lane >> 4;
   const int sblk = tid % BPR, srow0 = tid / BPR;
   char *wlds = dyn + wave * p.wave_lds;                    // 32 x 128 B weight tile
-  char *slds = wlds + 4096;                                // scale strip(s)
+  char *slds = wlds + 4096;                                // scale strip [32][strip_row]
+  const uint32_t msk = in_vgpr(0x000F000Fu);
+  const uint32_t mag = in_vgpr((FOLD && AT == DT_BF16) ? 0x43004300u : 0x64006400u);
 
-  int nr_routed, nr_shared;
-  if (p.tiles) {
-    nr_routed = p.tile_count[0];
-    nr_shared = p.tile_count[1];
-  } else {
-    nr_routed = 0;
-    nr_shared = (p.plain_rows + MOE_MC - 1) / MOE_MC;
-  }
-  const int units_r = nr_routed * p.seg[0].nblk;
-  const int total = units_r + nr_shared * p.seg[1].nblk;
+  // units: segment 1 (shared expert / plain rows, m-tiles computed here) first, then the
+  // routed m-tiles of the tile list
+  const int nblk0 = p.seg[0].nblk, nblk1 = max(p.seg[1].nblk, 1);
+  const int ns = p.seg[1].nblk > 0 ? (p.sh_rows + MT - 1) / MT : 0;
+  const int units_s = ns * nblk1;
+  const int nr_routed = p.tiles ? p.tile_count[0] : 0;
 
-  for (int u = blockIdx.x; u < total; u += gridDim.x) {
-    const bool sh = u >= units_r;
+  for (int u = blockIdx.x;; u += gridDim.x) {
+    const bool sh = u < units_s;
     int ti, nb;
-    if (!sh) {
-      ti = u / p.seg[0].nblk;
-      nb = u - ti * p.seg[0].nblk;
-    } else {
-      const int v = u - units_r;
-      const int q = v / p.seg[1].nblk;
-      nb = v - q * p.seg[1].nblk;
-      ti = nr_routed + q;
-    }
     int4 tile;
-    if (p.tiles)
-      tile = p.tiles[ti];
-    else
-      tile = make_int4(p.E, ti * MOE_MC, min(MOE_MC, p.plain_rows - ti * MOE_MC), 0);
+    if (sh) {
+      ti = u / nblk1;
+      nb = u - ti * nblk1;
+      tile = make_int4(0, p.sh_row0 + ti * MT, min(MT, p.sh_rows - ti * MT), 0);
+    } else {
+      const int v = u - units_s;
+      ti = v / max(nblk0, 1);
+      nb = v - ti * nblk0;
+      if (!p.tiles) break;
+      tile = p.tiles[min(ti, p.max_tiles - 1)];  // in bounds even past the end of the list
+      if (ti >= nr_routed) break;
+    }
     const int e = sh ? 0 : tile.x;
     const int r0 = tile.y, nr = tile.z;
+    const int nmb = (nr + 15) >> 4;               // 16-row blocks of the m-tile that hold rows
 
 #define SF(f) (sh ? p.seg[1].f : p.seg[0].f)
     const uint16_t *Ab = (const uint16_t *)SF(A.a);
@@ -196,6 +215,7 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, 3) void expert_gemm(const GemmPar
     const int32_t *gat = SF(A.gather);
     const int gdiv = SF(A.gdiv), rsub = SF(A.row_sub);
     const int Kd = SF(K);
+    const int svec = SF(svec);
     const float limit = SF(limit);
     const WMat W0 = sh ? p.seg[1].w0 : p.seg[0].w0;
     const WMat W1 = GATEUP ? (sh ? p.seg[1].w1 : p.seg[0].w1) : W0;
@@ -208,7 +228,6 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, 3) void expert_gemm(const GemmPar
     auto row_ok = [&](int t) { return row_of(t) < W0.rows; };
     auto mat_of = [&](int t) -> const WMat & { return (GATEUP && t >= 16) ? W1 : W0; };
     const int nchunks = (Kd + KC - 1) / KC;
-    const int nib = min(4, (nr + 7) >> 3);       // 8-row blocks of the m-tile that hold rows
 
     // this lane's loader rows (tile rows 8*i + lane/8) and their segment base pointers
     const char *lrow[4];
@@ -230,7 +249,7 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, 3) void expert_gemm(const GemmPar
 #pragma unroll
       for (int i = 0; i < 4; ++i) g[i] = *(const u32x4_t *)(lrow[i] + o2);
     };
-    load_w(0, gA);  // in flight during the setup below
+    load_w(0, gA);  // in flight during the set-up below
     load_w(KC, gB);
 
     __syncthreads();  // the previous unit is done with sRow / sA / the LDS tiles
@@ -239,41 +258,51 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, 3) void expert_gemm(const GemmPar
       sRow[tid] = arow * lda;
     }
 
-    // ---- scale strips -> LDS (once per unit): AFF: [32][G] bf16 scales then [32][G] qbias;
-    //      MX: [32][NB] e8m0 bytes.  Row t of a strip belongs to tile row t.
+    // ---- scale strips -> LDS (once per unit).  Row t of the strip belongs to tile row t.
+    //      AFF: entry g = scale_g | qbias_g << 16 (4 bytes);  MX: entry b = e8m0 byte.
     if constexpr (AFF || MX) {
-      const int G = AFF ? Kd / UE : Kd / 32;         // entries per row
-      const int esz = AFF ? 2 : 1;
-      const int rowb = G * esz;                      // bytes per strip row in LDS (unpadded)
-      const int nstrip = AFF ? 2 : 1;
-      // lanes walk the strip rows with 2-byte loads: lane -> (row offset, entry pair)
-      const int EPR = (rowb + 1) / 2;                // 2-byte words per row
-      int epp = 1;
-      while (epp < EPR) epp <<= 1;                   // <= 64 (checked on the host)
-      const int rps = 64 / epp;                      // rows per pass
-      for (int sidx = 0; sidx < nstrip; ++sidx) {
-        for (int t0 = 0; t0 < 32; t0 += 8 * rps) {
-          uint16_t v[8];
+      const int G = AFF ? Kd / GQ : Kd / 32;          // entries per row
+      const int per = svec ? (AFF ? 2 : 4) : 1;       // entries per load
+      const int npr = G / per;                        // loads per row
+      const int total = 32 * npr;
+      for (int i0 = 0; i0 < total; i0 += 64 * 8) {
+        uint32_t vs[8], vq[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int t = t0 + i * rps + lane / epp;
-            const int w = lane % epp;
-            v[i] = 0;
-            if (t < 32 && w < EPR) {
-              const WMat &M = mat_of(t);
-              const int64_t rr = row_ok(t) ? row_of(t) : 0;
-              const uint16_t *src = (const uint16_t *)((const char *)(sidx ? M.qbias : M.scales) +
-                                                       ((int64_t)e * M.s_stride + rr * M.lds) * esz);
-              v[i] = (esz == 2 || (rowb & 1) == 0 || w < EPR - 1)
-                         ? src[w]
-                         : (uint16_t)((const uint8_t *)src)[2 * w];
-            }
+        for (int k = 0; k < 8; ++k) {
+          const int idx = min(i0 + 64 * k + lane, total - 1);
+          const int t = idx / npr, j = idx - t * npr;
+          const WMat &M = mat_of(t);
+          const int64_t rr = row_ok(t) ? row_of(t) : 0;
+          const int64_t ent = (int64_t)e * M.s_stride + rr * M.lds + (int64_t)j * per;
+          if constexpr (AFF) {
+            const uint16_t *sp = (const uint16_t *)M.scales + ent, *qp = (const uint16_t *)M.qbias + ent;
+            vs[k] = svec ? *(const uint32_t *)sp : (uint32_t)*sp;
+            vq[k] = svec ? *(const uint32_t *)qp : (uint32_t)*qp;
+          } else {
+            const uint8_t *sp = (const uint8_t *)M.scales + ent;
+            vs[k] = svec ? *(const uint32_t *)sp : (uint32_t)*sp;
+            vq[k] = 0;
           }
+        }
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int t = t0 + i * rps + lane / epp;
-            const int w = lane % epp;
-            if (t < 32 && w < EPR) *(uint16_t *)(slds + sidx * 32 * p.strip_row + t * p.strip_row + 2 * w) = v[i];
+        for (int k = 0; k < 8; ++k) {
+          const int idx = i0 + 64 * k + lane;
+          if (idx < total) {
+            const int t = idx / npr, j = idx - t * npr;
+            char *dst = slds + t * p.strip_row;
+            if constexpr (AFF) {
+              if (svec) {
+                const u32x2_t v = {(vs[k] & 0xFFFFu) | (vq[k] << 16), (vs[k] >> 16) | (vq[k] & 0xFFFF0000u)};
+                *(u32x2_t *)(dst + 8 * j) = v;
+              } else {
+                *(uint32_t *)(dst + 4 * j) = vs[k] | (vq[k] << 16);
+              }
+            } else {
+              if (svec)
+                *(uint32_t *)(dst + 4 * j) = vs[k];
+              else
+                dst[j] = (char)vs[k];
+            }
           }
         }
       }
@@ -320,80 +349,91 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, 3) void expert_gemm(const GemmPar
       }
     };
 
-    f32x16_t acc;
+    f32x4_t acc[MB][2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[mb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const char *my_w = wlds + r32 * 128;
-    const int my_sw = (r32 >> 1) & 7;
     auto compute = [&](int kc) {
       if (!act) return;
       const int nunits = min(KC, Kd - kc) / UE;
 #pragma unroll
       for (int uu = 0; uu < NU; ++uu) {
         if (uu >= nunits) break;
-        // this lane's LB bytes of the unit: byte offset (UE*uu + UE/2*kb) * bytes-per-element
-        const int boff = DENSE ? (UE * uu + (UE / 2) * kb) * 2 : (UE * uu + (UE / 2) * kb) / 2;
-        uint32_t wv[LB / 4];
-        if constexpr (LB == 8) {
-          const int blk = boff >> 4;
-          const u32x2_t a = *(const u32x2_t *)(my_w + 16 * (blk ^ my_sw) + (boff & 15));
-          wv[0] = a[0];
-          wv[1] = a[1];
+        const int eoff = uu * UE + kq * QE;          // first element of this lane's quarter
+        const int boff = DENSE ? eoff * 2 : eoff / 2;
+        uint32_t wv[2][LB / 4];
+        float sc[2], cc[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int t = 16 * h + n16;
+          const char *rowp = wlds + t * 128;
+          const int sw = (t >> 1) & 7;
+          if constexpr (LB == 4) {
+            wv[h][0] = *(const uint32_t *)(rowp + 16 * ((boff >> 4) ^ sw) + (boff & 15));
+          } else if constexpr (LB == 8) {
+            const u32x2_t a = *(const u32x2_t *)(rowp + 16 * ((boff >> 4) ^ sw) + (boff & 15));
+            wv[h][0] = a[0];
+            wv[h][1] = a[1];
+          } else {
+#pragma unroll
+            for (int q = 0; q < LB / 16; ++q) {
+              const u32x4_t a = *(const u32x4_t *)(rowp + 16 * (((boff >> 4) + q) ^ sw));
+#pragma unroll
+              for (int i = 0; i < 4; ++i) wv[h][4 * q + i] = a[i];
+            }
+          }
+          if constexpr (AFF) {
+            const uint32_t v = *(const uint32_t *)(slds + t * p.strip_row + 4 * (kc / GQ + uu));
+            sc[h] = __uint_as_float(v << 16);
+            cc[h] = fmaf(-MAGIC, sc[h], __uint_as_float(v & 0xFFFF0000u));
+          } else if constexpr (MX) {
+            sc[h] = e8m0_to_f32(*(const uint8_t *)(slds + t * p.strip_row + (kc >> 5) + 2 * uu + (kq >> 1)));
+            cc[h] = 0.f;
+          } else {
+            sc[h] = cc[h] = 0.f;
+          }
+        }
+        const uint16_t *arow = &sA[n16 * LDA + eoff];
+        if constexpr (FOLD) {
+          // MB == 1: gate/up (or two row halves) share the A fragment and the group sums
+          constexpr uint32_t ONE2 = (AT == DT_BF16) ? 0x3F803F80u : 0x3C003C00u;  // (1.0, 1.0)
+          const u32x4_t ones = {ONE2, ONE2, ONE2, ONE2};
+          const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+          f32x4_t g0 = z, g1 = z, sx = z;
+#pragma unroll
+          for (int s = 0; s < SPU; ++s) {
+            const u32x4_t av = *(const u32x4_t *)(arow + 8 * s);
+            g0 = mfma16<AT>(av, magic_pairs(wv[0][s], msk, mag), g0);
+            g1 = mfma16<AT>(av, magic_pairs(wv[1][s], msk, mag), g1);
+            sx = mfma16<AT>(av, ones, sx);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[0][0][i] = fmaf(sc[0], g0[i], fmaf(cc[0], sx[i], acc[0][0][i]));
+            acc[0][1][i] = fmaf(sc[1], g1[i], fmaf(cc[1], sx[i], acc[0][1][i]));
+          }
         } else {
 #pragma unroll
-          for (int h = 0; h < LB / 16; ++h) {
-            const int blk = (boff >> 4) + h;
-            const u32x4_t a = *(const u32x4_t *)(my_w + 16 * (blk ^ my_sw));
+          for (int s = 0; s < SPU; ++s) {
+            u32x4_t b[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wv[4 * h + i] = a[i];
-          }
-        }
-        float sc = 0.f, qb = 0.f;
-        if constexpr (AFF) {
-          const int g = kc / UE + uu;
-          sc = bf16_bits_to_f32(*(const uint16_t *)(slds + r32 * p.strip_row + 2 * g));
-          qb = bf16_bits_to_f32(*(const uint16_t *)(slds + 32 * p.strip_row + r32 * p.strip_row + 2 * g));
-        } else if constexpr (MX) {
-          sc = e8m0_to_f32(*(const uint8_t *)(slds + r32 * p.strip_row + (kc >> 5) + 2 * uu + kb));
-        }
-        f32x16_t accg, accx;  // AFF: sum of (MAGIC+q)*a and of a over the unit (one group)
-#pragma unroll
-        for (int s = 0; s < SPU; ++s) {
-          u32x4_t bfr;
-          if constexpr (AFF)
-            bfr = cvt_affine<AT>(wv[s]);
-          else if constexpr (MX)
-            bfr = cvt_mxfp4<AT>(wv[s], sc);
-          else
-            bfr = cvt_dense<AT>(u32x4_t{wv[4 * s], wv[4 * s + 1], wv[4 * s + 2], wv[4 * s + 3]});
-          const int blk8 = uu * (UE / 8) + kb * (UE / 16) + s;
-          const u32x4_t av = *(const u32x4_t *)&sA[r32 * LDA + blk8 * 8];
-          if constexpr (AFF) {
-            constexpr uint32_t ONE2 = (AT == DT_BF16) ? 0x3F803F80u : 0x3C003C00u;  // (1.0, 1.0)
-            const u32x4_t ones = {ONE2, ONE2, ONE2, ONE2};
-            if (s == 0) {
-              f32x16_t z;
-#pragma unroll
-              for (int i = 0; i < 16; ++i) z[i] = 0.f;
-              accg = mfma32<AT>(av, bfr, z);
-              accx = mfma32<AT>(av, ones, z);
-            } else {
-              accg = mfma32<AT>(av, bfr, accg);
-              accx = mfma32<AT>(av, ones, accx);
+            for (int h = 0; h < 2; ++h) {
+              if constexpr (AFF)
+                b[h] = deq_affine<AT>(wv[h][s], msk, mag, sc[h], cc[h]);
+              else if constexpr (MX)
+                b[h] = cvt_mxfp4<AT>(wv[h][s], sc[h]);
+              else
+                b[h] = cvt_dense<AT>(u32x4_t{wv[h][4 * s], wv[h][4 * s + 1], wv[h][4 * s + 2], wv[h][4 * s + 3]});
             }
-          } else {
-            acc = mfma32<AT>(av, bfr, acc);
-          }
-        }
-        if constexpr (AFF) {
-          const float c_ = fmaf(-MAGIC, sc, qb);
 #pragma unroll
-          for (int ib = 0; ib < 4; ++ib) {
-            if (ib < nib) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                acc[4 * ib + j] = fmaf(sc, accg[4 * ib + j], fmaf(c_, accx[4 * ib + j], acc[4 * ib + j]));
+            for (int mb = 0; mb < MB; ++mb) {
+              if (MB == 1 || mb < nmb) {
+                const u32x4_t av = *(const u32x4_t *)(arow + mb * 16 * LDA + 8 * s);
+                acc[mb][0] = mfma16<AT>(av, b[0], acc[mb][0]);
+                acc[mb][1] = mfma16<AT>(av, b[1], acc[mb][1]);
+              }
             }
           }
         }
@@ -420,29 +460,42 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, 3) void expert_gemm(const GemmPar
       chunk(c + 2, gC, gB);
     }
 
-    // ---- epilogue: acc[4*ib + j] is row 8*ib + 4*kb + j of the m-chunk, tile row r32
+    // ---- epilogue: acc[mb][h][i] is token 16*mb + 4*kq + i of the m-tile, tile row 16*h + n16
     if (act) {
-      const bool lane_ok = row_ok(r32);
-      const int wrow_i = row_of(r32);
-      const WMat &M = mat_of(r32);
-      const float bo =
-          (lane_ok && M.bias) ? bf16_bits_to_f32(((const uint16_t *)M.bias)[(int64_t)e * M.rows + wrow_i]) : 0.f;
+      float bo[2];
+      bool ok[2];
+      int wrow[2];
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
-        if (ib < nib) {
+      for (int h = 0; h < 2; ++h) {
+        const int t = 16 * h + n16;
+        const WMat &M = mat_of(t);
+        ok[h] = row_ok(t);
+        wrow[h] = row_of(t);
+        bo[h] = (ok[h] && M.bias) ? bf16_bits_to_f32(((const uint16_t *)M.bias)[(int64_t)e * M.rows + wrow[h]]) : 0.f;
+      }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int m = 8 * ib + 4 * kb + j;
-            float v = acc[4 * ib + j] + bo;
-            if constexpr (GATEUP) {
-              if (limit > 0.f) v = fminf(fmaxf(v, -limit), limit);
-              const float up = __shfl_xor(v, 16, 64);   // lanes r32 >= 16 hold the up rows
-              if (r32 < 16 && m < nr)
-                store_act<OT>(p.out, (int64_t)(r0 + m) * p.ldo + col0 + r32, silu_f(v) * up);
-            } else {
-              if (lane_ok && m < nr) {
-                if (p.resid) v += p.resid[(int64_t)(r0 + m) * p.ldr + wrow_i];
-                store_act<OT>(p.out, (int64_t)(r0 + m) * p.ldo + wrow_i, v);
+      for (int mb = 0; mb < MB; ++mb) {
+        if (MB == 1 || mb < nmb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = 16 * mb + 4 * kq + i;
+            if (m < nr) {
+              if constexpr (GATEUP) {
+                float g = acc[mb][0][i] + bo[0], up = acc[mb][1][i] + bo[1];
+                if (limit > 0.f) {
+                  g = fminf(fmaxf(g, -limit), limit);
+                  up = fminf(fmaxf(up, -limit), limit);
+                }
+                if (ok[0]) store_act<OT>(p.out, (int64_t)(r0 + m) * p.ldo + wrow[0], silu_f(g) * up);
+              } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                  if (ok[h]) {
+                    float v = acc[mb][h][i] + bo[h];
+                    if (p.resid) v += p.resid[(int64_t)(r0 + m) * p.ldr + wrow[h]];
+                    store_act<OT>(p.out, (int64_t)(r0 + m) * p.ldo + wrow[h], v);
+                  }
+                }
               }
             }
           }
@@ -498,42 +551,48 @@ __global__ __launch_bounds__(64) void f32_gemm_kernel(const F32GemmParams p) {
 // host-side dispatch
 // ---------------------------------------------------------------------------
 template <int AT, int WF, int GQ, bool GU, int OT>
-static hipError_t launch_t(const GemmParams &p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((expert_gemm<AT, WF, GQ, GU, OT>), dim3(grid), dim3(MOE_GEMM_THREADS),
-                     (size_t)p.wave_lds * (MOE_GEMM_THREADS / 64), s, p);
+static hipError_t launch_t(int mb, const GemmParams &p, int grid, hipStream_t s) {
+  const size_t dyn = (size_t)p.wave_lds * (MOE_GEMM_THREADS / 64);
+  if (mb == 1)
+    hipLaunchKernelGGL((expert_gemm<AT, WF, GQ, GU, OT, 1>), dim3(grid), dim3(MOE_GEMM_THREADS), dyn, s, p);
+  else if (mb == 4)
+    hipLaunchKernelGGL((expert_gemm<AT, WF, GQ, GU, OT, 4>), dim3(grid), dim3(MOE_GEMM_THREADS), dyn, s, p);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 template <int AT, int WF, int GQ>
-static hipError_t launch_o(bool gateup, int odt, const GemmParams &p, int grid, hipStream_t s) {
+static hipError_t launch_o(bool gateup, int odt, int mb, const GemmParams &p, int grid, hipStream_t s) {
   if (gateup) {
-    if (odt == DT_BF16) return launch_t<AT, WF, GQ, true, DT_BF16>(p, grid, s);
-    if (odt == DT_F16) return launch_t<AT, WF, GQ, true, DT_F16>(p, grid, s);
+    if (odt == DT_BF16) return launch_t<AT, WF, GQ, true, DT_BF16>(mb, p, grid, s);
+    if (odt == DT_F16) return launch_t<AT, WF, GQ, true, DT_F16>(mb, p, grid, s);
   } else {
-    if (odt == DT_F32) return launch_t<AT, WF, GQ, false, DT_F32>(p, grid, s);
-    if (odt == DT_BF16) return launch_t<AT, WF, GQ, false, DT_BF16>(p, grid, s);
-    if (odt == DT_F16) return launch_t<AT, WF, GQ, false, DT_F16>(p, grid, s);
+    if (odt == DT_F32) return launch_t<AT, WF, GQ, false, DT_F32>(mb, p, grid, s);
+    if (odt == DT_BF16) return launch_t<AT, WF, GQ, false, DT_BF16>(mb, p, grid, s);
+    if (odt == DT_F16) return launch_t<AT, WF, GQ, false, DT_F16>(mb, p, grid, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <int AT>
-static hipError_t launch_w(int wfmt, int group, bool gateup, int odt, const GemmParams &p, int grid, hipStream_t s) {
-  if (wfmt == WF_DENSE) return launch_o<AT, WF_DENSE, 0>(gateup, odt, p, grid, s);
-  if (wfmt == WF_MXFP4) return launch_o<AT, WF_MXFP4, 0>(gateup, odt, p, grid, s);
+static hipError_t launch_w(int wfmt, int group, bool gateup, int odt, int mb, const GemmParams &p, int grid,
+                           hipStream_t s) {
+  if (wfmt == WF_DENSE) return launch_o<AT, WF_DENSE, 0>(gateup, odt, mb, p, grid, s);
+  if (wfmt == WF_MXFP4) return launch_o<AT, WF_MXFP4, 0>(gateup, odt, mb, p, grid, s);
   if (wfmt == WF_AFFINE4) {
-    if (group == 32) return launch_o<AT, WF_AFFINE4, 32>(gateup, odt, p, grid, s);
-    if (group == 64) return launch_o<AT, WF_AFFINE4, 64>(gateup, odt, p, grid, s);
-    if (group == 128) return launch_o<AT, WF_AFFINE4, 128>(gateup, odt, p, grid, s);
+    if (group == 32) return launch_o<AT, WF_AFFINE4, 32>(gateup, odt, mb, p, grid, s);
+    if (group == 64) return launch_o<AT, WF_AFFINE4, 64>(gateup, odt, mb, p, grid, s);
+    if (group == 128) return launch_o<AT, WF_AFFINE4, 128>(gateup, odt, mb, p, grid, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_expert_gemm(int adt, int wfmt, int group, bool gateup, int odt, const GemmParams &p, int grid,
-                              hipStream_t s) {
+hipError_t launch_expert_gemm(int adt, int wfmt, int group, bool gateup, int odt, int mb, const GemmParams &p,
+                              int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (adt == DT_BF16) return launch_w<DT_BF16>(wfmt, group, gateup, odt, p, grid, s);
-  if (adt == DT_F16) return launch_w<DT_F16>(wfmt, group, gateup, odt, p, grid, s);
+  if (adt == DT_BF16) return launch_w<DT_BF16>(wfmt, group, gateup, odt, mb, p, grid, s);
+  if (adt == DT_F16) return launch_w<DT_F16>(wfmt, group, gateup, odt, mb, p, grid, s);
   return hipErrorInvalidValue;
 }
 

@@ -5,7 +5,7 @@
 
 #define MOE_MAX_EXPERTS 512  // router top-k keeps 8 experts per lane of a wave64
 #define MOE_MAX_TOPK 32      // chosen experts live one per lane (K <= 32)
-#define MOE_MC 32            // rows (slots or tokens) per m-chunk of the grouped GEMM
+#define MOE_MT_MIN 16        // smallest m-tile (rows of one segment per work unit) of the grouped GEMM
 #define MOE_KC 256           // reduction elements per chunk for 4-bit weights (128 B per row)
 #define MOE_GEMM_THREADS 256 // 4 waves
 
@@ -52,19 +52,21 @@ struct SegSet {
   float limit;          // GATEUP clamp (<= 0: none)
   int K;                // reduction length
   int nblk;             // column blocks of the output
+  int svec;             // scale entries load as aligned 4-byte words (AFFINE4 pairs, MXFP4 quads)
 };
 
 struct GemmParams {
-  SegSet seg[2];        // [0] routed experts (tile.x < E), [1] shared / plain (tile.x == E)
-  const int4 *tiles;    // m-chunk list, or nullptr for a plain GEMM over plain_rows rows
-  const int *tile_count;// [2]: routed chunks, shared chunks
-  int plain_rows;
+  SegSet seg[2];        // [0] routed experts (m-tiles from the tile list), [1] shared expert / plain rows
+  const int4 *tiles;    // routed m-tiles (expert, first sorted row, rows), or nullptr
+  const int *tile_count;// [0]: routed m-tiles in the list
+  int max_tiles;        // entries allocated in tiles (loads are clamped into them)
+  int sh_row0, sh_rows; // segment 1: first row (in the sorted-row numbering of out) and row count
   int E;
   void *out;
   int64_t ldo;
   const float *resid;   // LINEAR: optional f32 [rows][ldr] added before the store
   int64_t ldr;
-  int wave_lds;         // dynamic LDS bytes per wave: 4 KB weight tile + scale strips
+  int wave_lds;         // dynamic LDS bytes per wave: 4 KB weight tile + scale strip
   int strip_row;        // bytes per scale-strip row in LDS
 };
 
@@ -100,15 +102,15 @@ __global__ void router_logits_f32(const float *x, const float *W, const float *l
 template <int XDT> __global__ void topk_kernel(TopkArgs a);
 __global__ void perm_count(const int32_t *idx, int T, int K, int E, int32_t *chunk_counts);
 __global__ void perm_scan(int32_t *chunk_counts, int nchunks, int E, int TK, int32_t *counts, int32_t *offsets,
-                          int4 *tiles, int *tile_count, int Tsh);
+                          int4 *tiles, int *tile_count, int mt);
 __global__ void perm_scatter(const int32_t *idx, int T, int K, int E, const int32_t *chunk_base,
                              int32_t *sorted_slot, int32_t *slot_pos);
 __global__ void perm_small(const int32_t *idx, int T, int K, int E, int32_t *counts, int32_t *offsets,
-                           int32_t *sorted_slot, int32_t *slot_pos, int4 *tiles, int *tile_count, int Tsh);
-__global__ void build_tiles(const int32_t *offsets, int E, int TK, int4 *tiles, int *tile_count, int Tsh);
+                           int32_t *sorted_slot, int32_t *slot_pos, int4 *tiles, int *tile_count, int mt);
+__global__ void build_tiles(const int32_t *offsets, int E, int4 *tiles, int *tile_count, int mt);
 
 // host-side launchers (moe_gemm.hip, moe_combine.hip)
-hipError_t launch_expert_gemm(int adt, int wfmt, int group, bool gateup, int odt, const GemmParams &p, int grid,
-                              hipStream_t s);
+hipError_t launch_expert_gemm(int adt, int wfmt, int group, bool gateup, int odt, int mb, const GemmParams &p,
+                              int grid, hipStream_t s);
 hipError_t launch_f32_gemm(const F32GemmParams &p, int rows, hipStream_t s);
 hipError_t launch_combine(int odt, int ydt, const CombineArgs &a, hipStream_t s);

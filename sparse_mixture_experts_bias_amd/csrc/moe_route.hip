@@ -233,27 +233,21 @@ static __device__ int block_exclusive_scan(int *v, int n, int *tmp /* >= blockDi
   return total;
 }
 
-// m-chunk list for the grouped expert GEMMs: routed segments (expert e's slots,
-// sorted rows offsets[e]..offsets[e+1]) cut into chunks of MOE_MC rows, then the
-// shared segment (rows TK..TK+Tsh).  offs: shared-memory copy of offsets[0..E].
-static __device__ void emit_tiles(const int *offs, int E, int TK, int Tsh, int4 *tiles, int *tile_count,
+// m-tile list for the grouped expert GEMMs: every routed segment (expert e's slots,
+// sorted rows offsets[e]..offsets[e+1]) cut into tiles of mt rows, in expert order.
+// offs: shared-memory copy of offsets[0..E].
+static __device__ void emit_tiles(const int *offs, int E, int mt, int4 *tiles, int *tile_count,
                                   int *nmc /* shared, E ints */, int *tmp) {
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += blockDim.x) nmc[e] = (offs[e + 1] - offs[e] + MOE_MC - 1) / MOE_MC;
+  for (int e = tid; e < E; e += blockDim.x) nmc[e] = (offs[e + 1] - offs[e] + mt - 1) / mt;
   __syncthreads();
   const int R = block_exclusive_scan(nmc, E, tmp);
   for (int e = tid; e < E; e += blockDim.x) {
     const int n = offs[e + 1] - offs[e];
-    for (int i = 0, base = nmc[e]; i * MOE_MC < n; ++i)
-      tiles[base + i] = make_int4(e, offs[e] + i * MOE_MC, min(MOE_MC, n - i * MOE_MC), 0);
+    for (int i = 0, base = nmc[e]; i * mt < n; ++i)
+      tiles[base + i] = make_int4(e, offs[e] + i * mt, min(mt, n - i * mt), 0);
   }
-  const int ns = (Tsh + MOE_MC - 1) / MOE_MC;
-  for (int i = tid; i < ns; i += blockDim.x)
-    tiles[R + i] = make_int4(E, TK + i * MOE_MC, min(MOE_MC, Tsh - i * MOE_MC), 0);
-  if (tid == 0) {
-    tile_count[0] = R;
-    tile_count[1] = ns;
-  }
+  if (tid == 0) tile_count[0] = R;
 }
 
 __global__ __launch_bounds__(256) void perm_count(const int32_t *__restrict__ idx, int T, int K, int E,
@@ -271,7 +265,7 @@ __global__ __launch_bounds__(256) void perm_count(const int32_t *__restrict__ id
 // single workgroup: per-expert totals, offsets, per-(chunk, expert) bases, tiles.
 __global__ __launch_bounds__(1024) void perm_scan(int32_t *__restrict__ chunk_counts, int nchunks, int E, int TK,
                                                   int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-                                                  int4 *tiles, int *tile_count, int Tsh) {
+                                                  int4 *tiles, int *tile_count, int mt) {
   __shared__ int offs[MOE_MAX_EXPERTS + 1];
   __shared__ int nmc[MOE_MAX_EXPERTS];
   __shared__ int tmp[1024];
@@ -294,7 +288,7 @@ __global__ __launch_bounds__(1024) void perm_scan(int32_t *__restrict__ chunk_co
     for (int c = 0; c < nchunks; ++c) chunk_counts[(int64_t)c * E + e] += offs[e];
   if (tiles) {
     __syncthreads();
-    emit_tiles(offs, E, TK, Tsh, tiles, tile_count, nmc, tmp);
+    emit_tiles(offs, E, mt, tiles, tile_count, nmc, tmp);
   }
 }
 
@@ -339,7 +333,7 @@ __global__ __launch_bounds__(256) void perm_scatter(const int32_t *__restrict__ 
 __global__ __launch_bounds__(256) void perm_small(const int32_t *__restrict__ idx, int T, int K, int E,
                                                   int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                                   int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_pos,
-                                                  int4 *tiles, int *tile_count, int Tsh) {
+                                                  int4 *tiles, int *tile_count, int mt) {
   __shared__ uint32_t mask[MOE_MAX_EXPERTS][8];
   __shared__ int offs[MOE_MAX_EXPERTS + 1];
   __shared__ int nmc[MOE_MAX_EXPERTS];
@@ -359,17 +353,17 @@ __global__ __launch_bounds__(256) void perm_small(const int32_t *__restrict__ id
   scatter_chunk(idx, T, K, E, 0, offs, mask, sorted_slot, slot_pos);
   if (tiles) {
     __syncthreads();
-    emit_tiles(offs, E, T * K, Tsh, tiles, tile_count, nmc, tmp);
+    emit_tiles(offs, E, mt, tiles, tile_count, nmc, tmp);
   }
 }
 
 // tile list from caller-provided offsets (moe_experts_forward)
-__global__ __launch_bounds__(256) void build_tiles(const int32_t *__restrict__ offsets, int E, int TK,
-                                                   int4 *tiles, int *tile_count, int Tsh) {
+__global__ __launch_bounds__(256) void build_tiles(const int32_t *__restrict__ offsets, int E, int4 *tiles,
+                                                   int *tile_count, int mt) {
   __shared__ int offs[MOE_MAX_EXPERTS + 1];
   __shared__ int nmc[MOE_MAX_EXPERTS];
   __shared__ int tmp[256];
   for (int e = threadIdx.x; e <= E; e += 256) offs[e] = offsets[e];
   __syncthreads();
-  emit_tiles(offs, E, TK, Tsh, tiles, tile_count, nmc, tmp);
+  emit_tiles(offs, E, mt, tiles, tile_count, nmc, tmp);
 }
