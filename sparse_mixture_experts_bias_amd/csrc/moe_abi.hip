@@ -250,23 +250,27 @@ struct Timed {  // brackets one launch with events when its class is being timed
 // ---------------------------------------------------------------------------
 // launch helpers
 // ---------------------------------------------------------------------------
-moe_status launch_router(const void *x, int x_dt, int T, int H, const moe_router *r, float *logits, hipStream_t s) {
+// router logits (+ the blend head's two logits into clog when coef_w is given)
+moe_status launch_router(const void *x, int x_dt, int T, int H, const moe_router *r, const void *coef_w,
+                         const float *coef_b, float *logits, float *clog, hipStream_t s) {
   const int E = r->num_experts;
+  const int R = E + (coef_w ? 2 : 0);
   Timed tm(TK_ROUTER, s);
   if (x_dt == MOE_BF16) {
-    hipLaunchKernelGGL(router_logits_bf16, dim3((T + 15) / 16, (E + 15) / 16), dim3(512), 0, s, (const uint16_t *)x,
-                       (const uint16_t *)r->w, r->logit_bias, logits, T, H, E);
+    hipLaunchKernelGGL(router_logits_bf16, dim3((T + 15) / 16, (R + 15) / 16), dim3(512), 0, s, (const uint16_t *)x,
+                       (const uint16_t *)r->w, r->logit_bias, logits, T, H, E, (const uint16_t *)coef_w, coef_b,
+                       clog);
   } else {
-    const int64_t n = (int64_t)T * E;
+    const int64_t n = (int64_t)T * R;
     hipLaunchKernelGGL(router_logits_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float *)x,
-                       (const float *)r->w, r->logit_bias, logits, T, H, E);
+                       (const float *)r->w, r->logit_bias, logits, T, H, E, (const float *)coef_w, coef_b, clog);
   }
   HIPCHK(hipGetLastError());
   return MOE_OK;
 }
 
-moe_status launch_topk(const void *x, int x_dt, int T, int H, const moe_router *r, const float *logits, int32_t *idx,
-                       float *w, const void *coef_w, const float *coef_b, float *coef, hipStream_t s) {
+TopkArgs topk_args(int T, const moe_router *r, const float *logits, int32_t *idx, float *w, const float *clog,
+                   float *coef) {
   TopkArgs a;
   a.logits = logits;
   a.T = T;
@@ -278,16 +282,46 @@ moe_status launch_topk(const void *x, int x_dt, int T, int H, const moe_router *
   a.sbias = r->select_bias;
   a.idx = idx;
   a.w = w;
-  a.x = x;
-  a.H = H;
-  a.coef_w = coef_w;
-  a.coef_b = coef_b;
+  a.clog = clog;
   a.coef = coef;
+  return a;
+}
+
+// experts per lane of a 32-lane selection group (K <= 16), or 0 for the wave-per-token path
+int topk_slots(int E, int K) {
+  if (K > 16) return 0;
+  return E <= 128 ? 4 : (E <= 256 ? 8 : 16);
+}
+
+moe_status launch_topk(const TopkArgs &a, hipStream_t s) {
   Timed tm(TK_TOPK, s);
-  if (x_dt == MOE_BF16)
-    hipLaunchKernelGGL(topk_kernel<DT_BF16>, dim3((T + 3) / 4), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(topk_kernel<DT_F32>, dim3((T + 3) / 4), dim3(256), 0, s, a);
+  const dim3 g((a.T + 7) / 8);
+  switch (topk_slots(a.E, a.K)) {
+    case 4: hipLaunchKernelGGL(topk_half_kernel<4>, g, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(topk_half_kernel<8>, g, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL(topk_half_kernel<16>, g, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL(topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a); break;
+  }
+  HIPCHK(hipGetLastError());
+  return MOE_OK;
+}
+
+// selection + permutation + tile list in one workgroup (T <= MOE_ROUTE_SMALL_T, K <= 16)
+moe_status launch_route_small(const TopkArgs &a, int32_t *counts, int32_t *offsets, int32_t *ss, int32_t *sp,
+                              int4 *tiles, int *tc, int mt, hipStream_t s) {
+  Timed tm(TK_TOPK, s);
+  switch (topk_slots(a.E, a.K)) {
+    case 4:
+      hipLaunchKernelGGL((route_small<4, 1024>), dim3(1), dim3(1024), 0, s, a, counts, offsets, ss, sp, tiles, tc, mt);
+      break;
+    case 8:
+      hipLaunchKernelGGL((route_small<8, 1024>), dim3(1), dim3(1024), 0, s, a, counts, offsets, ss, sp, tiles, tc, mt);
+      break;
+    case 16:
+      hipLaunchKernelGGL((route_small<16, 512>), dim3(1), dim3(512), 0, s, a, counts, offsets, ss, sp, tiles, tc, mt);
+      break;
+    default: return fail(MOE_ERR_UNSUPPORTED, "route_small needs top_k <= 16");
+  }
   HIPCHK(hipGetLastError());
   return MOE_OK;
 }
@@ -518,8 +552,8 @@ moe_status moe_route(const void *x, int32_t x_dtype, int64_t T, int32_t H, const
   CHECK(aligned(x, 16), MOE_ERR_ARG, "x not 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   float *lg = logits ? logits : at<float>(ws, o_logits);
-  TRY(launch_router(x, x_dtype, (int)T, H, r, lg, s));
-  TRY(launch_topk(x, x_dtype, (int)T, H, r, lg, topk_idx, topk_w, nullptr, nullptr, nullptr, s));
+  TRY(launch_router(x, x_dtype, (int)T, H, r, nullptr, nullptr, lg, nullptr, s));
+  TRY(launch_topk(topk_args((int)T, r, lg, topk_idx, topk_w, nullptr, nullptr), s));
   return MOE_OK;
 }
 
@@ -697,6 +731,7 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   Plan pl;
   const size_t o_logits = pl.take((size_t)T * E * 4);
   const size_t o_coef = pl.take((size_t)T * 2 * 4);
+  const size_t o_clog = pl.take((size_t)T * 2 * 4);
   const size_t o_idx = topk_idx ? 0 : pl.take((size_t)TK * 4);
   const size_t o_w = topk_w ? 0 : pl.take((size_t)TK * 4);
   const size_t o_counts = pl.take((size_t)E * 4);
@@ -736,13 +771,19 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   const int Ti = (int)T;
 
   // 1. router + selection (+ blend coefficients)
-  TRY(launch_router(x, x_dtype, Ti, H, &b->router, logits, s));
   const bool blend = b->shared_mode == MOE_SHARED_BLEND;
-  TRY(launch_topk(x, x_dtype, Ti, H, &b->router, logits, idx, wts, blend ? b->coef_w : nullptr,
-                  blend ? b->coef_b : nullptr, coef, s));
-  // 2. permutation + tile list
-  TRY(launch_permute(idx, Ti, K, E, counts, offsets, ss, sp, at<int32_t>(ws, o_chunk), mf ? tiles : nullptr,
-                     mf ? tc : nullptr, 16 * mb, s));
+  float *clog = at<float>(ws, o_clog);
+  TRY(launch_router(x, x_dtype, Ti, H, &b->router, blend ? b->coef_w : nullptr, blend ? b->coef_b : nullptr, logits,
+                    clog, s));
+  const TopkArgs ta = topk_args(Ti, &b->router, logits, idx, wts, blend ? clog : nullptr, coef);
+  // 2. permutation + tile list (for a few tokens in the same workgroup as the selection)
+  if (Ti <= MOE_ROUTE_SMALL_T && topk_slots(E, K) > 0) {
+    TRY(launch_route_small(ta, counts, offsets, ss, sp, mf ? tiles : nullptr, mf ? tc : nullptr, 16 * mb, s));
+  } else {
+    TRY(launch_topk(ta, s));
+    TRY(launch_permute(idx, Ti, K, E, counts, offsets, ss, sp, at<int32_t>(ws, o_chunk), mf ? tiles : nullptr,
+                       mf ? tc : nullptr, 16 * mb, s));
+  }
 
   if (!mf) {
     // ---- f32 path

@@ -50,6 +50,7 @@ MOE_DEV void store8(void *base, int64_t i, const float *f) {
 constexpr int CMB_T = 256;      // threads per block
 constexpr int CMB_COLS = 8 * CMB_T;
 constexpr int CMB_MAXIT = 4;    // rms-norm mode keeps up to 4*2048 columns in registers
+constexpr int CMB_JB = 8;       // slot rows loaded together
 
 template <int ODT, int YDT>
 __global__ __launch_bounds__(CMB_T) void combine_kernel(const CombineArgs a) {
@@ -71,13 +72,23 @@ __global__ __launch_bounds__(CMB_T) void combine_kernel(const CombineArgs a) {
     if (cb >= ncb) break;
     const int c = cb * CMB_COLS + tid * 8;
     if (c >= a.D) continue;
+    float s[8];
+    if (a.mode >= 2) load8<ODT>(a.o, (int64_t)(a.TK + t) * a.ldo + c, s);  // in flight with the slot rows
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < a.K; ++j) {
-      float f[8];
-      load8<ODT>(a.o, (int64_t)pos[j] * a.ldo + c, f);
-      const float w = wt[j];
+    // slot rows in batches of CMB_JB, every load of a batch issued before the first FMA;
+    // the sum still runs over j in ascending order
+    for (int j0 = 0; j0 < a.K; j0 += CMB_JB) {
+      float f[CMB_JB][8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = fmaf(w, f[q], v[q]);
+      for (int jj = 0; jj < CMB_JB; ++jj) load8<ODT>(a.o, (int64_t)pos[min(j0 + jj, a.K - 1)] * a.ldo + c, f[jj]);
+#pragma unroll
+      for (int jj = 0; jj < CMB_JB; ++jj) {
+        if (j0 + jj < a.K) {
+          const float w = wt[j0 + jj];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] = fmaf(w, f[jj][q], v[q]);
+        }
+      }
     }
     if (a.mode == 1) {
 #pragma unroll
@@ -88,8 +99,6 @@ __global__ __launch_bounds__(CMB_T) void combine_kernel(const CombineArgs a) {
       continue;
     }
     if (a.mode >= 2) {
-      float s[8];
-      load8<ODT>(a.o, (int64_t)(a.TK + t) * a.ldo + c, s);
       if (a.mode == 2) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) v[q] += s[q];

@@ -8,19 +8,17 @@
 #define MOE_MT_MIN 16        // smallest m-tile (rows of one segment per work unit) of the grouped GEMM
 #define MOE_KC 256           // reduction elements per chunk for 4-bit weights (128 B per row)
 #define MOE_GEMM_THREADS 256 // 4 waves
+#define MOE_ROUTE_SMALL_T 64 // tokens (K <= 16) up to which selection and permutation share one workgroup
 
 struct TopkArgs {
-  const float *logits;
+  const float *logits;  // [T][E]
   int T, E, K, scoring, norm;
   float rscale;
   const float *sbias;
   int32_t *idx;
   float *w;
-  const void *x;  // blend head input [T, H] (XDT)
-  int H;
-  const void *coef_w;  // [2, H] or nullptr
-  const float *coef_b;
-  float *coef;         // [T, 2]
+  const float *clog;    // blend head logits [T][2], or nullptr
+  float *coef;          // blend coefficients [T][2]
 };
 
 // one stacked weight operand [n][rows][cols] (see moe_linear)
@@ -96,10 +94,14 @@ struct CombineArgs {
 
 // ---- kernels ----
 __global__ void router_logits_bf16(const uint16_t *x, const uint16_t *W, const float *lbias, float *logits,
-                                   int T, int H, int E);
+                                   int T, int H, int E, const uint16_t *cw, const float *cb, float *clog);
 __global__ void router_logits_f32(const float *x, const float *W, const float *lbias, float *logits, int T,
-                                  int H, int E);
-template <int XDT> __global__ void topk_kernel(TopkArgs a);
+                                  int H, int E, const float *cw, const float *cb, float *clog);
+__global__ void topk_kernel(TopkArgs a);
+template <int SL> __global__ void topk_half_kernel(TopkArgs a);
+template <int SL, int NT>
+__global__ void route_small(TopkArgs a, int32_t *counts, int32_t *offsets, int32_t *sorted_slot, int32_t *slot_pos,
+                            int4 *tiles, int *tile_count, int mt);
 __global__ void perm_count(const int32_t *idx, int T, int K, int E, int32_t *chunk_counts);
 __global__ void perm_scan(int32_t *chunk_counts, int nchunks, int E, int TK, int32_t *counts, int32_t *offsets,
                           int4 *tiles, int *tile_count, int mt);

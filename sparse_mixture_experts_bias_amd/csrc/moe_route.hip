@@ -10,37 +10,44 @@
 #include "moe_kernels.h"
 
 // ---------------------------------------------------------------------------
-// router logits, bf16 x and W_r: MFMA 16x16x32, 16 tokens x 16 experts per
-// workgroup, the reduction split over 8 waves and summed in a fixed order.
+// router logits, bf16 x and W_r: MFMA 16x16x32, 16 tokens x 16 rows per workgroup,
+// the reduction split over 8 waves and summed in a fixed order.  Rows 0..E-1 are the
+// experts (W_r, + logit_bias); with a blend head, rows E and E+1 are its two rows
+// (coef_w, + coef_b), written to clog [T][2].  Every wave issues the loads of up to 8
+// of its reduction steps before the first MFMA.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(512) void router_logits_bf16(const uint16_t *__restrict__ x,
                                                           const uint16_t *__restrict__ W,
                                                           const float *__restrict__ lbias,
-                                                          float *__restrict__ logits, int T, int H, int E) {
+                                                          float *__restrict__ logits, int T, int H, int E,
+                                                          const uint16_t *__restrict__ cw,
+                                                          const float *__restrict__ cb, float *__restrict__ clog) {
   __shared__ float red[8][16][17];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
   const int r = lane & 15, kb = lane >> 4;
-  const int trow = min(t0 + r, T - 1), erow = min(e0 + r, E - 1);
+  const int trow = min(t0 + r, T - 1), er = e0 + r;
+  const uint16_t *wrow = er < E ? W + (int64_t)er * H
+                                : ((cw && er < E + 2) ? cw + (int64_t)(er - E) * H : W + (int64_t)(E - 1) * H);
   const u32x4_t *xa = (const u32x4_t *)(x + (int64_t)trow * H + kb * 8);
-  const u32x4_t *wb = (const u32x4_t *)(W + (int64_t)erow * H + kb * 8);
+  const u32x4_t *wb = (const u32x4_t *)(wrow + kb * 8);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   const int nsteps = H >> 5;
-  int s = wave;
-  for (; s + 8 < nsteps; s += 16) {
-    u32x4_t a0 = xa[s * 4], b0 = wb[s * 4];
-    u32x4_t a1 = xa[(s + 8) * 4], b1 = wb[(s + 8) * 4];
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0),
-                                                  __builtin_bit_cast(bf16x8_t, b0), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1),
-                                                  __builtin_bit_cast(bf16x8_t, b1), acc, 0, 0, 0);
+  for (int s0 = wave; s0 < nsteps; s0 += 64) {
+    u32x4_t av[8], bv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int st = min(s0 + 8 * i, nsteps - 1);
+      av[i] = xa[st * 4];
+      bv[i] = wb[st * 4];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (s0 + 8 * i < nsteps)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[i]),
+                                                      __builtin_bit_cast(bf16x8_t, bv[i]), acc, 0, 0, 0);
   }
-  for (; s < nsteps; s += 8) {
-    u32x4_t a0 = xa[s * 4], b0 = wb[s * 4];
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0),
-                                                  __builtin_bit_cast(bf16x8_t, b0), acc, 0, 0, 0);
-  }
-  // acc[i] holds row (token) 4*kb+i, column (expert) r of the 16x16 tile
+  // acc[i] holds row (token) 4*kb+i, column r of the 16x16 tile
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave][4 * kb + i][r] = acc[i];
   __syncthreads();
@@ -50,42 +57,92 @@ __global__ __launch_bounds__(512) void router_logits_bf16(const uint16_t *__rest
 #pragma unroll
     for (int w = 0; w < 8; ++w) v += red[w][m][n];
     const int t = t0 + m, e = e0 + n;
-    if (t < T && e < E) logits[(int64_t)t * E + e] = v + (lbias ? lbias[e] : 0.f);
+    if (t < T) {
+      if (e < E)
+        logits[(int64_t)t * E + e] = v + (lbias ? lbias[e] : 0.f);
+      else if (cw && e < E + 2)
+        clog[2 * t + (e - E)] = v + cb[e - E];
+    }
   }
 }
 
-// router logits, f32 x and W_r: one thread per (token, expert), sequential fp32 sum.
+// router logits, f32 x and W_r: one thread per (token, row), sequential fp32 sum; rows as above.
 __global__ void router_logits_f32(const float *__restrict__ x, const float *__restrict__ W,
                                   const float *__restrict__ lbias, float *__restrict__ logits, int T, int H,
-                                  int E) {
+                                  int E, const float *__restrict__ cw, const float *__restrict__ cb,
+                                  float *__restrict__ clog) {
+  const int R = E + (cw ? 2 : 0);
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)T * E) return;
-  const int t = (int)(i / E), e = (int)(i % E);
-  const float *xr = x + (int64_t)t * H, *wr = W + (int64_t)e * H;
+  if (i >= (int64_t)T * R) return;
+  const int t = (int)(i / R), e = (int)(i % R);
+  const float *xr = x + (int64_t)t * H, *wr = e < E ? W + (int64_t)e * H : cw + (int64_t)(e - E) * H;
   float v = 0.f;
   for (int h = 0; h < H; ++h) v = fmaf(xr[h], wr[h], v);
-  logits[i] = v + (lbias ? lbias[e] : 0.f);
+  if (e < E)
+    logits[(int64_t)t * E + e] = v + (lbias ? lbias[e] : 0.f);
+  else
+    clog[2 * t + (e - E)] = v + cb[e - E];
 }
 
 // ---------------------------------------------------------------------------
-// scores + top-k + weights (+ the blend coefficient head): one wave per token.
+// scores + top-k + weights (+ the blend coefficients): one wave per token.
+// The selection key of expert e is (score + select_bias) mapped to an order-preserving
+// u32 in the high word and ~e in the low word, so the largest key is the largest
+// selection value with ties to the lower id.  Each of the K rounds takes the wave-wide
+// maximum key (DPP within rows of 16 lanes, then the four row maxima) and retires it.
 // ---------------------------------------------------------------------------
-template <int XDT>
-__global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
+namespace {
+
+MOE_DEV uint32_t ord_key(float f) {
+  const uint32_t b = __float_as_uint(f + 0.0f);  // -0 -> +0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+template <int CTRL>
+MOE_DEV uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+MOE_DEV uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// maximum over the 64 lanes (every lane must be active); the result is wave-uniform
+MOE_DEV uint64_t wave_max_u64(uint64_t v) {
+  v = umax64(v, dpp64<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = umax64(v, dpp64<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = umax64(v, dpp64<0x141>(v));  // row_half_mirror
+  v = umax64(v, dpp64<0x140>(v));  // row_mirror: every lane holds its row's maximum
+  uint64_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
+    m = umax64(m, ((uint64_t)hi << 32) | lo);
+  }
+  return m;
+}
+
+// token t on the calling wave (all 64 lanes).  sl: E floats of LDS, el: K ints of LDS,
+// both private to the wave.  sidx: optional copy of the chosen ids ([T][K], LDS).
+MOE_DEV void topk_token(const TopkArgs &a, int t, int lane, float *sl, int *el, int32_t *sidx) {
   constexpr int EPL = MOE_MAX_EXPERTS / 64;
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
   const float *lrow = a.logits + (int64_t)t * a.E;
-  float s[EPL], sel[EPL];
-  float mx = -INFINITY;
+  // every load issued before the first use (clamped ids; out-of-range slots masked below)
+  float s[EPL], sb[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
-    const int e = lane + 64 * j;
-    s[j] = (e < a.E) ? lrow[e] : -INFINITY;
-    mx = fmaxf(mx, s[j]);
+    const int ec = min(lane + 64 * j, a.E - 1);
+    s[j] = lrow[ec];
+    sb[j] = a.sbias ? a.sbias[ec] : 0.f;
   }
+#pragma unroll
+  for (int j = 0; j < EPL; ++j)
+    if (lane + 64 * j >= a.E) s[j] = -INFINITY;
   if (a.scoring == 1) {  // softmax over experts, max-subtracted, fp32
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) mx = fmaxf(mx, s[j]);
     mx = wave_max(mx);
     float sum = 0.f;
 #pragma unroll
@@ -105,124 +162,229 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
       s[j] = (e < a.E) ? 1.0f / (1.0f + expf(-s[j])) : 0.f;
     }
   }
+  uint64_t key[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
-    sel[j] = s[j] + ((a.sbias && e < a.E) ? a.sbias[e] : 0.f);
+    if (e < a.E) {
+      sl[e] = s[j];
+      const float sel = s[j] + sb[j];
+      key[j] = ((uint64_t)ord_key(sel) << 32) | (uint32_t)~e;
+    } else {
+      key[j] = 0;
+    }
   }
-  uint32_t taken = 0;
-  int my_e = 0x7fffffff;
-  float my_s = 0.f;
+  int my_e = 0;
   for (int k = 0; k < a.K; ++k) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-    float bs = 0.f;
+    uint64_t loc = key[0];
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const int e = lane + 64 * j;
-      const bool ok = (e < a.E) && !((taken >> j) & 1u);
-      if (ok && (be == 0x7fffffff || sel[j] > bv || (sel[j] == bv && e < be))) {
-        bv = sel[j];
-        be = e;
-        bs = s[j];
-      }
-    }
+    for (int j = 1; j < EPL; ++j) loc = umax64(loc, key[j]);
+    const uint64_t best = wave_max_u64(loc);
+    const int be = (int)~(uint32_t)best;
+    if (lane == k) my_e = be;
+    if ((be & 63) == lane) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oe = __shfl_xor(be, o, 64);
-      const float os = __shfl_xor(bs, o, 64);
-      const bool take = (oe != 0x7fffffff) &&
-                        (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
-      if (take) {
-        bv = ov;
-        be = oe;
-        bs = os;
-      }
+      for (int j = 0; j < EPL; ++j)
+        if (j == (be >> 6)) key[j] = 0;
     }
-    if (lane == k) {
-      my_e = be;
-      my_s = bs;
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
   }
-  // ascending-id order and the weight sum (over the K chosen, fixed order)
-  int rank = 0;
-  float wsum = 0.f;
-  for (int i = 0; i < a.K; ++i) {
-    const int ei = __shfl(my_e, i, 64);
-    wsum += __shfl(my_s, i, 64);
-    rank += (ei < my_e) ? 1 : 0;
-  }
+  if (lane < a.K) el[lane] = my_e;
+  // the chosen ids in ascending order, their unbiased scores and the weight sum
+  const float my_s = lane < a.K ? sl[my_e] : 0.f;
+  const float wsum = wave_sum(my_s);
   if (lane < a.K) {
+    int rank = 0;
+    for (int i = 0; i < a.K; ++i) rank += (el[i] < my_e) ? 1 : 0;
     float w = a.norm ? my_s / wsum : my_s;
     w *= a.rscale;
     a.idx[(int64_t)t * a.K + rank] = my_e;
     a.w[(int64_t)t * a.K + rank] = w;
+    if (sidx) sidx[t * a.K + rank] = my_e;
   }
-  // blend coefficients: softmax over the 2-way head, fp32
-  if (a.coef_w) {
-    float c0 = 0.f, c1 = 0.f;
-    if constexpr (XDT == DT_F32) {
-      const float *xr = (const float *)a.x + (int64_t)t * a.H;
-      const float *w0 = (const float *)a.coef_w, *w1 = w0 + a.H;
-      for (int h = lane; h < a.H; h += 64) {
-        c0 = fmaf(xr[h], w0[h], c0);
-        c1 = fmaf(xr[h], w1[h], c1);
-      }
-    } else {
-      const uint16_t *xr = (const uint16_t *)a.x + (int64_t)t * a.H;
-      const uint16_t *w0 = (const uint16_t *)a.coef_w, *w1 = w0 + a.H;
-      for (int h = lane * 8; h < a.H; h += 512) {
-        float xf[8], af[8], bf[8];
-        unpack8<DT_BF16>(*(const u32x4_t *)(xr + h), xf);
-        unpack8<DT_BF16>(*(const u32x4_t *)(w0 + h), af);
-        unpack8<DT_BF16>(*(const u32x4_t *)(w1 + h), bf);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          c0 = fmaf(xf[q], af[q], c0);
-          c1 = fmaf(xf[q], bf[q], c1);
-        }
-      }
-    }
-    c0 = wave_sum(c0) + a.coef_b[0];
-    c1 = wave_sum(c1) + a.coef_b[1];
+  // blend coefficients: softmax over the 2-way head's logits, fp32
+  if (a.clog && lane == 0) {
+    const float c0 = a.clog[2 * t], c1 = a.clog[2 * t + 1];
     const float m = fmaxf(c0, c1);
     const float x0 = expf(c0 - m), x1 = expf(c1 - m);
-    if (lane == 0) {
-      a.coef[2 * t] = x0 / (x0 + x1);
-      a.coef[2 * t + 1] = x1 / (x0 + x1);
-    }
+    a.coef[2 * t] = x0 / (x0 + x1);
+    a.coef[2 * t + 1] = x1 / (x0 + x1);
   }
 }
 
-template __global__ void topk_kernel<DT_F32>(TopkArgs);
-template __global__ void topk_kernel<DT_BF16>(TopkArgs);
+// ---- 32 lanes per token (two DPP rows), 2 tokens per wave.  Lane l32 of the half-wave
+// holds experts l32 + 32*j, j < SL.  Reductions: DPP within each 16-lane row, then
+// v_permlane16_swap, which hands every lane the value of the same lane in the other row
+// of its half (the pair it returns holds both rows' values, in either order).
+
+template <int CTRL>
+MOE_DEV float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+MOE_DEV uint64_t half_max_u64(uint64_t v) {
+  v = umax64(v, dpp64<0xB1>(v));
+  v = umax64(v, dpp64<0x4E>(v));
+  v = umax64(v, dpp64<0x141>(v));
+  v = umax64(v, dpp64<0x140>(v));
+  const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+  return umax64(((uint64_t)hi[0] << 32) | lo[0], ((uint64_t)hi[1] << 32) | lo[1]);
+}
+MOE_DEV float half_max_f32(float v) {
+  v = fmaxf(v, dppf<0xB1>(v));
+  v = fmaxf(v, dppf<0x4E>(v));
+  v = fmaxf(v, dppf<0x141>(v));
+  v = fmaxf(v, dppf<0x140>(v));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// the two rows are added in the same order in every lane, so all 32 lanes agree bitwise
+MOE_DEV float half_sum_f32(float v) {
+  v += dppf<0xB1>(v);
+  v += dppf<0x4E>(v);
+  v += dppf<0x141>(v);
+  v += dppf<0x140>(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// token t on one half-wave (both halves of the wave call this together; a half with
+// t >= T computes on a clamped token and stores nothing).  el / esc: 16 ints / floats of
+// LDS private to the half (chosen ids and their unbiased scores, in selection order).
+template <int SL>
+MOE_DEV void topk_half(const TopkArgs &a, int t, int l32, int *el, float *esc, int32_t *sidx) {
+  const bool live = t < a.T;
+  const float *lrow = a.logits + (int64_t)(live ? t : a.T - 1) * a.E;
+  float lg[SL], sb[SL];
+#pragma unroll
+  for (int j = 0; j < SL; ++j) {
+    const int ec = min(l32 + 32 * j, a.E - 1);
+    lg[j] = lrow[ec];
+    sb[j] = a.sbias ? a.sbias[ec] : 0.f;
+  }
+  float sc[SL];
+  if (a.scoring == 1) {  // softmax over experts, max-subtracted, fp32
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < SL; ++j)
+      if (l32 + 32 * j < a.E) m = fmaxf(m, lg[j]);
+    const float mx = half_max_f32(m);
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < SL; ++j) {
+      sc[j] = (l32 + 32 * j < a.E) ? expf(lg[j] - mx) : 0.f;
+      sum += sc[j];
+    }
+    const float inv = 1.0f / half_sum_f32(sum);
+#pragma unroll
+    for (int j = 0; j < SL; ++j) sc[j] *= inv;
+  } else {  // sigmoid
+#pragma unroll
+    for (int j = 0; j < SL; ++j) sc[j] = 1.0f / (1.0f + expf(-lg[j]));
+  }
+  uint64_t key[SL];
+#pragma unroll
+  for (int j = 0; j < SL; ++j) {
+    const int e = l32 + 32 * j;
+    key[j] = (e < a.E) ? (((uint64_t)ord_key(sc[j] + sb[j]) << 32) | (uint32_t)~e) : 0ull;
+  }
+  for (int k = 0; k < a.K; ++k) {
+    uint64_t loc = key[0];
+#pragma unroll
+    for (int j = 1; j < SL; ++j) loc = umax64(loc, key[j]);
+    const int be = (int)~(uint32_t)half_max_u64(loc);
+    if ((be & 31) == l32) {  // the owner retires the winner and records its score
+      float ws = 0.f;
+#pragma unroll
+      for (int j = 0; j < SL; ++j)
+        if (j == (be >> 5)) {
+          ws = sc[j];
+          key[j] = 0ull;
+        }
+      esc[k] = ws;
+      el[k] = be;
+    }
+  }
+  // the chosen ids in ascending order and the weight sum
+  const int my_e = l32 < a.K ? el[l32] : 0x7fffffff;
+  const float my_s = l32 < a.K ? esc[l32] : 0.f;
+  const float wsum = half_sum_f32(my_s);
+  if (live && l32 < a.K) {
+    int rank = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int4 v = *(const int4 *)(el + 4 * q);
+      rank += (4 * q + 0 < a.K && v.x < my_e) + (4 * q + 1 < a.K && v.y < my_e) +
+              (4 * q + 2 < a.K && v.z < my_e) + (4 * q + 3 < a.K && v.w < my_e);
+    }
+    float w = a.norm ? my_s / wsum : my_s;
+    w *= a.rscale;
+    a.idx[(int64_t)t * a.K + rank] = my_e;
+    a.w[(int64_t)t * a.K + rank] = w;
+    if (sidx) sidx[t * a.K + rank] = my_e;
+  }
+  if (a.clog && live && l32 == 0) {
+    const float c0 = a.clog[2 * t], c1 = a.clog[2 * t + 1];
+    const float m = fmaxf(c0, c1);
+    const float x0 = expf(c0 - m), x1 = expf(c1 - m);
+    a.coef[2 * t] = x0 / (x0 + x1);
+    a.coef[2 * t + 1] = x1 / (x0 + x1);
+  }
+}
+
+}  // namespace
+
+// one wave per token (K > 16)
+__global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
+  __shared__ float sl[4][MOE_MAX_EXPERTS];
+  __shared__ int el[4][MOE_MAX_TOPK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.T) return;  // wave-uniform
+  topk_token(a, t, lane, sl[wave], el[wave], nullptr);
+}
+
+// one half-wave per token (K <= 16), 8 tokens per workgroup
+template <int SL>
+__global__ __launch_bounds__(256) void topk_half_kernel(TopkArgs a) {
+  __shared__ __attribute__((aligned(16))) int el[8][16];
+  __shared__ float esc[8][16];
+  const int lane = threadIdx.x & 63, half = threadIdx.x >> 5;
+  topk_half<SL>(a, blockIdx.x * 8 + half, lane & 31, el[half], esc[half], nullptr);
+}
+template __global__ void topk_half_kernel<4>(TopkArgs);
+template __global__ void topk_half_kernel<8>(TopkArgs);
+template __global__ void topk_half_kernel<16>(TopkArgs);
 
 // ---------------------------------------------------------------------------
 // permutation: per-chunk expert histograms, a scan in expert-major order, and a
 // deterministic scatter (rank inside a chunk from per-expert token bitmasks).
 // ---------------------------------------------------------------------------
 
-// exclusive scan of v[0..n) in place (shared memory, n <= 4*blockDim); returns the total.
-static __device__ int block_exclusive_scan(int *v, int n, int *tmp /* >= blockDim ints */) {
-  const int tid = threadIdx.x, nt = blockDim.x;
+// exclusive scan of v[0..n) in place (shared memory, n <= 4*blockDim, blockDim a multiple
+// of 64); returns the total.  Each thread owns consecutive elements; waves scan with
+// shuffles and combine their totals through tmp (>= blockDim/64 ints).
+static __device__ int block_exclusive_scan(int *v, int n, int *tmp) {
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
   const int per = (n + nt - 1) / nt;
   const int b = tid * per;
   int local = 0;
   for (int i = 0; i < per; ++i)
     if (b + i < n) local += v[b + i];
-  tmp[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < nt; off <<= 1) {
-    const int add = (tid >= off) ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
   }
-  const int total = tmp[nt - 1];
-  int run = tmp[tid] - local;
+  if (lane == 63) tmp[wave] = incl;
   __syncthreads();
+  int base = 0, total = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int c = tmp[w];
+    base += (w < wave) ? c : 0;
+    total += c;
+  }
+  int run = base + incl - local;
   for (int i = 0; i < per; ++i)
     if (b + i < n) {
       const int c = v[b + i];
@@ -231,6 +393,14 @@ static __device__ int block_exclusive_scan(int *v, int n, int *tmp /* >= blockDi
     }
   __syncthreads();
   return total;
+}
+
+// ids j0 .. j0+7 of token t, all loads in flight together (entries past K repeat id K-1
+// and are never used)
+constexpr int kIdBatch = 8;
+static __device__ void load_ids(const int32_t *__restrict__ idx, int t, int K, int j0, int (&ids)[kIdBatch]) {
+#pragma unroll
+  for (int j = 0; j < kIdBatch; ++j) ids[j] = idx[(int64_t)t * K + min(j0 + j, K - 1)];
 }
 
 // m-tile list for the grouped expert GEMMs: every routed segment (expert e's slots,
@@ -256,8 +426,15 @@ __global__ __launch_bounds__(256) void perm_count(const int32_t *__restrict__ id
   for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
   __syncthreads();
   const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t < T)
-    for (int j = 0; j < K; ++j) atomicAdd(&cnt[idx[(int64_t)t * K + j]], 1);
+  if (t < T) {
+    for (int j0 = 0; j0 < K; j0 += kIdBatch) {
+      int ids[kIdBatch];
+      load_ids(idx, t, K, j0, ids);
+#pragma unroll
+      for (int j = 0; j < kIdBatch; ++j)
+        if (j0 + j < K) atomicAdd(&cnt[ids[j]], 1);
+    }
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) chunk_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
@@ -268,7 +445,7 @@ __global__ __launch_bounds__(1024) void perm_scan(int32_t *__restrict__ chunk_co
                                                   int4 *tiles, int *tile_count, int mt) {
   __shared__ int offs[MOE_MAX_EXPERTS + 1];
   __shared__ int nmc[MOE_MAX_EXPERTS];
-  __shared__ int tmp[1024];
+  __shared__ int tmp[16];
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int run = 0;
     for (int c = 0; c < nchunks; ++c) {
@@ -298,23 +475,37 @@ static __device__ void scatter_chunk(const int32_t *__restrict__ idx, int T, int
                                      uint32_t (*mask)[8], int32_t *__restrict__ sorted_slot,
                                      int32_t *__restrict__ slot_pos) {
   const int tid = threadIdx.x;
+  const int t = chunk * 256 + tid;
   for (int i = tid; i < E * 8; i += blockDim.x) mask[i >> 3][i & 7] = 0u;
   __syncthreads();
-  const int t = chunk * 256 + tid;
-  if (t < T)
-    for (int j = 0; j < K; ++j) atomicOr(&mask[idx[(int64_t)t * K + j]][tid >> 5], 1u << (tid & 31));
+  if (t < T) {
+    for (int j0 = 0; j0 < K; j0 += kIdBatch) {
+      int ids[kIdBatch];
+      load_ids(idx, t, K, j0, ids);
+#pragma unroll
+      for (int j = 0; j < kIdBatch; ++j)
+        if (j0 + j < K) atomicOr(&mask[ids[j]][tid >> 5], 1u << (tid & 31));
+    }
+  }
   __syncthreads();
   if (t < T) {
     const int wd = tid >> 5;
     const uint32_t below = (1u << (tid & 31)) - 1u;
-    for (int j = 0; j < K; ++j) {
-      const int e = idx[(int64_t)t * K + j];
-      int rank = __popc(mask[e][wd] & below);
-      for (int w = 0; w < wd; ++w) rank += __popc(mask[e][w]);
-      const int pos = base[e] + rank;
-      const int p = t * K + j;
-      sorted_slot[pos] = p;
-      slot_pos[p] = pos;
+    for (int j0 = 0; j0 < K; j0 += kIdBatch) {
+      int ids[kIdBatch];
+      load_ids(idx, t, K, j0, ids);
+#pragma unroll
+      for (int j = 0; j < kIdBatch; ++j) {
+        if (j0 + j < K) {
+          const int e = ids[j];
+          int rank = __popc(mask[e][wd] & below);
+          for (int w = 0; w < wd; ++w) rank += __popc(mask[e][w]);
+          const int pos = base[e] + rank;
+          const int p = t * K + j0 + j;
+          sorted_slot[pos] = p;
+          slot_pos[p] = pos;
+        }
+      }
     }
   }
 }
@@ -329,40 +520,141 @@ __global__ __launch_bounds__(256) void perm_scatter(const int32_t *__restrict__ 
   scatter_chunk(idx, T, K, E, blockIdx.x, base, mask, sorted_slot, slot_pos);
 }
 
-// T <= 256: the whole permutation (and the tile list) in one workgroup.
+// T <= 256: the whole permutation (and the tile list) in one workgroup (blockDim >= 256).
+// idx may point to global or shared memory.
+struct PermSmem {
+  uint32_t mask[MOE_MAX_EXPERTS][8];
+  int offs[MOE_MAX_EXPERTS + 1];
+  int nmc[MOE_MAX_EXPERTS];
+  int tmp[16];
+};
+
+static __device__ void perm_block(const int32_t *idx, int T, int K, int E, int32_t *__restrict__ counts,
+                                  int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_slot,
+                                  int32_t *__restrict__ slot_pos, int4 *tiles, int *tile_count, int mt,
+                                  PermSmem &sm) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += blockDim.x) sm.offs[e] = 0;
+  __syncthreads();
+  if (tid < T) {
+    for (int j0 = 0; j0 < K; j0 += kIdBatch) {
+      int ids[kIdBatch];
+      load_ids(idx, tid, K, j0, ids);
+#pragma unroll
+      for (int j = 0; j < kIdBatch; ++j)
+        if (j0 + j < K) atomicAdd(&sm.offs[ids[j]], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) counts[e] = sm.offs[e];
+  __syncthreads();
+  const int total = block_exclusive_scan(sm.offs, E, sm.tmp);
+  if (tid == 0) sm.offs[E] = total;
+  __syncthreads();
+  for (int e = tid; e <= E; e += blockDim.x) offsets[e] = sm.offs[e];
+  scatter_chunk(idx, T, K, E, 0, sm.offs, sm.mask, sorted_slot, slot_pos);
+  if (tiles) {
+    __syncthreads();
+    emit_tiles(sm.offs, E, mt, tiles, tile_count, sm.nmc, sm.tmp);
+  }
+}
+
 __global__ __launch_bounds__(256) void perm_small(const int32_t *__restrict__ idx, int T, int K, int E,
                                                   int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                                   int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_pos,
                                                   int4 *tiles, int *tile_count, int mt) {
-  __shared__ uint32_t mask[MOE_MAX_EXPERTS][8];
-  __shared__ int offs[MOE_MAX_EXPERTS + 1];
-  __shared__ int nmc[MOE_MAX_EXPERTS];
-  __shared__ int tmp[256];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 256) offs[e] = 0;
+  __shared__ PermSmem sm;
+  perm_block(idx, T, K, E, counts, offsets, sorted_slot, slot_pos, tiles, tile_count, mt, sm);
+}
+
+// T <= MOE_ROUTE_SMALL_T, K <= 16: selection (one half-wave per token) and the permutation
+// in one workgroup of NT threads (1024, or 512 when a lane holds 16 experts and needs the
+// registers).  The per-expert (slot count, tile count) pairs go through a single scan,
+// packed in one int (T*K <= 1024).
+template <int SL, int NT>
+__global__ __launch_bounds__(NT) void route_small(TopkArgs a, int32_t *__restrict__ counts,
+                                                 int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_slot,
+                                                 int32_t *__restrict__ slot_pos, int4 *tiles, int *tile_count, int mt) {
+  constexpr int NH = NT / 32, NW = NT / 64;
+  __shared__ __attribute__((aligned(16))) int el[NH][16];
+  __shared__ float esc[NH][16];
+  __shared__ int32_t sidx[MOE_ROUTE_SMALL_T * 16];
+  __shared__ int cnt[MOE_MAX_EXPERTS], offs[MOE_MAX_EXPERTS];
+  __shared__ uint32_t tmask[MOE_MAX_EXPERTS][MOE_ROUTE_SMALL_T / 32];
+  __shared__ int wtot[NW];
+  static_assert(NT >= MOE_MAX_EXPERTS, "one expert per thread in the scan");
+  const int tid = threadIdx.x, lane = tid & 63, half = tid >> 5, wave = tid >> 6;
+  const int E = a.E, K = a.K, TK = a.T * a.K;
+  for (int e = tid; e < E; e += NT) {
+    cnt[e] = 0;
+#pragma unroll
+    for (int w = 0; w < MOE_ROUTE_SMALL_T / 32; ++w) tmask[e][w] = 0u;
+  }
+  for (int t0 = 0; t0 < a.T; t0 += NH) topk_half<SL>(a, t0 + half, lane & 31, el[half], esc[half], sidx);
   __syncthreads();
-  if (tid < T)
-    for (int j = 0; j < K; ++j) atomicAdd(&offs[idx[(int64_t)tid * K + j]], 1);
+  // slot p = t*K + j: per-expert counts and per-expert token masks
+  for (int p = tid; p < TK; p += NT) {
+    const int ep = sidx[p], tp = p / K;
+    atomicAdd(&cnt[ep], 1);
+    atomicOr(&tmask[ep][tp >> 5], 1u << (tp & 31));
+  }
   __syncthreads();
-  for (int e = tid; e < E; e += 256) counts[e] = offs[e];
+  // exclusive scan over experts of (count | tiles << 16)
+  const int c = tid < E ? cnt[tid] : 0;
+  const int nt = (c + mt - 1) / mt;
+  const int packed = c | (nt << 16);
+  int incl = packed;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wtot[wave] = incl;
   __syncthreads();
-  const int total = block_exclusive_scan(offs, E, tmp);
-  if (tid == 0) offs[E] = total;
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int v = wtot[w];
+    base += (w < wave) ? v : 0;
+    total += v;
+  }
+  if (tid < E) {
+    const int ex = base + incl - packed;
+    const int off = ex & 0xFFFF, tb = ex >> 16;
+    offs[tid] = off;
+    counts[tid] = c;
+    offsets[tid] = off;
+    if (tiles)
+      for (int i = 0; i < nt; ++i) tiles[tb + i] = make_int4(tid, off + i * mt, min(mt, c - i * mt), 0);
+  }
+  if (tid == 0) {
+    offsets[E] = total & 0xFFFF;
+    if (tiles) tile_count[0] = total >> 16;
+  }
   __syncthreads();
-  for (int e = tid; e <= E; e += 256) offsets[e] = offs[e];
-  scatter_chunk(idx, T, K, E, 0, offs, mask, sorted_slot, slot_pos);
-  if (tiles) {
-    __syncthreads();
-    emit_tiles(offs, E, mt, tiles, tile_count, nmc, tmp);
+  // rank of slot p among the slots of its expert: earlier tokens that chose the same expert
+  for (int p = tid; p < TK; p += NT) {
+    const int ep = sidx[p], tp = p / K;
+    int rank = __popc(tmask[ep][tp >> 5] & ((1u << (tp & 31)) - 1u));
+    for (int w = 0; w < (tp >> 5); ++w) rank += __popc(tmask[ep][w]);
+    const int pos = offs[ep] + rank;
+    sorted_slot[pos] = p;
+    slot_pos[p] = pos;
   }
 }
+template __global__ void route_small<4, 1024>(TopkArgs, int32_t *, int32_t *, int32_t *, int32_t *, int4 *, int *,
+                                              int);
+template __global__ void route_small<8, 1024>(TopkArgs, int32_t *, int32_t *, int32_t *, int32_t *, int4 *, int *,
+                                              int);
+template __global__ void route_small<16, 512>(TopkArgs, int32_t *, int32_t *, int32_t *, int32_t *, int4 *, int *,
+                                              int);
 
 // tile list from caller-provided offsets (moe_experts_forward)
 __global__ __launch_bounds__(256) void build_tiles(const int32_t *__restrict__ offsets, int E, int4 *tiles,
                                                    int *tile_count, int mt) {
   __shared__ int offs[MOE_MAX_EXPERTS + 1];
   __shared__ int nmc[MOE_MAX_EXPERTS];
-  __shared__ int tmp[256];
+  __shared__ int tmp[16];
   for (int e = threadIdx.x; e <= E; e += 256) offs[e] = offsets[e];
   __syncthreads();
   emit_tiles(offs, E, mt, tiles, tile_count, nmc, tmp);
