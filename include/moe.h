@@ -84,6 +84,10 @@ typedef enum { MOE_SHARED_NONE = 0, MOE_SHARED_ADD = 1, MOE_SHARED_BLEND = 2 } m
  *           scales: uint8 E8M0 [n, rows, cols/32]; weight = e2m1 * 2^(scale-127)
  *           (group_size must be 32, bits 4; scale byte 255 (NaN) is out of contract)
  *   bias (optional, any format): output bias [n, rows], bf16 (f32 for DENSE F32).
+ *   packed: the stream moe_pack_weights wrote for this stack (for gate/up: the one
+ *           stream of the pair, set on `gate`; `up.packed` is not read).  Required by
+ *           every BF16/F16-activation GEMM; there w, scales and qbias are not read
+ *           (they describe the source of the stream).  Unused on the F32 path.
  * "qbias" (the affine offset of each group) and "bias" (the linear layer's output
  * bias) are different things on purpose.
  */
@@ -97,6 +101,7 @@ typedef struct {
   const void *scales;
   const void *qbias;
   const void *bias;
+  const void *packed;
 } moe_linear;
 
 /* SwiGLU expert stack: h = silu(gate z) * (up z) with gate/up [n, I, D], down [n, D, I].
@@ -134,6 +139,25 @@ typedef struct {
   int32_t inter_dtype;       /* storage of z, h, expert outputs: MOE_BF16 or MOE_F16
                                 (MOE_F32 when x is f32) */
 } moe_block;
+
+/*
+ * moe_pack_weights - write the GEMM's packed stream of a weight stack (once, at load time).
+ *   a      the stack (natural layout above: DENSE BF16, AFFINE4 or MXFP4)
+ *   b      NULL: `a` alone, in blocks of 32 rows (down projections, latent maps);
+ *          else the up stack of a gate/up pair (`a` = gate, same format and shape):
+ *          blocks of 16 gate rows followed by the same 16 up rows
+ *   out    device buffer, 256-byte aligned; NULL: write the size to *out_bytes
+ *   out_bytes  in: size of out; too small -> MOE_ERR_WORKSPACE
+ * The stream is a permutation of the stored words, scales and qbias (nothing is
+ * converted); rows and reduction elements are zero-padded to whole blocks of 32 rows
+ * and 256 elements (64 for DENSE).  Layout: per matrix, per row block, per chunk a
+ * record of 4096 bytes of weights in MFMA lane order followed by the chunk's scales
+ * (AFFINE4: 4 bytes per row and group, MXFP4: 1 byte per row and block).
+ * Source: the gather_qmm weight planes of mlxcel issue #974 and libmir-metal's
+ * ExpertLayout, re-laid for gfx950's 16x16x32 MFMA operand order.
+ */
+MOE_API moe_status moe_pack_weights(const moe_linear *a, const moe_linear *b, void *out, size_t *out_bytes,
+                                    void *stream);
 
 /*
  * moe_route - router projection, scoring, selection and weights.

@@ -27,8 +27,8 @@ FMT_CODES = {"dense": MOE_W_DENSE, "affine4": MOE_W_AFFINE4, "mxfp4": MOE_W_MXFP
 SHARED_CODES = {"none": MOE_SHARED_NONE, "add": MOE_SHARED_ADD, "blend": MOE_SHARED_BLEND}
 SCORING_CODES = {"sigmoid": MOE_SIGMOID, "softmax": MOE_SOFTMAX}
 
-EXPORTS = ("moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward", "moe_timing_enable",
-           "moe_timing_read", "moe_status_str", "moe_last_error", "moe_abi_version")
+EXPORTS = ("moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward", "moe_pack_weights",
+           "moe_timing_enable", "moe_timing_read", "moe_status_str", "moe_last_error", "moe_abi_version")
 
 # kernel classes of moe_timing_enable
 TIMING_GATEUP, TIMING_DOWN, TIMING_ROUTER, TIMING_TOPK, TIMING_PERM, TIMING_COMBINE, TIMING_PLAIN = range(1, 8)
@@ -48,7 +48,7 @@ class MoeLinear(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("dense_dtype", ctypes.c_int32), ("n", ctypes.c_int32),
                 ("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("bits", ctypes.c_int32), ("w", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("qbias", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+                ("qbias", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("packed", ctypes.c_void_p)]
 
 
 class MoeMLP(ctypes.Structure):
@@ -85,7 +85,8 @@ def lib() -> ctypes.CDLL:
         L.moe_experts_forward.argtypes = [vp, i32, i64, i32, ctypes.POINTER(MoeMLP), i32, i32, vp, vp, vp, vp, vp,
                                           i32, vp, vp, sz, vp]
         L.moe_block_forward.argtypes = [vp, i32, i64, ctypes.POINTER(MoeBlock), vp, i32, vp, vp, vp, sz, vp]
-        for f in ("moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward"):
+        L.moe_pack_weights.argtypes = [ctypes.POINTER(MoeLinear), ctypes.POINTER(MoeLinear), vp, sz, vp]
+        for f in ("moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward", "moe_pack_weights"):
             getattr(L, f).restype = ctypes.c_int32
         L.moe_status_str.argtypes = [i32]
         L.moe_status_str.restype = ctypes.c_char_p
@@ -154,7 +155,49 @@ def linear(fmt: str, w: torch.Tensor, scales=None, qbias=None, bias=None, group_
     return Desc(c, [w, scales, qbias, bias])
 
 
+def _packable(d: Desc) -> bool:
+    c = d.c
+    return c.fmt != MOE_W_DENSE or c.dense_dtype == MOE_BF16
+
+
+def _on_gpu(d: Desc) -> bool:
+    return d.keep[0] is not None and d.keep[0].is_cuda
+
+
+def packed_bytes(a: Desc, b: Optional[Desc] = None) -> int:
+    """Size of the packed stream moe_pack_weights writes for a (gate/up pair: a, b)."""
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_pack_weights(ctypes.byref(a.c), ctypes.byref(b.c) if b is not None else None, None,
+                                  ctypes.byref(n), None))
+    return n.value
+
+
+def moe_pack_weights(a: Desc, b: Optional[Desc] = None, stream=None) -> torch.Tensor:
+    """The packed stream of stack a (or of the gate/up pair a, b) in a new 256-byte
+    aligned device buffer; the descriptor is not modified."""
+    nbytes = packed_bytes(a, b)
+    dev = a.keep[0].device
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    off = (-buf.data_ptr()) % 256
+    out = buf[off:off + nbytes]
+    n = ctypes.c_size_t(nbytes)
+    _check(lib().moe_pack_weights(ctypes.byref(a.c), ctypes.byref(b.c) if b is not None else None, out.data_ptr(),
+                                  ctypes.byref(n), _stream(stream)))
+    return out
+
+
+def attach_packed(d: Desc, b: Optional[Desc] = None):
+    """Pack d (the gate/up pair d, b) and point d.packed at the stream (kept alive by d)."""
+    t = moe_pack_weights(d, b)
+    d.c.packed = t.data_ptr()
+    d.keep.append(t)
+
+
 def mlp(gate: Desc, up: Desc, down: Desc, swiglu_limit: float = 0.0) -> Desc:
+    """SwiGLU stack; on the GPU the gate/up pair and the down stack are packed here."""
+    if _on_gpu(gate) and _packable(gate):
+        attach_packed(gate, up)
+        attach_packed(down)
     return Desc(MoeMLP(gate.c, up.c, down.c, float(swiglu_limit)), [gate, up, down])
 
 
@@ -169,6 +212,9 @@ def block(hidden: int, router_d: Desc, experts: Desc, shared: Optional[Desc] = N
           coef_w=None, coef_b=None, latent_down: Optional[Desc] = None, latent_up: Optional[Desc] = None,
           latent_norm_w=None, norm_eps: float = 1e-5, inter_dtype: int = MOE_BF16) -> Desc:
     D = experts.c.gate.cols
+    for lin in (latent_down, latent_up):
+        if lin is not None and _on_gpu(lin) and _packable(lin) and not lin.c.packed:
+            attach_packed(lin)
     empty_mlp = MoeMLP()
     c = MoeBlock(int(hidden), int(D), router_d.c, experts.c, SHARED_CODES[shared_mode],
                  shared.c if shared is not None else empty_mlp, _ptr(coef_w), _ptr(coef_b),

@@ -44,42 +44,30 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int dt_size(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
-// dynamic LDS of the grouped GEMM: per wave a 4 KB weight tile plus the scale strip of
-// its 32 rows (AFFINE4: one 4-byte word per group, scale | qbias << 16; MXFP4: one e8m0
-// byte per block).  Rows are padded so that 16 rows read at one column hit 16 banks.
-constexpr int kMaxWaveLds = 16384;
-constexpr int kMaxAffineGroups = (kMaxWaveLds - 4096) / 32 / 4 - 2;  // 94
-constexpr int kMaxMxBlocks = (kMaxWaveLds - 4096) / 32 - 4;           // 380
-void strip_layout(const moe_linear &L, int Kmax, int *wave_lds, int *strip_row) {
-  if (L.fmt == MOE_W_AFFINE4) {
-    *strip_row = (4 * (Kmax / L.group_size) + 4 + 7) & ~7;
-  } else if (L.fmt == MOE_W_MXFP4) {
-    *strip_row = (((Kmax / 32) + 3) & ~3) + 4;
-  } else {
-    *strip_row = 0;
-  }
-  *wave_lds = 4096 + 32 * *strip_row;
-}
-bool strip_fits(const moe_linear &L) {
-  int wl, sr;
-  strip_layout(L, L.cols, &wl, &sr);
-  return wl <= kMaxWaveLds;
-}
-
 // ---------------------------------------------------------------------------
 // validation
 // ---------------------------------------------------------------------------
 
+// how a descriptor is used: as the source of moe_pack_weights, or by a forward pass (the
+// BF16/F16 GEMM reads the packed stream; the up stack of a gate/up pair has none of its own)
+enum { USE_SOURCE = 0, USE_GEMM = 1, USE_GEMM_PAIRED = 2 };
+
 // act_dt: dtype of the activations this linear is applied to
-moe_status check_linear(const moe_linear *L, const char *name, int n, int rows, int cols, int act_dt) {
+moe_status check_linear(const moe_linear *L, const char *name, int n, int rows, int cols, int act_dt, int use) {
   CHECK(L != nullptr, MOE_ERR_ARG, "%s: descriptor is NULL", name);
   CHECK(L->n > 0 && L->rows > 0 && L->cols > 0, MOE_ERR_SHAPE, "%s: zero or negative dimension (n=%d rows=%d cols=%d)",
         name, L->n, L->rows, L->cols);
   CHECK(L->n == n, MOE_ERR_SHAPE, "%s: stack holds %d matrices, expected %d", name, L->n, n);
   CHECK(L->rows == rows && L->cols == cols, MOE_ERR_SHAPE, "%s: shape [%d, %d], expected [%d, %d]", name, L->rows,
         L->cols, rows, cols);
-  CHECK(L->w != nullptr, MOE_ERR_ARG, "%s: weight pointer is NULL", name);
-  CHECK(aligned(L->w, 16), MOE_ERR_ARG, "%s: weight pointer not 16-byte aligned", name);
+  const bool natural = use == USE_SOURCE || act_dt == MOE_F32;  // the natural-layout pointers are read
+  if (natural) {
+    CHECK(L->w != nullptr, MOE_ERR_ARG, "%s: weight pointer is NULL", name);
+    CHECK(aligned(L->w, 16), MOE_ERR_ARG, "%s: weight pointer not 16-byte aligned", name);
+  } else if (use == USE_GEMM) {
+    CHECK(L->packed != nullptr, MOE_ERR_ARG, "%s: packed stream is NULL (write it with moe_pack_weights)", name);
+    CHECK(aligned(L->packed, 256), MOE_ERR_ARG, "%s: packed stream not 256-byte aligned", name);
+  }
   CHECK(L->bias == nullptr || aligned(L->bias, 4), MOE_ERR_ARG, "%s: bias pointer misaligned", name);
   switch (L->fmt) {
     case MOE_W_DENSE:
@@ -97,15 +85,17 @@ moe_status check_linear(const moe_linear *L, const char *name, int n, int rows, 
             "%s: affine group_size %d (32, 64 or 128)", name, L->group_size);
       CHECK(cols % L->group_size == 0, MOE_ERR_SHAPE, "%s: cols %d not a multiple of group_size %d", name, cols,
             L->group_size);
-      CHECK(L->scales != nullptr && L->qbias != nullptr, MOE_ERR_ARG, "%s: affine scales/qbias missing", name);
-      CHECK(aligned(L->scales, 2) && aligned(L->qbias, 2), MOE_ERR_ARG, "%s: scales/qbias misaligned", name);
+      if (natural) {
+        CHECK(L->scales != nullptr && L->qbias != nullptr, MOE_ERR_ARG, "%s: affine scales/qbias missing", name);
+        CHECK(aligned(L->scales, 2) && aligned(L->qbias, 2), MOE_ERR_ARG, "%s: scales/qbias misaligned", name);
+      }
       CHECK(act_dt != MOE_F32, MOE_ERR_UNSUPPORTED, "%s: quantized weights need BF16/F16 activations", name);
       break;
     case MOE_W_MXFP4:
       CHECK(L->bits == 4, MOE_ERR_QUANT, "%s: mxfp4 bits %d (must be 4)", name, L->bits);
       CHECK(L->group_size == 32, MOE_ERR_QUANT, "%s: mxfp4 group_size %d (must be 32)", name, L->group_size);
       CHECK(cols % 64 == 0, MOE_ERR_SHAPE, "%s: mxfp4 cols %d not a multiple of 64", name, cols);
-      CHECK(L->scales != nullptr, MOE_ERR_ARG, "%s: mxfp4 scales missing", name);
+      if (natural) CHECK(L->scales != nullptr, MOE_ERR_ARG, "%s: mxfp4 scales missing", name);
       CHECK(act_dt != MOE_F32, MOE_ERR_UNSUPPORTED, "%s: quantized weights need BF16/F16 activations", name);
       break;
     default:
@@ -114,9 +104,6 @@ moe_status check_linear(const moe_linear *L, const char *name, int n, int rows, 
   if (act_dt != MOE_F32) {
     CHECK(rows % 16 == 0, MOE_ERR_SHAPE, "%s: rows %d not a multiple of 16", name, rows);
     CHECK(cols % 32 == 0, MOE_ERR_SHAPE, "%s: cols %d not a multiple of 32", name, cols);
-    CHECK(strip_fits(*L), MOE_ERR_UNSUPPORTED,
-          "%s: %d scale groups per row exceed this build's per-tile scale staging (affine: %d, mxfp4: %d)", name,
-          L->fmt == MOE_W_AFFINE4 ? cols / L->group_size : cols / 32, kMaxAffineGroups, kMaxMxBlocks);
   }
   return MOE_OK;
 }
@@ -124,11 +111,13 @@ moe_status check_linear(const moe_linear *L, const char *name, int n, int rows, 
 moe_status check_mlp(const moe_mlp *m, const char *name, int n, int I, int D, int act_in, int act_mid) {
   char nm[64];
   snprintf(nm, sizeof nm, "%s.gate", name);
-  TRY(check_linear(&m->gate, nm, n, I, D, act_in));
+  TRY(check_linear(&m->gate, nm, n, I, D, act_in, USE_GEMM));
   snprintf(nm, sizeof nm, "%s.up", name);
-  TRY(check_linear(&m->up, nm, n, I, D, act_in));
+  TRY(check_linear(&m->up, nm, n, I, D, act_in, USE_GEMM_PAIRED));
+  CHECK(m->up.fmt == m->gate.fmt && m->up.group_size == m->gate.group_size && m->up.dense_dtype == m->gate.dense_dtype,
+        MOE_ERR_UNSUPPORTED, "%s: gate and up stacks must share one format", name);
   snprintf(nm, sizeof nm, "%s.down", name);
-  TRY(check_linear(&m->down, nm, n, D, I, act_mid));
+  TRY(check_linear(&m->down, nm, n, D, I, act_mid, USE_GEMM));
   CHECK(std::isfinite(m->swiglu_limit), MOE_ERR_ARG, "%s: swiglu_limit not finite", name);
   return MOE_OK;
 }
@@ -199,8 +188,13 @@ int device_cus() {
   return cached[dev];
 }
 
-WMat wmat(const moe_linear &L) {
+WMat wmat(const moe_linear &L, bool gateup = false) {
   WMat m;
+  const int wf = L.fmt == MOE_W_DENSE ? WF_DENSE : (L.fmt == MOE_W_AFFINE4 ? WF_AFFINE4 : WF_MXFP4);
+  m.pk = (const char *)L.packed;
+  m.pk_nblk = gateup ? (L.rows + 15) / 16 : (L.rows + 31) / 32;
+  m.pk_nch = (L.cols + pk_kc(wf) - 1) / pk_kc(wf);
+  m.pk_mat = (int64_t)m.pk_nblk * m.pk_nch * pk_record_bytes(wf, L.group_size);
   m.w = L.w;
   m.scales = L.scales;
   m.qbias = L.qbias;
@@ -371,25 +365,14 @@ AOp aop(const void *a, int64_t lda, const int32_t *gather, int gdiv, int row_sub
   return o;
 }
 
-// scale entries of L loadable as aligned 4-byte words (AFFINE4: 2 entries, MXFP4: 4)
-bool scales_vec(const moe_linear &L) {
-  if (L.fmt == MOE_W_AFFINE4) {
-    const int G = L.cols / L.group_size;
-    return G % 2 == 0 && aligned(L.scales, 4) && aligned(L.qbias, 4);
-  }
-  if (L.fmt == MOE_W_MXFP4) return (L.cols / 32) % 4 == 0 && aligned(L.scales, 4);
-  return false;
-}
-
 SegSet segset(AOp A, const moe_linear &w0, const moe_linear *w1, float limit, bool gateup) {
   SegSet s;
   s.A = A;
-  s.w0 = wmat(w0);
-  s.w1 = w1 ? wmat(*w1) : s.w0;
+  s.w0 = wmat(w0, gateup);
+  s.w1 = w1 ? wmat(*w1, gateup) : s.w0;
   s.limit = limit;
   s.K = w0.cols;
   s.nblk = gateup ? (w0.rows + 63) / 64 : (w0.rows + 127) / 128;
-  s.svec = scales_vec(w0) && (!w1 || scales_vec(*w1)) ? 1 : 0;
   return s;
 }
 
@@ -418,7 +401,6 @@ moe_status run_gemm(int adt, const moe_linear &fmt_of, bool gateup, int odt, int
   p.ldo = ldo;
   p.resid = resid;
   p.ldr = ldr;
-  strip_layout(fmt_of, shared && shared->K > routed.K ? shared->K : routed.K, &p.wave_lds, &p.strip_row);
   const int units_ub = routed_tiles_ub(TK, E, mt) * routed.nblk + ((sh_rows + mt - 1) / mt) * p.seg[1].nblk;
   const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
   const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
@@ -452,7 +434,6 @@ moe_status run_plain(int adt, const moe_linear &W, const moe_linear *W1, float l
   p.ldo = ldo;
   p.resid = resid;
   p.ldr = ldr;
-  strip_layout(W, W.cols, &p.wave_lds, &p.strip_row);
   const int units = ((rows + mt - 1) / mt) * sg.nblk;
   const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
   const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
@@ -507,7 +488,48 @@ const char *moe_status_str(int32_t st) {
 
 const char *moe_last_error(void) { return g_err; }
 
-int32_t moe_abi_version(void) { return (1 << 16) | 0; }
+int32_t moe_abi_version(void) { return (2 << 16) | 0; }
+
+moe_status moe_pack_weights(const moe_linear *a, const moe_linear *b, void *out, size_t *out_bytes, void *stream) {
+  g_err[0] = 0;
+  CHECK(out_bytes != nullptr, MOE_ERR_ARG, "out_bytes is NULL");
+  CHECK(a != nullptr, MOE_ERR_ARG, "weight descriptor is NULL");
+  CHECK(a->fmt == MOE_W_AFFINE4 || a->fmt == MOE_W_MXFP4 || (a->fmt == MOE_W_DENSE && a->dense_dtype == MOE_BF16),
+        MOE_ERR_UNSUPPORTED, "packing needs AFFINE4, MXFP4 or DENSE BF16 weights (fmt %d)", a->fmt);
+  TRY(check_linear(a, b ? "gate" : "weights", a->n, a->rows, a->cols, MOE_BF16, USE_SOURCE));
+  if (b) {
+    TRY(check_linear(b, "up", a->n, a->rows, a->cols, MOE_BF16, USE_SOURCE));
+    CHECK(b->fmt == a->fmt && b->group_size == a->group_size && b->dense_dtype == a->dense_dtype,
+          MOE_ERR_UNSUPPORTED, "gate and up stacks must share one format");
+  }
+  const WMat m = wmat(*a, b != nullptr);
+  const size_t need = (size_t)a->n * (size_t)m.pk_mat;
+  if (out == nullptr) {
+    *out_bytes = need;
+    return MOE_OK;
+  }
+  CHECK(*out_bytes >= need, MOE_ERR_WORKSPACE, "packed buffer %zu bytes, need %zu", *out_bytes, need);
+  CHECK(aligned(out, 256), MOE_ERR_ARG, "packed buffer not 256-byte aligned");
+  PackArgs pa;
+  pa.wf = wf_of(*a);
+  pa.gq = a->fmt == MOE_W_AFFINE4 ? a->group_size : (a->fmt == MOE_W_MXFP4 ? 32 : 0);
+  pa.n = a->n;
+  pa.rows = a->rows;
+  pa.cols = a->cols;
+  pa.gateup = b != nullptr;
+  pa.dense_f32 = 0;
+  pa.a_w = a->w;
+  pa.a_s = a->scales;
+  pa.a_q = a->qbias;
+  pa.b_w = b ? b->w : nullptr;
+  pa.b_s = b ? b->scales : nullptr;
+  pa.b_q = b ? b->qbias : nullptr;
+  pa.out = (uint32_t *)out;
+  pa.nblk = m.pk_nblk;
+  pa.nch = m.pk_nch;
+  HIPCHK(launch_pack(pa, (hipStream_t)stream));
+  return MOE_OK;
+}
 
 moe_status moe_timing_enable(int32_t kind) {
   g_err[0] = 0;
@@ -706,8 +728,8 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
     CHECK(aligned(b->coef_w, 16), MOE_ERR_ARG, "coef_w not 16-byte aligned");
   }
   if (latent) {
-    TRY(check_linear(&b->latent_down, "latent_down", 1, D, H, x_dtype));
-    TRY(check_linear(&b->latent_up, "latent_up", 1, H, D, inter));
+    TRY(check_linear(&b->latent_down, "latent_down", 1, D, H, x_dtype, USE_GEMM));
+    TRY(check_linear(&b->latent_up, "latent_up", 1, H, D, inter, USE_GEMM));
     CHECK(b->latent_down.fmt == MOE_W_DENSE && b->latent_up.fmt == MOE_W_DENSE, MOE_ERR_UNSUPPORTED,
           "latent projections must be DENSE BF16");
     if (b->latent_norm_w) {

@@ -69,4 +69,5 @@ MOE_DEV float wave_max(float v) {
   return v;
 }
 
-MOE_DEV float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g * sigmoid(g); the reciprocal is the hardware one (1 ulp), the result is stored in 16 bits
+MOE_DEV float silu_f(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }

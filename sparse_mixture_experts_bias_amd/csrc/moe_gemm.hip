@@ -114,6 +114,21 @@ MOE_DEV u32x4_t cvt_mxfp4(uint32_t w, float scale) {
   return r;
 }
 
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0 and 15:14;
+// expcnt and lgkmcnt left at their maxima)
+template <int N>
+MOE_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// vector-memory instructions of one chunk's loads: 4 weight pieces, the scale words, SIT
+// activation blocks
+template <int WF, int GQ, int SIT>
+constexpr int LOADS_PER_CHUNK() {
+  return 4 + (WF == WF_AFFINE4 ? (pk_nu(WF, GQ) == 8 ? 4 : 2) : (WF == WF_MXFP4 ? 2 : 0)) + SIT;
+}
+
 MOE_DEV float e8m0_to_f32(uint32_t e) {
   return e == 0u ? __uint_as_float(0x00400000u) : (e == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float(e << 23));
 }
@@ -136,20 +151,20 @@ MOE_DEV u32x4_t cvt_dense(u32x4_t w) {
 
 }  // namespace
 
-// Every wave owns one 32-row weight tile: GATEUP: 16 gate rows (half 0) and the 16 up
-// rows of the same columns (half 1); LINEAR: 32 output rows.  Lane l works on tile rows
-// l%16 and 16 + l%16 and on the m-tile's tokens 16*mb + l%16 (A) / 16*mb + 4*(l/16) + i (D).
+// Every wave owns one 32-row weight tile, one row block of the packed stream: GATEUP: 16
+// gate rows (half 0) and the 16 up rows of the same outputs (half 1); LINEAR: 32 output
+// rows.  Lane l works on tile rows l%16 and 16 + l%16 and on the m-tile's tokens
+// 16*mb + l%16 (A operand) / 16*mb + 4*(l/16) + i (D).
 //
-// Weight stream: per chunk each tile row contributes one contiguous 128-byte segment; a
-// wave fetches its 4 KB with 16-byte loads, 8 lanes per row (whole cache lines), two
-// chunks ahead of the MFMAs, and writes them into its own LDS tile with the 16-byte
-// blocks of each row XOR-swizzled so that the MFMA-layout reads spread over the banks.
-// Scales/qbias (AFFINE4, one word per group: scale | qbias << 16) or E8M0 exponents
-// (MXFP4, one byte per block) of the tile's rows are copied to LDS once per unit.
+// Weight stream: a chunk record of the wave's row block is 4 KB of weights already in MFMA
+// lane order plus the chunk's scales, contiguous in HBM; every lane loads its own 64 bytes
+// with four 16-byte loads (each instruction reads 1 KB contiguous) and its scale words,
+// two chunks ahead of the MFMAs, straight into registers.  Only the activations go through
+// LDS (shared by the four waves).
 //
-// Reduction order: a "unit" of UE elements (AFFINE4: one quantisation group; MXFP4: 64; DENSE: 32)
-// is split into four contiguous quarters, one per lane quarter l/16; MFMA step s of the
-// unit takes elements [8s, 8s+8) of every quarter, so each step stays inside one group.
+// Reduction order: a "unit" of UE elements (AFFINE4: one quantisation group; MXFP4: 64;
+// DENSE: 32) is split into four contiguous quarters, one per lane quarter l/16; MFMA step s
+// of the unit takes elements [8s, 8s+8) of every quarter, so each step stays inside one group.
 template <int AT, int WF, int GQ, bool GATEUP, int OT, int MB>
 __global__ __launch_bounds__(MOE_GEMM_THREADS, MB == 1 ? 3 : 2) void expert_gemm(const GemmParams p) {
   constexpr bool AFF = (WF == WF_AFFINE4);
@@ -157,28 +172,28 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, MB == 1 ? 3 : 2) void expert_gemm
   constexpr bool DENSE = (WF == WF_DENSE);
   constexpr bool FOLD = AFF && MB == 1;                    // exact group fold; else dequantise
   constexpr int MT = 16 * MB;                              // rows per m-tile
-  constexpr int UE = AFF ? GQ : (MX ? 64 : 32);            // elements per unit
+  constexpr int UE = pk_ue(WF, GQ);                        // elements per unit
   constexpr int SPU = UE / 32;                             // MFMA steps per unit
   constexpr int QE = UE / 4;                               // elements per lane quarter per unit
-  constexpr int LB = DENSE ? 2 * QE : QE / 2;              // weight bytes per lane, unit and half
-  constexpr int KC = DENSE ? 64 : MOE_KC;                  // reduction elements per chunk (128 B per row)
-  constexpr int NU = KC / UE;                              // units per chunk
+  constexpr int LPU = pk_lb(WF, GQ) / 4;                   // weight words per lane, unit and half
+  constexpr int KC = pk_kc(WF);                            // reduction elements per chunk
+  constexpr int NU = pk_nu(WF, GQ);                        // units per chunk
+  constexpr int RB = pk_record_bytes(WF, GQ);              // bytes per chunk record
+  constexpr int NSW = AFF ? 2 * NU : (MX ? 4 : 1);         // scale words per lane per chunk
   constexpr int BPR = KC / 8;                              // 8-element activation blocks per chunk row
   constexpr int RPI = MOE_GEMM_THREADS / BPR;              // activation rows staged per iteration
   constexpr int SIT = (MT + RPI - 1) / RPI;                // activation staging iterations
   constexpr int LDA = KC + 8;                              // padded LDS activation row (16-bit elements)
+  constexpr int NSA = MB == 1 ? 2 : 1;                     // activation tiles (decode: double-buffered)
   constexpr float MAGIC = (FOLD && AT == DT_BF16) ? 128.0f : 1024.0f;
-  static_assert((DENSE ? KC * 2 : KC / 2) == 128, "128-byte row segments per chunk");
+  static_assert(2 * NU * LPU == 16, "64 weight bytes per lane per chunk");
   static_assert(KC % UE == 0 && UE % 32 == 0, "units of whole MFMA steps");
-  __shared__ __attribute__((aligned(16))) uint16_t sA[MT * LDA];
+  __shared__ __attribute__((aligned(16))) uint16_t sAbuf[NSA][MT * LDA];
   __shared__ int64_t sRow[MT];
-  extern __shared__ __attribute__((aligned(16))) char dyn[];  // per wave: weight tile + scale strip
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, kq = lane >> 4;
   const int sblk = tid % BPR, srow0 = tid / BPR;
-  char *wlds = dyn + wave * p.wave_lds;                    // 32 x 128 B weight tile
-  char *slds = wlds + 4096;                                // scale strip [32][strip_row]
   const uint32_t msk = in_vgpr(0x000F000Fu);
   const uint32_t mag = in_vgpr((FOLD && AT == DT_BF16) ? 0x43004300u : 0x64006400u);
 
@@ -215,10 +230,9 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, MB == 1 ? 3 : 2) void expert_gemm
     const int32_t *gat = SF(A.gather);
     const int gdiv = SF(A.gdiv), rsub = SF(A.row_sub);
     const int Kd = SF(K);
-    const int svec = SF(svec);
     const float limit = SF(limit);
     const WMat W0 = sh ? p.seg[1].w0 : p.seg[0].w0;
-    const WMat W1 = GATEUP ? (sh ? p.seg[1].w1 : p.seg[0].w1) : W0;
+    const uint16_t *bias1 = (const uint16_t *)(GATEUP ? SF(w1.bias) : W0.bias);  // bias of tile half 1
 #undef SF
 
     // tile row t (0..31) -> weight matrix row; GATEUP: rows 0-15 gate, 16-31 up
@@ -226,123 +240,99 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, MB == 1 ? 3 : 2) void expert_gemm
     const bool act = col0 < W0.rows;
     auto row_of = [&](int t) { return GATEUP ? col0 + (t & 15) : col0 + t; };
     auto row_ok = [&](int t) { return row_of(t) < W0.rows; };
-    auto mat_of = [&](int t) -> const WMat & { return (GATEUP && t >= 16) ? W1 : W0; };
     const int nchunks = (Kd + KC - 1) / KC;
 
-    // this lane's loader rows (tile rows 8*i + lane/8) and their segment base pointers
-    const char *lrow[4];
+    // this wave's row block of the packed stream (a clamped valid block when the wave idles)
+    const char *wbase = W0.pk + (int64_t)e * W0.pk_mat +
+                        (int64_t)min(nb * 4 + wave, W0.pk_nblk - 1) * W0.pk_nch * RB;
+    struct Ch {
+      u32x4_t w[4];
+      uint32_t s[NSW];
+    };
+    auto load_ch = [&](int kc, Ch &ch) {
+      const char *rec = wbase + (int64_t)(min(kc, (nchunks - 1) * KC) / KC) * RB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 8 * i + (lane >> 3);
-      const WMat &M = mat_of(t);
-      const int64_t rr = row_ok(t) ? row_of(t) : 0;
-      lrow[i] = (const char *)M.w + (int64_t)e * M.w_stride + rr * M.ldw + 16 * (lane & 7);
+      for (int i = 0; i < 4; ++i) ch.w[i] = *(const u32x4_t *)(rec + i * 1024 + lane * 16);
+      if constexpr (AFF) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const char *sp = rec + 4096 + (h * 16 + n16) * NU * 4;
+          if constexpr (NU == 8) {
+            const u32x4_t x0 = *(const u32x4_t *)sp, x1 = *(const u32x4_t *)(sp + 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              ch.s[h * 8 + j] = x0[j];
+              ch.s[h * 8 + 4 + j] = x1[j];
+            }
+          } else if constexpr (NU == 4) {
+            const u32x4_t x0 = *(const u32x4_t *)sp;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ch.s[h * 4 + j] = x0[j];
+          } else {
+            const u32x2_t x0 = *(const u32x2_t *)sp;
+            ch.s[h * 2] = x0[0];
+            ch.s[h * 2 + 1] = x0[1];
+          }
+        }
+      } else if constexpr (MX) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x2_t x0 = *(const u32x2_t *)(rec + 4096 + (h * 16 + n16) * 8);
+          ch.s[h * 2] = x0[0];
+          ch.s[h * 2 + 1] = x0[1];
+        }
+      } else {
+        ch.s[0] = 0u;
+      }
+    };
+
+    // output bias of this lane's two tile rows, loaded now so that the epilogue waits on nothing
+    float bo[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = 16 * h + n16;
+      const uint16_t *bp = h ? bias1 : (const uint16_t *)W0.bias;
+      bo[h] = bp ? bf16_bits_to_f32(bp[(int64_t)e * W0.rows + (row_ok(t) ? row_of(t) : 0)]) : 0.f;
     }
 
-    u32x4_t gA[4], gB[4], gC[4];  // weight ring: chunk c, c+1 in flight, c+2 being loaded
-    auto load_w = [&](int kc, u32x4_t (&g)[4]) {
-      const int kcc = min(kc, (nchunks - 1) * KC);
-      const int64_t off = DENSE ? (int64_t)kcc * 2 : kcc / 2;
-      // the last chunk may be shorter than 128 B per row: clamp the piece into the row
-      const int rowbytes = DENSE ? Kd * 2 : Kd / 2;
-      const int64_t o2 = min((int64_t)rowbytes - 16, off + 16 * (lane & 7)) - 16 * (lane & 7);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) g[i] = *(const u32x4_t *)(lrow[i] + o2);
-    };
-    load_w(0, gA);  // in flight during the set-up below
-    load_w(KC, gB);
+    Ch cA, cB, cC;  // weight ring: chunk c, c+1 in flight, c+2 being loaded
+    load_ch(0, cA);  // in flight during the set-up below
+    load_ch(KC, cB);
 
-    __syncthreads();  // the previous unit is done with sRow / sA / the LDS tiles
+    __syncthreads();  // the previous unit is done with sRow / sA
     if (tid < nr) {
       const int64_t arow = gat ? (int64_t)(gat[r0 + tid] / gdiv) : (int64_t)(r0 + tid - rsub);
       sRow[tid] = arow * lda;
     }
-
-    // ---- scale strips -> LDS (once per unit).  Row t of the strip belongs to tile row t.
-    //      AFF: entry g = scale_g | qbias_g << 16 (4 bytes);  MX: entry b = e8m0 byte.
-    if constexpr (AFF || MX) {
-      const int G = AFF ? Kd / GQ : Kd / 32;          // entries per row
-      const int per = svec ? (AFF ? 2 : 4) : 1;       // entries per load
-      const int npr = G / per;                        // loads per row
-      const int total = 32 * npr;
-      for (int i0 = 0; i0 < total; i0 += 64 * 8) {
-        uint32_t vs[8], vq[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int idx = min(i0 + 64 * k + lane, total - 1);
-          const int t = idx / npr, j = idx - t * npr;
-          const WMat &M = mat_of(t);
-          const int64_t rr = row_ok(t) ? row_of(t) : 0;
-          const int64_t ent = (int64_t)e * M.s_stride + rr * M.lds + (int64_t)j * per;
-          if constexpr (AFF) {
-            const uint16_t *sp = (const uint16_t *)M.scales + ent, *qp = (const uint16_t *)M.qbias + ent;
-            vs[k] = svec ? *(const uint32_t *)sp : (uint32_t)*sp;
-            vq[k] = svec ? *(const uint32_t *)qp : (uint32_t)*qp;
-          } else {
-            const uint8_t *sp = (const uint8_t *)M.scales + ent;
-            vs[k] = svec ? *(const uint32_t *)sp : (uint32_t)*sp;
-            vq[k] = 0;
-          }
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int idx = i0 + 64 * k + lane;
-          if (idx < total) {
-            const int t = idx / npr, j = idx - t * npr;
-            char *dst = slds + t * p.strip_row;
-            if constexpr (AFF) {
-              if (svec) {
-                const u32x2_t v = {(vs[k] & 0xFFFFu) | (vq[k] << 16), (vs[k] >> 16) | (vq[k] & 0xFFFF0000u)};
-                *(u32x2_t *)(dst + 8 * j) = v;
-              } else {
-                *(uint32_t *)(dst + 4 * j) = vs[k] | (vq[k] << 16);
-              }
-            } else {
-              if (svec)
-                *(uint32_t *)(dst + 4 * j) = vs[k];
-              else
-                dst[j] = (char)vs[k];
-            }
-          }
-        }
-      }
-    }
     __syncthreads();
 
-    // ---- loaders: raw bits only; every call issues the same loads (addresses clamped
-    // into valid memory) so the compiler can count them; out-of-chunk data is masked
-    // when consumed.
-    u32x4_t areg[SIT];
-    uint32_t amask = 0;
-    auto load_a = [&](int kc) {
+    // ---- activation staging: raw bits only; every call issues the same loads (addresses
+    // clamped into valid memory) so the compiler can count them; out-of-range data is zeroed
+    // when stored
+    auto load_a = [&](int kc, u32x4_t (&areg)[SIT]) {
       const int kcc = min(kc, (nchunks - 1) * KC);
       const int kn = min(KC, Kd - kcc);
-      amask = 0;
 #pragma unroll
       for (int it = 0; it < SIT; ++it) {
         const int row = srow0 + RPI * it;
-        const bool ok = row < nr && sblk * 8 < kn && kc < Kd;
-        amask |= ok ? (1u << it) : 0u;
         const int rr = row < nr ? row : 0;
         const int cc = sblk * 8 < kn ? sblk * 8 : 0;
         areg[it] = *(const u32x4_t *)(Ab + sRow[rr] + kcc + cc);
       }
     };
-    auto put_w = [&](const u32x4_t (&g)[4]) {  // registers -> swizzled LDS tile
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 8 * i + (lane >> 3);
-        const int pos = (lane & 7) ^ ((t >> 1) & 7);
-        *(u32x4_t *)(wlds + t * 128 + 16 * pos) = g[i];
-      }
-    };
-    auto store_a = [&]() {
+    // branch-free (rows past nr and columns past K are written as zeros), so that the
+    // compiler can count the loads still in flight instead of draining them all
+    auto store_a = [&](int kc, const u32x4_t (&areg)[SIT]) {
+      uint16_t *sA = sAbuf[(kc / KC) % NSA];
+      const bool colok = sblk * 8 < Kd - kc;
 #pragma unroll
       for (int it = 0; it < SIT; ++it) {
         const int row = srow0 + RPI * it;
-        if (row < nr) {
+        if (RPI * SIT <= MT || row < MT) {
           u32x4_t v = areg[it];
-          if (!((amask >> it) & 1u)) v = u32x4_t{0u, 0u, 0u, 0u};
+          const bool ok = colok && row < nr;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = ok ? v[q] : 0u;
           if constexpr (AFF) v = pair_i_i4(v);
           *(u32x4_t *)&sA[row * LDA + sblk * 8] = v;
         }
@@ -355,41 +345,30 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, MB == 1 ? 3 : 2) void expert_gemm
 #pragma unroll
       for (int h = 0; h < 2; ++h) acc[mb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int kc) {
+    auto compute = [&](int kc, const Ch &ch) {
       if (!act) return;
       const int nunits = min(KC, Kd - kc) / UE;
+      const uint16_t *sA = sAbuf[(kc / KC) % NSA];
 #pragma unroll
       for (int uu = 0; uu < NU; ++uu) {
         if (uu >= nunits) break;
         const int eoff = uu * UE + kq * QE;          // first element of this lane's quarter
-        const int boff = DENSE ? eoff * 2 : eoff / 2;
-        uint32_t wv[2][LB / 4];
+        uint32_t wv[2][LPU];
         float sc[2], cc[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int t = 16 * h + n16;
-          const char *rowp = wlds + t * 128;
-          const int sw = (t >> 1) & 7;
-          if constexpr (LB == 4) {
-            wv[h][0] = *(const uint32_t *)(rowp + 16 * ((boff >> 4) ^ sw) + (boff & 15));
-          } else if constexpr (LB == 8) {
-            const u32x2_t a = *(const u32x2_t *)(rowp + 16 * ((boff >> 4) ^ sw) + (boff & 15));
-            wv[h][0] = a[0];
-            wv[h][1] = a[1];
-          } else {
 #pragma unroll
-            for (int q = 0; q < LB / 16; ++q) {
-              const u32x4_t a = *(const u32x4_t *)(rowp + 16 * (((boff >> 4) + q) ^ sw));
-#pragma unroll
-              for (int i = 0; i < 4; ++i) wv[h][4 * q + i] = a[i];
-            }
+          for (int wi = 0; wi < LPU; ++wi) {
+            const int q = (uu * 2 + h) * LPU + wi;   // compile-time
+            wv[h][wi] = ch.w[q >> 2][q & 3];
           }
           if constexpr (AFF) {
-            const uint32_t v = *(const uint32_t *)(slds + t * p.strip_row + 4 * (kc / GQ + uu));
+            const uint32_t v = ch.s[h * NU + uu];
             sc[h] = __uint_as_float(v << 16);
             cc[h] = fmaf(-MAGIC, sc[h], __uint_as_float(v & 0xFFFF0000u));
           } else if constexpr (MX) {
-            sc[h] = e8m0_to_f32(*(const uint8_t *)(slds + t * p.strip_row + (kc >> 5) + 2 * uu + (kq >> 1)));
+            const uint32_t v = ch.s[h * 2 + (uu >> 1)];
+            sc[h] = e8m0_to_f32((v >> (8 * (2 * (uu & 1) + (kq >> 1)))) & 0xFFu);
             cc[h] = 0.f;
           } else {
             sc[h] = cc[h] = 0.f;
@@ -397,7 +376,7 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, MB == 1 ? 3 : 2) void expert_gemm
         }
         const uint16_t *arow = &sA[n16 * LDA + eoff];
         if constexpr (FOLD) {
-          // MB == 1: gate/up (or two row halves) share the A fragment and the group sums
+          // MB == 1: both halves share the A fragment and the group sums
           constexpr uint32_t ONE2 = (AT == DT_BF16) ? 0x3F803F80u : 0x3C003C00u;  // (1.0, 1.0)
           const u32x4_t ones = {ONE2, ONE2, ONE2, ONE2};
           const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
@@ -439,39 +418,61 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, MB == 1 ? 3 : 2) void expert_gemm
         }
       }
     };
-    // one chunk: stage its activations and weights, launch the loads two chunks ahead, compute
-    auto chunk = [&](int c, const u32x4_t (&gcur)[4], u32x4_t (&gnext2)[4]) {
-      const int kc = c * KC;
-      __syncthreads();  // readers of the previous chunk's activations are done
-      if (c < nchunks) {
-        store_a();
-        put_w(gcur);
-      }
-      load_a(kc + KC);
-      load_w(kc + 2 * KC, gnext2);
-      __syncthreads();
-      if (c < nchunks) compute(kc);
-    };
 
-    load_a(0);
-    for (int c = 0; c < nchunks; c += 3) {
-      chunk(c, gA, gC);
-      chunk(c + 1, gB, gA);
-      chunk(c + 2, gC, gB);
+    if constexpr (MB == 1) {
+      // decode tiles: activations and weights two chunks ahead (3-deep register rings); the
+      // activation tile is double-buffered, so one barrier per chunk suffices: a wave stores
+      // chunk c+1 only after every wave has passed chunk c's barrier, i.e. has finished
+      // computing chunk c-1, the last reader of that buffer.
+      u32x4_t aA[SIT], aB[SIT], aC[SIT];
+      auto chunk = [&](int c, const Ch &ccur, Ch &cnext2, const u32x4_t (&acur)[SIT], u32x4_t (&anext2)[SIT]) {
+        const int kc = c * KC;
+        store_a(kc, acur);  // chunks past the end stage clamped data that nobody reads
+        load_a(kc + 2 * KC, anext2);
+        load_ch(kc + 2 * KC, cnext2);
+        __syncthreads();
+        if (c < nchunks) compute(kc, ccur);
+      };
+      load_a(0, aA);
+      __builtin_amdgcn_sched_barrier(0);  // keep chunk 0's loads ahead of chunk 1's (in-order vmcnt)
+      load_a(KC, aB);
+      for (int c = 0; c < nchunks; c += 3) {
+        chunk(c, cA, cC, aA, aC);
+        chunk(c + 1, cB, cA, aB, aA);
+        chunk(c + 2, cC, cB, aC, aB);
+        // the next iteration starts on the loads of chunk c+1 (aA, cA); only chunk c+2's may
+        // stay in flight.  Waiting here, where it is due anyway, keeps the compiler from
+        // draining every load at the loop header.
+        wait_vmcnt<LOADS_PER_CHUNK<WF, GQ, SIT>()>();
+      }
+    } else {
+      u32x4_t aA[SIT];
+      auto chunk = [&](int c, const Ch &ccur, Ch &cnext2) {
+        const int kc = c * KC;
+        __syncthreads();
+        store_a(kc, aA);
+        load_a(kc + KC, aA);
+        load_ch(kc + 2 * KC, cnext2);
+        __syncthreads();
+        if (c < nchunks) compute(kc, ccur);
+      };
+      load_a(0, aA);
+      for (int c = 0; c < nchunks; c += 3) {
+        chunk(c, cA, cC);
+        chunk(c + 1, cB, cA);
+        chunk(c + 2, cC, cB);
+        wait_vmcnt<LOADS_PER_CHUNK<WF, GQ, 0>()>();  // as above: the weights of chunk c+2 may stay in flight
+      }
     }
 
     // ---- epilogue: acc[mb][h][i] is token 16*mb + 4*kq + i of the m-tile, tile row 16*h + n16
     if (act) {
-      float bo[2];
       bool ok[2];
       int wrow[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int t = 16 * h + n16;
-        const WMat &M = mat_of(t);
-        ok[h] = row_ok(t);
-        wrow[h] = row_of(t);
-        bo[h] = (ok[h] && M.bias) ? bf16_bits_to_f32(((const uint16_t *)M.bias)[(int64_t)e * M.rows + wrow[h]]) : 0.f;
+        ok[h] = row_ok(16 * h + n16);
+        wrow[h] = row_of(16 * h + n16);
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -552,11 +553,10 @@ __global__ __launch_bounds__(64) void f32_gemm_kernel(const F32GemmParams p) {
 // ---------------------------------------------------------------------------
 template <int AT, int WF, int GQ, bool GU, int OT>
 static hipError_t launch_t(int mb, const GemmParams &p, int grid, hipStream_t s) {
-  const size_t dyn = (size_t)p.wave_lds * (MOE_GEMM_THREADS / 64);
   if (mb == 1)
-    hipLaunchKernelGGL((expert_gemm<AT, WF, GQ, GU, OT, 1>), dim3(grid), dim3(MOE_GEMM_THREADS), dyn, s, p);
+    hipLaunchKernelGGL((expert_gemm<AT, WF, GQ, GU, OT, 1>), dim3(grid), dim3(MOE_GEMM_THREADS), 0, s, p);
   else if (mb == 4)
-    hipLaunchKernelGGL((expert_gemm<AT, WF, GQ, GU, OT, 4>), dim3(grid), dim3(MOE_GEMM_THREADS), dyn, s, p);
+    hipLaunchKernelGGL((expert_gemm<AT, WF, GQ, GU, OT, 4>), dim3(grid), dim3(MOE_GEMM_THREADS), 0, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

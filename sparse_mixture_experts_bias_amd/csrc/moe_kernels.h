@@ -21,9 +21,28 @@ struct TopkArgs {
   float *coef;          // blend coefficients [T][2]
 };
 
+// ---- packed weight stream (written by moe_pack_weights, read by the grouped GEMM) ----
+// Per matrix: row blocks of 32 tile rows (GATEUP: 16 gate rows then the 16 up rows of the
+// same outputs; LINEAR: 32 consecutive rows, zero-padded), each a run of chunk records, one
+// per PK_KC reduction elements (zero-padded past cols).  A record is 4096 bytes of weights
+// in MFMA lane order, piece (i, lane) at i*1024 + lane*16 holding words 4i..4i+3 of the
+// lane's 16-word sequence q = (unit*2 + half)*LPU + w (see pk_word_source), followed by the
+// chunk's scales: AFFINE4 [half][lane%16][unit] words (scale | qbias << 16), MXFP4
+// [half][lane%16][8] E8M0 bytes.
+__host__ __device__ constexpr int pk_kc(int wf) { return wf == WF_DENSE ? 64 : 256; }
+__host__ __device__ constexpr int pk_ue(int wf, int gq) { return wf == WF_AFFINE4 ? gq : (wf == WF_MXFP4 ? 64 : 32); }
+__host__ __device__ constexpr int pk_lb(int wf, int gq) {  // weight bytes per lane, unit and half
+  return wf == WF_DENSE ? 2 * (pk_ue(wf, gq) / 4) : pk_ue(wf, gq) / 8;
+}
+__host__ __device__ constexpr int pk_nu(int wf, int gq) { return pk_kc(wf) / pk_ue(wf, gq); }
+__host__ __device__ constexpr int pk_scale_bytes(int wf, int gq) {
+  return wf == WF_AFFINE4 ? 32 * pk_nu(wf, gq) * 4 : (wf == WF_MXFP4 ? 32 * 8 : 0);
+}
+__host__ __device__ constexpr int pk_record_bytes(int wf, int gq) { return 4096 + pk_scale_bytes(wf, gq); }
+
 // one stacked weight operand [n][rows][cols] (see moe_linear)
 struct WMat {
-  const void *w;
+  const void *w;        // natural layout (f32 path)
   const void *scales;
   const void *qbias;
   const void *bias;     // output bias [n][rows], bf16 (or nullptr)
@@ -32,6 +51,10 @@ struct WMat {
   int64_t ldw;          // bytes per row of w
   int lds;              // elements per row of scales/qbias
   int rows, cols;
+  const char *pk;       // packed stream (GATEUP: gate and up together, in w0)
+  int64_t pk_mat;       // bytes per matrix of the packed stream
+  int pk_nblk;          // row blocks per matrix
+  int pk_nch;           // chunk records per row block
 };
 
 // activation rows feeding a segment set: sorted row r reads A row
@@ -50,7 +73,6 @@ struct SegSet {
   float limit;          // GATEUP clamp (<= 0: none)
   int K;                // reduction length
   int nblk;             // column blocks of the output
-  int svec;             // scale entries load as aligned 4-byte words (AFFINE4 pairs, MXFP4 quads)
 };
 
 struct GemmParams {
@@ -64,8 +86,6 @@ struct GemmParams {
   int64_t ldo;
   const float *resid;   // LINEAR: optional f32 [rows][ldr] added before the store
   int64_t ldr;
-  int wave_lds;         // dynamic LDS bytes per wave: 4 KB weight tile + scale strip
-  int strip_row;        // bytes per scale-strip row in LDS
 };
 
 struct F32GemmParams {   // f32 activations with DENSE F32 weights (one thread per output)
@@ -115,4 +135,13 @@ __global__ void build_tiles(const int32_t *offsets, int E, int4 *tiles, int *til
 hipError_t launch_expert_gemm(int adt, int wfmt, int group, bool gateup, int odt, int mb, const GemmParams &p,
                               int grid, hipStream_t s);
 hipError_t launch_f32_gemm(const F32GemmParams &p, int rows, hipStream_t s);
+// packed stream of one matrix stack (b: the up stack of a gate/up pair, or nullptr)
+struct PackArgs {
+  int wf, gq, n, rows, cols, gateup, dense_f32;
+  const void *a_w, *a_s, *a_q;   // gate (or the only) stack, natural layout
+  const void *b_w, *b_s, *b_q;   // up stack (gateup) or nullptr
+  uint32_t *out;
+  int nblk, nch;
+};
+hipError_t launch_pack(const PackArgs &a, hipStream_t s);
 hipError_t launch_combine(int odt, int ydt, const CombineArgs &a, hipStream_t s);

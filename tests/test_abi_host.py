@@ -29,7 +29,8 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert set(names) == {"moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward", "moe_status_str",
+    assert set(names) == {"moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward", "moe_pack_weights",
+                          "moe_status_str",
                           "moe_last_error", "moe_abi_version", "moe_timing_enable", "moe_timing_read"}
     L = moe.lib()
     for n in names:
@@ -43,7 +44,7 @@ def test_status_strings_and_version():
                                  "MOE_ERR_DEVICE", "MOE_ERR_UNSUPPORTED"]):
         assert L.moe_status_str(code).decode() == name
     assert L.moe_status_str(99).decode() == "MOE_ERR_UNKNOWN"
-    assert moe.abi_version() >> 16 == 1
+    assert moe.abi_version() >> 16 == 2   # 2: moe_linear.packed and moe_pack_weights
     assert L.moe_timing_enable(42) == moe.MOE_ERR_ARG
     assert L.moe_timing_enable(0) == moe.MOE_OK
     assert moe.moe_timing_read() == (0, 0.0)
@@ -51,7 +52,7 @@ def test_status_strings_and_version():
 
 def test_struct_layouts_match_c():
     """ctypes mirrors of the C structs have the C sizes (x86-64 SysV alignment)."""
-    assert ctypes.sizeof(moe.MoeLinear) == 7 * 4 + 4 + 4 * 8
+    assert ctypes.sizeof(moe.MoeLinear) == 7 * 4 + 4 + 5 * 8
     assert ctypes.sizeof(moe.MoeMLP) == 3 * ctypes.sizeof(moe.MoeLinear) + 8
     assert ctypes.sizeof(moe.MoeRouter) == 5 * 4 + 4 + 3 * 8
 
@@ -67,6 +68,27 @@ def layers():
         b = synth.make_block(synth.SMALL_SPECS[cfg], "cpu")
         out[cfg] = b
     return out
+
+
+_HOST_PACKED = []
+
+
+def host_packed(desc):
+    """Point every packed stream of a host-side block descriptor at an aligned host buffer.
+    Only validation runs on these descriptors (workspace queries and rejected calls), which
+    checks the pointers and never reads through them."""
+    buf = (ctypes.c_uint8 * 1024)()
+    _HOST_PACKED.append(buf)
+    addr = ctypes.addressof(buf) + ((-ctypes.addressof(buf)) % 256)
+    c = desc.c
+    for lin in (c.experts.gate, c.experts.down, c.shared.gate, c.shared.down, c.latent_down, c.latent_up):
+        if lin.n > 0 and not (lin.fmt == moe.MOE_W_DENSE and lin.dense_dtype == moe.MOE_F32):
+            lin.packed = addr
+    return desc
+
+
+def bdesc(b):
+    return host_packed(block_desc(b))
 
 
 def query_block(b, desc, T=None, x_dtype=None, y_dtype=None):
@@ -108,7 +130,10 @@ HOSTILE = [
     ("c2", "experts.up.rows", 0, moe.MOE_ERR_SHAPE),                # zero checked before divisibility
     ("c2", "experts.down.cols", 100, moe.MOE_ERR_SHAPE),
     ("c2", "experts.gate.fmt", 9, moe.MOE_ERR_ARG),
-    ("c2", "experts.gate.scales", None, moe.MOE_ERR_ARG),
+    ("c2", "experts.gate.packed", None, moe.MOE_ERR_ARG),          # the GEMM reads only the packed stream
+    ("c2", "experts.down.packed", "misaligned", moe.MOE_ERR_ARG),
+    ("c2", "experts.up.fmt", moe.MOE_W_MXFP4, moe.MOE_ERR_QUANT),  # up checked on its own first (group 64)
+    ("c5", "latent_down.packed", None, moe.MOE_ERR_ARG),
     ("c2", "experts.swiglu_limit", float("inf"), moe.MOE_ERR_ARG),
     ("c2", "shared_mode", 5, moe.MOE_ERR_ARG),
     ("c2", "coef_w", None, moe.MOE_ERR_ARG),                        # blend without its coefficient head
@@ -130,10 +155,15 @@ HOSTILE = [
 def test_hostile_block_argument(case, layers):
     cfg, path, val, want = HOSTILE[case]
     b = layers[cfg]
-    desc = block_desc(b)
+    desc = bdesc(b)
     st, need = query_block(b, desc)
     assert st == moe.MOE_OK and need > 0, "positive control must validate"
-    bad = block_desc(b)
+    bad = bdesc(b)
+    if val == "misaligned":
+        obj = bad.c
+        for part in path.split(".")[:-1]:
+            obj = getattr(obj, part)
+        val = getattr(obj, path.split(".")[-1]) + 8
     _set(path)(bad.c, val)
     st, _ = query_block(b, bad)
     assert st == want, (path, val, moe.lib().moe_status_str(st), moe.lib().moe_last_error())
@@ -142,26 +172,26 @@ def test_hostile_block_argument(case, layers):
 
 def test_token_count_guards(layers):
     b = layers["c2"]
-    d = block_desc(b)
+    d = bdesc(b)
     assert query_block(b, d, T=-1)[0] == moe.MOE_ERR_SHAPE
     assert query_block(b, d, T=2 ** 40)[0] == moe.MOE_ERR_SHAPE     # T*K would overflow int32 slot ids
     st, n0 = query_block(b, d, T=0)
     assert st == moe.MOE_OK
     assert query_block(b, d, x_dtype=moe.MOE_F16)[0] == moe.MOE_ERR_ARG
     assert query_block(b, d, y_dtype=moe.MOE_F16)[0] == moe.MOE_ERR_ARG
-    assert query_block(layers["c1"], block_desc(layers["c1"]), y_dtype=moe.MOE_BF16)[0] == moe.MOE_ERR_UNSUPPORTED
+    assert query_block(layers["c1"], bdesc(layers["c1"]), y_dtype=moe.MOE_BF16)[0] == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_workspace_grows_with_tokens(layers):
     b = layers["c2"]
-    d = block_desc(b)
+    d = bdesc(b)
     sizes = [query_block(b, d, T=t)[1] for t in (1, 64, 1024)]
     assert sizes[0] < sizes[1] < sizes[2]
 
 
 def test_workspace_too_small_or_misaligned(layers):
     b = layers["c2"]
-    d = block_desc(b)
+    d = bdesc(b)
     st, need = query_block(b, d)
     buf = (ctypes.c_uint8 * (need + 512))()
     base = ctypes.addressof(buf)
@@ -199,9 +229,64 @@ def test_route_permute_experts_queries(layers):
     assert L.moe_permute(None, 10, 9, 8, None, None, None, None, None, ctypes.byref(n), None) == moe.MOE_ERR_SHAPE
     assert L.moe_permute(None, 10, 2, 8, None, None, None, None, None, None, None) == moe.MOE_ERR_ARG
     ex = synth.descs.mlp_desc(b.experts)
+    buf = (ctypes.c_uint8 * 512)()
+    _HOST_PACKED.append(buf)
+    ex.c.gate.packed = ex.c.down.packed = ctypes.addressof(buf) + ((-ctypes.addressof(buf)) % 256)
     assert L.moe_experts_forward(None, moe.MOE_BF16, b.T, b.H, ctypes.byref(ex.c), b.E, b.K, None, None, None, None,
                                  None, moe.MOE_BF16, None, None, ctypes.byref(n), None) == moe.MOE_OK
     assert L.moe_experts_forward(None, moe.MOE_BF16, b.T, b.H, ctypes.byref(ex.c), b.E + 1, b.K, None, None, None,
                                  None, None, moe.MOE_BF16, None, None, ctypes.byref(n), None) == moe.MOE_ERR_SHAPE
     assert L.moe_experts_forward(None, moe.MOE_BF16, b.T, b.H, ctypes.byref(ex.c), b.E, b.K, None, None, None, None,
                                  None, moe.MOE_F32, None, None, ctypes.byref(n), None) == moe.MOE_ERR_ARG
+
+
+# ----------------------------------------------------------------------------
+# moe_pack_weights: size queries and rejected arguments (nothing is launched)
+# ----------------------------------------------------------------------------
+
+def _pack_query(a, b=None):
+    n = ctypes.c_size_t(0)
+    st = moe.lib().moe_pack_weights(ctypes.byref(a.c), ctypes.byref(b.c) if b is not None else None, None,
+                                    ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_pack_sizes_follow_the_documented_layout(layers):
+    """n * row blocks * chunks * record bytes; records are 4096 bytes of weights plus the
+    chunk's scales (affine: 4 bytes per row and group, mxfp4: 1 byte per row and block)."""
+    from synth.descs import linear_desc
+    b2 = layers["c2"]
+    g, u, d = (linear_desc(m) for m in (b2.experts.gate, b2.experts.up, b2.experts.down))
+    E, I, H, G = b2.E, b2.I, b2.H, b2.experts.gate.group_size
+    ceil = lambda a, q: -(-a // q)
+    rec_aff = 4096 + 32 * (256 // G) * 4
+    assert _pack_query(g, u) == (moe.MOE_OK, E * ceil(I, 16) * ceil(H, 256) * rec_aff)
+    assert _pack_query(d) == (moe.MOE_OK, E * ceil(H, 32) * ceil(I, 256) * rec_aff)
+    b5 = layers["c5"]
+    g5, u5 = linear_desc(b5.experts.gate), linear_desc(b5.experts.up)
+    assert _pack_query(g5, u5) == (moe.MOE_OK, b5.E * ceil(b5.I, 16) * ceil(b5.D, 256) * (4096 + 32 * 8))
+    ld = linear_desc(b5.latent_down)
+    assert _pack_query(ld) == (moe.MOE_OK, ceil(b5.D, 32) * ceil(b5.H, 64) * 4096)
+
+
+def test_pack_rejects_bad_arguments(layers):
+    from synth.descs import linear_desc
+    L = moe.lib()
+    b2 = layers["c2"]
+    g, u = linear_desc(b2.experts.gate), linear_desc(b2.experts.up)
+    assert _pack_query(g, u)[0] == moe.MOE_OK
+    bad = linear_desc(b2.experts.gate)
+    bad.c.scales = None                                   # the source planes are read by the packing
+    assert _pack_query(bad)[0] == moe.MOE_ERR_ARG
+    f32 = linear_desc(layers["c1"].experts.gate)          # dense f32 has no packed form
+    assert _pack_query(f32)[0] == moe.MOE_ERR_UNSUPPORTED
+    u5 = linear_desc(layers["c5"].experts.up)             # gate and up must share one format and shape
+    assert _pack_query(g, u5)[0] in (moe.MOE_ERR_SHAPE, moe.MOE_ERR_UNSUPPORTED)
+    assert L.moe_pack_weights(ctypes.byref(g.c), None, None, None, None) == moe.MOE_ERR_ARG
+    st, need = _pack_query(g)
+    buf = (ctypes.c_uint8 * 1024)()
+    base = ctypes.addressof(buf) + ((-ctypes.addressof(buf)) % 256)
+    n = ctypes.c_size_t(need - 1)
+    assert L.moe_pack_weights(ctypes.byref(g.c), None, base, ctypes.byref(n), None) == moe.MOE_ERR_WORKSPACE
+    n = ctypes.c_size_t(need)
+    assert L.moe_pack_weights(ctypes.byref(g.c), None, base + 8, ctypes.byref(n), None) == moe.MOE_ERR_ARG

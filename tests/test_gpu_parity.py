@@ -257,3 +257,97 @@ def test_swiglu_limit_engages():
     spec = synth.replace(synth.SMALL_SPECS["c5"], swiglu_limit=0.5, seed=77)
     b = synth.make_block(spec, DEV)
     _full_check(b, "clamp 0.5")
+
+
+# ----------------------------------------------------------------------------
+# the packed weight stream: a pure permutation of the stored planes
+# ----------------------------------------------------------------------------
+
+def _expect_packed(lins, gateup: bool, fmt: str, group: int):
+    """The stream rebuilt in numpy from the layout stated in include/moe.h / moe_kernels.h:
+    per matrix, per 32-row block, per chunk: 4096 bytes of weights (piece (i, lane) at
+    i*1024 + lane*16 holds words 4i..4i+3 of the lane's sequence q = (unit*2 + half)*LPU + w)
+    followed by the chunk's scales; zero past the rows and columns."""
+    a = lins[0]
+    n, R, K = a.n, a.rows, a.cols
+    dense = fmt == synth.FMT_DENSE
+    aff = fmt == synth.FMT_AFFINE4
+    KC = 64 if dense else 256
+    UE = group if aff else (64 if fmt == synth.FMT_MXFP4 else 32)
+    QE = UE // 4
+    LPU = (2 * QE if dense else QE // 2) // 4
+    NU = KC // UE
+    SW = (32 * NU) if aff else (64 if fmt == synth.FMT_MXFP4 else 0)   # scale words per record
+    nblk = -(-R // 16) if gateup else -(-R // 32)
+    nch = -(-K // KC)
+    words = [l.w.cpu().contiguous().view(torch.int32).numpy().view(np.uint32).reshape(n, R, -1) for l in lins]
+    wpr = words[0].shape[2]
+    out = np.zeros((n, nblk, nch, 1024 + SW), dtype=np.uint32)
+    lane = np.arange(64)
+    n16, kq = lane % 16, lane // 16
+    for q in range(16):
+        i, j = q // 4, q % 4
+        uu, h, wi = q // (2 * LPU), (q // LPU) % 2, q % LPU
+        for bk in range(nblk):
+            src = words[h] if gateup else words[0]
+            row = (16 * bk + n16) if gateup else (32 * bk + 16 * h + n16)
+            for c in range(nch):
+                e0 = c * KC + uu * UE + kq * QE
+                word = (e0 // 2 + wi) if dense else (e0 // 8 + wi)
+                ok = (row < R) & (e0 < K)
+                vals = np.where(ok[None, :], src[:, np.minimum(row, R - 1), np.minimum(word, wpr - 1)], 0)
+                out[:, bk, c, i * 256 + lane * 4 + j] = vals
+    if aff:
+        G = K // group
+        sc = [l.scales.cpu().view(torch.int16).numpy().astype(np.uint16).reshape(n, R, G) for l in lins]
+        qb = [l.qbias.cpu().view(torch.int16).numpy().astype(np.uint16).reshape(n, R, G) for l in lins]
+        for h in range(2):
+            for r16 in range(16):
+                for un in range(NU):
+                    ent = h * 16 * NU + r16 * NU + un
+                    for bk in range(nblk):
+                        li = h if gateup else 0
+                        row = (16 * bk + r16) if gateup else (32 * bk + 16 * h + r16)
+                        for c in range(nch):
+                            g = c * KC // group + un
+                            if row < R and g < G:
+                                out[:, bk, c, 1024 + ent] = (sc[li][:, row, g].astype(np.uint32) |
+                                                            (qb[li][:, row, g].astype(np.uint32) << 16))
+    elif fmt == synth.FMT_MXFP4:
+        NB = K // 32
+        e8 = [l.scales.cpu().contiguous().numpy().view(np.uint8).reshape(n, R, NB) for l in lins]
+        by = np.zeros((n, nblk, nch, 256), dtype=np.uint32)
+        for h in range(2):
+            for r16 in range(16):
+                for jj in range(8):
+                    for bk in range(nblk):
+                        li = h if gateup else 0
+                        row = (16 * bk + r16) if gateup else (32 * bk + 16 * h + r16)
+                        for c in range(nch):
+                            g = c * KC // 32 + jj
+                            if row < R and g < NB:
+                                by[:, bk, c, h * 128 + r16 * 8 + jj] = e8[li][:, row, g]
+        b4 = by.reshape(n, nblk, nch, 64, 4)
+        out[..., 1024:] = b4[..., 0] | (b4[..., 1] << 8) | (b4[..., 2] << 16) | (b4[..., 3] << 24)
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("cfg,which", [("c2", "gateup"), ("c4", "down"), ("c5", "gateup"), ("c5", "latent_down")])
+def test_packed_stream_is_the_documented_permutation(cfg, which):
+    from synth.descs import linear_desc
+    announce(f"packed layout {cfg} {which}")
+    b = synth.make_block(synth.SMALL_SPECS[cfg], "cuda:0")
+    if which == "gateup":
+        lins, gu = [b.experts.gate, b.experts.up], True
+        got = moe.moe_pack_weights(linear_desc(lins[0]), linear_desc(lins[1]))
+    elif which == "down":
+        lins, gu = [b.experts.down], False
+        got = moe.moe_pack_weights(linear_desc(lins[0]))
+    else:
+        lins, gu = [b.latent_down], False
+        got = moe.moe_pack_weights(linear_desc(lins[0]))
+    torch.cuda.synchronize()
+    want = _expect_packed(lins, gu, lins[0].fmt, lins[0].group_size)
+    have = got.cpu().numpy().view(np.uint32)
+    assert have.shape == want.shape
+    assert np.array_equal(have, want)
