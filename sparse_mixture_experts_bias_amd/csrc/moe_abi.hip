@@ -227,17 +227,24 @@ struct Timing {
   int used = 0;
 } g_timing;
 
-struct Timed {  // brackets one launch with events when its class is being timed
+// Times one launch of a class when that class is being timed.  By default the launch is
+// bracketed with event records on its stream; with `in_dispatch` the caller hands start()
+// and stop() to hipExtLaunchKernelGGL, which stamps them at the kernel's own start and end
+// (what a kernel-trace profiler reports), without the cost of the records themselves.
+struct Timed {
   int slot = -1;
+  bool ext;
   hipStream_t s;
-  Timed(int kind, hipStream_t st) : s(st) {
+  Timed(int kind, hipStream_t st, bool in_dispatch = false) : ext(in_dispatch), s(st) {
     if (g_timing.kind == kind && g_timing.used < kTimingPairs) {
       slot = g_timing.used++;
-      (void)hipEventRecord(g_timing.ev[2 * slot], s);
+      if (!ext) (void)hipEventRecord(g_timing.ev[2 * slot], s);
     }
   }
+  hipEvent_t start() const { return slot >= 0 ? g_timing.ev[2 * slot] : nullptr; }
+  hipEvent_t stop() const { return slot >= 0 ? g_timing.ev[2 * slot + 1] : nullptr; }
   ~Timed() {
-    if (slot >= 0) (void)hipEventRecord(g_timing.ev[2 * slot + 1], s);
+    if (slot >= 0 && !ext) (void)hipEventRecord(g_timing.ev[2 * slot + 1], s);
   }
 };
 
@@ -404,9 +411,9 @@ moe_status run_gemm(int adt, const moe_linear &fmt_of, bool gateup, int odt, int
   const int units_ub = routed_tiles_ub(TK, E, mt) * routed.nblk + ((sh_rows + mt - 1) / mt) * p.seg[1].nblk;
   const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
   const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
-  Timed tm(gateup ? TK_GATEUP : TK_DOWN, s);
+  Timed tm(gateup ? TK_GATEUP : TK_DOWN, s, true);
   HIPCHK(launch_expert_gemm(adt_k, wf_of(fmt_of), fmt_of.group_size, gateup, odt_k, mb, p, gemm_grid(units_ub, mb),
-                            s));
+                            s, tm.start(), tm.stop()));
   return MOE_OK;
 }
 
@@ -437,8 +444,9 @@ moe_status run_plain(int adt, const moe_linear &W, const moe_linear *W1, float l
   const int units = ((rows + mt - 1) / mt) * sg.nblk;
   const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
   const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
-  Timed tm(TK_PLAIN, s);
-  HIPCHK(launch_expert_gemm(adt_k, wf_of(W), W.group_size, gateup, odt_k, mb, p, gemm_grid(units, mb), s));
+  Timed tm(TK_PLAIN, s, true);
+  HIPCHK(launch_expert_gemm(adt_k, wf_of(W), W.group_size, gateup, odt_k, mb, p, gemm_grid(units, mb), s, tm.start(),
+                            tm.stop()));
   return MOE_OK;
 }
 

@@ -31,6 +31,8 @@
 //     conversion turns E2M1 codes times the block's 2^(e-127) into bf16/f16
 //     exactly; the block scale is applied in that conversion.
 //   DENSE bf16: used as is (converted to f16 when the activations are f16).
+#include <hip/hip_ext.h>
+
 #include "moe_kernels.h"
 
 namespace {
@@ -204,7 +206,12 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, MB == 1 ? 3 : 2) void expert_gemm
   const int units_s = ns * nblk1;
   const int nr_routed = p.tiles ? p.tile_count[0] : 0;
 
-  for (int u = blockIdx.x;; u += gridDim.x) {
+  // workgroups are dealt to the 8 XCDs round-robin; renumber them so that consecutive units
+  // (the column blocks of one m-tile, which share its activation rows) run on one XCD and
+  // share its L2
+  const int G = gridDim.x;
+  const int b0 = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  for (int u = b0;; u += G) {
     const bool sh = u < units_s;
     int ti, nb;
     int4 tile;
@@ -551,48 +558,56 @@ __global__ __launch_bounds__(64) void f32_gemm_kernel(const F32GemmParams p) {
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
+// e0/e1: optional events stamped at the kernel's start and end (timing)
 template <int AT, int WF, int GQ, bool GU, int OT>
-static hipError_t launch_t(int mb, const GemmParams &p, int grid, hipStream_t s) {
+static hipError_t launch_t(int mb, const GemmParams &p, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  auto go = [&](auto kern) {
+    if (e0)
+      hipExtLaunchKernelGGL(kern, dim3(grid), dim3(MOE_GEMM_THREADS), 0, s, e0, e1, 0, p);
+    else
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(MOE_GEMM_THREADS), 0, s, p);
+  };
   if (mb == 1)
-    hipLaunchKernelGGL((expert_gemm<AT, WF, GQ, GU, OT, 1>), dim3(grid), dim3(MOE_GEMM_THREADS), 0, s, p);
+    go(expert_gemm<AT, WF, GQ, GU, OT, 1>);
   else if (mb == 4)
-    hipLaunchKernelGGL((expert_gemm<AT, WF, GQ, GU, OT, 4>), dim3(grid), dim3(MOE_GEMM_THREADS), 0, s, p);
+    go(expert_gemm<AT, WF, GQ, GU, OT, 4>);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 template <int AT, int WF, int GQ>
-static hipError_t launch_o(bool gateup, int odt, int mb, const GemmParams &p, int grid, hipStream_t s) {
+static hipError_t launch_o(bool gateup, int odt, int mb, const GemmParams &p, int grid, hipStream_t s, hipEvent_t e0,
+                           hipEvent_t e1) {
   if (gateup) {
-    if (odt == DT_BF16) return launch_t<AT, WF, GQ, true, DT_BF16>(mb, p, grid, s);
-    if (odt == DT_F16) return launch_t<AT, WF, GQ, true, DT_F16>(mb, p, grid, s);
+    if (odt == DT_BF16) return launch_t<AT, WF, GQ, true, DT_BF16>(mb, p, grid, s, e0, e1);
+    if (odt == DT_F16) return launch_t<AT, WF, GQ, true, DT_F16>(mb, p, grid, s, e0, e1);
   } else {
-    if (odt == DT_F32) return launch_t<AT, WF, GQ, false, DT_F32>(mb, p, grid, s);
-    if (odt == DT_BF16) return launch_t<AT, WF, GQ, false, DT_BF16>(mb, p, grid, s);
-    if (odt == DT_F16) return launch_t<AT, WF, GQ, false, DT_F16>(mb, p, grid, s);
+    if (odt == DT_F32) return launch_t<AT, WF, GQ, false, DT_F32>(mb, p, grid, s, e0, e1);
+    if (odt == DT_BF16) return launch_t<AT, WF, GQ, false, DT_BF16>(mb, p, grid, s, e0, e1);
+    if (odt == DT_F16) return launch_t<AT, WF, GQ, false, DT_F16>(mb, p, grid, s, e0, e1);
   }
   return hipErrorInvalidValue;
 }
 
 template <int AT>
 static hipError_t launch_w(int wfmt, int group, bool gateup, int odt, int mb, const GemmParams &p, int grid,
-                           hipStream_t s) {
-  if (wfmt == WF_DENSE) return launch_o<AT, WF_DENSE, 0>(gateup, odt, mb, p, grid, s);
-  if (wfmt == WF_MXFP4) return launch_o<AT, WF_MXFP4, 0>(gateup, odt, mb, p, grid, s);
+                           hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (wfmt == WF_DENSE) return launch_o<AT, WF_DENSE, 0>(gateup, odt, mb, p, grid, s, e0, e1);
+  if (wfmt == WF_MXFP4) return launch_o<AT, WF_MXFP4, 0>(gateup, odt, mb, p, grid, s, e0, e1);
   if (wfmt == WF_AFFINE4) {
-    if (group == 32) return launch_o<AT, WF_AFFINE4, 32>(gateup, odt, mb, p, grid, s);
-    if (group == 64) return launch_o<AT, WF_AFFINE4, 64>(gateup, odt, mb, p, grid, s);
-    if (group == 128) return launch_o<AT, WF_AFFINE4, 128>(gateup, odt, mb, p, grid, s);
+    if (group == 32) return launch_o<AT, WF_AFFINE4, 32>(gateup, odt, mb, p, grid, s, e0, e1);
+    if (group == 64) return launch_o<AT, WF_AFFINE4, 64>(gateup, odt, mb, p, grid, s, e0, e1);
+    if (group == 128) return launch_o<AT, WF_AFFINE4, 128>(gateup, odt, mb, p, grid, s, e0, e1);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_expert_gemm(int adt, int wfmt, int group, bool gateup, int odt, int mb, const GemmParams &p,
-                              int grid, hipStream_t s) {
+                              int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (grid <= 0) return hipSuccess;
-  if (adt == DT_BF16) return launch_w<DT_BF16>(wfmt, group, gateup, odt, mb, p, grid, s);
-  if (adt == DT_F16) return launch_w<DT_F16>(wfmt, group, gateup, odt, mb, p, grid, s);
+  if (adt == DT_BF16) return launch_w<DT_BF16>(wfmt, group, gateup, odt, mb, p, grid, s, e0, e1);
+  if (adt == DT_F16) return launch_w<DT_F16>(wfmt, group, gateup, odt, mb, p, grid, s, e0, e1);
   return hipErrorInvalidValue;
 }
 

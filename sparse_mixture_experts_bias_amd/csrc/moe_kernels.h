@@ -133,7 +133,7 @@ __global__ void build_tiles(const int32_t *offsets, int E, int4 *tiles, int *til
 
 // host-side launchers (moe_gemm.hip, moe_combine.hip)
 hipError_t launch_expert_gemm(int adt, int wfmt, int group, bool gateup, int odt, int mb, const GemmParams &p,
-                              int grid, hipStream_t s);
+                              int grid, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 hipError_t launch_f32_gemm(const F32GemmParams &p, int rows, hipStream_t s);
 // packed stream of one matrix stack (b: the up stack of a gate/up pair, or nullptr)
 struct PackArgs {
