@@ -357,9 +357,16 @@ int max_tiles(int TK, int E) { return routed_tiles_ub(TK, E, MOE_MT_MIN) + 1; }
 int pick_mb(double avg_rows) { return avg_rows <= 16.0 ? 1 : 4; }
 int mb_for_routing(int TK, int E) { return pick_mb((double)TK / (E < TK ? E : (TK > 0 ? TK : 1))); }
 
+// mb: 1 (decode tiles), 4 (prefill tiles) or 0 (decode tiles, SHORT variant)
 int gemm_grid(int units_ub, int mb) {
-  const int cap = (mb == 1 ? 3 : 2) * device_cus();  // resident workgroups of the grouped GEMM per CU
+  const int cap = (mb == 0 ? 4 : (mb == 1 ? 3 : 2)) * device_cus();  // resident workgroups per CU
   return units_ub < cap ? units_ub : cap;
+}
+
+// decode LINEAR launches whose longest reduction spans at most three chunks use the SHORT variant
+int kernel_mb(int mb, bool gateup, const moe_linear &w, int kmax) {
+  const int kc = w.fmt == MOE_W_DENSE ? 64 : 256;
+  return (mb == 1 && !gateup && (kmax + kc - 1) / kc <= 3) ? 0 : mb;
 }
 
 AOp aop(const void *a, int64_t lda, const int32_t *gather, int gdiv, int row_sub) {
@@ -411,9 +418,10 @@ moe_status run_gemm(int adt, const moe_linear &fmt_of, bool gateup, int odt, int
   const int units_ub = routed_tiles_ub(TK, E, mt) * routed.nblk + ((sh_rows + mt - 1) / mt) * p.seg[1].nblk;
   const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
   const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
+  const int kmb = kernel_mb(mb, gateup, fmt_of, shared && shared->K > routed.K ? shared->K : routed.K);
   Timed tm(gateup ? TK_GATEUP : TK_DOWN, s, true);
-  HIPCHK(launch_expert_gemm(adt_k, wf_of(fmt_of), fmt_of.group_size, gateup, odt_k, mb, p, gemm_grid(units_ub, mb),
-                            s, tm.start(), tm.stop()));
+  HIPCHK(launch_expert_gemm(adt_k, wf_of(fmt_of), fmt_of.group_size, gateup, odt_k, kmb, p,
+                            gemm_grid(units_ub, kmb), s, tm.start(), tm.stop()));
   return MOE_OK;
 }
 
@@ -444,9 +452,10 @@ moe_status run_plain(int adt, const moe_linear &W, const moe_linear *W1, float l
   const int units = ((rows + mt - 1) / mt) * sg.nblk;
   const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
   const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
+  const int kmb = kernel_mb(mb, gateup, W, W.cols);
   Timed tm(TK_PLAIN, s, true);
-  HIPCHK(launch_expert_gemm(adt_k, wf_of(W), W.group_size, gateup, odt_k, mb, p, gemm_grid(units, mb), s, tm.start(),
-                            tm.stop()));
+  HIPCHK(launch_expert_gemm(adt_k, wf_of(W), W.group_size, gateup, odt_k, kmb, p, gemm_grid(units, kmb), s,
+                            tm.start(), tm.stop()));
   return MOE_OK;
 }
 

@@ -167,8 +167,13 @@ MOE_DEV u32x4_t cvt_dense(u32x4_t w) {
 // Reduction order: a "unit" of UE elements (AFFINE4: one quantisation group; MXFP4: 64;
 // DENSE: 32) is split into four contiguous quarters, one per lane quarter l/16; MFMA step s
 // of the unit takes elements [8s, 8s+8) of every quarter, so each step stays inside one group.
-template <int AT, int WF, int GQ, bool GATEUP, int OT, int MB>
-__global__ __launch_bounds__(MOE_GEMM_THREADS, MB == 1 ? 3 : 2) void expert_gemm(const GemmParams p) {
+//
+// SHORT (decode tiles with at most three chunks, e.g. down projections of a few hundred
+// reduction elements): the whole unit is loaded at once, weights into registers and the
+// activations into three LDS tiles, then computed without further barriers; the smaller
+// register footprint gives four workgroups per CU.
+template <int AT, int WF, int GQ, bool GATEUP, int OT, int MB, bool SHORT = false>
+__global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : (MB == 1 ? 3 : 2)) void expert_gemm(const GemmParams p) {
   constexpr bool AFF = (WF == WF_AFFINE4);
   constexpr bool MX = (WF == WF_MXFP4);
   constexpr bool DENSE = (WF == WF_DENSE);
@@ -186,7 +191,8 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, MB == 1 ? 3 : 2) void expert_gemm
   constexpr int RPI = MOE_GEMM_THREADS / BPR;              // activation rows staged per iteration
   constexpr int SIT = (MT + RPI - 1) / RPI;                // activation staging iterations
   constexpr int LDA = KC + 8;                              // padded LDS activation row (16-bit elements)
-  constexpr int NSA = MB == 1 ? 2 : 1;                     // activation tiles (decode: double-buffered)
+  constexpr int NSA = SHORT ? 3 : (MB == 1 ? 2 : 1);       // activation tiles (decode: double-buffered)
+  static_assert(!SHORT || MB == 1, "SHORT is a decode-tile variant");
   constexpr float MAGIC = (FOLD && AT == DT_BF16) ? 128.0f : 1024.0f;
   static_assert(2 * NU * LPU == 16, "64 weight bytes per lane per chunk");
   static_assert(KC % UE == 0 && UE % 32 == 0, "units of whole MFMA steps");
@@ -305,6 +311,7 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, MB == 1 ? 3 : 2) void expert_gemm
     Ch cA, cB, cC;  // weight ring: chunk c, c+1 in flight, c+2 being loaded
     load_ch(0, cA);  // in flight during the set-up below
     load_ch(KC, cB);
+    if constexpr (SHORT) load_ch(2 * KC, cC);
 
     __syncthreads();  // the previous unit is done with sRow / sA
     if (tid < nr) {
@@ -426,7 +433,19 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, MB == 1 ? 3 : 2) void expert_gemm
       }
     };
 
-    if constexpr (MB == 1) {
+    if constexpr (SHORT) {
+      u32x4_t a0[SIT], a1[SIT], a2[SIT];
+      load_a(0, a0);
+      load_a(KC, a1);
+      load_a(2 * KC, a2);
+      store_a(0, a0);
+      store_a(KC, a1);
+      store_a(2 * KC, a2);
+      __syncthreads();
+      compute(0, cA);
+      if (nchunks > 1) compute(KC, cB);
+      if (nchunks > 2) compute(2 * KC, cC);
+    } else if constexpr (MB == 1) {
       // decode tiles: activations and weights two chunks ahead (3-deep register rings); the
       // activation tile is double-buffered, so one barrier per chunk suffices: a wave stores
       // chunk c+1 only after every wave has passed chunk c's barrier, i.e. has finished
@@ -558,7 +577,8 @@ __global__ __launch_bounds__(64) void f32_gemm_kernel(const F32GemmParams p) {
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
-// e0/e1: optional events stamped at the kernel's start and end (timing)
+// e0/e1: optional events stamped at the kernel's start and end (timing).  mb == 0 selects
+// the SHORT decode variant (LINEAR only).
 template <int AT, int WF, int GQ, bool GU, int OT>
 static hipError_t launch_t(int mb, const GemmParams &p, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   auto go = [&](auto kern) {
@@ -567,6 +587,12 @@ static hipError_t launch_t(int mb, const GemmParams &p, int grid, hipStream_t s,
     else
       hipLaunchKernelGGL(kern, dim3(grid), dim3(MOE_GEMM_THREADS), 0, s, p);
   };
+  if constexpr (!GU) {
+    if (mb == 0) {
+      go(expert_gemm<AT, WF, GQ, GU, OT, 1, true>);
+      return hipGetLastError();
+    }
+  }
   if (mb == 1)
     go(expert_gemm<AT, WF, GQ, GU, OT, 1>);
   else if (mb == 4)
