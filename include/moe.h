@@ -148,8 +148,10 @@ typedef struct {
  *          blocks of 16 gate rows followed by the same 16 up rows
  *   out    device buffer, 256-byte aligned; NULL: write the size to *out_bytes
  *   out_bytes  in: size of out; too small -> MOE_ERR_WORKSPACE
- * The stream is a permutation of the stored words, scales and qbias (nothing is
- * converted); rows and reduction elements are zero-padded to whole blocks of 32 rows
+ * The stream is a permutation of the stored codes, scales and qbias (nothing is
+ * converted; AFFINE4 words hold their 8 codes with the even elements in the low
+ * half-word and the odd ones in the high half-word, element 2j at bit 4j and 2j+1 at
+ * bit 16+4j); rows and reduction elements are zero-padded to whole blocks of 32 rows
  * and 256 elements (64 for DENSE).  Layout: per matrix, per row block, per chunk a
  * record of 4096 bytes of weights in MFMA lane order followed by the chunk's scales
  * (AFFINE4: 4 bytes per row and group, MXFP4: 1 byte per row and block).

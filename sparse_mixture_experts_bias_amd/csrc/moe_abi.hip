@@ -353,14 +353,34 @@ moe_status launch_permute(const int32_t *idx, int T, int K, int E, int32_t *coun
 int routed_tiles_ub(int TK, int E, int mt) { return TK / mt + (E < TK ? E : TK); }
 int max_tiles(int TK, int E) { return routed_tiles_ub(TK, E, MOE_MT_MIN) + 1; }
 
-// m-blocks (16 rows each) per m-tile: 1 for decode-sized segments, 4 otherwise
-int pick_mb(double avg_rows) { return avg_rows <= 16.0 ? 1 : 4; }
+// m-blocks (16 rows each) per m-tile: 1 for decode-sized segments (the HBM-streaming
+// kernel), 8 otherwise (the 128-row MFMA kernel of moe_gemm_tall.hip)
+constexpr int MB_TALL = 8;
+int pick_mb(double avg_rows) { return avg_rows <= 16.0 ? 1 : MB_TALL; }
 int mb_for_routing(int TK, int E) { return pick_mb((double)TK / (E < TK ? E : (TK > 0 ? TK : 1))); }
 
-// mb: 1 (decode tiles), 4 (prefill tiles) or 0 (decode tiles, SHORT variant)
+// mb: 1 (decode tiles), 0 (decode tiles, SHORT variant) or MB_TALL
 int gemm_grid(int units_ub, int mb) {
-  const int cap = (mb == 0 ? 4 : (mb == 1 ? 3 : 2)) * device_cus();  // resident workgroups per CU
+  const int cap = (mb == 0 ? 4 : (mb == 1 ? 3 : 1)) * device_cus();  // resident workgroups per CU
   return units_ub < cap ? units_ub : cap;
+}
+
+// output column blocks of a segment: the decode kernel's 4 waves cover 64 gate/up outputs or
+// 128 rows, the tall kernel's 8 waves twice that
+int col_blocks(const SegSet &sg, bool gateup, int mb) {
+  const int w = (gateup ? 64 : 128) * (mb == MB_TALL ? 2 : 1);
+  return (sg.w0.rows + w - 1) / w;
+}
+
+hipError_t launch_gemm_kernel(int adt, const moe_linear &fmt_of, bool gateup, int odt, int kmb, const GemmParams &p,
+                              int units_ub, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
+  const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
+  if (kmb == MB_TALL)
+    return launch_expert_gemm_tall(adt_k, wf_of(fmt_of), fmt_of.group_size, gateup, odt_k, p,
+                                   gemm_grid(units_ub, kmb), s, e0, e1);
+  return launch_expert_gemm(adt_k, wf_of(fmt_of), fmt_of.group_size, gateup, odt_k, kmb, p, gemm_grid(units_ub, kmb),
+                            s, e0, e1);
 }
 
 // decode LINEAR launches whose longest reduction spans at most three chunks use the SHORT variant
@@ -386,7 +406,7 @@ SegSet segset(AOp A, const moe_linear &w0, const moe_linear *w1, float limit, bo
   s.w1 = w1 ? wmat(*w1, gateup) : s.w0;
   s.limit = limit;
   s.K = w0.cols;
-  s.nblk = gateup ? (w0.rows + 63) / 64 : (w0.rows + 127) / 128;
+  s.nblk = 0;  // set by the launch (col_blocks) for the kernel it picks
   return s;
 }
 
@@ -400,11 +420,10 @@ moe_status run_gemm(int adt, const moe_linear &fmt_of, bool gateup, int odt, int
   GemmParams p;
   memset(&p, 0, sizeof p);
   p.seg[0] = routed;
+  p.seg[0].nblk = col_blocks(routed, gateup, mb);
   p.seg[1] = shared ? *shared : routed;
-  if (!shared) {
-    p.seg[1].nblk = 0;
-    sh_rows = 0;
-  }
+  p.seg[1].nblk = shared ? col_blocks(*shared, gateup, mb) : 0;
+  if (!shared) sh_rows = 0;
   p.tiles = tiles;
   p.tile_count = tile_count;
   p.max_tiles = ntiles_alloc;
@@ -415,13 +434,10 @@ moe_status run_gemm(int adt, const moe_linear &fmt_of, bool gateup, int odt, int
   p.ldo = ldo;
   p.resid = resid;
   p.ldr = ldr;
-  const int units_ub = routed_tiles_ub(TK, E, mt) * routed.nblk + ((sh_rows + mt - 1) / mt) * p.seg[1].nblk;
-  const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
-  const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
+  const int units_ub = routed_tiles_ub(TK, E, mt) * p.seg[0].nblk + ((sh_rows + mt - 1) / mt) * p.seg[1].nblk;
   const int kmb = kernel_mb(mb, gateup, fmt_of, shared && shared->K > routed.K ? shared->K : routed.K);
   Timed tm(gateup ? TK_GATEUP : TK_DOWN, s, true);
-  HIPCHK(launch_expert_gemm(adt_k, wf_of(fmt_of), fmt_of.group_size, gateup, odt_k, kmb, p,
-                            gemm_grid(units_ub, kmb), s, tm.start(), tm.stop()));
+  HIPCHK(launch_gemm_kernel(adt, fmt_of, gateup, odt, kmb, p, units_ub, s, tm.start(), tm.stop()));
   return MOE_OK;
 }
 
@@ -432,6 +448,7 @@ moe_status run_plain(int adt, const moe_linear &W, const moe_linear *W1, float l
   const int mb = pick_mb(rows);
   const int mt = 16 * mb;
   SegSet sg = segset(aop(a, lda, nullptr, 1, 0), W, W1, limit, gateup);
+  sg.nblk = col_blocks(sg, gateup, mb);
   SegSet none = sg;
   none.nblk = 0;
   // plain mode: every m-tile is a segment-1 tile; the routed set has no units
@@ -450,12 +467,9 @@ moe_status run_plain(int adt, const moe_linear &W, const moe_linear *W1, float l
   p.resid = resid;
   p.ldr = ldr;
   const int units = ((rows + mt - 1) / mt) * sg.nblk;
-  const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
-  const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
   const int kmb = kernel_mb(mb, gateup, W, W.cols);
   Timed tm(TK_PLAIN, s, true);
-  HIPCHK(launch_expert_gemm(adt_k, wf_of(W), W.group_size, gateup, odt_k, kmb, p, gemm_grid(units, kmb), s,
-                            tm.start(), tm.stop()));
+  HIPCHK(launch_gemm_kernel(adt, W, gateup, odt, kmb, p, units, s, tm.start(), tm.stop()));
   return MOE_OK;
 }
 

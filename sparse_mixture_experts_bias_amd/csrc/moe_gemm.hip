@@ -25,133 +25,15 @@
 //     gives scale*(1024+q) + (qbias - 1024*scale) in fp32, rounded once to the
 //     MFMA's 16-bit type; the per-group fold would cost VALU in proportion to the
 //     tile height, the dequantisation only per weight.
-//     The nibble pairs come out as (q_i, q_{i+4}), so the activation rows are
-//     staged with the matching element order inside every 8-element block.
+//     The packed words hold the codes in pair order, so the nibble pairs come out
+//     as adjacent elements (q_2j, q_2j+1) and the activations are used as stored.
 //   MXFP4 (libmir-metal ExpertLayout blocks/scales): gfx950's scaled FP4
 //     conversion turns E2M1 codes times the block's 2^(e-127) into bf16/f16
 //     exactly; the block scale is applied in that conversion.
 //   DENSE bf16: used as is (converted to f16 when the activations are f16).
 #include <hip/hip_ext.h>
 
-#include "moe_kernels.h"
-
-namespace {
-
-// 16x16x32 MFMA: lane l holds A[m = l%16][k = 8*(l/16) .. +8), B[k = 8*(l/16) .. +8][n = l%16]
-// and D[m = 4*(l/16) + i][n = l%16], i = 0..3.
-template <int AT>
-MOE_DEV f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
-  if constexpr (AT == DT_BF16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                   c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
-                                                  0, 0, 0);
-}
-
-// a constant the compiler must keep in a VGPR (so that mask-and-or with two constants is one v_and_or_b32)
-MOE_DEV uint32_t in_vgpr(uint32_t v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
-// 8 nibbles (element i in bits 4i..4i+3) -> 4 words holding (mag+q_i, mag+q_{i+4}), i = 0..3
-MOE_DEV u32x4_t magic_pairs(uint32_t w, uint32_t msk, uint32_t mag) {
-  u32x4_t r;
-  r[0] = (w & msk) | mag;
-  r[1] = ((w >> 4) & msk) | mag;
-  r[2] = ((w >> 8) & msk) | mag;
-  r[3] = ((w >> 12) & msk) | mag;
-  return r;
-}
-
-MOE_DEV float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
-MOE_DEV float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
-
-// 8 nibbles -> 4 words of dequantised (w_i, w_{i+4}) in the MFMA type; w = sc*(1024+q) + c,
-// c = qbias - 1024*sc (one fp32 FMA from the exact f16 1024+q, one rounding to 16 bits)
-template <int AT>
-MOE_DEV u32x4_t deq_affine(uint32_t w, uint32_t msk, uint32_t mag16, float sc, float c) {
-  const u32x4_t m = magic_pairs(w, msk, mag16);
-  u32x4_t r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float lo = fmaf(f16lo(m[j]), sc, c), hi = fmaf(f16hi(m[j]), sc, c);
-    if constexpr (AT == DT_BF16) {
-      const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
-      r[j] = __builtin_bit_cast(uint32_t, v);
-    } else {
-      r[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
-    }
-  }
-  return r;
-}
-
-// activation block (e0..e7) -> (e0,e4),(e1,e5),(e2,e6),(e3,e7): the order of magic_pairs
-MOE_DEV u32x4_t pair_i_i4(u32x4_t v) {
-  u32x4_t o;
-  o[0] = (v[0] & 0xFFFFu) | (v[2] << 16);
-  o[1] = (v[0] >> 16) | (v[2] & 0xFFFF0000u);
-  o[2] = (v[1] & 0xFFFFu) | (v[3] << 16);
-  o[3] = (v[1] >> 16) | (v[3] & 0xFFFF0000u);
-  return o;
-}
-
-// 8 E2M1 codes (two per byte, low nibble first) times a power-of-two scale
-template <int AT>
-MOE_DEV u32x4_t cvt_mxfp4(uint32_t w, float scale) {
-  u32x4_t r;
-  if constexpr (AT == DT_BF16) {
-    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
-    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
-    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
-    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
-  } else {
-    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 0));
-    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 1));
-    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 2));
-    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 3));
-  }
-  return r;
-}
-
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0 and 15:14;
-// expcnt and lgkmcnt left at their maxima)
-template <int N>
-MOE_DEV void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// vector-memory instructions of one chunk's loads: 4 weight pieces, the scale words, SIT
-// activation blocks
-template <int WF, int GQ, int SIT>
-constexpr int LOADS_PER_CHUNK() {
-  return 4 + (WF == WF_AFFINE4 ? (pk_nu(WF, GQ) == 8 ? 4 : 2) : (WF == WF_MXFP4 ? 2 : 0)) + SIT;
-}
-
-MOE_DEV float e8m0_to_f32(uint32_t e) {
-  return e == 0u ? __uint_as_float(0x00400000u) : (e == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float(e << 23));
-}
-
-template <int AT>
-MOE_DEV u32x4_t cvt_dense(u32x4_t w) {
-  if constexpr (AT == DT_BF16) {
-    return w;
-  } else {
-    u32x4_t r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const _Float16 lo = (_Float16)__uint_as_float(w[i] << 16);
-      const _Float16 hi = (_Float16)__uint_as_float(w[i] & 0xFFFF0000u);
-      r[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-    }
-    return r;
-  }
-}
-
-}  // namespace
+#include "moe_mfma.h"
 
 // Every wave owns one 32-row weight tile, one row block of the packed stream: GATEUP: 16
 // gate rows (half 0) and the 16 up rows of the same outputs (half 1); LINEAR: 32 output
@@ -347,7 +229,6 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : (MB == 1 ? 3 : 2)) vo
           const bool ok = colok && row < nr;
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = ok ? v[q] : 0u;
-          if constexpr (AFF) v = pair_i_i4(v);
           *(u32x4_t *)&sA[row * LDA + sblk * 8] = v;
         }
       }
@@ -595,8 +476,6 @@ static hipError_t launch_t(int mb, const GemmParams &p, int grid, hipStream_t s,
   }
   if (mb == 1)
     go(expert_gemm<AT, WF, GQ, GU, OT, 1>);
-  else if (mb == 4)
-    go(expert_gemm<AT, WF, GQ, GU, OT, 4>);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -28,7 +28,8 @@ struct TopkArgs {
 // in MFMA lane order, piece (i, lane) at i*1024 + lane*16 holding words 4i..4i+3 of the
 // lane's 16-word sequence q = (unit*2 + half)*LPU + w (see pk_word_source), followed by the
 // chunk's scales: AFFINE4 [half][lane%16][unit] words (scale | qbias << 16), MXFP4
-// [half][lane%16][8] E8M0 bytes.
+// [half][lane%16][8] E8M0 bytes.  AFFINE4 weight words keep their 8 codes in pair order:
+// element 2j at bits 4j..4j+3, element 2j+1 at bits 16+4j..19+4j.
 __host__ __device__ constexpr int pk_kc(int wf) { return wf == WF_DENSE ? 64 : 256; }
 __host__ __device__ constexpr int pk_ue(int wf, int gq) { return wf == WF_AFFINE4 ? gq : (wf == WF_MXFP4 ? 64 : 32); }
 __host__ __device__ constexpr int pk_lb(int wf, int gq) {  // weight bytes per lane, unit and half
@@ -134,6 +135,9 @@ __global__ void build_tiles(const int32_t *offsets, int E, int4 *tiles, int *til
 // host-side launchers (moe_gemm.hip, moe_combine.hip)
 hipError_t launch_expert_gemm(int adt, int wfmt, int group, bool gateup, int odt, int mb, const GemmParams &p,
                               int grid, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+// prefill-sized segments: 128-row m-tiles, 8-wave workgroups (moe_gemm_tall.hip)
+hipError_t launch_expert_gemm_tall(int adt, int wfmt, int group, bool gateup, int odt, const GemmParams &p,
+                                   int grid, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 hipError_t launch_f32_gemm(const F32GemmParams &p, int rows, hipStream_t s);
 // packed stream of one matrix stack (b: the up stack of a gate/up pair, or nullptr)
 struct PackArgs {

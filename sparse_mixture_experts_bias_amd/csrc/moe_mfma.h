@@ -1,0 +1,113 @@
+// moe_mfma.h - operand helpers of the grouped GEMMs: the 16x16x32 MFMA, 4-bit and FP4
+// weight conversion to the MFMA's 16-bit types, and explicit vector-memory waits.
+#pragma once
+
+#include "moe_kernels.h"
+
+namespace {
+
+// 16x16x32 MFMA: lane l holds A[m = l%16][k = 8*(l/16) .. +8), B[k = 8*(l/16) .. +8][n = l%16]
+// and D[m = 4*(l/16) + i][n = l%16], i = 0..3.
+template <int AT>
+MOE_DEV f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  if constexpr (AT == DT_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+}
+
+// a constant the compiler must keep in a VGPR (so that mask-and-or with two constants is one v_and_or_b32)
+MOE_DEV uint32_t in_vgpr(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// 8 nibbles in pair order (nibble position i in bits 4i..4i+3) -> 4 words holding the
+// 16-bit values (mag + nibble i, mag + nibble i+4), i = 0..3: elements (2i, 2i+1)
+MOE_DEV u32x4_t magic_pairs(uint32_t w, uint32_t msk, uint32_t mag) {
+  u32x4_t r;
+  r[0] = (w & msk) | mag;
+  r[1] = ((w >> 4) & msk) | mag;
+  r[2] = ((w >> 8) & msk) | mag;
+  r[3] = ((w >> 12) & msk) | mag;
+  return r;
+}
+
+MOE_DEV float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+MOE_DEV float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// 8 nibbles -> 4 words of dequantised element pairs in the MFMA type; w = sc*(1024+q) + c,
+// c = qbias - 1024*sc (one fp32 FMA from the exact f16 1024+q, one rounding to 16 bits)
+template <int AT>
+MOE_DEV u32x4_t deq_affine(uint32_t w, uint32_t msk, uint32_t mag16, float sc, float c) {
+  const u32x4_t m = magic_pairs(w, msk, mag16);
+  u32x4_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = fmaf(f16lo(m[j]), sc, c), hi = fmaf(f16hi(m[j]), sc, c);
+    if constexpr (AT == DT_BF16) {
+      const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+      r[j] = __builtin_bit_cast(uint32_t, v);
+    } else {
+      const f16x2_t v = {(_Float16)lo, (_Float16)hi};  // one v_cvt_pk_f16_f32
+      r[j] = __builtin_bit_cast(uint32_t, v);
+    }
+  }
+  return r;
+}
+
+// 8 E2M1 codes (two per byte, low nibble first) times a power-of-two scale
+template <int AT>
+MOE_DEV u32x4_t cvt_mxfp4(uint32_t w, float scale) {
+  u32x4_t r;
+  if constexpr (AT == DT_BF16) {
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  } else {
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 0));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 1));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 2));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 3));
+  }
+  return r;
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0 and 15:14;
+// expcnt and lgkmcnt left at their maxima)
+template <int N>
+MOE_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// vector-memory instructions of one chunk's loads: 4 weight pieces, the scale words, SIT
+// activation blocks
+template <int WF, int GQ, int SIT>
+constexpr int LOADS_PER_CHUNK() {
+  return 4 + (WF == WF_AFFINE4 ? (pk_nu(WF, GQ) == 8 ? 4 : 2) : (WF == WF_MXFP4 ? 2 : 0)) + SIT;
+}
+
+MOE_DEV float e8m0_to_f32(uint32_t e) {
+  return e == 0u ? __uint_as_float(0x00400000u) : (e == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float(e << 23));
+}
+
+template <int AT>
+MOE_DEV u32x4_t cvt_dense(u32x4_t w) {
+  if constexpr (AT == DT_BF16) {
+    return w;
+  } else {
+    u32x4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2_t v = {(_Float16)__uint_as_float(w[i] << 16), (_Float16)__uint_as_float(w[i] & 0xFFFF0000u)};
+      r[i] = __builtin_bit_cast(uint32_t, v);
+    }
+    return r;
+  }
+}
+
+}  // namespace

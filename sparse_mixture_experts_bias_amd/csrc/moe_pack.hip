@@ -7,6 +7,19 @@
 // never converted, so a GEMM over the packed stream sees exactly the stored values.
 #include "moe_kernels.h"
 
+// AFFINE4 word of 8 codes (element j in bits 4j..4j+3) -> even elements in the low
+// half-word, odd ones in the high half-word (element 2j at bits 4j, element 2j+1 at bits
+// 16+4j), so that (w >> 4j) & 0x000F000F is the adjacent pair (2j, 2j+1)
+static __device__ uint32_t pair_order(uint32_t v) {
+  uint32_t r = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r |= ((v >> (8 * j)) & 0xFu) << (4 * j);
+    r |= ((v >> (8 * j + 4)) & 0xFu) << (16 + 4 * j);
+  }
+  return r;
+}
+
 __global__ __launch_bounds__(256) void pack_kernel(const PackArgs a) {
   const int kc_len = pk_kc(a.wf), ue = pk_ue(a.wf, a.gq), qe = ue / 4, lpu = pk_lb(a.wf, a.gq) / 4;
   const int nu = pk_nu(a.wf, a.gq), rw = pk_record_bytes(a.wf, a.gq) / 4;
@@ -39,6 +52,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const PackArgs a) {
         const uint32_t *w = (const uint32_t *)(upper ? a.b_w : a.a_w);
         const int word = a.wf == WF_DENSE ? e0 / 2 + wi : e0 / 8 + wi;
         v = w[((int64_t)m * a.rows + row) * wpr + word];
+        if (a.wf == WF_AFFINE4) v = pair_order(v);
       }
     } else if (a.wf == WF_AFFINE4) {  // [half][n16][unit]: scale | qbias << 16
       const int ent = o - 1024;

@@ -412,10 +412,17 @@ static __device__ void emit_tiles(const int *offs, int E, int mt, int4 *tiles, i
   for (int e = tid; e < E; e += blockDim.x) nmc[e] = (offs[e + 1] - offs[e] + mt - 1) / mt;
   __syncthreads();
   const int R = block_exclusive_scan(nmc, E, tmp);
+  // a segment of n rows becomes t = ceil(n / mt) tiles of q rows (the last one takes the
+  // rest, 1..q rows), q = ceil(n / t) rounded up to whole 16-row blocks and capped at mt: the
+  // fewest tiles, all but the last made of whole 16-row blocks, so that they hold
+  // ceil(n / 16) blocks in all
   for (int e = tid; e < E; e += blockDim.x) {
     const int n = offs[e + 1] - offs[e];
-    for (int i = 0, base = nmc[e]; i * mt < n; ++i)
-      tiles[base + i] = make_int4(e, offs[e] + i * mt, min(mt, n - i * mt), 0);
+    if (n == 0) continue;
+    const int t = (n + mt - 1) / mt;
+    const int q = min(mt, (((n + t - 1) / t) + 15) & ~15);
+    for (int i = 0, base = nmc[e]; i < t; ++i)
+      tiles[base + i] = make_int4(e, offs[e] + i * q, min(q, n - i * q), 0);
   }
   if (tid == 0) tile_count[0] = R;
 }

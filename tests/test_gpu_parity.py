@@ -263,11 +263,22 @@ def test_swiglu_limit_engages():
 # the packed weight stream: a pure permutation of the stored planes
 # ----------------------------------------------------------------------------
 
+def _pair_order(v):
+    """AFFINE4 word, element j in bits 4j..4j+3 -> element 2j at bits 4j, 2j+1 at 16+4j."""
+    v = v.astype(np.uint32)
+    r = np.zeros_like(v)
+    for j in range(4):
+        r |= ((v >> np.uint32(8 * j)) & np.uint32(0xF)) << np.uint32(4 * j)
+        r |= ((v >> np.uint32(8 * j + 4)) & np.uint32(0xF)) << np.uint32(16 + 4 * j)
+    return r
+
+
 def _expect_packed(lins, gateup: bool, fmt: str, group: int):
     """The stream rebuilt in numpy from the layout stated in include/moe.h / moe_kernels.h:
     per matrix, per 32-row block, per chunk: 4096 bytes of weights (piece (i, lane) at
     i*1024 + lane*16 holds words 4i..4i+3 of the lane's sequence q = (unit*2 + half)*LPU + w)
-    followed by the chunk's scales; zero past the rows and columns."""
+    followed by the chunk's scales; zero past the rows and columns; AFFINE4 codes in pair
+    order (element 2j at bit 4j, element 2j+1 at bit 16+4j)."""
     a = lins[0]
     n, R, K = a.n, a.rows, a.cols
     dense = fmt == synth.FMT_DENSE
@@ -296,6 +307,8 @@ def _expect_packed(lins, gateup: bool, fmt: str, group: int):
                 word = (e0 // 2 + wi) if dense else (e0 // 8 + wi)
                 ok = (row < R) & (e0 < K)
                 vals = np.where(ok[None, :], src[:, np.minimum(row, R - 1), np.minimum(word, wpr - 1)], 0)
+                if aff:
+                    vals = _pair_order(vals)
                 out[:, bk, c, i * 256 + lane * 4 + j] = vals
     if aff:
         G = K // group
