@@ -389,14 +389,22 @@ int kernel_mb(int mb, bool gateup, const moe_linear &w, int kmax) {
   return (mb == 1 && !gateup && (kmax + kc - 1) / kc <= 3) ? 0 : mb;
 }
 
-AOp aop(const void *a, int64_t lda, const int32_t *gather, int gdiv, int row_sub) {
+AOp aop(const void *a, int64_t lda, const int32_t *gather, int gdiv, int row_sub, int64_t rows) {
   AOp o;
   o.a = a;
   o.lda = lda;
   o.gather = gather;
   o.gdiv = gdiv;
   o.row_sub = row_sub;
+  o.rows = rows;
   return o;
+}
+
+// the tall kernel addresses its activation rows with 32-bit byte offsets
+bool tall_offsets_fit(const GemmParams &p) {
+  for (int i = 0; i < 2; ++i)
+    if (p.seg[i].nblk > 0 && p.seg[i].A.rows * p.seg[i].A.lda * 2 > (int64_t)UINT32_MAX) return false;
+  return true;
 }
 
 SegSet segset(AOp A, const moe_linear &w0, const moe_linear *w1, float limit, bool gateup) {
@@ -436,6 +444,7 @@ moe_status run_gemm(int adt, const moe_linear &fmt_of, bool gateup, int odt, int
   p.ldr = ldr;
   const int units_ub = routed_tiles_ub(TK, E, mt) * p.seg[0].nblk + ((sh_rows + mt - 1) / mt) * p.seg[1].nblk;
   const int kmb = kernel_mb(mb, gateup, fmt_of, shared && shared->K > routed.K ? shared->K : routed.K);
+  CHECK(kmb != MB_TALL || tall_offsets_fit(p), MOE_ERR_SHAPE, "activation operand of over 4 GiB");
   Timed tm(gateup ? TK_GATEUP : TK_DOWN, s, true);
   HIPCHK(launch_gemm_kernel(adt, fmt_of, gateup, odt, kmb, p, units_ub, s, tm.start(), tm.stop()));
   return MOE_OK;
@@ -447,7 +456,7 @@ moe_status run_plain(int adt, const moe_linear &W, const moe_linear *W1, float l
                      hipStream_t s) {
   const int mb = pick_mb(rows);
   const int mt = 16 * mb;
-  SegSet sg = segset(aop(a, lda, nullptr, 1, 0), W, W1, limit, gateup);
+  SegSet sg = segset(aop(a, lda, nullptr, 1, 0, rows), W, W1, limit, gateup);
   sg.nblk = col_blocks(sg, gateup, mb);
   SegSet none = sg;
   none.nblk = 0;
@@ -468,6 +477,7 @@ moe_status run_plain(int adt, const moe_linear &W, const moe_linear *W1, float l
   p.ldr = ldr;
   const int units = ((rows + mt - 1) / mt) * sg.nblk;
   const int kmb = kernel_mb(mb, gateup, W, W.cols);
+  CHECK(kmb != MB_TALL || tall_offsets_fit(p), MOE_ERR_SHAPE, "activation operand of over 4 GiB");
   Timed tm(TK_PLAIN, s, true);
   HIPCHK(launch_gemm_kernel(adt, W, gateup, odt, kmb, p, units, s, tm.start(), tm.stop()));
   return MOE_OK;
@@ -673,10 +683,10 @@ moe_status moe_experts_forward(const void *z, int32_t z_dtype, int64_t T, int32_
     const int mb = mb_for_routing(TK, E);
     hipLaunchKernelGGL(build_tiles, dim3(1), dim3(256), 0, s, offsets, E, tiles, tc, 16 * mb);
     HIPCHK(hipGetLastError());
-    SegSet gu = segset(aop(z, D, sorted_slot, K, 0), ex->gate, &ex->up, ex->swiglu_limit, true);
+    SegSet gu = segset(aop(z, D, sorted_slot, K, 0, T), ex->gate, &ex->up, ex->swiglu_limit, true);
     TRY(run_gemm(z_dtype, ex->gate, true, inter_dtype, mb, gu, nullptr, 0, 0, tiles, tc, ntile, TK, E, h, I, nullptr,
                  0, s));
-    SegSet dn = segset(aop(h, I, nullptr, 1, 0), ex->down, nullptr, 0.f, false);
+    SegSet dn = segset(aop(h, I, nullptr, 1, 0, TK), ex->down, nullptr, 0.f, false);
     TRY(run_gemm(inter_dtype, ex->down, false, inter_dtype, mb, dn, nullptr, 0, 0, tiles, tc, ntile, TK, E, o, D,
                  nullptr, 0, s));
   } else {
@@ -889,18 +899,18 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
 
   if (!latent) {
     // 3. gate/up (+ SwiGLU) for every slot, shared rows appended
-    SegSet gu = segset(aop(x, H, ss, K, 0), b->experts.gate, &b->experts.up, b->experts.swiglu_limit, true);
+    SegSet gu = segset(aop(x, H, ss, K, 0, Ti), b->experts.gate, &b->experts.up, b->experts.swiglu_limit, true);
     SegSet gus;
-    if (has_shared) gus = segset(aop(x, H, nullptr, 1, TK), b->shared.gate, &b->shared.up, b->shared.swiglu_limit, true);
+    if (has_shared) gus = segset(aop(x, H, nullptr, 1, TK, Ti), b->shared.gate, &b->shared.up, b->shared.swiglu_limit, true);
     TRY(run_gemm(x_dtype, b->experts.gate, true, inter, mb, gu, fuse_shared ? &gus : nullptr, TK, Tsh, tiles, tc,
                  ntile, TK, E, h, ldh, nullptr, 0, s));
     if (has_shared && !fuse_shared)
       TRY(run_plain(x_dtype, b->shared.gate, &b->shared.up, b->shared.swiglu_limit, true, inter, x, H, Ti,
                     (char *)h + (size_t)TK * ldh * isz, ldh, nullptr, 0, s));
     // 4. down
-    SegSet dn = segset(aop(h, ldh, nullptr, 1, 0), b->experts.down, nullptr, 0.f, false);
+    SegSet dn = segset(aop(h, ldh, nullptr, 1, 0, TK + Tsh), b->experts.down, nullptr, 0.f, false);
     SegSet dns;
-    if (has_shared) dns = segset(aop(h, ldh, nullptr, 1, 0), b->shared.down, nullptr, 0.f, false);
+    if (has_shared) dns = segset(aop(h, ldh, nullptr, 1, 0, TK + Tsh), b->shared.down, nullptr, 0.f, false);
     TRY(run_gemm(inter, b->experts.down, false, inter, mb, dn, fuse_shared ? &dns : nullptr, TK, Tsh, tiles, tc,
                  ntile, TK, E, o, D, nullptr, 0, s));
     if (has_shared && !fuse_shared)
@@ -916,10 +926,10 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   void *z = at<char>(ws, o_z);
   void *yn = at<char>(ws, o_yn);
   TRY(run_plain(x_dtype, b->latent_down, nullptr, 0.f, false, inter, x, H, Ti, z, D, nullptr, 0, s));
-  SegSet gu = segset(aop(z, D, ss, K, 0), b->experts.gate, &b->experts.up, b->experts.swiglu_limit, true);
+  SegSet gu = segset(aop(z, D, ss, K, 0, Ti), b->experts.gate, &b->experts.up, b->experts.swiglu_limit, true);
   TRY(run_gemm(inter, b->experts.gate, true, inter, mb, gu, nullptr, 0, 0, tiles, tc, ntile, TK, E, h, ldh, nullptr,
                0, s));
-  SegSet dn = segset(aop(h, ldh, nullptr, 1, 0), b->experts.down, nullptr, 0.f, false);
+  SegSet dn = segset(aop(h, ldh, nullptr, 1, 0, TK), b->experts.down, nullptr, 0.f, false);
   TRY(run_gemm(inter, b->experts.down, false, inter, mb, dn, nullptr, 0, 0, tiles, tc, ntile, TK, E, o, D, nullptr, 0,
                s));
   TRY(combine(inter, inter, o, D, sp, wts, K, TK, Ti, D, yn, D, nullptr, b->latent_norm_w, b->norm_eps,

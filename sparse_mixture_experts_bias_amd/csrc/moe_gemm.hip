@@ -1,4 +1,5 @@
-// moe_gemm.hip - grouped expert GEMM for gfx950 (the gather_qmm pattern).
+// moe_gemm.hip - grouped expert GEMM for decode-sized segments on gfx950 (the gather_qmm
+// pattern); prefill-sized segments go to moe_gemm_tall.hip.
 //
 // One launch applies a stack of expert weight matrices to activation rows that
 // are grouped by expert (the sorted slots of the permutation), plus optionally
@@ -8,23 +9,19 @@
 //           libmir-metal's gate/up kernel, read as a clamp of both to [-L, L])
 //   LINEAR: o = W a + b (+ an f32 residual)      (down projections, latent maps)
 //
-// Work unit = (m-tile of up to 16*MB activation rows of one segment, block of
-// output columns).  A 256-thread workgroup (4 waves) stages the m-tile's rows in
+// Work unit = (m-tile of up to 16 activation rows of one segment, block of output
+// columns).  A 256-thread workgroup (4 waves) stages the m-tile's rows in
 // LDS one reduction chunk at a time; each wave streams its own 32 weight rows from
 // HBM and feeds v_mfma_f32_16x16x32_{bf16,f16} with tokens as the A operand and
 // weight rows as the B operand (two 16-row halves per wave).
 //
 // Weight formats (see moe_linear in include/moe.h):
 //   AFFINE4 (mlxcel issue #974's affine gather_qmm plane): a nibble q becomes the
-//     16-bit value MAGIC+q by OR-ing it into the mantissa of MAGIC, which is exact.
-//     Decode tiles (MB == 1) keep it that way and fold every quantisation group in
-//     fp32:  acc += scale * sum((MAGIC+q) a) + (qbias - MAGIC*scale) * sum(a),
+//     16-bit value MAGIC+q by OR-ing it into the mantissa of MAGIC, which is exact;
+//     every quantisation group is folded in fp32:
+//       acc += scale * sum((MAGIC+q) a) + (qbias - MAGIC*scale) * sum(a),
 //     which equals sum (scale*q + qbias) a with the weights never rounded; the
 //     group sums of a come from one extra MFMA against a vector of ones.
-//     Prefill tiles (MB > 1) dequantise instead: one mixed-precision FMA per weight
-//     gives scale*(1024+q) + (qbias - 1024*scale) in fp32, rounded once to the
-//     MFMA's 16-bit type; the per-group fold would cost VALU in proportion to the
-//     tile height, the dequantisation only per weight.
 //     The packed words hold the codes in pair order, so the nibble pairs come out
 //     as adjacent elements (q_2j, q_2j+1) and the activations are used as stored.
 //   MXFP4 (libmir-metal ExpertLayout blocks/scales): gfx950's scaled FP4
@@ -38,7 +35,7 @@
 // Every wave owns one 32-row weight tile, one row block of the packed stream: GATEUP: 16
 // gate rows (half 0) and the 16 up rows of the same outputs (half 1); LINEAR: 32 output
 // rows.  Lane l works on tile rows l%16 and 16 + l%16 and on the m-tile's tokens
-// 16*mb + l%16 (A operand) / 16*mb + 4*(l/16) + i (D).
+// l%16 (A operand) / 4*(l/16) + i (D).
 //
 // Weight stream: a chunk record of the wave's row block is 4 KB of weights already in MFMA
 // lane order plus the chunk's scales, contiguous in HBM; every lane loads its own 64 bytes
@@ -54,13 +51,12 @@
 // reduction elements): the whole unit is loaded at once, weights into registers and the
 // activations into three LDS tiles, then computed without further barriers; the smaller
 // register footprint gives four workgroups per CU.
-template <int AT, int WF, int GQ, bool GATEUP, int OT, int MB, bool SHORT = false>
-__global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : (MB == 1 ? 3 : 2)) void expert_gemm(const GemmParams p) {
+template <int AT, int WF, int GQ, bool GATEUP, int OT, bool SHORT = false>
+__global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : 3) void expert_gemm(const GemmParams p) {
   constexpr bool AFF = (WF == WF_AFFINE4);
   constexpr bool MX = (WF == WF_MXFP4);
   constexpr bool DENSE = (WF == WF_DENSE);
-  constexpr bool FOLD = AFF && MB == 1;                    // exact group fold; else dequantise
-  constexpr int MT = 16 * MB;                              // rows per m-tile
+  constexpr int MT = 16;                                   // rows per m-tile
   constexpr int UE = pk_ue(WF, GQ);                        // elements per unit
   constexpr int SPU = UE / 32;                             // MFMA steps per unit
   constexpr int QE = UE / 4;                               // elements per lane quarter per unit
@@ -73,9 +69,8 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : (MB == 1 ? 3 : 2)) vo
   constexpr int RPI = MOE_GEMM_THREADS / BPR;              // activation rows staged per iteration
   constexpr int SIT = (MT + RPI - 1) / RPI;                // activation staging iterations
   constexpr int LDA = KC + 8;                              // padded LDS activation row (16-bit elements)
-  constexpr int NSA = SHORT ? 3 : (MB == 1 ? 2 : 1);       // activation tiles (decode: double-buffered)
-  static_assert(!SHORT || MB == 1, "SHORT is a decode-tile variant");
-  constexpr float MAGIC = (FOLD && AT == DT_BF16) ? 128.0f : 1024.0f;
+  constexpr int NSA = SHORT ? 3 : 2;                       // activation tiles (double-buffered)
+  constexpr float MAGIC = AT == DT_BF16 ? 128.0f : 1024.0f;
   static_assert(2 * NU * LPU == 16, "64 weight bytes per lane per chunk");
   static_assert(KC % UE == 0 && UE % 32 == 0, "units of whole MFMA steps");
   __shared__ __attribute__((aligned(16))) uint16_t sAbuf[NSA][MT * LDA];
@@ -85,7 +80,7 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : (MB == 1 ? 3 : 2)) vo
   const int n16 = lane & 15, kq = lane >> 4;
   const int sblk = tid % BPR, srow0 = tid / BPR;
   const uint32_t msk = in_vgpr(0x000F000Fu);
-  const uint32_t mag = in_vgpr((FOLD && AT == DT_BF16) ? 0x43004300u : 0x64006400u);
+  const uint32_t mag = in_vgpr(AT == DT_BF16 ? 0x43004300u : 0x64006400u);
 
   // units: segment 1 (shared expert / plain rows, m-tiles computed here) first, then the
   // routed m-tiles of the tile list
@@ -117,7 +112,6 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : (MB == 1 ? 3 : 2)) vo
     }
     const int e = sh ? 0 : tile.x;
     const int r0 = tile.y, nr = tile.z;
-    const int nmb = (nr + 15) >> 4;               // 16-row blocks of the m-tile that hold rows
 
 #define SF(f) (sh ? p.seg[1].f : p.seg[0].f)
     const uint16_t *Ab = (const uint16_t *)SF(A.a);
@@ -234,11 +228,7 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : (MB == 1 ? 3 : 2)) vo
       }
     };
 
-    f32x4_t acc[MB][2];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) acc[mb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 
     auto compute = [&](int kc, const Ch &ch) {
       if (!act) return;
@@ -270,8 +260,8 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : (MB == 1 ? 3 : 2)) vo
           }
         }
         const uint16_t *arow = &sA[n16 * LDA + eoff];
-        if constexpr (FOLD) {
-          // MB == 1: both halves share the A fragment and the group sums
+        if constexpr (AFF) {
+          // exact group fold: both halves share the A fragment and the group sums
           constexpr uint32_t ONE2 = (AT == DT_BF16) ? 0x3F803F80u : 0x3C003C00u;  // (1.0, 1.0)
           const u32x4_t ones = {ONE2, ONE2, ONE2, ONE2};
           const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
@@ -285,8 +275,8 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : (MB == 1 ? 3 : 2)) vo
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            acc[0][0][i] = fmaf(sc[0], g0[i], fmaf(cc[0], sx[i], acc[0][0][i]));
-            acc[0][1][i] = fmaf(sc[1], g1[i], fmaf(cc[1], sx[i], acc[0][1][i]));
+            acc[0][i] = fmaf(sc[0], g0[i], fmaf(cc[0], sx[i], acc[0][i]));
+            acc[1][i] = fmaf(sc[1], g1[i], fmaf(cc[1], sx[i], acc[1][i]));
           }
         } else {
 #pragma unroll
@@ -294,21 +284,14 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : (MB == 1 ? 3 : 2)) vo
             u32x4_t b[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-              if constexpr (AFF)
-                b[h] = deq_affine<AT>(wv[h][s], msk, mag, sc[h], cc[h]);
-              else if constexpr (MX)
+              if constexpr (MX)
                 b[h] = cvt_mxfp4<AT>(wv[h][s], sc[h]);
               else
                 b[h] = cvt_dense<AT>(u32x4_t{wv[h][4 * s], wv[h][4 * s + 1], wv[h][4 * s + 2], wv[h][4 * s + 3]});
             }
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-              if (MB == 1 || mb < nmb) {
-                const u32x4_t av = *(const u32x4_t *)(arow + mb * 16 * LDA + 8 * s);
-                acc[mb][0] = mfma16<AT>(av, b[0], acc[mb][0]);
-                acc[mb][1] = mfma16<AT>(av, b[1], acc[mb][1]);
-              }
-            }
+            const u32x4_t av = *(const u32x4_t *)(arow + 8 * s);
+            acc[0] = mfma16<AT>(av, b[0], acc[0]);
+            acc[1] = mfma16<AT>(av, b[1], acc[1]);
           }
         }
       }
@@ -326,8 +309,8 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : (MB == 1 ? 3 : 2)) vo
       compute(0, cA);
       if (nchunks > 1) compute(KC, cB);
       if (nchunks > 2) compute(2 * KC, cC);
-    } else if constexpr (MB == 1) {
-      // decode tiles: activations and weights two chunks ahead (3-deep register rings); the
+    } else {
+      // activations and weights two chunks ahead (3-deep register rings); the
       // activation tile is double-buffered, so one barrier per chunk suffices: a wave stores
       // chunk c+1 only after every wave has passed chunk c's barrier, i.e. has finished
       // computing chunk c-1, the last reader of that buffer.
@@ -352,27 +335,9 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : (MB == 1 ? 3 : 2)) vo
         // draining every load at the loop header.
         wait_vmcnt<LOADS_PER_CHUNK<WF, GQ, SIT>()>();
       }
-    } else {
-      u32x4_t aA[SIT];
-      auto chunk = [&](int c, const Ch &ccur, Ch &cnext2) {
-        const int kc = c * KC;
-        __syncthreads();
-        store_a(kc, aA);
-        load_a(kc + KC, aA);
-        load_ch(kc + 2 * KC, cnext2);
-        __syncthreads();
-        if (c < nchunks) compute(kc, ccur);
-      };
-      load_a(0, aA);
-      for (int c = 0; c < nchunks; c += 3) {
-        chunk(c, cA, cC);
-        chunk(c + 1, cB, cA);
-        chunk(c + 2, cC, cB);
-        wait_vmcnt<LOADS_PER_CHUNK<WF, GQ, 0>()>();  // as above: the weights of chunk c+2 may stay in flight
-      }
     }
 
-    // ---- epilogue: acc[mb][h][i] is token 16*mb + 4*kq + i of the m-tile, tile row 16*h + n16
+    // ---- epilogue: acc[h][i] is token 4*kq + i of the m-tile, tile row 16*h + n16
     if (act) {
       bool ok[2];
       int wrow[2];
@@ -382,28 +347,23 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : (MB == 1 ? 3 : 2)) vo
         wrow[h] = row_of(16 * h + n16);
       }
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        if (MB == 1 || mb < nmb) {
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * kq + i;
+        if (m < nr) {
+          if constexpr (GATEUP) {
+            float g = acc[0][i] + bo[0], up = acc[1][i] + bo[1];
+            if (limit > 0.f) {
+              g = fminf(fmaxf(g, -limit), limit);
+              up = fminf(fmaxf(up, -limit), limit);
+            }
+            if (ok[0]) store_act<OT>(p.out, (int64_t)(r0 + m) * p.ldo + wrow[0], silu_f(g) * up);
+          } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = 16 * mb + 4 * kq + i;
-            if (m < nr) {
-              if constexpr (GATEUP) {
-                float g = acc[mb][0][i] + bo[0], up = acc[mb][1][i] + bo[1];
-                if (limit > 0.f) {
-                  g = fminf(fmaxf(g, -limit), limit);
-                  up = fminf(fmaxf(up, -limit), limit);
-                }
-                if (ok[0]) store_act<OT>(p.out, (int64_t)(r0 + m) * p.ldo + wrow[0], silu_f(g) * up);
-              } else {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                  if (ok[h]) {
-                    float v = acc[mb][h][i] + bo[h];
-                    if (p.resid) v += p.resid[(int64_t)(r0 + m) * p.ldr + wrow[h]];
-                    store_act<OT>(p.out, (int64_t)(r0 + m) * p.ldo + wrow[h], v);
-                  }
-                }
+            for (int h = 0; h < 2; ++h) {
+              if (ok[h]) {
+                float v = acc[h][i] + bo[h];
+                if (p.resid) v += p.resid[(int64_t)(r0 + m) * p.ldr + wrow[h]];
+                store_act<OT>(p.out, (int64_t)(r0 + m) * p.ldo + wrow[h], v);
               }
             }
           }
@@ -470,12 +430,12 @@ static hipError_t launch_t(int mb, const GemmParams &p, int grid, hipStream_t s,
   };
   if constexpr (!GU) {
     if (mb == 0) {
-      go(expert_gemm<AT, WF, GQ, GU, OT, 1, true>);
+      go(expert_gemm<AT, WF, GQ, GU, OT, true>);
       return hipGetLastError();
     }
   }
   if (mb == 1)
-    go(expert_gemm<AT, WF, GQ, GU, OT, 1>);
+    go(expert_gemm<AT, WF, GQ, GU, OT>);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -66,6 +66,7 @@ struct AOp {
   const int32_t *gather;
   int gdiv;
   int row_sub;
+  int64_t rows;         // rows of a (bounds of the byte offsets the tall kernel uses)
 };
 
 struct SegSet {

@@ -38,14 +38,22 @@ MOE_DEV u32x4_t magic_pairs(uint32_t w, uint32_t msk, uint32_t mag) {
 MOE_DEV float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
 MOE_DEV float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
-// 8 nibbles -> 4 words of dequantised element pairs in the MFMA type; w = sc*(1024+q) + c,
-// c = qbias - 1024*sc (one fp32 FMA from the exact f16 1024+q, one rounding to 16 bits)
+// 8 nibbles in pair order -> 4 words of dequantised element pairs (2j, 2j+1) in the MFMA
+// type.  The nibbles at bits 0-3 (of either half-word) become the exact f16 value 1024 + q
+// under the magic 0x6400, those at bits 4-7 the exact 64 + q under 0x5400 (the mantissa's
+// bit 4 weighs 1 at that exponent), so one shift by 8 serves the other two positions.  Each
+// weight is then one fp32 FMA, sc * (1024 + q) + c0 or sc * (64 + q) + c1 with
+// c0 = qbias - 1024 sc, c1 = qbias - 64 sc (both exact), i.e. sc*q + qbias rounded once to
+// fp32, then rounded to 16 bits.
 template <int AT>
-MOE_DEV u32x4_t deq_affine(uint32_t w, uint32_t msk, uint32_t mag16, float sc, float c) {
-  const u32x4_t m = magic_pairs(w, msk, mag16);
+MOE_DEV u32x4_t deq_affine(uint32_t w, uint32_t m0, uint32_t m1, uint32_t g0, uint32_t g1, float sc, float c0,
+                           float c1) {
+  const uint32_t w8 = w >> 8;
+  const uint32_t m[4] = {(w & m0) | g0, (w & m1) | g1, (w8 & m0) | g0, (w8 & m1) | g1};
   u32x4_t r;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
+    const float c = (j & 1) ? c1 : c0;
     const float lo = fmaf(f16lo(m[j]), sc, c), hi = fmaf(f16hi(m[j]), sc, c);
     if constexpr (AT == DT_BF16) {
       const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
