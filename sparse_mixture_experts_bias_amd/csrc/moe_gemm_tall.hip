@@ -34,27 +34,9 @@
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
 
-// source of the activation blocks past the reduction length
+// zeros: the source of absent biases
 __device__ u32x4_t g_zero_block = {0u, 0u, 0u, 0u};
-
-// 16-byte direct load: lane i's 16 bytes land at lds + 16 i (lds must be wave-uniform)
-MOE_DEV void load_lds16(const void *src, void *lds) {
-  __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)lds, 16, 0, 0);
-}
-typedef __attribute__((address_space(1))) const char glb_char_t;
-// a pointer known to be the same in every lane, as a scalar value
-MOE_DEV const char *uniform_ptr(const char *p) {
-  const uint64_t v = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const char *)(((uint64_t)hi << 32) | lo);
-}
-// same, from a wave-uniform global base plus a per-lane 32-bit byte offset (saddr form)
-MOE_DEV void load_lds16_off(const char *base, uint32_t off, void *lds) {
-  glb_char_t *g = (glb_char_t *)base;
-  __builtin_amdgcn_global_load_lds((glb_void_t *)(g + off), (lds_void_t *)lds, 16, 0, 0);
-}
 
 // barrier without the compiler's release fence (which would drain every outstanding load,
 // the prefetched stages included); callers wait for their own loads first.  LDS reads are
@@ -131,68 +113,120 @@ MOE_DEV void store4(void *out, int64_t idx, const float (&v)[4], int nv, bool ve
   }
 }
 
-template <int AT, int WF, int GQ, bool GATEUP, int OT, int NMB>
-MOE_DEV void tall_unit(const GemmParams &p, bool sh, int4 tile, int nb, const StageBufs &sA, int64_t *sRow) {
-  using C = TallCfg<WF, GQ>;
-  constexpr bool AFF = C::AFF, MX = C::MX;
-  constexpr int KS = C::KS, SPR = C::SPR, PPS = C::PPS, BPR = C::BPR, ROWB = C::ROWB, ABUF = C::ABUF;
-  constexpr int NBUF = C::NBUF, D = C::D, NI = C::NI, RPI = C::RPI, NU = C::NU, NUS = C::NUS;
-  constexpr int NSW = C::NSW, LPS = C::LPS;
-  constexpr int UE = pk_ue(WF, GQ);                        // elements per unit
-  constexpr int SPU = UE / 32;                             // MFMA steps per unit
-  constexpr int QE = UE / 4;                               // elements per lane quarter per unit
-  constexpr int LPU = pk_lb(WF, GQ) / 4;                   // weight words per lane, unit and half
-  constexpr int RB = pk_record_bytes(WF, GQ);
-  static_assert(2 * NU * LPU == 16, "64 weight bytes per lane per record");
+// A work unit: the m-tile and column block, with everything its loads and epilogue read
+// (all wave-uniform, so it lives in scalar registers).
+struct TallUnit {
+  bool sh;
+  int e, r0, nr, nb, Kd;
+  float limit;
+  const char *Ab;
+  int64_t lda, arows;
+  const int32_t *gat;
+  int gdiv, rsub;
+  int rows;                 // weight rows (output columns, GATEUP: per half)
+  const char *pk;           // packed stream, its matrix stride and row blocks
+  int64_t pk_mat;
+  int pk_nblk, pk_nch;
+  const uint16_t *bias0;    // output bias of tile half 0 (GATEUP: the gate rows)
+  const uint16_t *bias1;    // ... and of tile half 1 (GATEUP: the up rows)
+};
 
-  // lane-dependent values are recomputed per unit (opaque thread id): hoisted out of the
-  // unit loop they would stay live across it and crowd the registers
-  const int tid = (int)in_vgpr(threadIdx.x), lane = tid & 63, wave = tid >> 6;
-  const int n16 = lane & 15, kq = lane >> 4;
-  const uint32_t m0 = in_vgpr(0x000F000Fu), m1 = in_vgpr(0x00F000F0u);
-  const uint32_t g0 = in_vgpr(0x64006400u), g1 = in_vgpr(0x54005400u);
-
-  // the tile is the same for the whole workgroup: keep it (and what derives from it) scalar
-  const int e = sh ? 0 : __builtin_amdgcn_readfirstlane(tile.x);
-  const int r0 = __builtin_amdgcn_readfirstlane(tile.y), nr = __builtin_amdgcn_readfirstlane(tile.z);
-
+template <bool GATEUP>
+MOE_DEV TallUnit tall_unit_of(const GemmParams &p, bool sh, int4 tile, int nb) {
+  TallUnit t;
+  t.sh = sh;
+  t.e = sh ? 0 : __builtin_amdgcn_readfirstlane(tile.x);
+  t.r0 = __builtin_amdgcn_readfirstlane(tile.y);
+  t.nr = __builtin_amdgcn_readfirstlane(tile.z);
+  t.nb = nb;
 #define SF(f) (sh ? p.seg[1].f : p.seg[0].f)
-  const char *Ab = (const char *)SF(A.a);
-  const int64_t lda = SF(A.lda);
-  const int64_t arows = SF(A.rows);
-  const int32_t *gat = SF(A.gather);
-  const int gdiv = SF(A.gdiv), rsub = SF(A.row_sub);
-  const int Kd = SF(K);
-  const float limit = SF(limit);
-  const WMat W0 = sh ? p.seg[1].w0 : p.seg[0].w0;
-  const uint16_t *bias1 = (const uint16_t *)(GATEUP ? SF(w1.bias) : W0.bias);  // bias of tile half 1
+  t.Ab = (const char *)SF(A.a);
+  t.lda = SF(A.lda);
+  t.arows = SF(A.rows);
+  t.gat = SF(A.gather);
+  t.gdiv = SF(A.gdiv);
+  t.rsub = SF(A.row_sub);
+  t.Kd = SF(K);
+  t.limit = SF(limit);
+  t.rows = SF(w0.rows);
+  t.pk = SF(w0.pk);
+  t.pk_mat = SF(w0.pk_mat);
+  t.pk_nblk = SF(w0.pk_nblk);
+  t.pk_nch = SF(w0.pk_nch);
+  t.bias0 = (const uint16_t *)SF(w0.bias);
+  t.bias1 = (const uint16_t *)(GATEUP ? SF(w1.bias) : SF(w0.bias));
 #undef SF
+  return t;
+}
 
-  // tile row t (0..31) of this wave -> weight matrix row; GATEUP: rows 0-15 gate, 16-31 up
-  const int col0 = GATEUP ? nb * 128 + wave * 16 : nb * 256 + wave * 32;
-  const bool act = col0 < W0.rows;
-  auto row_of = [&](int t) { return GATEUP ? col0 + (t & 15) : col0 + t; };
-  auto row_ok = [&](int t) { return row_of(t) < W0.rows; };
-  const int nst = (Kd + KS - 1) / KS;                      // stages (the last record may hold one)
+// byte offsets of the unit's activation rows (rows past nr read row 0: their results are
+// never stored), written by the first MT threads
+template <int MT>
+MOE_DEV void tall_fill_rows(const TallUnit &u, int64_t *sRow, int tid) {
+  if (tid < MT) {
+    const int t = tid < u.nr ? tid : 0;
+    const int64_t arow = u.gat ? (int64_t)(u.gat[u.r0 + t] / u.gdiv) : (int64_t)(u.r0 + t - u.rsub);
+    sRow[tid] = arow * u.lda * 2;
+  }
+}
 
-  const char *wbase = W0.pk + (int64_t)e * W0.pk_mat +
-                      (int64_t)min(nb * C::NW + wave, W0.pk_nblk - 1) * W0.pk_nch * RB;
-  // weight ring slot: the stage's PPS pieces (the lane's 16 bytes of each) and scale words
-  struct Ch {
-    u32x4_t w[PPS];
-    uint32_t s[NSW > 0 ? NSW : 1];
-  };
+// weight ring slot: one stage's PPS weight pieces (the lane's 16 bytes of each) and scales
+template <int WF, int GQ>
+struct TallSlot {
+  u32x4_t w[TallCfg<WF, GQ>::PPS];
+  uint32_t s[TallCfg<WF, GQ>::NSW > 0 ? TallCfg<WF, GQ>::NSW : 1];
+};
+
+// what a lane needs to issue a unit's loads
+template <int WF, int GQ, bool GATEUP>
+struct TallLoader {
+  using C = TallCfg<WF, GQ>;
+  static constexpr int NI = C::NI, PPS = C::PPS, NU = C::NU, NUS = C::NUS, SPR = C::SPR, KS = C::KS;
+  static constexpr int RB = pk_record_bytes(WF, GQ);
+  __amdgpu_buffer_rsrc_t arsrc;
+  uint32_t aoff[NI];
+  int ablk[NI];
+  const char *wbase;
+  int wave_u, lane, n16, Kd, nst;
+
+  // this lane's direct-load sources: load n of the wave stages tile row
+  // rr = 16 wave + n RPI + lane / BPR into LDS slot lane % BPR, which holds block
+  // (lane % BPR) ^ swizzle(rr) of that row.  The activations are read through a buffer
+  // resource over their rows: the lane's byte offset is the fixed aoff[n] (32 bits, checked
+  // by the host), the stage's column offset a scalar, and bytes past the rows read as zero.
+  // (Keeping a lane's address register fixed matters: rewriting a register that a direct
+  // load in flight addresses makes the compiler wait for that load.)
+  __device__ __forceinline__ TallLoader(const TallUnit &u, const int64_t *sRow, int wave, int lane_) {
+    lane = lane_;
+    n16 = lane & 15;
+    wave_u = __builtin_amdgcn_readfirstlane(wave);
+    Kd = u.Kd;
+    nst = (u.Kd + KS - 1) / KS;
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+      const int rr = 16 * wave + n * C::RPI + lane / C::BPR;
+      ablk[n] = (lane % C::BPR) ^ row_swizzle<C::BPR>(rr);
+      aoff[n] = (uint32_t)sRow[rr] + (uint32_t)(ablk[n] * 16);
+    }
+    arsrc = __builtin_amdgcn_make_buffer_rsrc((void *)u.Ab, (short)0, (int)(uint32_t)(u.arows * u.lda * 2), 0x00020000);
+    wbase = u.pk + (int64_t)u.e * u.pk_mat + (int64_t)min(u.nb * C::NW + wave, u.pk_nblk - 1) * u.pk_nch * RB;
+  }
+  // direct load n (0 .. NI-1) of stage c's activations into LDS stage buffer dst
+  __device__ __forceinline__ void load_a1(int c, char *buf, int n) const {
+    char *dst = buf + wave_u * (NI * 1024) + n * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void_t *)dst, 16, aoff[n], c * KS * 2, 0, 0);
+  }
   // load k (0 .. PPS + NSL - 1) of stage c's weights into ring slot ch: the weight pieces,
   // then one scale load per tile half.  The slot's old values are "used" right before the
   // load, so that the registers stay the slot's until it is reloaded: reused for something
   // else in between, they would carry a false wait on the load in flight.
-  auto load_w1 = [&](int c, Ch &ch, int k) {
+  __device__ __forceinline__ void load_w1(int c, TallSlot<WF, GQ> &ch, int k) const {
     const char *rec = wbase + (int64_t)(c / SPR) * RB;
     const int half = c % SPR;
     if (k < PPS) {
       asm volatile("" : "+v"(ch.w[k]));
       ch.w[k] = *(const u32x4_t *)(rec + (half * PPS + k) * 1024 + lane * 16);
-    } else if constexpr (AFF) {
+    } else if constexpr (C::AFF) {
       const int h = k - PPS;
 #pragma unroll
       for (int j = 0; j < NUS; ++j) asm volatile("" : "+v"(ch.s[h * NUS + j]));
@@ -208,64 +242,86 @@ MOE_DEV void tall_unit(const GemmParams &p, bool sh, int4 tile, int nb, const St
       } else {
         ch.s[h] = *(const uint32_t *)sp;
       }
-    } else if constexpr (MX) {
+    } else if constexpr (C::MX) {
       const int h = k - PPS;
       asm volatile("" : "+v"(ch.s[h]));
       ch.s[h] = *(const uint32_t *)(rec + 4096 + (h * 16 + n16) * 8 + half * 4);
     }
-  };
-  auto load_w = [&](int c, Ch &ch) {
+  }
+  // load k (0 .. LPS-1) of stage c: activations first, then the weights
+  __device__ __forceinline__ void load_k(int c, char *buf, TallSlot<WF, GQ> &ch, int k) const {
+    if (k < NI)
+      load_a1(c, buf, k);
+    else
+      load_w1(c, ch, k - NI);
+  }
+  // the activations of the unit's first D stages (repeats of its last stage if it has fewer)
+  __device__ __forceinline__ void load_first_a(const StageBufs &sA) const {
 #pragma unroll
-    for (int k = 0; k < PPS + C::NSL; ++k) load_w1(c, ch, k);
-  };
+    for (int j = 0; j < C::D; ++j)
+#pragma unroll
+      for (int n = 0; n < NI; ++n) load_a1(min(j, nst - 1), sA.b[j], n);
+  }
+  // ... and their weights
+  __device__ __forceinline__ void load_first_w(TallSlot<WF, GQ> (&ring)[C::NBUF]) const {
+#pragma unroll
+    for (int j = 0; j < C::D; ++j)
+#pragma unroll
+      for (int k = 0; k < PPS + C::NSL; ++k) load_w1(min(j, nst - 1), ring[j], k);
+  }
+};
+
+// One unit's stages and epilogue.  On entry the activations of its first D stages are in
+// flight (buffers 0 .. D-1); before the epilogue it issues those of the next unit (has_nxt),
+// whose rows are in sRow_nxt, so that they load while this epilogue runs.
+template <int AT, int WF, int GQ, bool GATEUP, int OT, int NMB>
+MOE_DEV void tall_unit(const GemmParams &p, const TallUnit &u, const int64_t *sRow, const StageBufs &sA,
+                       bool has_nxt, bool nsh, int4 ntile, int nnb, const int64_t *sRow_nxt) {
+  using C = TallCfg<WF, GQ>;
+  using L = TallLoader<WF, GQ, GATEUP>;
+  using Ch = TallSlot<WF, GQ>;
+  constexpr bool AFF = C::AFF, MX = C::MX;
+  constexpr int KS = C::KS, ROWB = C::ROWB, BPR = C::BPR;
+  constexpr int NBUF = C::NBUF, D = C::D, NI = C::NI, NUS = C::NUS, LPS = C::LPS;
+  constexpr int WPS = C::PPS + C::NSL;                     // weight loads per stage
+  constexpr int UE = pk_ue(WF, GQ);                        // elements per unit
+  constexpr int SPU = UE / 32;                             // MFMA steps per unit
+  constexpr int QE = UE / 4;                               // elements per lane quarter per unit
+  constexpr int LPU = pk_lb(WF, GQ) / 4;                   // weight words per lane, unit and half
+  static_assert(2 * C::NU * LPU == 16, "64 weight bytes per lane per record");
+
+  // lane-dependent values are recomputed per unit (opaque thread id): hoisted out of the
+  // unit loop they would stay live across it and crowd the registers
+  const int tid = (int)in_vgpr(threadIdx.x), lane = tid & 63, wave = tid >> 6;
+  const int n16 = lane & 15, kq = lane >> 4;
+  const uint32_t m0 = in_vgpr(0x000F000Fu), m1 = in_vgpr(0x00F000F0u);
+  const uint32_t g0 = in_vgpr(0x64006400u), g1 = in_vgpr(0x54005400u);
+
+  const int rows = u.rows;
+  // tile row t (0..31) of this wave -> weight matrix row; GATEUP: rows 0-15 gate, 16-31 up
+  const int col0 = GATEUP ? u.nb * 128 + wave * 16 : u.nb * 256 + wave * 32;
+  const bool act = col0 < rows;
+  auto row_of = [&](int t) { return GATEUP ? col0 + (t & 15) : col0 + t; };
+  auto row_ok = [&](int t) { return row_of(t) < rows; };
+  const L ld(u, sRow, wave, lane);
+  const int nst = ld.nst, Kd = u.Kd;
+  Ch ring[NBUF];
+  ld.load_first_w(ring);
 
   // output bias of this lane's tile rows 16 h + 4 kq + i: loaded now (no bias: from a zero
-  // block) and kept as raw bits, so nothing waits for them before the epilogue
-  uint16_t bo_raw[2][4];
+  // block) and kept as raw bits until the epilogue, so nothing waits for them
+  uint32_t bo_raw[2][4];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint16_t *bp = h ? bias1 : (const uint16_t *)W0.bias;
+    const uint16_t *bp = h ? u.bias1 : u.bias0;
     const uint16_t *bz = (const uint16_t *)&g_zero_block;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * h + 4 * kq + i;
-      bo_raw[h][i] = bp ? bp[(int64_t)e * W0.rows + (row_ok(t) ? row_of(t) : 0)] : bz[0];
+      bo_raw[h][i] = bp ? bp[(int64_t)u.e * rows + (row_ok(t) ? row_of(t) : 0)] : bz[0];
     }
   }
 
-  // activation rows of the tile (rows past nr read row 0: their results are never stored)
-  if (tid < C::MT) {
-    const int t = tid < nr ? tid : 0;
-    const int64_t arow = gat ? (int64_t)(gat[r0 + t] / gdiv) : (int64_t)(r0 + t - rsub);
-    sRow[tid] = arow * lda * 2;
-  }
-  __syncthreads();
-
-  // this lane's direct-load sources: load n of the wave stages tile row
-  // rr = 16 wave + n RPI + lane / BPR into LDS slot lane % BPR, which holds block
-  // (lane % BPR) ^ swizzle(rr) of that row.  Byte offsets from the activation base fit in
-  // 32 bits (checked by the host), so full stages issue the loads with a scalar base and a
-  // fixed vector offset per load.
-  uint32_t aoff[NI];
-  int ablk[NI];
-#pragma unroll
-  for (int n = 0; n < NI; ++n) {
-    const int rr = 16 * wave + n * RPI + lane / BPR;
-    ablk[n] = (lane % BPR) ^ row_swizzle<BPR>(rr);
-    aoff[n] = (uint32_t)sRow[rr] + (uint32_t)(ablk[n] * 16);
-  }
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  // direct load n (0 .. NI-1) of stage c's activations into LDS stage buffer buf, through a
-  // buffer resource over the activation rows: the lane's byte offset is the fixed aoff[n],
-  // the stage's column offset a scalar, and bytes past the rows read as zero.  (Keeping the
-  // lane's address register fixed matters: rewriting a register that a direct load in flight
-  // addresses makes the compiler wait for that load.)
-  const __amdgpu_buffer_rsrc_t arsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void *)Ab, (short)0, (int)(uint32_t)(arows * lda * 2), 0x00020000);
-  auto load_a1 = [&](int c, int buf, int n) {
-    char *dst = sA.b[buf] + wave_u * (NI * 1024) + n * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void_t *)dst, 16, aoff[n], c * KS * 2, 0, 0);
-  };
   // the stage that holds the end of the reduction: its blocks past Kd hold the next row's
   // elements (or zeros past the rows); each lane zeroes its own, once its loads are in
   // (before the stage's barrier)
@@ -273,19 +329,8 @@ MOE_DEV void tall_unit(const GemmParams &p, bool sh, int4 tile, int nb, const St
     const int kc = c * KS;
 #pragma unroll
     for (int n = 0; n < NI; ++n)
-      if (kc + ablk[n] * 8 >= Kd)
-        *(u32x4_t *)(sA.b[buf] + wave_u * (NI * 1024) + n * 1024 + lane * 16) = u32x4_t{0u, 0u, 0u, 0u};
-  };
-  auto load_a = [&](int c, int buf) {
-#pragma unroll
-    for (int n = 0; n < NI; ++n) load_a1(c, buf, n);
-  };
-  // load k (0 .. LPS-1) of stage c: activations first, then the weights
-  auto load_k = [&](int c, int buf, Ch &ch, int k) {
-    if (k < NI)
-      load_a1(c, buf, k);
-    else
-      load_w1(c, ch, k - NI);
+      if (kc + ld.ablk[n] * 8 >= Kd)
+        *(u32x4_t *)(sA.b[buf] + ld.wave_u * (NI * 1024) + n * 1024 + lane * 16) = u32x4_t{0u, 0u, 0u, 0u};
   };
 
   f32x4_t acc[NMB][2];
@@ -326,11 +371,12 @@ MOE_DEV void tall_unit(const GemmParams &p, bool sh, int4 tile, int nb, const St
   // a stage, software-pipelined by hand: step t+1's fragment reads and dequantisation are
   // issued with step t's MFMAs, interleaved (per row block: MFMA, VALU, MFMA, VALU, LDS read)
   // so that the conversion work runs under the matrix pipe; nothing moves across steps,
-  // which bounds the live registers
+  // which bounds the live registers.  The loads of stage cl are issued from inside the
+  // steps, LPS/NS per step: issued all at once they stall every wave on the address path.
+  // The wave priority falls with the step, so that the wave of a SIMD pair that is behind
+  // issues first and the pair reaches the stage barrier together.
   constexpr int VPS = AFF ? 40 : 12;                       // VALU of one step's dequantisation
   constexpr int VPM = (VPS + 2 * NMB - 1) / (2 * NMB);     // ... per MFMA
-  // The loads of stage cl are issued from inside the MFMA steps, LPS/NS per step:
-  // issued all at once they stall every wave on the address path for ~100 cycles each.
   auto compute = [&](int c, int buf, const Ch &ch, bool issue, int cl, int bufl, Ch &chl) {
     constexpr int NS = NUS * SPU;
     constexpr int LPT = (LPS + NS - 1) / NS;               // loads issued per step
@@ -340,9 +386,15 @@ MOE_DEV void tall_unit(const GemmParams &p, bool sh, int4 tile, int nb, const St
     deq_step(ch, 0, bC);
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
+      switch (3 - (t * 4) / NS) {
+        case 3: __builtin_amdgcn_s_setprio(3); break;
+        case 2: __builtin_amdgcn_s_setprio(2); break;
+        case 1: __builtin_amdgcn_s_setprio(1); break;
+        default: __builtin_amdgcn_s_setprio(0); break;
+      }
       if (issue) {
 #pragma unroll
-        for (int k = t * LPT; k < (t + 1) * LPT && k < LPS; ++k) load_k(cl, bufl, chl, k);
+        for (int k = t * LPT; k < (t + 1) * LPT && k < LPS; ++k) ld.load_k(cl, sA.b[bufl], chl, k);
       }
       if (t + 1 < NS) deq_step(ch, t + 1, bN);
       const char *apn = sAb + ((((t + 1) / SPU * (UE / 8) + (t + 1) % SPU) ^ lx) << 4);
@@ -372,48 +424,62 @@ MOE_DEV void tall_unit(const GemmParams &p, bool sh, int4 tile, int nb, const St
   // Whole groups of NBUF stages run in a branch-free loop (its back edge is then only taken
   // with exactly D stages of loads in flight, which lets the compiler count them exactly);
   // every stage there issues LPS loads, past the last stage repeats of the last stage's
-  // sources into the buffer and ring slot that no later stage reads.  The remaining < NBUF
-  // stages follow, in ring slots 0.., loading nothing.  The unit-start barrier (a full
-  // __syncthreads) drains the repeats.
-  Ch ring[NBUF];
-#pragma unroll
-  for (int j = 0; j < D; ++j) {
-    const int cj = min(j, nst - 1);
-    load_a(cj, j);
-    load_w(cj, ring[j]);
-  }
-  // waves past the matrix's rows (act false) run the same code on a clamped row block and
-  // drop the result: one code path keeps the compiler's wait counts exact
+  // sources into the buffer and ring slot that no later stage of the unit reads.  The
+  // remaining < NBUF stages follow, in ring slots 0.., loading nothing.
+  // Waves past the matrix's rows (act false) run the same code on a clamped row block and
+  // drop the result: one code path keeps the compiler's wait counts exact.
+  // (stage j < D of the first group: its weights were issued last in the unit's prologue,
+  // followed by those of the D - 1 - j later prologue stages and the j stages' loads issued
+  // since; its activations are older)
   int c0 = 0;
   for (; c0 + NBUF <= nst; c0 += NBUF) {
 #pragma unroll
     for (int j = 0; j < NBUF; ++j) {
       const int c = c0 + j;
-      wait_vmcnt<(D - 1) * LPS>();
+      if (j < D && c0 == 0) {
+        switch (j) {   // j is known after unrolling
+          case 0: wait_vmcnt<(D - 1) * WPS>(); break;
+          case 1: wait_vmcnt<(D - 2) * WPS + LPS>(); break;
+          default: wait_vmcnt<(D - 3 > 0 ? D - 3 : 0) * WPS + 2 * LPS>(); break;
+        }
+      } else {
+        wait_vmcnt<(D - 1) * LPS>();
+      }
       if ((c + 1) * KS > Kd) zero_tail(c, j);
       stage_barrier();
       compute(c, j, ring[j], true, min(c + D, nst - 1), (j + D) % NBUF, ring[(j + D) % NBUF]);
     }
   }
   // remainder stage c0 + j: its loads were issued D stages before it, followed by those of
-  // D - 1 - j more stages
-  auto last = [&](int j, auto wait) {
+  // D - 1 - j more stages (whole stages after the loop; only weights when it did not run)
+  auto last = [&](int j, auto wait_full, auto wait_w) {
     const int c = c0 + j;
-    wait();
+    if (c0 > 0)
+      wait_full();
+    else
+      wait_w();
     if ((c + 1) * KS > Kd) zero_tail(c, j);
     stage_barrier();
     compute(c, j, ring[j], false, 0, 0, ring[j]);
   };
   if (c0 < nst) {
-    last(0, [] { wait_vmcnt<(D - 1) * LPS>(); });
+    last(0, [] { wait_vmcnt<(D - 1) * LPS>(); }, [] { wait_vmcnt<(D - 1) * WPS>(); });
     if constexpr (NBUF > 2) {
       if (c0 + 1 < nst) {
-        last(1, [] { wait_vmcnt<(D - 2) * LPS>(); });
+        last(1, [] { wait_vmcnt<(D - 2) * LPS>(); }, [] { wait_vmcnt<(D - 2) * WPS>(); });
         if constexpr (NBUF > 3) {
-          if (c0 + 2 < nst) last(2, [] { wait_vmcnt<0>(); });
+          if (c0 + 2 < nst) last(2, [] { wait_vmcnt<0>(); }, [] { wait_vmcnt<0>(); });
         }
       }
     }
+  }
+  __builtin_amdgcn_s_setprio(0);
+
+  // every wave is done with the stages: the next unit's first stages can load
+  stage_barrier();
+  if (has_nxt) {
+    const L ldn(tall_unit_of<GATEUP>(p, nsh, ntile, nnb), sRow_nxt, wave, lane);
+    ldn.load_first_a(sA);
   }
 
   // ---- epilogue: acc[mb][h][i] is tile row 16*h + 4*kq + i (weights are the MFMA's A
@@ -424,7 +490,13 @@ MOE_DEV void tall_unit(const GemmParams &p, bool sh, int4 tile, int nb, const St
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bo[h][i] = bf16_bits_to_f32(bo_raw[h][i]);
+      for (int i = 0; i < 4; ++i) {
+        uint32_t b = bo_raw[h][i];
+        asm volatile("" : "+v"(b));   // converted here, not next to the load
+        bo[h][i] = bf16_bits_to_f32(b);
+      }
+    const float limit = u.limit;
+    const int nr = u.nr, r0 = u.r0;
     const bool vec = (p.ldo & 3) == 0 && ((uintptr_t)p.out & (OT == DT_F32 ? 15 : 7)) == 0;
     const bool rvec = p.resid && (p.ldr & 3) == 0 && ((uintptr_t)p.resid & 15) == 0;
 #pragma unroll
@@ -444,12 +516,12 @@ MOE_DEV void tall_unit(const GemmParams &p, bool sh, int4 tile, int nb, const St
             v[i] = silu_f(g) * up;
           }
           const int col = row_of(4 * kq);
-          store4<OT>(p.out, orow + col, v, min(4, W0.rows - col), vec);
+          store4<OT>(p.out, orow + col, v, min(4, rows - col), vec);
         } else {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int col = row_of(16 * h + 4 * kq);
-            const int nv = min(4, W0.rows - col);
+            const int nv = min(4, rows - col);
             float v[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] = acc[mb][h][i] + bo[h][i];
@@ -483,44 +555,68 @@ __global__ __launch_bounds__(512, 2) void expert_gemm_tall(const GemmParams p) {
   __shared__ __attribute__((aligned(1024))) char sA2[C::ABUF];
   __shared__ __attribute__((aligned(1024))) char sA3[C::NBUF > 3 ? C::ABUF : 16];
   const StageBufs sA = {{sA0, sA1, sA2, sA3}};
-  __shared__ int64_t sRow[C::MT];
+  __shared__ int64_t sRow[2][C::MT];
 
   // units: segment 1 (shared expert / plain rows) first, then the routed m-tiles
   const int nblk0 = p.seg[0].nblk, nblk1 = max(p.seg[1].nblk, 1);
   const int ns = p.seg[1].nblk > 0 ? (p.sh_rows + C::MT - 1) / C::MT : 0;
   const int units_s = ns * nblk1;
   const int nr_routed = p.tiles ? p.tile_count[0] : 0;
-
-  // consecutive units (the column blocks of one m-tile, which share its activation rows) on
-  // one XCD, so that they share its L2
-  const int G = gridDim.x;
-  const int b0 = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
-  for (int u = b0;; u += G) {
-    const bool sh = u < units_s;
-    int ti, nb;
-    int4 tile;
+  auto decode = [&](int u, bool &sh, int4 &tile, int &nb) {
+    sh = u < units_s;
     if (sh) {
-      ti = u / nblk1;
+      const int ti = u / nblk1;
       nb = u - ti * nblk1;
       tile = make_int4(0, p.sh_row0 + ti * C::MT, min(C::MT, p.sh_rows - ti * C::MT), 0);
     } else {
       const int v = u - units_s;
-      ti = v / max(nblk0, 1);
+      const int ti = v / max(nblk0, 1);
       nb = v - ti * nblk0;
-      if (!p.tiles) break;
+      if (!p.tiles) return false;
       tile = p.tiles[min(ti, p.max_tiles - 1)];  // in bounds even past the end of the list
-      if (ti >= nr_routed) break;
+      if (ti >= nr_routed) return false;
     }
-    __syncthreads();  // the previous unit is done with sRow and the stages
-    const int nmb = (min(tile.z, C::MT) + 15) >> 4;
+    tile.x = __builtin_amdgcn_readfirstlane(tile.x);
+    tile.y = __builtin_amdgcn_readfirstlane(tile.y);
+    tile.z = __builtin_amdgcn_readfirstlane(tile.z);
+    return true;
+  };
+
+  // consecutive units (the column blocks of one m-tile, which share its activation rows) on
+  // one XCD, so that they share its L2
+  const int G = gridDim.x;
+  const int tid = threadIdx.x;
+  int u = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  bool csh, nsh;
+  int4 ctile, ntile;
+  int cnb, nnb;
+  if (!decode(u, csh, ctile, cnb)) return;
+  {
+    const TallUnit cur = tall_unit_of<GATEUP>(p, csh, ctile, cnb);
+    tall_fill_rows<C::MT>(cur, sRow[0], tid);
+    __syncthreads();
+    const TallLoader<WF, GQ, GATEUP> ld(cur, sRow[0], tid >> 6, tid & 63);
+    ld.load_first_a(sA);
+  }
+  for (int par = 0;; par ^= 1) {
+    const bool has_nxt = decode(u + G, nsh, ntile, nnb);
+    // the next unit's rows: published by this unit's stage barriers
+    if (has_nxt) tall_fill_rows<C::MT>(tall_unit_of<GATEUP>(p, nsh, ntile, nnb), sRow[par ^ 1], tid);
+    const TallUnit cur = tall_unit_of<GATEUP>(p, csh, ctile, cnb);
+    const int nmb = (min(cur.nr, C::MT) + 15) >> 4;
     if (nmb <= 2)
-      tall_unit<AT, WF, GQ, GATEUP, OT, 2>(p, sh, tile, nb, sA, sRow);
+      tall_unit<AT, WF, GQ, GATEUP, OT, 2>(p, cur, sRow[par], sA, has_nxt, nsh, ntile, nnb, sRow[par ^ 1]);
     else if (nmb <= 4)
-      tall_unit<AT, WF, GQ, GATEUP, OT, 4>(p, sh, tile, nb, sA, sRow);
+      tall_unit<AT, WF, GQ, GATEUP, OT, 4>(p, cur, sRow[par], sA, has_nxt, nsh, ntile, nnb, sRow[par ^ 1]);
     else if (nmb <= 6)
-      tall_unit<AT, WF, GQ, GATEUP, OT, 6>(p, sh, tile, nb, sA, sRow);
+      tall_unit<AT, WF, GQ, GATEUP, OT, 6>(p, cur, sRow[par], sA, has_nxt, nsh, ntile, nnb, sRow[par ^ 1]);
     else
-      tall_unit<AT, WF, GQ, GATEUP, OT, 8>(p, sh, tile, nb, sA, sRow);
+      tall_unit<AT, WF, GQ, GATEUP, OT, 8>(p, cur, sRow[par], sA, has_nxt, nsh, ntile, nnb, sRow[par ^ 1]);
+    if (!has_nxt) break;
+    csh = nsh;
+    ctile = ntile;
+    cnb = nnb;
+    u += G;
   }
   // the last unit's look-ahead loads (repeats of its last stage) may still be writing LDS
   __builtin_amdgcn_s_waitcnt(0);
