@@ -257,7 +257,11 @@ moe_status launch_router(const void *x, int x_dt, int T, int H, const moe_router
   const int E = r->num_experts;
   const int R = E + (coef_w ? 2 : 0);
   Timed tm(TK_ROUTER, s);
-  if (x_dt == MOE_BF16) {
+  if (x_dt == MOE_BF16 && T >= MOE_ROUTER_GEMM_T) {
+    hipLaunchKernelGGL(router_gemm_bf16, dim3((T + 63) / 64, (R + 63) / 64), dim3(256), 0, s, (const uint16_t *)x,
+                       (const uint16_t *)r->w, r->logit_bias, logits, T, H, E, (const uint16_t *)coef_w, coef_b,
+                       clog);
+  } else if (x_dt == MOE_BF16) {
     hipLaunchKernelGGL(router_logits_bf16, dim3((T + 15) / 16, (R + 15) / 16), dim3(512), 0, s, (const uint16_t *)x,
                        (const uint16_t *)r->w, r->logit_bias, logits, T, H, E, (const uint16_t *)coef_w, coef_b,
                        clog);

@@ -117,6 +117,9 @@ struct CombineArgs {
 // ---- kernels ----
 __global__ void router_logits_bf16(const uint16_t *x, const uint16_t *W, const float *lbias, float *logits,
                                    int T, int H, int E, const uint16_t *cw, const float *cb, float *clog);
+__global__ void router_gemm_bf16(const uint16_t *x, const uint16_t *W, const float *lbias, float *logits, int T,
+                                 int H, int E, const uint16_t *cw, const float *cb, float *clog);
+#define MOE_ROUTER_GEMM_T 256  // tokens from which the router runs as a tiled GEMM
 __global__ void router_logits_f32(const float *x, const float *W, const float *lbias, float *logits, int T,
                                   int H, int E, const float *cw, const float *cb, float *clog);
 __global__ void topk_kernel(TopkArgs a);

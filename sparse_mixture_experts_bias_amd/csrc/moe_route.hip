@@ -66,6 +66,111 @@ __global__ __launch_bounds__(512) void router_logits_bf16(const uint16_t *__rest
   }
 }
 
+// router logits for many tokens (bf16): a tiled MFMA GEMM.  A 256-thread workgroup owns 64
+// tokens x 64 rows of [W_r; coef head] (4 waves of 32 x 32); the reduction runs in chunks
+// of 64 elements staged through LDS (double-buffered, loaded one chunk ahead through
+// registers), rows 16-byte-block XOR-swizzled so that fragment reads spread over the banks.
+// Elements past H read as zero.
+__global__ __launch_bounds__(256) void router_gemm_bf16(const uint16_t *__restrict__ x,
+                                                        const uint16_t *__restrict__ W,
+                                                        const float *__restrict__ lbias,
+                                                        float *__restrict__ logits, int T, int H, int E,
+                                                        const uint16_t *__restrict__ cw,
+                                                        const float *__restrict__ cb, float *__restrict__ clog) {
+  constexpr int TM = 64, TN = 64, KC = 64;
+  __shared__ __attribute__((aligned(16))) uint16_t sX[2][TM * KC];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2][TN * KC];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n16 = lane & 15, kq = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t0 = blockIdx.x * TM, r0 = blockIdx.y * TN;
+  const int R = E + (cw ? 2 : 0);
+
+  // staging: each tile is 64 rows x 8 blocks of 16 bytes; thread q loads blocks q and q+256
+  // of both tiles (row = q / 8, block = q % 8), stored at slot block ^ ((row / 2) % 8)
+  const uint16_t *xs[2], *ws[2];
+  int soff[2], sblk[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + 256 * i, row = q >> 3, blk = q & 7;
+    const int t = min(t0 + row, T - 1), rr = r0 + row;
+    xs[i] = x + (int64_t)t * H + blk * 8;
+    ws[i] = (rr < E ? W + (int64_t)rr * H : (rr < R ? cw + (int64_t)(rr - E) * H : W)) + blk * 8;
+    soff[i] = row * KC + ((blk ^ ((row >> 1) & 7)) << 3);
+    sblk[i] = blk;
+  }
+  u32x4_t xa[2], wa[2];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bool ok = k0 + sblk[i] * 8 < H;
+      xa[i] = ok ? *(const u32x4_t *)(xs[i] + k0) : u32x4_t{0u, 0u, 0u, 0u};
+      wa[i] = ok ? *(const u32x4_t *)(ws[i] + k0) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *(u32x4_t *)&sX[b][soff[i]] = xa[i];
+      *(u32x4_t *)&sW[b][soff[i]] = wa[i];
+    }
+  };
+
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) acc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // fragment rows 16 mb + n16 of the wave's 32; block 4 s + kq of the chunk
+  const int sw = (n16 >> 1) & 7;
+  const int nk = (H + KC - 1) / KC;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int c = 0; c < nk; ++c) {
+    const int b = c & 1;
+    if (c + 1 < nk) load((c + 1) * KC);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int slot = ((4 * s + kq) ^ sw) << 3;
+      u32x4_t af[2], bf[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) af[mb] = *(const u32x4_t *)&sX[b][(wm * 32 + 16 * mb + n16) * KC + slot];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) bf[nb] = *(const u32x4_t *)&sW[b][(wn * 32 + 16 * nb + n16) * KC + slot];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[mb]),
+                                                               __builtin_bit_cast(bf16x8_t, bf[nb]), acc[mb][nb], 0, 0,
+                                                               0);
+    }
+    if (c + 1 < nk) {
+      store(b ^ 1);   // the other buffer: last read in chunk c - 1, before the barrier below
+      __syncthreads();
+    }
+  }
+  // acc[mb][nb][i]: token 32 wm + 16 mb + 4 kq + i, row 32 wn + 16 nb + n16
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int e = r0 + wn * 32 + 16 * nb + n16;
+    const float add = e < E ? (lbias ? lbias[e] : 0.f) : (e < R ? cb[e - E] : 0.f);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + wm * 32 + 16 * mb + 4 * kq + i;
+        if (t < T) {
+          if (e < E)
+            logits[(int64_t)t * E + e] = acc[mb][nb][i] + add;
+          else if (e < R)
+            clog[2 * t + (e - E)] = acc[mb][nb][i] + add;
+        }
+      }
+  }
+}
+
 // router logits, f32 x and W_r: one thread per (token, row), sequential fp32 sum; rows as above.
 __global__ void router_logits_f32(const float *__restrict__ x, const float *__restrict__ W,
                                   const float *__restrict__ lbias, float *__restrict__ logits, int T, int H,

@@ -57,6 +57,16 @@ def test_block_small(cfg):
     _full_check(b, f"{cfg}-small")
 
 
+@pytest.mark.parametrize("T,H,E", [(256, 544, 72), (301, 2080, 130)])
+def test_router_tiled_ragged(T, H, E):
+    """Router as a tiled GEMM (many tokens): a reduction that ends inside a chunk,
+    ragged token and expert tiles, the blend head's two rows in the last tile."""
+    from dataclasses import replace
+    spec = replace(synth.FULL_SPECS["c3"], name="router-tiled", T=T, H=H, E=E, K=6, I=64, I_s=64,
+                   group=32, seed=T + E)
+    _full_check(synth.make_block(spec, DEV), f"router-tiled T={T} H={H} E={E}")
+
+
 def test_block_full_c1():
     b = synth.make_block(synth.FULL_SPECS["c1"], DEV)
     _full_check(b, "c1-full")
