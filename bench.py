@@ -138,6 +138,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for 1 GiB)")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the workload's layer on this many tokens instead of its own count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (the reference kernel that scales the "
@@ -166,6 +168,9 @@ def main():
     dev = "cuda:0"
     wl = args.workload
     spec = synth.FULL_SPECS[wl]
+    if args.tokens > 0:
+        from dataclasses import replace
+        spec = replace(spec, T=args.tokens)
     log(f"workload {wl}: generating the layer on {dev}")
     b = synth.make_block(spec, dev)
     moe.lib()
@@ -232,7 +237,8 @@ def main():
         "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if b.x.dtype == torch.bfloat16 else "f32", "data": "synthetic",
-        "config": {"workload": f"{wl}: {WORKLOADS[wl]}", "tokens": b.T, "hidden": b.H, "experts": b.E,
+        "config": {"workload": f"{wl}: {WORKLOADS[wl]}" + (f" (run on {b.T} tokens)" if args.tokens > 0 else ""),
+                   "tokens": b.T, "hidden": b.H, "experts": b.E,
                    "top_k": b.K, "intermediate": b.I, "weight_copies": copies,
                    "inter_dtype": {0: "f32", 1: "bf16", 2: "f16"}[desc0.c.inter_dtype], "output": "f32"},
         "step_hbm_gbs": round(wm["step_bytes"] / (ms_step / 1e3) / 1e9, 1),
