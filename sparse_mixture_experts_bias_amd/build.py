@@ -16,7 +16,8 @@ import tempfile
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["moe_gemm_tall.hip", "moe_abi.hip", "moe_route.hip", "moe_gemm.hip", "moe_combine.hip", "moe_pack.hip"]
+SOURCES = ["moe_gemm_tall.hip", "moe_gemm_ws.hip", "moe_abi.hip", "moe_route.hip", "moe_gemm.hip", "moe_combine.hip",
+           "moe_pack.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

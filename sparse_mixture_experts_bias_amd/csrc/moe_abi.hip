@@ -358,14 +358,18 @@ int routed_tiles_ub(int TK, int E, int mt) { return TK / mt + (E < TK ? E : TK);
 int max_tiles(int TK, int E) { return routed_tiles_ub(TK, E, MOE_MT_MIN) + 1; }
 
 // m-blocks (16 rows each) per m-tile: 1 for decode-sized segments (the HBM-streaming
-// kernel), 8 otherwise (the 128-row MFMA kernel of moe_gemm_tall.hip)
+// kernels), 8 otherwise (the 128-row MFMA kernel of moe_gemm_tall.hip).  Kernel codes: 0 and
+// 1 the decode kernels of moe_gemm.hip (0: SHORT), MB_WS the loader-wave decode kernel of
+// moe_gemm_ws.hip (4-bit weights; same units as 1), MB_TALL the prefill kernel.
+constexpr int MB_WS = 2;
 constexpr int MB_TALL = 8;
 int pick_mb(double avg_rows) { return avg_rows <= 16.0 ? 1 : MB_TALL; }
 int mb_for_routing(int TK, int E) { return pick_mb((double)TK / (E < TK ? E : (TK > 0 ? TK : 1))); }
 
-// mb: 1 (decode tiles), 0 (decode tiles, SHORT variant) or MB_TALL
-int gemm_grid(int units_ub, int mb) {
-  const int cap = (mb == 0 ? 4 : (mb == 1 ? 3 : 1)) * device_cus();  // resident workgroups per CU
+// kmb: a kernel code (see above); per_cu: resident workgroups per CU
+int gemm_grid(int units_ub, int kmb, int per_cu = 0) {
+  if (per_cu <= 0) per_cu = kmb == 0 ? 4 : (kmb == 1 ? 3 : 1);
+  const int cap = per_cu * device_cus();
   return units_ub < cap ? units_ub : cap;
 }
 
@@ -380,6 +384,10 @@ hipError_t launch_gemm_kernel(int adt, const moe_linear &fmt_of, bool gateup, in
                               int units_ub, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
   const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
+  if (kmb == MB_WS)
+    return launch_expert_gemm_ws(adt_k, wf_of(fmt_of), fmt_of.group_size, gateup, odt_k, p,
+                                 gemm_grid(units_ub, kmb, ws_wgs_per_cu(wf_of(fmt_of), fmt_of.group_size)), s, e0,
+                                 e1);
   if (kmb == MB_TALL)
     return launch_expert_gemm_tall(adt_k, wf_of(fmt_of), fmt_of.group_size, gateup, odt_k, p,
                                    gemm_grid(units_ub, kmb), s, e0, e1);
@@ -387,10 +395,14 @@ hipError_t launch_gemm_kernel(int adt, const moe_linear &fmt_of, bool gateup, in
                             s, e0, e1);
 }
 
-// decode LINEAR launches whose longest reduction spans at most three chunks use the SHORT variant
+// decode launches of 4-bit weights use the loader-wave kernel (also for short reductions, where
+// it measured faster than the SHORT variant); DENSE decode LINEAR launches whose longest
+// reduction spans at most three chunks use the SHORT variant
 int kernel_mb(int mb, bool gateup, const moe_linear &w, int kmax) {
-  const int kc = w.fmt == MOE_W_DENSE ? 64 : 256;
-  return (mb == 1 && !gateup && (kmax + kc - 1) / kc <= 3) ? 0 : mb;
+  if (mb != 1) return mb;
+  if (w.fmt != MOE_W_DENSE) return MB_WS;
+  const int kc = 64;
+  return (!gateup && (kmax + kc - 1) / kc <= 3) ? 0 : mb;
 }
 
 AOp aop(const void *a, int64_t lda, const int32_t *gather, int gdiv, int row_sub, int64_t rows) {
@@ -404,12 +416,14 @@ AOp aop(const void *a, int64_t lda, const int32_t *gather, int gdiv, int row_sub
   return o;
 }
 
-// the tall kernel addresses its activation rows with 32-bit byte offsets
-bool tall_offsets_fit(const GemmParams &p) {
+// the tall kernel addresses its activation rows with 32-bit byte offsets, the loader-wave
+// kernel with 31-bit ones (and the packed matrices likewise)
+bool offsets_fit(const GemmParams &p, int64_t lim) {
   for (int i = 0; i < 2; ++i)
-    if (p.seg[i].nblk > 0 && p.seg[i].A.rows * p.seg[i].A.lda * 2 > (int64_t)UINT32_MAX) return false;
+    if (p.seg[i].nblk > 0 && (p.seg[i].A.rows * p.seg[i].A.lda * 2 > lim || p.seg[i].w0.pk_mat > lim)) return false;
   return true;
 }
+bool tall_offsets_fit(const GemmParams &p) { return offsets_fit(p, (int64_t)UINT32_MAX); }
 
 SegSet segset(AOp A, const moe_linear &w0, const moe_linear *w1, float limit, bool gateup) {
   SegSet s;
@@ -447,7 +461,8 @@ moe_status run_gemm(int adt, const moe_linear &fmt_of, bool gateup, int odt, int
   p.resid = resid;
   p.ldr = ldr;
   const int units_ub = routed_tiles_ub(TK, E, mt) * p.seg[0].nblk + ((sh_rows + mt - 1) / mt) * p.seg[1].nblk;
-  const int kmb = kernel_mb(mb, gateup, fmt_of, shared && shared->K > routed.K ? shared->K : routed.K);
+  int kmb = kernel_mb(mb, gateup, fmt_of, shared && shared->K > routed.K ? shared->K : routed.K);
+  if (kmb == MB_WS && !offsets_fit(p, INT32_MAX)) kmb = 1;
   CHECK(kmb != MB_TALL || tall_offsets_fit(p), MOE_ERR_SHAPE, "activation operand of over 4 GiB");
   Timed tm(gateup ? TK_GATEUP : TK_DOWN, s, true);
   HIPCHK(launch_gemm_kernel(adt, fmt_of, gateup, odt, kmb, p, units_ub, s, tm.start(), tm.stop()));
@@ -480,7 +495,8 @@ moe_status run_plain(int adt, const moe_linear &W, const moe_linear *W1, float l
   p.resid = resid;
   p.ldr = ldr;
   const int units = ((rows + mt - 1) / mt) * sg.nblk;
-  const int kmb = kernel_mb(mb, gateup, W, W.cols);
+  int kmb = kernel_mb(mb, gateup, W, W.cols);
+  if (kmb == MB_WS && !offsets_fit(p, INT32_MAX)) kmb = 1;
   CHECK(kmb != MB_TALL || tall_offsets_fit(p), MOE_ERR_SHAPE, "activation operand of over 4 GiB");
   Timed tm(TK_PLAIN, s, true);
   HIPCHK(launch_gemm_kernel(adt, W, gateup, odt, kmb, p, units, s, tm.start(), tm.stop()));

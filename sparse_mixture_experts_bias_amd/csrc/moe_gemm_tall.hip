@@ -33,20 +33,8 @@
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 // zeros: the source of absent biases
 __device__ u32x4_t g_zero_block = {0u, 0u, 0u, 0u};
-
-// barrier without the compiler's release fence (which would drain every outstanding load,
-// the prefetched stages included); callers wait for their own loads first.  LDS reads are
-// drained here (lgkmcnt 0, vmcnt and expcnt untouched), so no wave's direct loads can
-// overwrite a stage that another wave is still reading.
-MOE_DEV void stage_barrier() {
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
 
 // A stage is the reduction slice that one barrier covers: half a packed record for the
 // 4-bit formats (128 elements: two of its four 1 KB weight pieces), one record for DENSE

@@ -139,6 +139,11 @@ __global__ void build_tiles(const int32_t *offsets, int E, int4 *tiles, int *til
 // host-side launchers (moe_gemm.hip, moe_combine.hip)
 hipError_t launch_expert_gemm(int adt, int wfmt, int group, bool gateup, int odt, int mb, const GemmParams &p,
                               int grid, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+// decode-sized segments with 4-bit weights: loader waves stream the records through LDS
+// (moe_gemm_ws.hip); same units as launch_expert_gemm with mb == 1
+hipError_t launch_expert_gemm_ws(int adt, int wfmt, int group, bool gateup, int odt, const GemmParams &p, int grid,
+                                 hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+int ws_wgs_per_cu(int wfmt, int group);  // resident workgroups per CU (LDS)
 // prefill-sized segments: 128-row m-tiles, 8-wave workgroups (moe_gemm_tall.hip)
 hipError_t launch_expert_gemm_tall(int adt, int wfmt, int group, bool gateup, int odt, const GemmParams &p,
                                    int grid, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);

@@ -99,6 +99,33 @@ constexpr int LOADS_PER_CHUNK() {
   return 4 + (WF == WF_AFFINE4 ? (pk_nu(WF, GQ) == 8 ? 4 : 2) : (WF == WF_MXFP4 ? 2 : 0)) + SIT;
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// workgroup barrier without the compiler's release fence (which would drain every
+// outstanding load, prefetched ones included); callers wait for their own global loads
+// first.  LDS accesses are drained here (lgkmcnt 0, vmcnt and expcnt untouched), so LDS
+// written before the barrier is visible after it and no wave's direct loads can overwrite
+// LDS that another wave is still reading.
+MOE_DEV void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// uniform values through the scalar data cache, so that reading them does not wait on the
+// vector loads in flight; each load is waited for in its own asm block
+MOE_DEV int4 load_uniform_int4(const int4 *ptr) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  i32x4 v;
+  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr));
+  return make_int4(v[0], v[1], v[2], v[3]);
+}
+MOE_DEV int load_uniform_int(const int *ptr) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr));
+  return v;
+}
+
 MOE_DEV float e8m0_to_f32(uint32_t e) {
   return e == 0u ? __uint_as_float(0x00400000u) : (e == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float(e << 23));
 }
