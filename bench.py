@@ -87,7 +87,7 @@ def work_model(b, hit):
 
 def kernel_source_sha():
     h = hashlib.sha256()
-    for f in ("moe_gemm.hip", "moe_kernels.h", "moe_device.h"):
+    for f in ("moe_gemm_ws.hip", "moe_gemm.hip", "moe_mfma.h", "moe_kernels.h", "moe_device.h"):
         with open(os.path.join(ROOT, "sparse_mixture_experts_bias_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
