@@ -253,22 +253,23 @@ struct Timed {
 // ---------------------------------------------------------------------------
 // router logits (+ the blend head's two logits into clog when coef_w is given)
 moe_status launch_router(const void *x, int x_dt, int T, int H, const moe_router *r, const void *coef_w,
-                         const float *coef_b, float *logits, float *clog, hipStream_t s) {
+                         const float *coef_b, float *logits, float *clog, hipStream_t s, int *zero = nullptr) {
   const int E = r->num_experts;
   const int R = E + (coef_w ? 2 : 0);
   Timed tm(TK_ROUTER, s);
   if (x_dt == MOE_BF16 && T >= MOE_ROUTER_GEMM_T) {
     hipLaunchKernelGGL(router_gemm_bf16, dim3((T + 63) / 64, (R + 63) / 64), dim3(256), 0, s, (const uint16_t *)x,
                        (const uint16_t *)r->w, r->logit_bias, logits, T, H, E, (const uint16_t *)coef_w, coef_b,
-                       clog);
+                       clog, zero);
   } else if (x_dt == MOE_BF16) {
     hipLaunchKernelGGL(router_logits_bf16, dim3((T + 15) / 16, (R + 15) / 16), dim3(512), 0, s, (const uint16_t *)x,
                        (const uint16_t *)r->w, r->logit_bias, logits, T, H, E, (const uint16_t *)coef_w, coef_b,
-                       clog);
+                       clog, zero);
   } else {
     const int64_t n = (int64_t)T * R;
     hipLaunchKernelGGL(router_logits_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float *)x,
-                       (const float *)r->w, r->logit_bias, logits, T, H, E, (const float *)coef_w, coef_b, clog);
+                       (const float *)r->w, r->logit_bias, logits, T, H, E, (const float *)coef_w, coef_b, clog,
+                       zero);
   }
   HIPCHK(hipGetLastError());
   return MOE_OK;
@@ -311,21 +312,17 @@ moe_status launch_topk(const TopkArgs &a, hipStream_t s) {
   return MOE_OK;
 }
 
-// selection + permutation + tile list in one workgroup (T <= MOE_ROUTE_SMALL_T, K <= 16)
-moe_status launch_route_small(const TopkArgs &a, int32_t *counts, int32_t *offsets, int32_t *ss, int32_t *sp,
-                              int4 *tiles, int *tc, int mt, hipStream_t s) {
+// selection + permutation + tile list in one launch (T <= MOE_ROUTE_SMALL_T, K <= 16); done:
+// a counter the router launch has set to zero
+moe_status launch_route_decode(const TopkArgs &a, int32_t *counts, int32_t *offsets, int32_t *ss, int32_t *sp,
+                               int4 *tiles, int *tc, int mt, int *done, hipStream_t s) {
   Timed tm(TK_TOPK, s);
+  const dim3 g((a.T + 7) / 8), b(256);
   switch (topk_slots(a.E, a.K)) {
-    case 4:
-      hipLaunchKernelGGL((route_small<4, 1024>), dim3(1), dim3(1024), 0, s, a, counts, offsets, ss, sp, tiles, tc, mt);
-      break;
-    case 8:
-      hipLaunchKernelGGL((route_small<8, 1024>), dim3(1), dim3(1024), 0, s, a, counts, offsets, ss, sp, tiles, tc, mt);
-      break;
-    case 16:
-      hipLaunchKernelGGL((route_small<16, 512>), dim3(1), dim3(512), 0, s, a, counts, offsets, ss, sp, tiles, tc, mt);
-      break;
-    default: return fail(MOE_ERR_UNSUPPORTED, "route_small needs top_k <= 16");
+    case 4: hipLaunchKernelGGL(route_decode<4>, g, b, 0, s, a, counts, offsets, ss, sp, tiles, tc, mt, done); break;
+    case 8: hipLaunchKernelGGL(route_decode<8>, g, b, 0, s, a, counts, offsets, ss, sp, tiles, tc, mt, done); break;
+    case 16: hipLaunchKernelGGL(route_decode<16>, g, b, 0, s, a, counts, offsets, ss, sp, tiles, tc, mt, done); break;
+    default: return fail(MOE_ERR_UNSUPPORTED, "route_decode needs top_k <= 16");
   }
   HIPCHK(hipGetLastError());
   return MOE_OK;
@@ -826,6 +823,7 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   const int mb = mb_for_routing(TK, E);
   const size_t o_tiles = pl.take((size_t)ntile * 16);
   const size_t o_tc = pl.take(16);
+  const size_t o_done = pl.take(16);
   const size_t o_z = latent ? pl.take((size_t)T * D * isz) : 0;
   const size_t o_h = pl.take((size_t)(TK + Tsh) * ldh * isz);
   const size_t o_o = pl.take((size_t)(TK + Tsh) * D * isz);
@@ -856,12 +854,14 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   // 1. router + selection (+ blend coefficients)
   const bool blend = b->shared_mode == MOE_SHARED_BLEND;
   float *clog = at<float>(ws, o_clog);
+  const bool small = Ti <= MOE_ROUTE_SMALL_T && topk_slots(E, K) > 0;
+  int *done = at<int>(ws, o_done);
   TRY(launch_router(x, x_dtype, Ti, H, &b->router, blend ? b->coef_w : nullptr, blend ? b->coef_b : nullptr, logits,
-                    clog, s));
+                    clog, s, small ? done : nullptr));
   const TopkArgs ta = topk_args(Ti, &b->router, logits, idx, wts, blend ? clog : nullptr, coef);
   // 2. permutation + tile list (for a few tokens in the same workgroup as the selection)
-  if (Ti <= MOE_ROUTE_SMALL_T && topk_slots(E, K) > 0) {
-    TRY(launch_route_small(ta, counts, offsets, ss, sp, mf ? tiles : nullptr, mf ? tc : nullptr, 16 * mb, s));
+  if (small) {
+    TRY(launch_route_decode(ta, counts, offsets, ss, sp, mf ? tiles : nullptr, mf ? tc : nullptr, 16 * mb, done, s));
   } else {
     TRY(launch_topk(ta, s));
     TRY(launch_permute(idx, Ti, K, E, counts, offsets, ss, sp, at<int32_t>(ws, o_chunk), mf ? tiles : nullptr,

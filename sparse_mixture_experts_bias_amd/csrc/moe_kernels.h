@@ -8,7 +8,7 @@
 #define MOE_MT_MIN 16        // smallest m-tile (rows of one segment per work unit) of the grouped GEMM
 #define MOE_KC 256           // reduction elements per chunk for 4-bit weights (128 B per row)
 #define MOE_GEMM_THREADS 256 // 4 waves
-#define MOE_ROUTE_SMALL_T 64 // tokens (K <= 16) up to which selection and permutation share one workgroup
+#define MOE_ROUTE_SMALL_T 64 // tokens (K <= 16) up to which selection and permutation share one launch
 
 struct TopkArgs {
   const float *logits;  // [T][E]
@@ -115,18 +115,19 @@ struct CombineArgs {
 };
 
 // ---- kernels ----
+// router kernels: zero (optional) is set to 0 by the launch (the counter of route_decode)
 __global__ void router_logits_bf16(const uint16_t *x, const uint16_t *W, const float *lbias, float *logits,
-                                   int T, int H, int E, const uint16_t *cw, const float *cb, float *clog);
+                                   int T, int H, int E, const uint16_t *cw, const float *cb, float *clog, int *zero);
 __global__ void router_gemm_bf16(const uint16_t *x, const uint16_t *W, const float *lbias, float *logits, int T,
-                                 int H, int E, const uint16_t *cw, const float *cb, float *clog);
+                                 int H, int E, const uint16_t *cw, const float *cb, float *clog, int *zero);
 #define MOE_ROUTER_GEMM_T 256  // tokens from which the router runs as a tiled GEMM
 __global__ void router_logits_f32(const float *x, const float *W, const float *lbias, float *logits, int T,
-                                  int H, int E, const float *cw, const float *cb, float *clog);
+                                  int H, int E, const float *cw, const float *cb, float *clog, int *zero);
 __global__ void topk_kernel(TopkArgs a);
 template <int SL> __global__ void topk_half_kernel(TopkArgs a);
-template <int SL, int NT>
-__global__ void route_small(TopkArgs a, int32_t *counts, int32_t *offsets, int32_t *sorted_slot, int32_t *slot_pos,
-                            int4 *tiles, int *tile_count, int mt);
+template <int SL>
+__global__ void route_decode(TopkArgs a, int32_t *counts, int32_t *offsets, int32_t *sorted_slot, int32_t *slot_pos,
+                             int4 *tiles, int *tile_count, int mt, int *done);
 __global__ void perm_count(const int32_t *idx, int T, int K, int E, int32_t *chunk_counts);
 __global__ void perm_scan(int32_t *chunk_counts, int nchunks, int E, int TK, int32_t *counts, int32_t *offsets,
                           int4 *tiles, int *tile_count, int mt);

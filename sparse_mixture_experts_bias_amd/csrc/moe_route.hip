@@ -21,7 +21,9 @@ __global__ __launch_bounds__(512) void router_logits_bf16(const uint16_t *__rest
                                                           const float *__restrict__ lbias,
                                                           float *__restrict__ logits, int T, int H, int E,
                                                           const uint16_t *__restrict__ cw,
-                                                          const float *__restrict__ cb, float *__restrict__ clog) {
+                                                          const float *__restrict__ cb, float *__restrict__ clog,
+                                                          int *__restrict__ zero) {
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *zero = 0;
   __shared__ float red[8][16][17];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
@@ -76,7 +78,9 @@ __global__ __launch_bounds__(256) void router_gemm_bf16(const uint16_t *__restri
                                                         const float *__restrict__ lbias,
                                                         float *__restrict__ logits, int T, int H, int E,
                                                         const uint16_t *__restrict__ cw,
-                                                        const float *__restrict__ cb, float *__restrict__ clog) {
+                                                        const float *__restrict__ cb, float *__restrict__ clog,
+                                                        int *__restrict__ zero) {
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *zero = 0;
   constexpr int TM = 64, TN = 64, KC = 64;
   __shared__ __attribute__((aligned(16))) uint16_t sX[2][TM * KC];
   __shared__ __attribute__((aligned(16))) uint16_t sW[2][TN * KC];
@@ -175,7 +179,8 @@ __global__ __launch_bounds__(256) void router_gemm_bf16(const uint16_t *__restri
 __global__ void router_logits_f32(const float *__restrict__ x, const float *__restrict__ W,
                                   const float *__restrict__ lbias, float *__restrict__ logits, int T, int H,
                                   int E, const float *__restrict__ cw, const float *__restrict__ cb,
-                                  float *__restrict__ clog) {
+                                  float *__restrict__ clog, int *__restrict__ zero) {
+  if (zero && blockIdx.x == 0 && threadIdx.x == 0) *zero = 0;
   const int R = E + (cw ? 2 : 0);
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)T * R) return;
@@ -325,14 +330,25 @@ template <int CTRL>
 MOE_DEV float dppf(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-MOE_DEV uint64_t half_max_u64(uint64_t v) {
-  v = umax64(v, dpp64<0xB1>(v));
-  v = umax64(v, dpp64<0x4E>(v));
-  v = umax64(v, dpp64<0x141>(v));
-  v = umax64(v, dpp64<0x140>(v));
-  const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
-  const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
-  return umax64(((uint64_t)hi[0] << 32) | lo[0], ((uint64_t)hi[1] << 32) | lo[1]);
+template <int CTRL>
+MOE_DEV uint32_t dppu(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+MOE_DEV uint32_t half_max_u32(uint32_t v) {
+  v = max(v, dppu<0xB1>(v));
+  v = max(v, dppu<0x4E>(v));
+  v = max(v, dppu<0x141>(v));
+  v = max(v, dppu<0x140>(v));
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max((uint32_t)r[0], (uint32_t)r[1]);
+}
+MOE_DEV uint32_t half_min_u32(uint32_t v) {
+  v = min(v, dppu<0xB1>(v));
+  v = min(v, dppu<0x4E>(v));
+  v = min(v, dppu<0x141>(v));
+  v = min(v, dppu<0x140>(v));
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return min((uint32_t)r[0], (uint32_t)r[1]);
 }
 MOE_DEV float half_max_f32(float v) {
   v = fmaxf(v, dppf<0xB1>(v));
@@ -386,27 +402,40 @@ MOE_DEV void topk_half(const TopkArgs &a, int t, int l32, int *el, float *esc, i
 #pragma unroll
     for (int j = 0; j < SL; ++j) sc[j] = 1.0f / (1.0f + expf(-lg[j]));
   }
-  uint64_t key[SL];
+  // selection keys: the order-preserving u32 of score + bias (0, below every key, for absent
+  // or retired experts).  Each round takes the half-wave maximum key, then the lowest expert
+  // id holding it (each lane offers its lowest slot with its own maximum), and the owner
+  // retires that slot.
+  uint32_t key[SL];
 #pragma unroll
-  for (int j = 0; j < SL; ++j) {
-    const int e = l32 + 32 * j;
-    key[j] = (e < a.E) ? (((uint64_t)ord_key(sc[j] + sb[j]) << 32) | (uint32_t)~e) : 0ull;
-  }
+  for (int j = 0; j < SL; ++j) key[j] = (l32 + 32 * j < a.E) ? ord_key(sc[j] + sb[j]) : 0u;
+  uint32_t bv;
+  int bj;
+  auto local_best = [&]() {
+    bv = key[0];
+    bj = 0;
+#pragma unroll
+    for (int j = 1; j < SL; ++j)
+      if (key[j] > bv) {
+        bv = key[j];
+        bj = j;
+      }
+  };
+  local_best();
   for (int k = 0; k < a.K; ++k) {
-    uint64_t loc = key[0];
-#pragma unroll
-    for (int j = 1; j < SL; ++j) loc = umax64(loc, key[j]);
-    const int be = (int)~(uint32_t)half_max_u64(loc);
+    const uint32_t m = half_max_u32(bv);
+    const int be = (int)half_min_u32(bv == m ? (uint32_t)(32 * bj + l32) : 0xFFFFFFFFu);
     if ((be & 31) == l32) {  // the owner retires the winner and records its score
       float ws = 0.f;
 #pragma unroll
       for (int j = 0; j < SL; ++j)
-        if (j == (be >> 5)) {
+        if (j == bj) {
           ws = sc[j];
-          key[j] = 0ull;
+          key[j] = 0u;
         }
       esc[k] = ws;
       el[k] = be;
+      local_best();
     }
   }
   // the chosen ids in ascending order and the weight sum
@@ -679,43 +708,59 @@ __global__ __launch_bounds__(256) void perm_small(const int32_t *__restrict__ id
   perm_block(idx, T, K, E, counts, offsets, sorted_slot, slot_pos, tiles, tile_count, mt, sm);
 }
 
-// T <= MOE_ROUTE_SMALL_T, K <= 16: selection (one half-wave per token) and the permutation
-// in one workgroup of NT threads (1024, or 512 when a lane holds 16 experts and needs the
-// registers).  The per-expert (slot count, tile count) pairs go through a single scan,
-// packed in one int (T*K <= 1024).
-template <int SL, int NT>
-__global__ __launch_bounds__(NT) void route_small(TopkArgs a, int32_t *__restrict__ counts,
-                                                 int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_slot,
-                                                 int32_t *__restrict__ slot_pos, int4 *tiles, int *tile_count, int mt) {
-  constexpr int NH = NT / 32, NW = NT / 64;
-  __shared__ __attribute__((aligned(16))) int el[NH][16];
-  __shared__ float esc[NH][16];
-  __shared__ int32_t sidx[MOE_ROUTE_SMALL_T * 16];
+// T <= MOE_ROUTE_SMALL_T, K <= 16: selection and permutation in one launch.  Each 256-thread
+// workgroup selects for 8 tokens (one half-wave each), so that the selection, which is bound
+// by dependent cross-lane steps, runs on several CUs; the last workgroup to finish (a counter
+// that the router launch set to zero) builds the permutation and the tile list from the
+// stored selections: per-expert counts and token masks, one scan over the experts of the
+// packed (slot count, tile count) pairs (T*K <= 1024), then each slot's rank among the earlier
+// tokens of its expert.
+template <int SL>
+__global__ __launch_bounds__(256) void route_decode(TopkArgs a, int32_t *__restrict__ counts,
+                                                   int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_slot,
+                                                   int32_t *__restrict__ slot_pos, int4 *tiles, int *tile_count,
+                                                   int mt, int *done) {
+  constexpr int NTW = MOE_ROUTE_SMALL_T / 32;  // token mask words per expert
+  __shared__ __attribute__((aligned(16))) int el[8][16];
+  __shared__ float esc[8][16];
   __shared__ int cnt[MOE_MAX_EXPERTS], offs[MOE_MAX_EXPERTS];
-  __shared__ uint32_t tmask[MOE_MAX_EXPERTS][MOE_ROUTE_SMALL_T / 32];
-  __shared__ int wtot[NW];
-  static_assert(NT >= MOE_MAX_EXPERTS, "one expert per thread in the scan");
+  __shared__ uint32_t tmask[MOE_MAX_EXPERTS][NTW];
+  __shared__ int wtot[4];
+  __shared__ int last;
+  static_assert(2 * 256 >= MOE_MAX_EXPERTS, "two experts per thread in the scan");
   const int tid = threadIdx.x, lane = tid & 63, half = tid >> 5, wave = tid >> 6;
+  topk_half<SL>(a, blockIdx.x * 8 + half, tid & 31, el[half], esc[half], nullptr);
+  __threadfence();  // this workgroup's selections are visible before it is counted
+  __syncthreads();
+  if (tid == 0) last = atomicAdd(done, 1) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();  // every other workgroup's selections are visible to this one
   const int E = a.E, K = a.K, TK = a.T * a.K;
-  for (int e = tid; e < E; e += NT) {
+  for (int e = tid; e < E; e += 256) {
     cnt[e] = 0;
 #pragma unroll
-    for (int w = 0; w < MOE_ROUTE_SMALL_T / 32; ++w) tmask[e][w] = 0u;
+    for (int w = 0; w < NTW; ++w) tmask[e][w] = 0u;
   }
-  for (int t0 = 0; t0 < a.T; t0 += NH) topk_half<SL>(a, t0 + half, lane & 31, el[half], esc[half], sidx);
   __syncthreads();
   // slot p = t*K + j: per-expert counts and per-expert token masks
-  for (int p = tid; p < TK; p += NT) {
-    const int ep = sidx[p], tp = p / K;
+  for (int p = tid; p < TK; p += 256) {
+    const int ep = a.idx[p], tp = p / K;
     atomicAdd(&cnt[ep], 1);
     atomicOr(&tmask[ep][tp >> 5], 1u << (tp & 31));
   }
   __syncthreads();
-  // exclusive scan over experts of (count | tiles << 16)
-  const int c = tid < E ? cnt[tid] : 0;
-  const int nt = (c + mt - 1) / mt;
-  const int packed = c | (nt << 16);
-  int incl = packed;
+  // exclusive scan over experts of (count | tiles << 16), experts 2 tid and 2 tid + 1
+  int c[2], nt[2], pk[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = 2 * tid + q;
+    c[q] = e < E ? cnt[e] : 0;
+    nt[q] = (c[q] + mt - 1) / mt;
+    pk[q] = c[q] | (nt[q] << 16);
+  }
+  const int local = pk[0] + pk[1];
+  int incl = local;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int y = __shfl_up(incl, o, 64);
@@ -725,19 +770,24 @@ __global__ __launch_bounds__(NT) void route_small(TopkArgs a, int32_t *__restric
   __syncthreads();
   int base = 0, total = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
+  for (int w = 0; w < 4; ++w) {
     const int v = wtot[w];
     base += (w < wave) ? v : 0;
     total += v;
   }
-  if (tid < E) {
-    const int ex = base + incl - packed;
-    const int off = ex & 0xFFFF, tb = ex >> 16;
-    offs[tid] = off;
-    counts[tid] = c;
-    offsets[tid] = off;
-    if (tiles)
-      for (int i = 0; i < nt; ++i) tiles[tb + i] = make_int4(tid, off + i * mt, min(mt, c - i * mt), 0);
+  int ex = base + incl - local;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = 2 * tid + q;
+    if (e < E) {
+      const int off = ex & 0xFFFF, tb = ex >> 16;
+      offs[e] = off;
+      counts[e] = c[q];
+      offsets[e] = off;
+      if (tiles)
+        for (int i = 0; i < nt[q]; ++i) tiles[tb + i] = make_int4(e, off + i * mt, min(mt, c[q] - i * mt), 0);
+    }
+    ex += pk[q];
   }
   if (tid == 0) {
     offsets[E] = total & 0xFFFF;
@@ -745,21 +795,22 @@ __global__ __launch_bounds__(NT) void route_small(TopkArgs a, int32_t *__restric
   }
   __syncthreads();
   // rank of slot p among the slots of its expert: earlier tokens that chose the same expert
-  for (int p = tid; p < TK; p += NT) {
-    const int ep = sidx[p], tp = p / K;
+  for (int p = tid; p < TK; p += 256) {
+    const int ep = a.idx[p], tp = p / K;
     int rank = __popc(tmask[ep][tp >> 5] & ((1u << (tp & 31)) - 1u));
     for (int w = 0; w < (tp >> 5); ++w) rank += __popc(tmask[ep][w]);
     const int pos = offs[ep] + rank;
     sorted_slot[pos] = p;
     slot_pos[p] = pos;
   }
+  if (tid == 0) *done = 0;
 }
-template __global__ void route_small<4, 1024>(TopkArgs, int32_t *, int32_t *, int32_t *, int32_t *, int4 *, int *,
-                                              int);
-template __global__ void route_small<8, 1024>(TopkArgs, int32_t *, int32_t *, int32_t *, int32_t *, int4 *, int *,
-                                              int);
-template __global__ void route_small<16, 512>(TopkArgs, int32_t *, int32_t *, int32_t *, int32_t *, int4 *, int *,
-                                              int);
+template __global__ void route_decode<4>(TopkArgs, int32_t *, int32_t *, int32_t *, int32_t *, int4 *, int *, int,
+                                         int *);
+template __global__ void route_decode<8>(TopkArgs, int32_t *, int32_t *, int32_t *, int32_t *, int4 *, int *, int,
+                                         int *);
+template __global__ void route_decode<16>(TopkArgs, int32_t *, int32_t *, int32_t *, int32_t *, int4 *, int *, int,
+                                          int *);
 
 // tile list from caller-provided offsets (moe_experts_forward)
 __global__ __launch_bounds__(256) void build_tiles(const int32_t *__restrict__ offsets, int E, int4 *tiles,
