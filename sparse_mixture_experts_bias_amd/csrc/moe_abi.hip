@@ -252,15 +252,40 @@ struct Timed {
 // launch helpers
 // ---------------------------------------------------------------------------
 // router logits (+ the blend head's two logits into clog when coef_w is given)
+// slices of the reduction for the tiled router (1 when it does not apply): enough 128x64 tiles
+// x slices for ~1.5 workgroups per CU, slices of whole 64-element chunks
+bool router_tiled(int x_dt, int T, int H, int E) {
+  return x_dt == MOE_BF16 && T >= MOE_ROUTER_GEMM_T && E % 8 == 0 && (int64_t)T * H * 2 <= INT32_MAX &&
+         (int64_t)E * H * 2 <= INT32_MAX;
+}
+int router_slice_len(int T, int H, int R) {
+  const int tiles = ((T + 127) / 128) * ((R + 63) / 64);
+  int S = (3 * device_cus() / 2 + tiles - 1) / tiles;
+  S = S < 1 ? 1 : (S > 16 ? 16 : S);
+  const int ks = (((H + S - 1) / S) + 63) / 64 * 64;
+  return ks;
+}
+int router_slices(int x_dt, int T, int H, int E, bool blend, bool split) {
+  if (!split || !router_tiled(x_dt, T, H, E)) return 1;
+  const int ks = router_slice_len(T, H, E + (blend ? 2 : 0));
+  return (H + ks - 1) / ks;
+}
+
+// router logits (+ the blend head's two logits into clog when coef_w is given).  split: the
+// tiled router may write `slices` partial sums (logits + z*T*E, clog + z*2T), added in order by
+// the selection.
 moe_status launch_router(const void *x, int x_dt, int T, int H, const moe_router *r, const void *coef_w,
-                         const float *coef_b, float *logits, float *clog, hipStream_t s, int *zero = nullptr) {
+                         const float *coef_b, float *logits, float *clog, hipStream_t s, int *zero = nullptr,
+                         bool split = false) {
   const int E = r->num_experts;
   const int R = E + (coef_w ? 2 : 0);
   Timed tm(TK_ROUTER, s);
-  if (x_dt == MOE_BF16 && T >= MOE_ROUTER_GEMM_T) {
-    hipLaunchKernelGGL(router_gemm_bf16, dim3((T + 63) / 64, (R + 63) / 64), dim3(256), 0, s, (const uint16_t *)x,
-                       (const uint16_t *)r->w, r->logit_bias, logits, T, H, E, (const uint16_t *)coef_w, coef_b,
-                       clog, zero);
+  if (router_tiled(x_dt, T, H, E)) {
+    const int ks = split ? router_slice_len(T, H, R) : ((H + 63) / 64) * 64;
+    const int S = (H + ks - 1) / ks;
+    hipLaunchKernelGGL(router_gemm_bf16, dim3((T + 127) / 128, (R + 63) / 64, S), dim3(256), 0, s,
+                       (const uint16_t *)x, (const uint16_t *)r->w, r->logit_bias, logits, T, H, E,
+                       (const uint16_t *)coef_w, coef_b, clog, zero, ks);
   } else if (x_dt == MOE_BF16) {
     hipLaunchKernelGGL(router_logits_bf16, dim3((T + 15) / 16, (R + 15) / 16), dim3(512), 0, s, (const uint16_t *)x,
                        (const uint16_t *)r->w, r->logit_bias, logits, T, H, E, (const uint16_t *)coef_w, coef_b,
@@ -276,9 +301,11 @@ moe_status launch_router(const void *x, int x_dt, int T, int H, const moe_router
 }
 
 TopkArgs topk_args(int T, const moe_router *r, const float *logits, int32_t *idx, float *w, const float *clog,
-                   float *coef) {
+                   float *coef, int slices = 1) {
   TopkArgs a;
   a.logits = logits;
+  a.slices = slices;
+  a.logits_out = nullptr;
   a.T = T;
   a.E = r->num_experts;
   a.K = r->top_k;
@@ -624,16 +651,21 @@ moe_status moe_route(const void *x, int32_t x_dtype, int64_t T, int32_t H, const
   TRY(check_router(r, H, x_dtype));
   TRY(check_tokens(T, r->top_k));
   Plan pl;
-  const size_t o_logits = logits ? 0 : pl.take((size_t)T * r->num_experts * 4);
+  // the router's slices as in moe_block_forward (same sums, same selection); the summed logits
+  // go to `logits` when given
+  const int rs = T > INT32_MAX ? 1 : router_slices(x_dtype, (int)T, H, r->num_experts, false, true);
+  const size_t o_logits = pl.take((size_t)rs * T * r->num_experts * 4);
   bool query;
   TRY(check_ws(ws, ws_bytes, pl.off, &query));
   if (query || T == 0) return MOE_OK;
   CHECK(x && topk_idx && topk_w, MOE_ERR_ARG, "x, topk_idx and topk_w must be non-NULL");
   CHECK(aligned(x, 16), MOE_ERR_ARG, "x not 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
-  float *lg = logits ? logits : at<float>(ws, o_logits);
-  TRY(launch_router(x, x_dtype, (int)T, H, r, nullptr, nullptr, lg, nullptr, s));
-  TRY(launch_topk(topk_args((int)T, r, lg, topk_idx, topk_w, nullptr, nullptr), s));
+  float *lg = at<float>(ws, o_logits);
+  TRY(launch_router(x, x_dtype, (int)T, H, r, nullptr, nullptr, lg, nullptr, s, nullptr, true));
+  TopkArgs ta = topk_args((int)T, r, lg, topk_idx, topk_w, nullptr, nullptr, rs);
+  ta.logits_out = logits;
+  TRY(launch_topk(ta, s));
   return MOE_OK;
 }
 
@@ -809,9 +841,11 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   const int Tsh = (has_shared && !latent) ? (int)T : 0;  // shared rows appended to h / o
   const int ldh = I > Is ? I : Is;
   Plan pl;
-  const size_t o_logits = pl.take((size_t)T * E * 4);
+  const bool blend = b->shared_mode == MOE_SHARED_BLEND;
+  const int rs = (T > INT32_MAX) ? 1 : router_slices(x_dtype, (int)T, H, E, blend, true);
+  const size_t o_logits = pl.take((size_t)rs * T * E * 4);
   const size_t o_coef = pl.take((size_t)T * 2 * 4);
-  const size_t o_clog = pl.take((size_t)T * 2 * 4);
+  const size_t o_clog = pl.take((size_t)rs * T * 2 * 4);
   const size_t o_idx = topk_idx ? 0 : pl.take((size_t)TK * 4);
   const size_t o_w = topk_w ? 0 : pl.take((size_t)TK * 4);
   const size_t o_counts = pl.take((size_t)E * 4);
@@ -852,13 +886,12 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   const int Ti = (int)T;
 
   // 1. router + selection (+ blend coefficients)
-  const bool blend = b->shared_mode == MOE_SHARED_BLEND;
   float *clog = at<float>(ws, o_clog);
   const bool small = Ti <= MOE_ROUTE_SMALL_T && topk_slots(E, K) > 0;
   int *done = at<int>(ws, o_done);
   TRY(launch_router(x, x_dtype, Ti, H, &b->router, blend ? b->coef_w : nullptr, blend ? b->coef_b : nullptr, logits,
-                    clog, s, small ? done : nullptr));
-  const TopkArgs ta = topk_args(Ti, &b->router, logits, idx, wts, blend ? clog : nullptr, coef);
+                    clog, s, small ? done : nullptr, true));
+  const TopkArgs ta = topk_args(Ti, &b->router, logits, idx, wts, blend ? clog : nullptr, coef, rs);
   // 2. permutation + tile list (for a few tokens in the same workgroup as the selection)
   if (small) {
     TRY(launch_route_decode(ta, counts, offsets, ss, sp, mf ? tiles : nullptr, mf ? tc : nullptr, 16 * mb, done, s));

@@ -11,13 +11,15 @@
 #define MOE_ROUTE_SMALL_T 64 // tokens (K <= 16) up to which selection and permutation share one launch
 
 struct TopkArgs {
-  const float *logits;  // [T][E]
+  const float *logits;  // [slices][T][E]: partial sums of the router's reduction slices, added in order
+  int slices;
+  float *logits_out;    // the summed logits [T][E], or nullptr
   int T, E, K, scoring, norm;
   float rscale;
   const float *sbias;
   int32_t *idx;
   float *w;
-  const float *clog;    // blend head logits [T][2], or nullptr
+  const float *clog;    // blend head logits [slices][T][2], or nullptr
   float *coef;          // blend coefficients [T][2]
 };
 
@@ -119,7 +121,7 @@ struct CombineArgs {
 __global__ void router_logits_bf16(const uint16_t *x, const uint16_t *W, const float *lbias, float *logits,
                                    int T, int H, int E, const uint16_t *cw, const float *cb, float *clog, int *zero);
 __global__ void router_gemm_bf16(const uint16_t *x, const uint16_t *W, const float *lbias, float *logits, int T,
-                                 int H, int E, const uint16_t *cw, const float *cb, float *clog, int *zero);
+                                 int H, int E, const uint16_t *cw, const float *cb, float *clog, int *zero, int ks);
 #define MOE_ROUTER_GEMM_T 256  // tokens from which the router runs as a tiled GEMM
 __global__ void router_logits_f32(const float *x, const float *W, const float *lbias, float *logits, int T,
                                   int H, int E, const float *cw, const float *cb, float *clog, int *zero);

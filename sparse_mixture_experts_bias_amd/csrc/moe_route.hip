@@ -7,7 +7,7 @@
 // scaling)).  Softmax scoring is the alternative that page contrasts with.
 // Ties in the selection key go to the lower expert id; the K chosen ids of a
 // token are written in ascending id order.
-#include "moe_kernels.h"
+#include "moe_mfma.h"
 
 // ---------------------------------------------------------------------------
 // router logits, bf16 x and W_r: MFMA 16x16x32, 16 tokens x 16 rows per workgroup,
@@ -68,108 +68,162 @@ __global__ __launch_bounds__(512) void router_logits_bf16(const uint16_t *__rest
   }
 }
 
-// router logits for many tokens (bf16): a tiled MFMA GEMM.  A 256-thread workgroup owns 64
-// tokens x 64 rows of [W_r; coef head] (4 waves of 32 x 32); the reduction runs in chunks
-// of 64 elements staged through LDS (double-buffered, loaded one chunk ahead through
-// registers), rows 16-byte-block XOR-swizzled so that fragment reads spread over the banks.
-// Elements past H read as zero.
+// router logits for many tokens (bf16): a tiled MFMA GEMM with the reduction split over
+// gridDim.z workgroups.  A 256-thread workgroup owns 128 tokens x 64 rows of [W_r; coef head]
+// (4 waves of 64 x 32) and one slice of the reduction, in chunks of 64 elements through a
+// 3-stage LDS ring filled two chunks ahead by 16-byte direct loads (buffer resources over x,
+// W_r and the coef head, fixed per-lane offsets; rows past the matrices read as zero, token
+// elements past the slice are zeroed in LDS).  Rows are 16-byte-block XOR-swizzled so that
+// fragment reads spread over the banks.  Slice z writes its partial
+// sums to logits + z*T*E and clog + z*2T (the bias with slice 0); the selection adds the
+// slices in order.
 __global__ __launch_bounds__(256) void router_gemm_bf16(const uint16_t *__restrict__ x,
                                                         const uint16_t *__restrict__ W,
                                                         const float *__restrict__ lbias,
                                                         float *__restrict__ logits, int T, int H, int E,
                                                         const uint16_t *__restrict__ cw,
                                                         const float *__restrict__ cb, float *__restrict__ clog,
-                                                        int *__restrict__ zero) {
-  if (zero && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *zero = 0;
-  constexpr int TM = 64, TN = 64, KC = 64;
-  __shared__ __attribute__((aligned(16))) uint16_t sX[2][TM * KC];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][TN * KC];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                                        int *__restrict__ zero, int ks) {
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *zero = 0;
+  constexpr int TM = 128, TN = 64, KC = 64;
+  // one LDS variable per stage: reads of one stage then do not wait for direct loads into others
+  __shared__ __attribute__((aligned(16))) uint16_t sX0[TM * KC], sX1[TM * KC], sX2[TM * KC];
+  __shared__ __attribute__((aligned(16))) uint16_t sW0[TN * KC], sW1[TN * KC], sW2[TN * KC];
+  uint16_t *const sX[3] = {sX0, sX1, sX2};
+  uint16_t *const sW[3] = {sW0, sW1, sW2};
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, kq = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
   const int t0 = blockIdx.x * TM, r0 = blockIdx.y * TN;
   const int R = E + (cw ? 2 : 0);
+  const int kb = blockIdx.z * ks, ke = min(H, kb + ks);
+  const int nk = (ke - kb + KC - 1) / KC;
+  auto swz = [](int row) { return (row >> 1) & 7; };
 
-  // staging: each tile is 64 rows x 8 blocks of 16 bytes; thread q loads blocks q and q+256
-  // of both tiles (row = q / 8, block = q % 8), stored at slot block ^ ((row / 2) % 8)
-  const uint16_t *xs[2], *ws[2];
-  int soff[2], sblk[2];
+  // token rows: direct load n (0..3) of wave w covers tile rows 8 (4 w + n) .. + 8, lane l row
+  // 8 (4 w + n) + l / 8 and LDS slot l % 8, which holds block (l % 8) ^ swz(row)
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc((void *)x, (short)0, (int)((int64_t)T * H * 2), 0x00020000);
+  uint32_t xo[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int q = tid + 256 * i, row = q >> 3, blk = q & 7;
-    const int t = min(t0 + row, T - 1), rr = r0 + row;
-    xs[i] = x + (int64_t)t * H + blk * 8;
-    ws[i] = (rr < E ? W + (int64_t)rr * H : (rr < R ? cw + (int64_t)(rr - E) * H : W)) + blk * 8;
-    soff[i] = row * KC + ((blk ^ ((row >> 1) & 7)) << 3);
-    sblk[i] = blk;
+  for (int n = 0; n < 4; ++n) {
+    const int row = 8 * (4 * wave + n) + (lane >> 3);
+    xo[n] = (uint32_t)min(t0 + row, T - 1) * (uint32_t)H * 2u + (uint32_t)(((lane & 7) ^ swz(row)) << 4);
   }
-  u32x4_t xa[2], wa[2];
-  auto load = [&](int k0) {
+  auto load_x = [&](int c, uint16_t *bx) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const bool ok = k0 + sblk[i] * 8 < H;
-      xa[i] = ok ? *(const u32x4_t *)(xs[i] + k0) : u32x4_t{0u, 0u, 0u, 0u};
-      wa[i] = ok ? *(const u32x4_t *)(ws[i] + k0) : u32x4_t{0u, 0u, 0u, 0u};
-    }
+    for (int n = 0; n < 4; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t *)&bx[(4 * wave + n) * 512], 16, xo[n],
+                                               (kb + min(c, nk - 1) * KC) * 2, 0, 0);
   };
-  auto store = [&](int b) {
+  // weight rows: direct load n (0..1) of wave w covers tile rows 8 (2 w + n) .. + 8 (the host
+  // keeps E a multiple of 8, so each group comes from W_r or from the coef head only); rows past
+  // the matrix read as zero
+  const __amdgpu_buffer_rsrc_t wrs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)W, (short)0, (int)((int64_t)E * H * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t crs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(cw ? cw : W), (short)0, cw ? 2 * H * 2 : 0, 0x00020000);
+  uint32_t wo[2];
+  bool wcoef[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *(u32x4_t *)&sX[b][soff[i]] = xa[i];
-      *(u32x4_t *)&sW[b][soff[i]] = wa[i];
+  for (int n = 0; n < 2; ++n) {
+    const int g0 = r0 + 8 * (2 * wave + n), row = 8 * (2 * wave + n) + (lane >> 3);
+    wcoef[n] = g0 >= E;
+    const int rr = r0 + row - (wcoef[n] ? E : 0);
+    wo[n] = (uint32_t)rr * (uint32_t)H * 2u + (uint32_t)(((lane & 7) ^ swz(row)) << 4);
+  }
+  auto load_w = [&](int c, uint16_t *bw) {
+    const int so = (kb + min(c, nk - 1) * KC) * 2;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      if (wcoef[n])
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, (lds_void_t *)&bw[(2 * wave + n) * 512], 16, wo[n], so, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_void_t *)&bw[(2 * wave + n) * 512], 16, wo[n], so, 0, 0);
     }
   };
 
-  f32x4_t acc[2][2];
+  f32x4_t acc[4][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) acc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // fragment rows 16 mb + n16 of the wave's 32; block 4 s + kq of the chunk
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int sw = (n16 >> 1) & 7;
-  const int nk = (H + KC - 1) / KC;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int c = 0; c < nk; ++c) {
-    const int b = c & 1;
-    if (c + 1 < nk) load((c + 1) * KC);
+  auto compute = [&](const uint16_t *bx, const uint16_t *bw) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int slot = ((4 * s + kq) ^ sw) << 3;
-      u32x4_t af[2], bf[2];
+    for (int st = 0; st < 2; ++st) {
+      const int slot = ((4 * st + kq) ^ sw) << 3;
+      u32x4_t af[4], bf[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) af[mb] = *(const u32x4_t *)&sX[b][(wm * 32 + 16 * mb + n16) * KC + slot];
+      for (int mb = 0; mb < 4; ++mb) af[mb] = *(const u32x4_t *)&bx[(wm * 64 + 16 * mb + n16) * KC + slot];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) bf[nb] = *(const u32x4_t *)&sW[b][(wn * 32 + 16 * nb + n16) * KC + slot];
+      for (int nb = 0; nb < 2; ++nb) bf[nb] = *(const u32x4_t *)&bw[(wn * 32 + 16 * nb + n16) * KC + slot];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[mb]),
                                                                __builtin_bit_cast(bf16x8_t, bf[nb]), acc[mb][nb], 0, 0,
                                                                0);
     }
-    if (c + 1 < nk) {
-      store(b ^ 1);   // the other buffer: last read in chunk c - 1, before the barrier below
-      __syncthreads();
+  };
+  // elements past the slice in the last chunk: the token blocks read there belong to the next
+  // row (or past x); each wave zeroes those of its own direct loads, once they have landed
+  auto zero_tail = [&](int c, uint16_t *bx) {
+    const int kn = ke - (kb + c * KC);
+    if (kn >= KC) return;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int row = 8 * (4 * wave + n) + (lane >> 3), slot = lane & 7, blk = slot ^ swz(row);
+      if (blk * 8 >= kn) *(u32x4_t *)&bx[row * KC + (slot << 3)] = u32x4_t{0u, 0u, 0u, 0u};
     }
+  };
+
+  load_x(0, sX[0]);
+  load_w(0, sW[0]);
+  load_x(1, sX[1]);
+  load_w(1, sW[1]);
+  // chunk c in buffer j = c % 3: loads of chunk c + 2 (clamped past the end) issued, chunk c
+  // computed.  Whole groups of three chunks run branch-free (compile-time buffers), then the
+  // remainder.
+  auto chunk = [&](int c, int j) {
+    load_x(c + 2, sX[(j + 2) % 3]);
+    load_w(c + 2, sW[(j + 2) % 3]);
+    wait_vmcnt<12>();  // chunk c has landed (the 6 loads of each of the two later chunks may not)
+    if (c == nk - 1) zero_tail(c, sX[j]);
+    stage_barrier();
+    compute(sX[j], sW[j]);
+    stage_barrier();  // every wave is done with chunk c before its buffer is loaded again
+  };
+  int c = 0;
+  for (; c + 3 <= nk; c += 3) {
+    chunk(c, 0);
+    chunk(c + 1, 1);
+    chunk(c + 2, 2);
   }
-  // acc[mb][nb][i]: token 32 wm + 16 mb + 4 kq + i, row 32 wn + 16 nb + n16
+  if (c < nk) chunk(c, 0);
+  if (c + 1 < nk) chunk(c + 1, 1);
+  wait_vmcnt<0>();  // the loads past the end
+
+  // acc[mb][nb][i]: token 64 wm + 16 mb + 4 kq + i, row 32 wn + 16 nb + n16
+  float *lg = logits + (int64_t)blockIdx.z * T * E;
+  float *cl = clog ? clog + (int64_t)blockIdx.z * 2 * T : nullptr;
+  const bool first = blockIdx.z == 0;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int e = r0 + wn * 32 + 16 * nb + n16;
-    const float add = e < E ? (lbias ? lbias[e] : 0.f) : (e < R ? cb[e - E] : 0.f);
+    const float add = !first ? 0.f : (e < E ? (lbias ? lbias[e] : 0.f) : (e < R ? cb[e - E] : 0.f));
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = t0 + wm * 32 + 16 * mb + 4 * kq + i;
+        const int t = t0 + wm * 64 + 16 * mb + 4 * kq + i;
         if (t < T) {
           if (e < E)
-            logits[(int64_t)t * E + e] = acc[mb][nb][i] + add;
+            lg[(int64_t)t * E + e] = acc[mb][nb][i] + add;
           else if (e < R)
-            clog[2 * t + (e - E)] = acc[mb][nb][i] + add;
+            cl[2 * t + (e - E)] = acc[mb][nb][i] + add;
         }
       }
   }
@@ -244,7 +298,13 @@ MOE_DEV void topk_token(const TopkArgs &a, int t, int lane, float *sl, int *el, 
   for (int j = 0; j < EPL; ++j) {
     const int ec = min(lane + 64 * j, a.E - 1);
     s[j] = lrow[ec];
+    for (int z = 1; z < a.slices; ++z) s[j] += lrow[(int64_t)z * a.T * a.E + ec];
     sb[j] = a.sbias ? a.sbias[ec] : 0.f;
+  }
+  if (a.logits_out) {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (lane + 64 * j < a.E) a.logits_out[(int64_t)t * a.E + lane + 64 * j] = s[j];
   }
 #pragma unroll
   for (int j = 0; j < EPL; ++j)
@@ -313,7 +373,11 @@ MOE_DEV void topk_token(const TopkArgs &a, int t, int lane, float *sl, int *el, 
   }
   // blend coefficients: softmax over the 2-way head's logits, fp32
   if (a.clog && lane == 0) {
-    const float c0 = a.clog[2 * t], c1 = a.clog[2 * t + 1];
+    float c0 = a.clog[2 * t], c1 = a.clog[2 * t + 1];
+    for (int z = 1; z < a.slices; ++z) {
+      c0 += a.clog[(int64_t)z * 2 * a.T + 2 * t];
+      c1 += a.clog[(int64_t)z * 2 * a.T + 2 * t + 1];
+    }
     const float m = fmaxf(c0, c1);
     const float x0 = expf(c0 - m), x1 = expf(c1 - m);
     a.coef[2 * t] = x0 / (x0 + x1);
@@ -380,7 +444,13 @@ MOE_DEV void topk_half(const TopkArgs &a, int t, int l32, int *el, float *esc, i
   for (int j = 0; j < SL; ++j) {
     const int ec = min(l32 + 32 * j, a.E - 1);
     lg[j] = lrow[ec];
+    for (int z = 1; z < a.slices; ++z) lg[j] += lrow[(int64_t)z * a.T * a.E + ec];
     sb[j] = a.sbias ? a.sbias[ec] : 0.f;
+  }
+  if (a.logits_out && live) {
+#pragma unroll
+    for (int j = 0; j < SL; ++j)
+      if (l32 + 32 * j < a.E) a.logits_out[(int64_t)t * a.E + l32 + 32 * j] = lg[j];
   }
   float sc[SL];
   if (a.scoring == 1) {  // softmax over experts, max-subtracted, fp32
@@ -457,7 +527,11 @@ MOE_DEV void topk_half(const TopkArgs &a, int t, int l32, int *el, float *esc, i
     if (sidx) sidx[t * a.K + rank] = my_e;
   }
   if (a.clog && live && l32 == 0) {
-    const float c0 = a.clog[2 * t], c1 = a.clog[2 * t + 1];
+    float c0 = a.clog[2 * t], c1 = a.clog[2 * t + 1];
+    for (int z = 1; z < a.slices; ++z) {
+      c0 += a.clog[(int64_t)z * 2 * a.T + 2 * t];
+      c1 += a.clog[(int64_t)z * 2 * a.T + 2 * t + 1];
+    }
     const float m = fmaxf(c0, c1);
     const float x0 = expf(c0 - m), x1 = expf(c1 - m);
     a.coef[2 * t] = x0 / (x0 + x1);

@@ -57,10 +57,12 @@ def test_block_small(cfg):
     _full_check(b, f"{cfg}-small")
 
 
-@pytest.mark.parametrize("T,H,E", [(256, 544, 72), (301, 2080, 130)])
+@pytest.mark.parametrize("T,H,E", [(256, 544, 72), (301, 2080, 136), (300, 1024, 130)])
 def test_router_tiled_ragged(T, H, E):
-    """Router as a tiled GEMM (many tokens): a reduction that ends inside a chunk,
-    ragged token and expert tiles, the blend head's two rows in the last tile."""
+    """Router for many tokens: the tiled GEMM with its reduction split into slices (a
+    slice and the reduction ending inside a chunk, ragged token and expert tiles, the
+    blend head's two rows in the last tile), and an expert count the tiled GEMM does not
+    take (not a multiple of 8)."""
     from dataclasses import replace
     spec = replace(synth.FULL_SPECS["c3"], name="router-tiled", T=T, H=H, E=E, K=6, I=64, I_s=64,
                    group=32, seed=T + E)
