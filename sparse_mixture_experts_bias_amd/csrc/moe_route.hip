@@ -287,6 +287,39 @@ MOE_DEV uint64_t wave_max_u64(uint64_t v) {
   return m;
 }
 
+// v[j] += the partial sums of slices 1 .. slices-1 at row[z * zs + ec[j]], added in slice
+// order.  Two slices per trip, every load of a trip issued before the first add (a slice
+// past the last is read at the last one's address and not added).
+template <int N>
+MOE_DEV void add_slices(float (&v)[N], const float *row, const int (&ec)[N], int slices,
+                        int64_t zs) {
+  for (int z = 1; z < slices; z += 2) {
+    const float *p1 = row + z * zs;
+    const float *p2 = row + min(z + 1, slices - 1) * zs;
+    float u[N], w[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      u[j] = p1[ec[j]];
+      w[j] = p2[ec[j]];
+    }
+    const bool two = z + 1 < slices;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      v[j] += u[j];
+      v[j] = two ? v[j] + w[j] : v[j];
+    }
+  }
+}
+
+// this lane's share of the blend-head logits of token t: slice l of [slices][T][2] on lane
+// l < slices, zero elsewhere (read at a valid address whatever the lane and whether or not
+// the head exists, so the load is unconditional).
+MOE_DEV float2 clog_part(const TopkArgs &a, int t, int l) {
+  const float *base = a.clog ? a.clog : a.logits;
+  const float2 v = *(const float2 *)(base + (int64_t)min(l, a.slices - 1) * 2 * a.T + 2 * t);
+  return (a.clog && l < a.slices) ? v : make_float2(0.f, 0.f);
+}
+
 // token t on the calling wave (all 64 lanes).  sl: E floats of LDS, el: K ints of LDS,
 // both private to the wave.  sidx: optional copy of the chosen ids ([T][K], LDS).
 MOE_DEV void topk_token(const TopkArgs &a, int t, int lane, float *sl, int *el, int32_t *sidx) {
@@ -294,13 +327,15 @@ MOE_DEV void topk_token(const TopkArgs &a, int t, int lane, float *sl, int *el, 
   const float *lrow = a.logits + (int64_t)t * a.E;
   // every load issued before the first use (clamped ids; out-of-range slots masked below)
   float s[EPL], sb[EPL];
+  int ec[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
-    const int ec = min(lane + 64 * j, a.E - 1);
-    s[j] = lrow[ec];
-    for (int z = 1; z < a.slices; ++z) s[j] += lrow[(int64_t)z * a.T * a.E + ec];
-    sb[j] = a.sbias ? a.sbias[ec] : 0.f;
+    ec[j] = min(lane + 64 * j, a.E - 1);
+    s[j] = lrow[ec[j]];
+    sb[j] = a.sbias ? a.sbias[ec[j]] : 0.f;
   }
+  const float2 cp = clog_part(a, t, lane);
+  add_slices<EPL>(s, lrow, ec, a.slices, (int64_t)a.T * a.E);
   if (a.logits_out) {
 #pragma unroll
     for (int j = 0; j < EPL; ++j)
@@ -372,16 +407,14 @@ MOE_DEV void topk_token(const TopkArgs &a, int t, int lane, float *sl, int *el, 
     if (sidx) sidx[t * a.K + rank] = my_e;
   }
   // blend coefficients: softmax over the 2-way head's logits, fp32
-  if (a.clog && lane == 0) {
-    float c0 = a.clog[2 * t], c1 = a.clog[2 * t + 1];
-    for (int z = 1; z < a.slices; ++z) {
-      c0 += a.clog[(int64_t)z * 2 * a.T + 2 * t];
-      c1 += a.clog[(int64_t)z * 2 * a.T + 2 * t + 1];
+  if (a.clog) {
+    const float c0 = wave_sum(cp.x), c1 = wave_sum(cp.y);
+    if (lane == 0) {
+      const float m = fmaxf(c0, c1);
+      const float x0 = expf(c0 - m), x1 = expf(c1 - m);
+      a.coef[2 * t] = x0 / (x0 + x1);
+      a.coef[2 * t + 1] = x1 / (x0 + x1);
     }
-    const float m = fmaxf(c0, c1);
-    const float x0 = expf(c0 - m), x1 = expf(c1 - m);
-    a.coef[2 * t] = x0 / (x0 + x1);
-    a.coef[2 * t + 1] = x1 / (x0 + x1);
   }
 }
 
@@ -440,13 +473,15 @@ MOE_DEV void topk_half(const TopkArgs &a, int t, int l32, int *el, float *esc, i
   const bool live = t < a.T;
   const float *lrow = a.logits + (int64_t)(live ? t : a.T - 1) * a.E;
   float lg[SL], sb[SL];
+  int ec[SL];
 #pragma unroll
   for (int j = 0; j < SL; ++j) {
-    const int ec = min(l32 + 32 * j, a.E - 1);
-    lg[j] = lrow[ec];
-    for (int z = 1; z < a.slices; ++z) lg[j] += lrow[(int64_t)z * a.T * a.E + ec];
-    sb[j] = a.sbias ? a.sbias[ec] : 0.f;
+    ec[j] = min(l32 + 32 * j, a.E - 1);
+    lg[j] = lrow[ec[j]];
+    sb[j] = a.sbias ? a.sbias[ec[j]] : 0.f;
   }
+  const float2 cp = clog_part(a, live ? t : a.T - 1, l32);
+  add_slices<SL>(lg, lrow, ec, a.slices, (int64_t)a.T * a.E);
   if (a.logits_out && live) {
 #pragma unroll
     for (int j = 0; j < SL; ++j)
@@ -526,16 +561,14 @@ MOE_DEV void topk_half(const TopkArgs &a, int t, int l32, int *el, float *esc, i
     a.w[(int64_t)t * a.K + rank] = w;
     if (sidx) sidx[t * a.K + rank] = my_e;
   }
-  if (a.clog && live && l32 == 0) {
-    float c0 = a.clog[2 * t], c1 = a.clog[2 * t + 1];
-    for (int z = 1; z < a.slices; ++z) {
-      c0 += a.clog[(int64_t)z * 2 * a.T + 2 * t];
-      c1 += a.clog[(int64_t)z * 2 * a.T + 2 * t + 1];
+  if (a.clog) {
+    const float c0 = half_sum_f32(cp.x), c1 = half_sum_f32(cp.y);
+    if (live && l32 == 0) {
+      const float m = fmaxf(c0, c1);
+      const float x0 = expf(c0 - m), x1 = expf(c1 - m);
+      a.coef[2 * t] = x0 / (x0 + x1);
+      a.coef[2 * t + 1] = x1 / (x0 + x1);
     }
-    const float m = fmaxf(c0, c1);
-    const float x0 = expf(c0 - m), x1 = expf(c1 - m);
-    a.coef[2 * t] = x0 / (x0 + x1);
-    a.coef[2 * t + 1] = x1 / (x0 + x1);
   }
 }
 
