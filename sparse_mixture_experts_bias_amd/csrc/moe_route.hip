@@ -644,28 +644,55 @@ static __device__ void load_ids(const int32_t *__restrict__ idx, int t, int K, i
   for (int j = 0; j < kIdBatch; ++j) ids[j] = idx[(int64_t)t * K + min(j0 + j, K - 1)];
 }
 
-// m-tile list for the grouped expert GEMMs: every routed segment (expert e's slots,
-// sorted rows offsets[e]..offsets[e+1]) cut into tiles of mt rows, in expert order.
-// offs: shared-memory copy of offsets[0..E].
-static __device__ void emit_tiles(const int *offs, int E, int mt, int4 *tiles, int *tile_count,
-                                  int *nmc /* shared, E ints */, int *tmp) {
+// m-tile list for the grouped expert GEMMs: every routed segment (expert e's slots, sorted
+// rows offsets[e]..offsets[e+1]) cut into tiles of at most mt rows (mt <= 128).  A segment of
+// n rows becomes t = ceil(n / mt) tiles: t - 1 of q rows, q = ceil(n / t) rounded up to whole
+// 16-row blocks and capped at mt, and a last one with the rest (1..q rows), so that the
+// fewest tiles hold ceil(n / 16) blocks in all.  The list is ordered by tile size, the most
+// 16-row blocks first: the GEMMs deal units to workgroups round-robin, so every workgroup
+// then gets a similar mix of large and small tiles.  Within one size the order is that of
+// arrival at a shared counter (a segment's tiles of one size stay together); every tile's
+// results are independent of its position.  offs: shared copy of offsets[0..E]; cls: 16
+// shared ints.
+static __device__ void emit_tiles(const int *offs, int E, int mt, int4 *tiles, int *tile_count, int *cls) {
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += blockDim.x) nmc[e] = (offs[e + 1] - offs[e] + mt - 1) / mt;
+  int *tot = cls, *cur = cls + 8;  // tiles per size class (blocks - 1), then placement cursors
+  auto shape = [&](int e, int &n, int &t, int &q, int &cq, int &cl) {
+    n = offs[e + 1] - offs[e];
+    t = (n + mt - 1) / mt;
+    q = t ? min(mt, (((n + t - 1) / t) + 15) & ~15) : 16;
+    cq = q / 16 - 1;                              // size class of the first t - 1 tiles
+    cl = t ? (n - (t - 1) * q + 15) / 16 - 1 : 0;  // ... and of the last
+  };
+  if (tid < 16) cls[tid] = 0;
   __syncthreads();
-  const int R = block_exclusive_scan(nmc, E, tmp);
-  // a segment of n rows becomes t = ceil(n / mt) tiles of q rows (the last one takes the
-  // rest, 1..q rows), q = ceil(n / t) rounded up to whole 16-row blocks and capped at mt: the
-  // fewest tiles, all but the last made of whole 16-row blocks, so that they hold
-  // ceil(n / 16) blocks in all
   for (int e = tid; e < E; e += blockDim.x) {
-    const int n = offs[e + 1] - offs[e];
+    int n, t, q, cq, cl;
+    shape(e, n, t, q, cq, cl);
     if (n == 0) continue;
-    const int t = (n + mt - 1) / mt;
-    const int q = min(mt, (((n + t - 1) / t) + 15) & ~15);
-    for (int i = 0, base = nmc[e]; i < t; ++i)
-      tiles[base + i] = make_int4(e, offs[e] + i * q, min(q, n - i * q), 0);
+    if (t > 1) atomicAdd(&tot[cq], t - 1);
+    atomicAdd(&tot[cl], 1);
   }
-  if (tid == 0) tile_count[0] = R;
+  __syncthreads();
+  if (tid == 0) {
+    int R = 0;
+    for (int b = 7; b >= 0; --b) {
+      cur[b] = R;
+      R += tot[b];
+    }
+    tile_count[0] = R;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
+    int n, t, q, cq, cl;
+    shape(e, n, t, q, cq, cl);
+    if (n == 0) continue;
+    if (t > 1) {
+      const int pq = atomicAdd(&cur[cq], t - 1);
+      for (int i = 0; i < t - 1; ++i) tiles[pq + i] = make_int4(e, offs[e] + i * q, q, 0);
+    }
+    tiles[atomicAdd(&cur[cl], 1)] = make_int4(e, offs[e] + (t - 1) * q, n - (t - 1) * q, 0);
+  }
 }
 
 __global__ __launch_bounds__(256) void perm_count(const int32_t *__restrict__ idx, int T, int K, int E,
@@ -692,14 +719,23 @@ __global__ __launch_bounds__(1024) void perm_scan(int32_t *__restrict__ chunk_co
                                                   int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                                   int4 *tiles, int *tile_count, int mt) {
   __shared__ int offs[MOE_MAX_EXPERTS + 1];
-  __shared__ int nmc[MOE_MAX_EXPERTS];
+  __shared__ int cls[16];
   __shared__ int tmp[16];
+  // the chunk counts of expert e, eight independent loads per trip (clamped, masked)
+  constexpr int B = 8;
+  auto chunk_batch = [&](int e, int c0, int (&v)[B]) {
+#pragma unroll
+    for (int j = 0; j < B; ++j) v[j] = chunk_counts[(int64_t)min(c0 + j, nchunks - 1) * E + e];
+#pragma unroll
+    for (int j = 0; j < B; ++j) v[j] = c0 + j < nchunks ? v[j] : 0;
+  };
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = chunk_counts[(int64_t)c * E + e];
-      chunk_counts[(int64_t)c * E + e] = run;
-      run += v;
+    for (int c0 = 0; c0 < nchunks; c0 += B) {
+      int v[B];
+      chunk_batch(e, c0, v);
+#pragma unroll
+      for (int j = 0; j < B; ++j) run += v[j];
     }
     offs[e] = run;
     counts[e] = run;
@@ -709,11 +745,22 @@ __global__ __launch_bounds__(1024) void perm_scan(int32_t *__restrict__ chunk_co
   if (threadIdx.x == 0) offs[E] = total;
   __syncthreads();
   for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = offs[e];
-  for (int e = threadIdx.x; e < E; e += blockDim.x)
-    for (int c = 0; c < nchunks; ++c) chunk_counts[(int64_t)c * E + e] += offs[e];
+  // chunk c's base for expert e: offsets[e] + the counts of e in chunks 0 .. c - 1
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = offs[e];
+    for (int c0 = 0; c0 < nchunks; c0 += B) {
+      int v[B];
+      chunk_batch(e, c0, v);
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        if (c0 + j < nchunks) chunk_counts[(int64_t)(c0 + j) * E + e] = run;
+        run += v[j];
+      }
+    }
+  }
   if (tiles) {
     __syncthreads();
-    emit_tiles(offs, E, mt, tiles, tile_count, nmc, tmp);
+    emit_tiles(offs, E, mt, tiles, tile_count, cls);
   }
 }
 
@@ -773,7 +820,7 @@ __global__ __launch_bounds__(256) void perm_scatter(const int32_t *__restrict__ 
 struct PermSmem {
   uint32_t mask[MOE_MAX_EXPERTS][8];
   int offs[MOE_MAX_EXPERTS + 1];
-  int nmc[MOE_MAX_EXPERTS];
+  int cls[16];
   int tmp[16];
 };
 
@@ -803,7 +850,7 @@ static __device__ void perm_block(const int32_t *idx, int T, int K, int E, int32
   scatter_chunk(idx, T, K, E, 0, sm.offs, sm.mask, sorted_slot, slot_pos);
   if (tiles) {
     __syncthreads();
-    emit_tiles(sm.offs, E, mt, tiles, tile_count, sm.nmc, sm.tmp);
+    emit_tiles(sm.offs, E, mt, tiles, tile_count, sm.cls);
   }
 }
 
@@ -923,9 +970,8 @@ template __global__ void route_decode<16>(TopkArgs, int32_t *, int32_t *, int32_
 __global__ __launch_bounds__(256) void build_tiles(const int32_t *__restrict__ offsets, int E, int4 *tiles,
                                                    int *tile_count, int mt) {
   __shared__ int offs[MOE_MAX_EXPERTS + 1];
-  __shared__ int nmc[MOE_MAX_EXPERTS];
-  __shared__ int tmp[16];
+  __shared__ int cls[16];
   for (int e = threadIdx.x; e <= E; e += 256) offs[e] = offsets[e];
   __syncthreads();
-  emit_tiles(offs, E, mt, tiles, tile_count, nmc, tmp);
+  emit_tiles(offs, E, mt, tiles, tile_count, cls);
 }
