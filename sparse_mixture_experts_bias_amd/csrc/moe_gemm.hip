@@ -89,12 +89,11 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : 3) void expert_gemm(c
   const int units_s = ns * nblk1;
   const int nr_routed = p.tiles ? p.tile_count[0] : 0;
 
-  // workgroups are dealt to the 8 XCDs round-robin; renumber them so that consecutive units
-  // (the column blocks of one m-tile, which share its activation rows) run on one XCD and
-  // share its L2
   const int G = gridDim.x;
-  const int b0 = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
-  for (int u = b0;; u += G) {
+  const int U = units_s + (p.tiles ? nr_routed * nblk0 : 0);
+  for (int r = 0;; ++r) {
+    const int u = sched_unit(blockIdx.x, r, G, U);
+    if (u < 0) break;
     const bool sh = u < units_s;
     int ti, nb;
     int4 tile;

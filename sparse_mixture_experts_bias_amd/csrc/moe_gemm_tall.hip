@@ -570,15 +570,14 @@ __global__ __launch_bounds__(512, 2) void expert_gemm_tall(const GemmParams p) {
     return true;
   };
 
-  // consecutive units (the column blocks of one m-tile, which share its activation rows) on
-  // one XCD, so that they share its L2
-  const int G = gridDim.x;
+  const int G = gridDim.x, g = blockIdx.x;
+  const int U = units_s + (p.tiles ? nr_routed * nblk0 : 0);
   const int tid = threadIdx.x;
-  int u = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  int r = 0, u = sched_unit(g, 0, G, U);
   bool csh, nsh;
   int4 ctile, ntile;
   int cnb, nnb;
-  if (!decode(u, csh, ctile, cnb)) return;
+  if (u < 0 || !decode(u, csh, ctile, cnb)) return;
   {
     const TallUnit cur = tall_unit_of<GATEUP>(p, csh, ctile, cnb);
     tall_fill_rows<C::MT>(cur, sRow[0], tid);
@@ -587,7 +586,8 @@ __global__ __launch_bounds__(512, 2) void expert_gemm_tall(const GemmParams p) {
     ld.load_first_a(sA);
   }
   for (int par = 0;; par ^= 1) {
-    const bool has_nxt = decode(u + G, nsh, ntile, nnb);
+    const int un = sched_unit(g, r + 1, G, U);
+    const bool has_nxt = un >= 0 && decode(un, nsh, ntile, nnb);
     // the next unit's rows: published by this unit's stage barriers
     if (has_nxt) tall_fill_rows<C::MT>(tall_unit_of<GATEUP>(p, nsh, ntile, nnb), sRow[par ^ 1], tid);
     const TallUnit cur = tall_unit_of<GATEUP>(p, csh, ctile, cnb);
@@ -604,7 +604,8 @@ __global__ __launch_bounds__(512, 2) void expert_gemm_tall(const GemmParams p) {
     csh = nsh;
     ctile = ntile;
     cnb = nnb;
-    u += G;
+    u = un;
+    ++r;
   }
   // the last unit's look-ahead loads (repeats of its last stage) may still be writing LDS
   __builtin_amdgcn_s_waitcnt(0);

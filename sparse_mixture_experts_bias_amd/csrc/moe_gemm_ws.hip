@@ -76,10 +76,7 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
   const int units_s = ns * nblk1;
   const int nr_routed = p.tiles ? min(load_uniform_int(p.tile_count), p.max_tiles) : 0;
   const int U = units_s + nr_routed * nblk0;
-  // workgroups are dealt to the 8 XCDs round-robin; consecutive units (the column blocks of
-  // one m-tile, which share its activation rows) go to one XCD
-  const int G = gridDim.x;
-  const int b0 = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int G = gridDim.x, g = blockIdx.x;
 
   struct Unit {
     bool sh;
@@ -115,7 +112,7 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
     __amdgpu_buffer_rsrc_t wrs, ars;
     uint32_t wvo = 0, svo = 0, avo[2] = {0u, 0u};
     bool aon[2] = {true, true};  // the activation load holds a row of the m-tile
-    int cu = b0, cc = 0, cn = 0;  // the stage to issue next: unit, chunk, chunks of the unit
+    int cr = 0, cu = sched_unit(g, 0, G, U), cc = 0, cn = 0;  // the stage to issue next: round, unit, chunk, chunks of the unit
     auto enter = [&](int u) {
       const Unit x = unit_of(u);
       cn = nch_of(x);
@@ -171,14 +168,18 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
     auto advance = [&]() {
       if (cc + 1 < cn) {
         ++cc;
-      } else if (cu + G < U) {
-        cu += G;
-        enter(cu);
-        cc = 0;
+      } else {
+        const int nu = sched_unit(g, cr + 1, G, U);
+        if (nu >= 0) {
+          ++cr;
+          cu = nu;
+          enter(cu);
+          cc = 0;
+        }
       }
     };
-    if (b0 >= U) return;
-    enter(b0);
+    if (cu < 0) return;
+    enter(cu);
 #pragma unroll
     for (int j = 0; j < NBUF - 1; ++j) {
       issue(j);
@@ -186,7 +187,9 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
     }
     wait_vmcnt<(NBUF - 2) * NDMA>();  // stage 0 has landed
     int s = 0;
-    for (int u = b0; u < U; u += G) {
+    for (int r = 0;; ++r) {
+      const int u = sched_unit(g, r, G, U);
+      if (u < 0) break;
       const int n = nch_of(unit_of(u));
       for (int c = 0; c < n; ++c, ++s) {
         stage_barrier();  // stage s is handed over; the buffer of stage s - 1 is free
@@ -204,7 +207,9 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
   const uint32_t msk = in_vgpr(0x000F000Fu);
   const uint32_t mag = in_vgpr(AT == DT_BF16 ? 0x43004300u : 0x64006400u);
   int s = 0;
-  for (int u = b0; u < U; u += G) {
+  for (int r = 0;; ++r) {
+    const int u = sched_unit(g, r, G, U);
+    if (u < 0) break;
     const Unit x = unit_of(u);
     const int Kd = SEG(x, K), n = nch_of(x), rows = SEG(x, w0.rows);
     const float limit = SEG(x, limit);

@@ -18,6 +18,21 @@ MOE_DEV f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                   0, 0, 0);
 }
 
+// Unit schedule of the grouped GEMMs: workgroup g takes at most one unit per round of G
+// units (round r: units r*G .. r*G + G - 1; only the last round may be partial) and -1 when
+// it has none.  Workgroups reach the 8 XCDs round-robin (XCD g % 8), and a round's units are
+// cut into 8 equal runs of consecutive units, one per XCD: the column blocks of one m-tile
+// (consecutive units, which read the same activation rows) share that XCD's L2, and a partial
+// round still spreads over every XCD (each XCD's path to memory carries only its share of
+// the bandwidth).
+MOE_DEV int sched_unit(int g, int r, int G, int U) {
+  const int base = r * G, n = min(G, U - base);
+  if (n <= 0) return -1;
+  if (G % 8) return g < n ? base + g : -1;
+  const int per = (n + 7) >> 3, slot = g >> 3, pos = (g & 7) * per + slot;
+  return (slot < per && pos < n) ? base + pos : -1;
+}
+
 // a constant the compiler must keep in a VGPR (so that mask-and-or with two constants is one v_and_or_b32)
 MOE_DEV uint32_t in_vgpr(uint32_t v) {
   asm volatile("" : "+v"(v));
