@@ -74,15 +74,24 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
   const int nblk0 = p.seg[0].nblk, nblk1 = max(p.seg[1].nblk, 1);
   const int ns = p.seg[1].nblk > 0 ? (p.sh_rows + MT - 1) / MT : 0;
   const int units_s = ns * nblk1;
-  const int nr_routed = p.tiles ? min(load_uniform_int(p.tile_count), p.max_tiles) : 0;
-  const int U = units_s + nr_routed * nblk0;
+  // workgroup g's first unit is unit g, its later ones g + G, g + 2G, ... (round-robin over
+  // the XCDs: decode-sized activation rows fit any L2); the first unit's tile is read
+  // together with the tile count
   const int G = gridDim.x, g = blockIdx.x;
+  int nr_routed = 0;
+  int4 t_first = make_int4(0, 0, 0, 0);
+  if (p.tiles && p.max_tiles > 0) {
+    const int ti = min(max(g - units_s, 0) / max(nblk0, 1), p.max_tiles - 1);
+    load_uniform_int_int4(p.tile_count, p.tiles + ti, nr_routed, t_first);
+    nr_routed = min(nr_routed, p.max_tiles);
+  }
+  const int U = units_s + nr_routed * nblk0;
 
   struct Unit {
     bool sh;
     int e, r0, nr, nb;
   };
-  auto unit_of = [&](int u) {
+  auto unit_at = [&](int u, bool first) {
     Unit x;
     x.sh = u < units_s;
     if (x.sh) {
@@ -95,7 +104,7 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
       const int v = u - units_s;
       const int ti = v / nblk0;
       x.nb = v - ti * nblk0;
-      const int4 t = load_uniform_int4(p.tiles + ti);
+      const int4 t = first ? t_first : load_uniform_int4(p.tiles + ti);
       x.e = t.x;
       x.r0 = t.y;
       x.nr = t.z;
@@ -104,7 +113,7 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
   };
   // a field of the unit's segment (selected field by field: a selected struct would go to scratch)
 #define SEG(x, f) ((x).sh ? p.seg[1].f : p.seg[0].f)
-  auto nch_of = [&](const Unit &x) { return (SEG(x, K) + KC - 1) / KC; };
+  auto nch_of = [&](int u) { return ((u < units_s ? p.seg[1].K : p.seg[0].K) + KC - 1) / KC; };
 
   if (wave >= 4) {
     // ---------------- loader waves: row block lw's records, activation rows 4 lw .. 4 lw + 3
@@ -112,26 +121,35 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
     __amdgpu_buffer_rsrc_t wrs, ars;
     uint32_t wvo = 0, svo = 0, avo[2] = {0u, 0u};
     bool aon[2] = {true, true};  // the activation load holds a row of the m-tile
-    int cr = 0, cu = sched_unit(g, 0, G, U), cc = 0, cn = 0;  // the stage to issue next: round, unit, chunk, chunks of the unit
-    auto enter = [&](int u) {
-      const Unit x = unit_of(u);
-      cn = nch_of(x);
+    int cu = g, cc = 0, cn = 0;  // the stage to issue next: unit, chunk, chunks of the unit
+    // unit x's weights and scales (no memory access) ...
+    auto enter_w = [&](const Unit &x, int u) {
+      cn = nch_of(u);
       const int64_t pk_mat = SEG(x, w0.pk_mat);
       wrs = __builtin_amdgcn_make_buffer_rsrc((void *)(SEG(x, w0.pk) + (int64_t)x.e * pk_mat), (short)0, (int)pk_mat,
                                               0x00020000);
       const uint32_t rbo = (uint32_t)min(x.nb * 4 + lw, SEG(x, w0.pk_nblk) - 1) * (uint32_t)(SEG(x, w0.pk_nch) * RB);
       wvo = rbo + lane * 16;
       svo = rbo + 4096 + lane * (C::SB == 1024 ? 16 : 4);
+    };
+    // ... and its activation rows (reads the gather indices)
+    auto enter_a = [&](const Unit &x) {
       const int64_t lda = SEG(x, A.lda);
       ars = __builtin_amdgcn_make_buffer_rsrc((void *)SEG(x, A.a), (short)0, (int)(SEG(x, A.rows) * lda * 2),
                                               0x00020000);
       const int32_t *gat = SEG(x, A.gather);
       const int gdiv = SEG(x, A.gdiv), rsub = SEG(x, A.row_sub);
       uint32_t ro[4];
+      int gi[4];
+      if (gat) {
+        const int *g0 = gat + x.r0;
+        load_uniform_ints4(g0 + min(4 * lw, x.nr - 1), g0 + min(4 * lw + 1, x.nr - 1), g0 + min(4 * lw + 2, x.nr - 1),
+                           g0 + min(4 * lw + 3, x.nr - 1), gi);
+      }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int m = min(4 * lw + k, x.nr - 1);
-        const int arow = gat ? load_uniform_int(gat + x.r0 + m) / gdiv : x.r0 + m - rsub;
+        const int arow = gat ? gi[k] / gdiv : x.r0 + m - rsub;
         ro[k] = (uint32_t)arow * (uint32_t)lda * 2u;
       }
 #pragma unroll
@@ -141,7 +159,7 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
         avo[n] = (lane < 32 ? ro[2 * n] : ro[2 * n + 1]) + (uint32_t)(((lane & 31) ^ (r & 15)) << 4);
       }
     };
-    auto issue = [&](int b) {
+    auto issue_w = [&](int b) {
       char *base = smem + b * STAGE;
       const int so = cc * RB;
       char *wl = base + lw * RB;
@@ -155,6 +173,9 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
         WS_DMA(4, 0, wrs, wl + 4096, svo, so);
         if constexpr (C::NSD == 2) WS_DMA(4, 256, wrs, wl + 4096, svo, so);
       }
+    };
+    auto issue_a = [&](int b) {
+      char *base = smem + b * STAGE;
       // activation rows past the m-tile are never stored: a 4-byte load keeps the count
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
@@ -168,32 +189,38 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
     auto advance = [&]() {
       if (cc + 1 < cn) {
         ++cc;
-      } else {
-        const int nu = sched_unit(g, cr + 1, G, U);
-        if (nu >= 0) {
-          ++cr;
-          cu = nu;
-          enter(cu);
-          cc = 0;
-        }
+      } else if (cu + G < U) {
+        cu += G;
+        const Unit x = unit_at(cu, false);
+        enter_w(x, cu);
+        enter_a(x);
+        cc = 0;
       }
     };
-    if (cu < 0) return;
-    enter(cu);
+    if (g >= U) return;
+    {
+      // the first stage's weights go out before the gather indices are read
+      const Unit x = unit_at(g, true);
+      enter_w(x, g);
+      issue_w(0);
+      enter_a(x);
+      issue_a(0);
+      advance();
+    }
 #pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j) {
-      issue(j);
+    for (int j = 1; j < NBUF - 1; ++j) {
+      issue_w(j);
+      issue_a(j);
       advance();
     }
     wait_vmcnt<(NBUF - 2) * NDMA>();  // stage 0 has landed
     int s = 0;
-    for (int r = 0;; ++r) {
-      const int u = sched_unit(g, r, G, U);
-      if (u < 0) break;
-      const int n = nch_of(unit_of(u));
+    for (int u = g; u < U; u += G) {
+      const int n = nch_of(u);
       for (int c = 0; c < n; ++c, ++s) {
         stage_barrier();  // stage s is handed over; the buffer of stage s - 1 is free
-        issue((s + NBUF - 1) % NBUF);
+        issue_w((s + NBUF - 1) % NBUF);
+        issue_a((s + NBUF - 1) % NBUF);
         advance();
         wait_vmcnt<(NBUF - 2) * NDMA>();  // stage s + 1 has landed
       }
@@ -207,11 +234,9 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
   const uint32_t msk = in_vgpr(0x000F000Fu);
   const uint32_t mag = in_vgpr(AT == DT_BF16 ? 0x43004300u : 0x64006400u);
   int s = 0;
-  for (int r = 0;; ++r) {
-    const int u = sched_unit(g, r, G, U);
-    if (u < 0) break;
-    const Unit x = unit_of(u);
-    const int Kd = SEG(x, K), n = nch_of(x), rows = SEG(x, w0.rows);
+  for (int u = g; u < U; u += G) {
+    const Unit x = unit_at(u, u == g);
+    const int Kd = SEG(x, K), n = nch_of(u), rows = SEG(x, w0.rows);
     const float limit = SEG(x, limit);
     const int col0 = GATEUP ? x.nb * 64 + wave * 16 : x.nb * 128 + wave * 32;
     const bool act = col0 < rows;

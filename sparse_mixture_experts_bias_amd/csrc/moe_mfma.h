@@ -140,6 +140,25 @@ MOE_DEV int load_uniform_int(const int *ptr) {
   asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr));
   return v;
 }
+// a uniform int and a uniform int4 read together (one wait)
+MOE_DEV void load_uniform_int_int4(const int *a, const int4 *b, int &x, int4 &y) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  i32x4 v;
+  int s;
+  asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dwordx4 %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=&s"(s), "=&s"(v)
+               : "s"(a), "s"(b));
+  x = s;
+  y = make_int4(v[0], v[1], v[2], v[3]);
+}
+// four uniform ints read together (one wait)
+MOE_DEV void load_uniform_ints4(const int *a, const int *b, const int *c, const int *d, int (&v)[4]) {
+  asm volatile(
+      "s_load_dword %0, %4, 0x0\n\ts_load_dword %1, %5, 0x0\n\ts_load_dword %2, %6, 0x0\n\t"
+      "s_load_dword %3, %7, 0x0\n\ts_waitcnt lgkmcnt(0)"
+      : "=&s"(v[0]), "=&s"(v[1]), "=&s"(v[2]), "=&s"(v[3])
+      : "s"(a), "s"(b), "s"(c), "s"(d));
+}
 
 MOE_DEV float e8m0_to_f32(uint32_t e) {
   return e == 0u ? __uint_as_float(0x00400000u) : (e == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float(e << 23));
