@@ -70,9 +70,16 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // units: segment 1 (shared expert / plain rows) first, then the routed m-tiles
-  const int nblk0 = p.seg[0].nblk, nblk1 = max(p.seg[1].nblk, 1);
-  const int ns = p.seg[1].nblk > 0 ? (p.sh_rows + MT - 1) / MT : 0;
+  // units: segment 1 (shared expert / plain rows) first, then the routed m-tiles.  The
+  // arguments the schedule needs are read in one batch (materialised together, so that the
+  // compiler does not fetch them one dependent round trip at a time)
+  const int nblk0 = p.seg[0].nblk, nb1 = p.seg[1].nblk, sh_rows = p.sh_rows, sh_row0 = p.sh_row0;
+  const int max_tiles = p.max_tiles;
+  const int4 *const tiles = p.tiles;
+  const int *const tcount = p.tile_count;
+  asm volatile("" ::"s"(nblk0), "s"(nb1), "s"(sh_rows), "s"(sh_row0), "s"(max_tiles), "s"(tiles), "s"(tcount));
+  const int nblk1 = max(nb1, 1);
+  const int ns = nb1 > 0 ? (sh_rows + MT - 1) / MT : 0;
   const int units_s = ns * nblk1;
   // workgroup g's first unit is unit g, its later ones g + G, g + 2G, ... (round-robin over
   // the XCDs: decode-sized activation rows fit any L2); the first unit's tile is read
@@ -80,10 +87,10 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
   const int G = gridDim.x, g = blockIdx.x;
   int nr_routed = 0;
   int4 t_first = make_int4(0, 0, 0, 0);
-  if (p.tiles && p.max_tiles > 0) {
-    const int ti = min(max(g - units_s, 0) / max(nblk0, 1), p.max_tiles - 1);
-    load_uniform_int_int4(p.tile_count, p.tiles + ti, nr_routed, t_first);
-    nr_routed = min(nr_routed, p.max_tiles);
+  if (tiles && max_tiles > 0) {
+    const int ti = min(max(g - units_s, 0) / max(nblk0, 1), max_tiles - 1);
+    load_uniform_int_int4(tcount, tiles + ti, nr_routed, t_first);
+    nr_routed = min(nr_routed, max_tiles);
   }
   const int U = units_s + nr_routed * nblk0;
 
@@ -98,8 +105,8 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
       const int ti = u / nblk1;
       x.nb = u - ti * nblk1;
       x.e = 0;
-      x.r0 = p.sh_row0 + ti * MT;
-      x.nr = min(MT, p.sh_rows - ti * MT);
+      x.r0 = sh_row0 + ti * MT;
+      x.nr = min(MT, sh_rows - ti * MT);
     } else {
       const int v = u - units_s;
       const int ti = v / nblk0;
@@ -124,21 +131,23 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
     int cu = g, cc = 0, cn = 0;  // the stage to issue next: unit, chunk, chunks of the unit
     // unit x's weights and scales (no memory access) ...
     auto enter_w = [&](const Unit &x, int u) {
+      const SegSet &S = p.seg[x.sh ? 1 : 0];
       cn = nch_of(u);
-      const int64_t pk_mat = SEG(x, w0.pk_mat);
-      wrs = __builtin_amdgcn_make_buffer_rsrc((void *)(SEG(x, w0.pk) + (int64_t)x.e * pk_mat), (short)0, (int)pk_mat,
+      const int64_t pk_mat = S.w0.pk_mat;
+      wrs = __builtin_amdgcn_make_buffer_rsrc((void *)(S.w0.pk + (int64_t)x.e * pk_mat), (short)0, (int)pk_mat,
                                               0x00020000);
-      const uint32_t rbo = (uint32_t)min(x.nb * 4 + lw, SEG(x, w0.pk_nblk) - 1) * (uint32_t)(SEG(x, w0.pk_nch) * RB);
+      const uint32_t rbo = (uint32_t)min(x.nb * 4 + lw, S.w0.pk_nblk - 1) * (uint32_t)(S.w0.pk_nch * RB);
       wvo = rbo + lane * 16;
       svo = rbo + 4096 + lane * (C::SB == 1024 ? 16 : 4);
     };
     // ... and its activation rows (reads the gather indices)
     auto enter_a = [&](const Unit &x) {
-      const int64_t lda = SEG(x, A.lda);
-      ars = __builtin_amdgcn_make_buffer_rsrc((void *)SEG(x, A.a), (short)0, (int)(SEG(x, A.rows) * lda * 2),
+      const SegSet &S = p.seg[x.sh ? 1 : 0];
+      const int64_t lda = S.A.lda;
+      ars = __builtin_amdgcn_make_buffer_rsrc((void *)S.A.a, (short)0, (int)(S.A.rows * lda * 2),
                                               0x00020000);
-      const int32_t *gat = SEG(x, A.gather);
-      const int gdiv = SEG(x, A.gdiv), rsub = SEG(x, A.row_sub);
+      const int32_t *gat = S.A.gather;
+      const int gdiv = S.A.gdiv, rsub = S.A.row_sub;
       uint32_t ro[4];
       int gi[4];
       if (gat) {
