@@ -251,23 +251,23 @@ struct Timed {
 // ---------------------------------------------------------------------------
 // launch helpers
 // ---------------------------------------------------------------------------
-// router logits (+ the blend head's two logits into clog when coef_w is given)
-// slices of the reduction for the tiled router (1 when it does not apply): enough 128x64 tiles
-// x slices for ~1.5 workgroups per CU, slices of whole 64-element chunks
+// slices of the tiled router's reduction (1 when it does not apply): enough 128x64 tiles x
+// slices for ~1.5 workgroups per CU, slices of whole 64-element chunks.  The slice length
+// depends on the experts, not on the blend head's two extra rows, so that moe_route and
+// moe_block_forward sum alike.
 bool router_tiled(int x_dt, int T, int H, int E) {
   return x_dt == MOE_BF16 && T >= MOE_ROUTER_GEMM_T && E % 8 == 0 && (int64_t)T * H * 2 <= INT32_MAX &&
          (int64_t)E * H * 2 <= INT32_MAX;
 }
-int router_slice_len(int T, int H, int R) {
-  const int tiles = ((T + 127) / 128) * ((R + 63) / 64);
+int router_slice_len(int T, int H, int E) {
+  const int tiles = ((T + 127) / 128) * ((E + 63) / 64);
   int S = (3 * device_cus() / 2 + tiles - 1) / tiles;
   S = S < 1 ? 1 : (S > 16 ? 16 : S);
-  const int ks = (((H + S - 1) / S) + 63) / 64 * 64;
-  return ks;
+  return (((H + S - 1) / S) + 63) / 64 * 64;
 }
-int router_slices(int x_dt, int T, int H, int E, bool blend, bool split) {
+int router_slices(int x_dt, int T, int H, int E, bool split) {
   if (!split || !router_tiled(x_dt, T, H, E)) return 1;
-  const int ks = router_slice_len(T, H, E + (blend ? 2 : 0));
+  const int ks = router_slice_len(T, H, E);
   return (H + ks - 1) / ks;
 }
 
@@ -281,7 +281,7 @@ moe_status launch_router(const void *x, int x_dt, int T, int H, const moe_router
   const int R = E + (coef_w ? 2 : 0);
   Timed tm(TK_ROUTER, s);
   if (router_tiled(x_dt, T, H, E)) {
-    const int ks = split ? router_slice_len(T, H, R) : ((H + 63) / 64) * 64;
+    const int ks = split ? router_slice_len(T, H, E) : ((H + 63) / 64) * 64;
     const int S = (H + ks - 1) / ks;
     hipLaunchKernelGGL(router_gemm_bf16, dim3((T + 127) / 128, (R + 63) / 64, S), dim3(256), 0, s,
                        (const uint16_t *)x, (const uint16_t *)r->w, r->logit_bias, logits, T, H, E,
@@ -653,7 +653,7 @@ moe_status moe_route(const void *x, int32_t x_dtype, int64_t T, int32_t H, const
   Plan pl;
   // the router's slices as in moe_block_forward (same sums, same selection); the summed logits
   // go to `logits` when given
-  const int rs = T > INT32_MAX ? 1 : router_slices(x_dtype, (int)T, H, r->num_experts, false, true);
+  const int rs = T > INT32_MAX ? 1 : router_slices(x_dtype, (int)T, H, r->num_experts, true);
   const size_t o_logits = pl.take((size_t)rs * T * r->num_experts * 4);
   bool query;
   TRY(check_ws(ws, ws_bytes, pl.off, &query));
@@ -842,7 +842,7 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   const int ldh = I > Is ? I : Is;
   Plan pl;
   const bool blend = b->shared_mode == MOE_SHARED_BLEND;
-  const int rs = (T > INT32_MAX) ? 1 : router_slices(x_dtype, (int)T, H, E, blend, true);
+  const int rs = (T > INT32_MAX) ? 1 : router_slices(x_dtype, (int)T, H, E, true);
   const size_t o_logits = pl.take((size_t)rs * T * E * 4);
   const size_t o_coef = pl.take((size_t)T * 2 * 4);
   const size_t o_clog = pl.take((size_t)rs * T * 2 * 4);

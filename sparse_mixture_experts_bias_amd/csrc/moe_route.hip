@@ -288,25 +288,24 @@ MOE_DEV uint64_t wave_max_u64(uint64_t v) {
 }
 
 // v[j] += the partial sums of slices 1 .. slices-1 at row[z * zs + ec[j]], added in slice
-// order.  Two slices per trip, every load of a trip issued before the first add (a slice
+// order.  Four slices per trip, every load of a trip issued before the first add (a slice
 // past the last is read at the last one's address and not added).
 template <int N>
 MOE_DEV void add_slices(float (&v)[N], const float *row, const int (&ec)[N], int slices,
                         int64_t zs) {
-  for (int z = 1; z < slices; z += 2) {
-    const float *p1 = row + z * zs;
-    const float *p2 = row + min(z + 1, slices - 1) * zs;
-    float u[N], w[N];
+  for (int z = 1; z < slices; z += 4) {
+    float u[4][N];
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      u[j] = p1[ec[j]];
-      w[j] = p2[ec[j]];
+    for (int q = 0; q < 4; ++q) {
+      const float *pq = row + min(z + q, slices - 1) * zs;
+#pragma unroll
+      for (int j = 0; j < N; ++j) u[q][j] = pq[ec[j]];
     }
-    const bool two = z + 1 < slices;
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      v[j] += u[j];
-      v[j] = two ? v[j] + w[j] : v[j];
+    for (int q = 0; q < 4; ++q) {
+      const bool on = z + q < slices;
+#pragma unroll
+      for (int j = 0; j < N; ++j) v[j] = on ? v[j] + u[q][j] : v[j];
     }
   }
 }
