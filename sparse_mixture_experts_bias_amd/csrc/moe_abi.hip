@@ -518,10 +518,15 @@ moe_status run_plain(int adt, const moe_linear &W, const moe_linear *W1, float l
   p.ldo = ldo;
   p.resid = resid;
   p.ldr = ldr;
-  const int units = ((rows + mt - 1) / mt) * sg.nblk;
+  int units = ((rows + mt - 1) / mt) * sg.nblk;
   int kmb = kernel_mb(mb, gateup, W, W.cols);
   if (kmb == MB_WS && !offsets_fit(p, INT32_MAX)) kmb = 1;
   CHECK(kmb != MB_TALL || tall_offsets_fit(p), MOE_ERR_SHAPE, "activation operand of over 4 GiB");
+  // prefill kernel: 64-row m-tiles when 128-row ones leave over a quarter of the CUs idle
+  if (kmb == MB_TALL && rows > 64 && 4 * units < 3 * device_cus()) {
+    p.sh_mt = 64;
+    units = ((rows + 63) / 64) * sg.nblk;
+  }
   Timed tm(TK_PLAIN, s, true);
   HIPCHK(launch_gemm_kernel(adt, W, gateup, odt, kmb, p, units, s, tm.start(), tm.stop()));
   return MOE_OK;

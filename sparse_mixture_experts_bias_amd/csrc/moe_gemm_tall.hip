@@ -547,7 +547,8 @@ __global__ __launch_bounds__(512, 2) void expert_gemm_tall(const GemmParams p) {
 
   // units: segment 1 (shared expert / plain rows) first, then the routed m-tiles
   const int nblk0 = p.seg[0].nblk, nblk1 = max(p.seg[1].nblk, 1);
-  const int ns = p.seg[1].nblk > 0 ? (p.sh_rows + C::MT - 1) / C::MT : 0;
+  const int smt = p.sh_mt > 0 ? min(p.sh_mt, C::MT) : C::MT;  // segment 1's m-tile rows
+  const int ns = p.seg[1].nblk > 0 ? (p.sh_rows + smt - 1) / smt : 0;
   const int units_s = ns * nblk1;
   const int nr_routed = p.tiles ? p.tile_count[0] : 0;
   auto decode = [&](int u, bool &sh, int4 &tile, int &nb) {
@@ -555,7 +556,7 @@ __global__ __launch_bounds__(512, 2) void expert_gemm_tall(const GemmParams p) {
     if (sh) {
       const int ti = u / nblk1;
       nb = u - ti * nblk1;
-      tile = make_int4(0, p.sh_row0 + ti * C::MT, min(C::MT, p.sh_rows - ti * C::MT), 0);
+      tile = make_int4(0, p.sh_row0 + ti * smt, min(smt, p.sh_rows - ti * smt), 0);
     } else {
       const int v = u - units_s;
       const int ti = v / max(nblk0, 1);

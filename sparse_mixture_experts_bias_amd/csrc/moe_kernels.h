@@ -85,6 +85,8 @@ struct GemmParams {
   const int *tile_count;// [0]: routed m-tiles in the list
   int max_tiles;        // entries allocated in tiles (loads are clamped into them)
   int sh_row0, sh_rows; // segment 1: first row (in the sorted-row numbering of out) and row count
+  int sh_mt;            // segment 1's m-tile rows in the prefill kernel (0: its full 128; 64 for
+                        // plain GEMMs with too few 128-row units to fill the CUs)
   int E;
   void *out;
   int64_t ldo;
