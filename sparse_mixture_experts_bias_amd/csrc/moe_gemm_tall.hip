@@ -365,13 +365,14 @@ MOE_DEV void tall_unit(const GemmParams &p, const TallUnit &u, const int64_t *sR
   // issues first and the pair reaches the stage barrier together.
   constexpr int VPS = AFF ? 40 : 12;                       // VALU of one step's dequantisation
   constexpr int VPM = (VPS + 2 * NMB - 1) / (2 * NMB);     // ... per MFMA
-  auto compute = [&](int c, int buf, const Ch &ch, bool issue, int cl, int bufl, Ch &chl) {
+  // (b0: step 0's B fragments, dequantised before the stage barrier, while the wave waits for
+  // the others)
+  auto compute = [&](int c, int buf, const Ch &ch, const u32x4_t (&b0)[2], bool issue, int cl, int bufl, Ch &chl) {
     constexpr int NS = NUS * SPU;
     constexpr int LPT = (LPS + NS - 1) / NS;               // loads issued per step
     const char *sAb = sA.b[buf] + n16 * ROWB;
-    u32x4_t a[NMB], bC[2], bN[2];
+    u32x4_t a[NMB], bC[2] = {b0[0], b0[1]}, bN[2];
     read_a(sAb, 0, a);
-    deq_step(ch, 0, bC);
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
       switch (3 - (t * 4) / NS) {
@@ -434,8 +435,11 @@ MOE_DEV void tall_unit(const GemmParams &p, const TallUnit &u, const int64_t *sR
         wait_vmcnt<(D - 1) * LPS>();
       }
       if ((c + 1) * KS > Kd) zero_tail(c, j);
+      u32x4_t b0[2];
+      deq_step(ring[j], 0, b0);
+      asm volatile("" : "+v"(b0[0]), "+v"(b0[1]));
       stage_barrier();
-      compute(c, j, ring[j], true, min(c + D, nst - 1), (j + D) % NBUF, ring[(j + D) % NBUF]);
+      compute(c, j, ring[j], b0, true, min(c + D, nst - 1), (j + D) % NBUF, ring[(j + D) % NBUF]);
     }
   }
   // remainder stage c0 + j: its loads were issued D stages before it, followed by those of
@@ -447,8 +451,11 @@ MOE_DEV void tall_unit(const GemmParams &p, const TallUnit &u, const int64_t *sR
     else
       wait_w();
     if ((c + 1) * KS > Kd) zero_tail(c, j);
+    u32x4_t b0[2];
+    deq_step(ring[j], 0, b0);
+    asm volatile("" : "+v"(b0[0]), "+v"(b0[1]));
     stage_barrier();
-    compute(c, j, ring[j], false, 0, 0, ring[j]);
+    compute(c, j, ring[j], b0, false, 0, 0, ring[j]);
   };
   if (c0 < nst) {
     last(0, [] { wait_vmcnt<(D - 1) * LPS>(); }, [] { wait_vmcnt<(D - 1) * WPS>(); });
