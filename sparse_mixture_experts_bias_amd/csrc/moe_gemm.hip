@@ -252,7 +252,7 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : 3) void expert_gemm(c
             cc[h] = fmaf(-MAGIC, sc[h], __uint_as_float(v & 0xFFFF0000u));
           } else if constexpr (MX) {
             const uint32_t v = ch.s[h * 2 + (uu >> 1)];
-            sc[h] = e8m0_to_f32((v >> (8 * (2 * (uu & 1) + (kq >> 1)))) & 0xFFu);
+            sc[h] = e8m0_scale((v >> (8 * (2 * (uu & 1) + (kq >> 1)))) & 0xFFu);
             cc[h] = 0.f;
           } else {
             sc[h] = cc[h] = 0.f;

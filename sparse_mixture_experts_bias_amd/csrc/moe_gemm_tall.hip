@@ -342,7 +342,7 @@ MOE_DEV void tall_unit(const GemmParams &p, const TallUnit &u, const int64_t *sR
         const float sc = __uint_as_float(v << 16), qb = __uint_as_float(v & 0xFFFF0000u);
         b[h] = deq_affine<AT>(ch.w[q >> 2][q & 3], m0, m1, g0, g1, sc, fmaf(-1024.0f, sc, qb), fmaf(-64.0f, sc, qb));
       } else if constexpr (MX) {
-        const float sc = e8m0_to_f32((ch.s[h] >> (8 * (2 * uu + (kq >> 1)))) & 0xFFu);
+        const float sc = e8m0_scale((ch.s[h] >> (8 * (2 * uu + (kq >> 1)))) & 0xFFu);
         b[h] = cvt_mxfp4<AT>(ch.w[q >> 2][q & 3], sc);
       } else {
         b[h] = cvt_dense<AT>(ch.w[q >> 2]);

@@ -300,7 +300,7 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
             sc[h] = __uint_as_float(v << 16);
             cc[h] = fmaf(-MAGIC, sc[h], __uint_as_float(v & 0xFFFF0000u));
           } else {
-            sc[h] = e8m0_to_f32((sw[h][uu >> 1] >> (8 * (2 * (uu & 1) + (kq >> 1)))) & 0xFFu);
+            sc[h] = e8m0_scale((sw[h][uu >> 1] >> (8 * (2 * (uu & 1) + (kq >> 1)))) & 0xFFu);
             cc[h] = 0.f;
           }
         }
