@@ -70,4 +70,7 @@ MOE_DEV float wave_max(float v) {
 }
 
 // silu(g) = g * sigmoid(g); the reciprocal is the hardware one (1 ulp), the result is stored in 16 bits
+// the SwiGLU clamp of a pre-activation to [-lim, lim]; NaN stays NaN (fminf / fmaxf alone
+// would return the bound)
+MOE_DEV float clamp_act(float v, float lim) { return __builtin_isnan(v) ? v : fminf(fmaxf(v, -lim), lim); }
 MOE_DEV float silu_f(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }

@@ -352,8 +352,8 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : 3) void expert_gemm(c
           if constexpr (GATEUP) {
             float g = acc[0][i] + bo[0], up = acc[1][i] + bo[1];
             if (limit > 0.f) {
-              g = fminf(fmaxf(g, -limit), limit);
-              up = fminf(fmaxf(up, -limit), limit);
+              g = clamp_act(g, limit);
+              up = clamp_act(up, limit);
             }
             if (ok[0]) store_act<OT>(p.out, (int64_t)(r0 + m) * p.ldo + wrow[0], silu_f(g) * up);
           } else {
@@ -404,8 +404,8 @@ __global__ __launch_bounds__(64) void f32_gemm_kernel(const F32GemmParams p) {
     for (int k = 0; k < M1.cols; ++k) v1 = fmaf(a[k], w1[k], v1);
     if (M1.bias) v1 += ((const float *)M1.bias)[(int64_t)e * M1.rows + c];
     if (p.limit > 0.f) {
-      v0 = fminf(fmaxf(v0, -p.limit), p.limit);
-      v1 = fminf(fmaxf(v1, -p.limit), p.limit);
+      v0 = clamp_act(v0, p.limit);
+      v1 = clamp_act(v1, p.limit);
     }
     out = v0 / (1.0f + expf(-v0)) * v1;
   } else {

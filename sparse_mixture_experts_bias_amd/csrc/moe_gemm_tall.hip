@@ -505,8 +505,8 @@ MOE_DEV void tall_unit(const GemmParams &p, const TallUnit &u, const int64_t *sR
           for (int i = 0; i < 4; ++i) {
             float g = acc[mb][0][i] + bo[0][i], up = acc[mb][1][i] + bo[1][i];
             if (limit > 0.f) {
-              g = fminf(fmaxf(g, -limit), limit);
-              up = fminf(fmaxf(up, -limit), limit);
+              g = clamp_act(g, limit);
+              up = clamp_act(up, limit);
             }
             v[i] = silu_f(g) * up;
           }

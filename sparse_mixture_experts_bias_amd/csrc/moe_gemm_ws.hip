@@ -372,8 +372,8 @@ __global__ __launch_bounds__(512, 6) void expert_gemm_ws(const GemmParams p) {  
           if (row_ok(n16)) {
             float g = acc[0][i] + bo[0], up = acc[1][i] + bo[1];
             if (limit > 0.f) {
-              g = fminf(fmaxf(g, -limit), limit);
-              up = fminf(fmaxf(up, -limit), limit);
+              g = clamp_act(g, limit);
+              up = clamp_act(up, limit);
             }
             store_act<OT>(p.out, (int64_t)(x.r0 + m) * p.ldo + row_of(n16), silu_f(g) * up);
           }

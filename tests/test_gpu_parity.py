@@ -172,6 +172,37 @@ def test_experts_forward_entry(cfg):
     check_output(np32(yr), ref, False, f"experts-{cfg}")
 
 
+def test_mxfp4_scale_extremes():
+    """E8M0 scale bytes 0 (2^-127) and 255 (NaN, OCP MX) in routed MXFP4 weights: the
+    kernels hand the byte to the scaled FP4 conversion as its scale exponent.  NaN reaches
+    exactly the output rows the oracle's does (every token routed to the poisoned expert);
+    an expert whose scales are all 0 contributes ~nothing; the rest matches the oracle."""
+    b = synth.make_block(synth.SMALL_SPECS["c5"], DEV)
+    announce("MXFP4 scale bytes 0 and 255, c5-small")
+    idx, w, _ = run_route(b)
+    e_nan, e_tiny = int(idx[0, 0]), int(idx[0, 1])
+    sc = b.experts.gate.scales.clone()
+    sc[e_nan, 3, 0] = 255
+    sc[e_tiny] = 0
+    b.experts.gate.scales = sc
+    counts, offsets, ss, sp = _check_permute(idx, b.E)
+    g = torch.Generator(device=DEV).manual_seed(98)
+    z = torch.randn(b.T, b.D, generator=g, device=DEV).to(torch.float16)
+    yr = torch.empty(b.T, b.D, dtype=torch.float32, device=DEV)
+    moe.moe_experts_forward(z, mlp_desc(b.experts), b.E, idx, w, offsets, ss, sp, yr, inter_dtype=inter_dtype_for(b))
+    torch.cuda.synchronize()
+    ob = O.from_block(b)
+    routing = {"idx": idx.cpu().numpy().astype(np.int64), "w": w.double().cpu().numpy()}
+    with np.errstate(invalid="ignore"):
+        o = O.routed_outputs(ob, z.double().cpu().numpy(), routing)
+        ref = np.einsum("tk,tkd->td", routing["w"], o)
+    got = np32(yr)
+    nan_ref, nan_got = np.isnan(ref).all(axis=1), np.isnan(got).all(axis=1)
+    assert nan_ref[0] and (nan_ref == nan_got).all(), "NaN rows differ from the oracle's"
+    assert not np.isnan(got[~nan_got]).any() and not np.isnan(ref[~nan_ref]).any()
+    check_output(got[~nan_ref], ref[~nan_ref], False, "mxfp4-scale-extremes")
+
+
 def test_zero_tokens_is_noop():
     b = synth.make_block(synth.SMALL_SPECS["c2"], DEV, T=0)
     announce("T=0")
