@@ -162,9 +162,9 @@ MOE_DEV void load_uniform_ints4(const int *a, const int *b, const int *c, const 
 
 // the scale operand of the scaled FP4 conversions for an E8M0 byte: the byte in the f32
 // exponent field.  The conversion reads that field as the E8M0 value itself (0 -> 2^-127,
-// 255 -> NaN): measured on gfx950 for every code and the exponents 0, 1, 2, 100 .. 254, 255,
-// identical to passing the decoded 2^(e-127) (with 2^-127 and NaN at the ends), in both f16
-// and bf16.
+// 255 -> NaN): measured on gfx950 for every exponent 0..255 and every code at every nibble
+// position, identical to passing the decoded 2^(e-127) (with 2^-127 and NaN at the ends), in
+// both f16 and bf16.
 MOE_DEV float e8m0_scale(uint32_t e) { return __uint_as_float(e << 23); }
 
 template <int AT>
