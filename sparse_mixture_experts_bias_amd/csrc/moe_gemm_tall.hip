@@ -9,10 +9,10 @@
 //     the packed stream (GATEUP: 16 gate + the 16 up rows of the same outputs), so each
 //     weight is dequantised once per 128 tokens and each activation fragment read from
 //     LDS feeds two MFMAs;
-//   * the activation tile goes HBM -> LDS with gfx950's 16-byte direct loads
-//     (global_load_lds_dwordx4), no registers and no VALU on the way, in a multi-stage
-//     ring (two 64 KB stages for 4-bit weights, four 16 KB stages for DENSE) with one
-//     barrier per stage; a stage is one record (reduction chunk) of the packed stream;
+//   * the activation tile goes HBM -> LDS with gfx950's 16-byte direct loads, no
+//     registers and no VALU on the way, in a ring of four stages with one barrier per
+//     stage; a stage is half a packed record (32 KB of activations) for the 4-bit formats
+//     and one record (16 KB) for DENSE, and its weights travel in a register ring;
 //   * LDS rows are 16-byte-block XOR-swizzled by row, so the MFMA fragment reads (16
 //     rows, one block each) spread over the banks while every direct load still writes
 //     1 KB contiguously;
@@ -52,7 +52,7 @@ struct TallCfg {
   static constexpr int BPR = KS / 8;                     // 16-byte blocks per staged row
   static constexpr int ROWB = KS * 2;                    // bytes per staged row
   static constexpr int ABUF = MT * ROWB;                 // activation bytes per stage
-  static constexpr int NBUF = DENSE ? 3 : 4;             // stages resident (LDS and registers)
+  static constexpr int NBUF = 4;                         // stages resident (LDS and registers)
   static constexpr int D = NBUF - 1;                     // stages loaded ahead
   static constexpr int NI = ABUF / (NW * 1024);          // direct loads per wave per stage
   static constexpr int RPI = 1024 / ROWB;                // rows per direct load
