@@ -188,13 +188,16 @@ struct TallLoader {
     lane = lane_;
     n16 = lane & 15;
     wave_u = __builtin_amdgcn_readfirstlane(wave);
+    // a wave whose 16 staged rows all lie past the m-tile (never stored) reads past the
+    // buffer's range: the loads return zeros without touching memory
+    const bool aon = 16 * wave_u < u.nr;
     Kd = u.Kd;
     nst = (u.Kd + KS - 1) / KS;
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
       const int rr = 16 * wave + n * C::RPI + lane / C::BPR;
       ablk[n] = (lane % C::BPR) ^ row_swizzle<C::BPR>(rr);
-      aoff[n] = (uint32_t)sRow[rr] + (uint32_t)(ablk[n] * 16);
+      aoff[n] = aon ? (uint32_t)sRow[rr] + (uint32_t)(ablk[n] * 16) : 0xF0000000u;
     }
     arsrc = __builtin_amdgcn_make_buffer_rsrc((void *)u.Ab, (short)0, (int)(uint32_t)(u.arows * u.lda * 2), 0x00020000);
     wbase = u.pk + (int64_t)u.e * u.pk_mat + (int64_t)min(u.nb * C::NW + wave, u.pk_nblk - 1) * u.pk_nch * RB;
