@@ -87,7 +87,7 @@ __global__ __launch_bounds__(MOE_GEMM_THREADS, SHORT ? 4 : 3) void expert_gemm(c
   const int nblk0 = p.seg[0].nblk, nblk1 = max(p.seg[1].nblk, 1);
   const int ns = p.seg[1].nblk > 0 ? (p.sh_rows + MT - 1) / MT : 0;
   const int units_s = ns * nblk1;
-  const int nr_routed = p.tiles ? p.tile_count[0] : 0;
+  const int nr_routed = p.tiles ? min(p.tile_count[0], p.max_tiles) : 0;
 
   const int G = gridDim.x;
   const int U = units_s + (p.tiles ? nr_routed * nblk0 : 0);

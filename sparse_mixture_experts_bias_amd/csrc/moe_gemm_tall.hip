@@ -560,7 +560,7 @@ __global__ __launch_bounds__(512, 2) void expert_gemm_tall(const GemmParams p) {
   const int smt = p.sh_mt > 0 ? min(p.sh_mt, C::MT) : C::MT;  // segment 1's m-tile rows
   const int ns = p.seg[1].nblk > 0 ? (p.sh_rows + smt - 1) / smt : 0;
   const int units_s = ns * nblk1;
-  const int nr_routed = p.tiles ? p.tile_count[0] : 0;
+  const int nr_routed = p.tiles ? min(p.tile_count[0], p.max_tiles) : 0;
   auto decode = [&](int u, bool &sh, int4 &tile, int &nb) {
     sh = u < units_s;
     if (sh) {
