@@ -468,7 +468,9 @@ MOE_DEV float half_sum_f32(float v) {
 // t >= T computes on a clamped token and stores nothing).  el / esc: 16 ints / floats of
 // LDS private to the half (chosen ids and their unbiased scores, in selection order).
 template <int SL>
-MOE_DEV void topk_half(const TopkArgs &a, int t, int l32, int *el, float *esc, int32_t *sidx) {
+// coherent: the ids are stored at device scope (written through to the point every XCD reads
+// from), for a workgroup on another XCD to read without a cache write-back and invalidate
+MOE_DEV void topk_half(const TopkArgs &a, int t, int l32, int *el, float *esc, int32_t *sidx, bool coherent = false) {
   const bool live = t < a.T;
   const float *lrow = a.logits + (int64_t)(live ? t : a.T - 1) * a.E;
   float lg[SL], sb[SL];
@@ -556,7 +558,10 @@ MOE_DEV void topk_half(const TopkArgs &a, int t, int l32, int *el, float *esc, i
     }
     float w = a.norm ? my_s / wsum : my_s;
     w *= a.rscale;
-    a.idx[(int64_t)t * a.K + rank] = my_e;
+    if (coherent)
+      __hip_atomic_store(a.idx + (int64_t)t * a.K + rank, my_e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      a.idx[(int64_t)t * a.K + rank] = my_e;
     a.w[(int64_t)t * a.K + rank] = w;
     if (sidx) sidx[t * a.K + rank] = my_e;
   }
@@ -882,13 +887,15 @@ __global__ __launch_bounds__(256) void route_decode(TopkArgs a, int32_t *__restr
   __shared__ int last;
   static_assert(2 * 256 >= MOE_MAX_EXPERTS, "two experts per thread in the scan");
   const int tid = threadIdx.x, lane = tid & 63, half = tid >> 5, wave = tid >> 6;
-  topk_half<SL>(a, blockIdx.x * 8 + half, tid & 31, el[half], esc[half], nullptr);
-  __threadfence();  // this workgroup's selections are visible before it is counted
+  // hand-over without cache maintenance: the ids are device-scope stores, complete (vmcnt 0)
+  // before the workgroup is counted; the last workgroup reads them with device-scope loads
+  topk_half<SL>(a, blockIdx.x * 8 + half, tid & 31, el[half], esc[half], nullptr, true);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): this thread's stores have completed
   __syncthreads();
-  if (tid == 0) last = atomicAdd(done, 1) == (int)gridDim.x - 1;
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
   __syncthreads();
   if (!last) return;
-  __threadfence();  // every other workgroup's selections are visible to this one
   const int E = a.E, K = a.K, TK = a.T * a.K;
   for (int e = tid; e < E; e += 256) {
     cnt[e] = 0;
@@ -898,7 +905,7 @@ __global__ __launch_bounds__(256) void route_decode(TopkArgs a, int32_t *__restr
   __syncthreads();
   // slot p = t*K + j: per-expert counts and per-expert token masks
   for (int p = tid; p < TK; p += 256) {
-    const int ep = a.idx[p], tp = p / K;
+    const int ep = __hip_atomic_load(a.idx + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), tp = p / K;
     atomicAdd(&cnt[ep], 1);
     atomicOr(&tmask[ep][tp >> 5], 1u << (tp & 31));
   }
@@ -949,7 +956,7 @@ __global__ __launch_bounds__(256) void route_decode(TopkArgs a, int32_t *__restr
   __syncthreads();
   // rank of slot p among the slots of its expert: earlier tokens that chose the same expert
   for (int p = tid; p < TK; p += 256) {
-    const int ep = a.idx[p], tp = p / K;
+    const int ep = __hip_atomic_load(a.idx + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), tp = p / K;
     int rank = __popc(tmask[ep][tp >> 5] & ((1u << (tp & 31)) - 1u));
     for (int w = 0; w < (tp >> 5); ++w) rank += __popc(tmask[ep][w]);
     const int pos = offs[ep] + rank;
