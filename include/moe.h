@@ -168,7 +168,10 @@ MOE_API moe_status moe_pack_weights(const moe_linear *a, const moe_linear *b, vo
  *            order; equal selection keys go to the lower expert id
  *   topk_w   [T, K] float out: weights gathered from the unbiased scores, in the
  *            same slot order
- *   logits   optional [T, E] float out: x W_r^T + logit_bias, fp32
+ *   logits   optional [T, E] float out: x W_r^T + logit_bias, fp32 (for 256 tokens
+ *            or more with BF16 x, the fp32 sum of the partial sums over slices of H,
+ *            added in slice order: the same values moe_block_forward selects on)
+ *   ws       holds the router's partial sums (the query reports its size)
  * Source: mlxcel PR #1044 point 3; latent_moe.rs route_top_k_sigmoid_with_bias.
  */
 MOE_API moe_status moe_route(const void *x, int32_t x_dtype, int64_t T, int32_t H, const moe_router *r,
