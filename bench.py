@@ -132,6 +132,42 @@ def cpu_baseline(b, workload):
             "cpu_seconds": round(cpu, 3), "wall_seconds": round(wall, 3)}
 
 
+def measured_peak(hbm: bool, dev) -> dict:
+    """What a plain library kernel reaches on this machine: a device-to-device copy of 1 GiB
+    (bytes read + written per second) or a bf16 8192^3 torch.mm (FLOP/s)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if hbm:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        v = 2 * n * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+        del src, dst
+        return {"value": round(v, 1), "unit": "GB/s", "by": "torch copy_ of 1 GiB device to device (read + write)"}
+    m = 8192
+    a = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    bm = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        c = torch.mm(a, bm)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        c = torch.mm(a, bm)
+    e1.record()
+    torch.cuda.synchronize()
+    v = 2 * m ** 3 * reps / (e0.elapsed_time(e1) / 1e3) / 1e12
+    del a, bm, c
+    return {"value": round(v, 1), "unit": "TFLOP/s", "by": "torch.mm bf16 8192x8192x8192"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +273,10 @@ def main():
         achieved = wm["gu_flops"] / gu_avg_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+    # the same roof as a plain library kernel reaches it on this machine (outside the timed region)
+    mp = measured_peak(hbm_bound, dev)
+    roof["measured_peak"] = mp
+    roof["frac_of_measured"] = round(roof["achieved"] / mp["value"], 4)
     roof["traffic"] = measured_traffic(wl)
     roof["kernel"] = "expert_gemm gate/up (grouped, SwiGLU epilogue)"
     roof["kernel_avg_us"] = round(gu_avg_s * 1e6, 2)
