@@ -57,6 +57,15 @@ def test_block_small(cfg):
     _full_check(b, f"{cfg}-small")
 
 
+@pytest.mark.parametrize("T", [64, 65, 255, 256, 257])
+def test_block_path_boundaries(T):
+    """Token counts at the switches between launch paths: one-launch routing (T <= 64) or
+    top-k + permutation kernels; the decode router or the tiled one (T >= 256); the
+    single-workgroup permutation (T <= 256) or the three-kernel one."""
+    b = synth.make_block(synth.SMALL_SPECS["c2"], DEV, T=T)
+    _full_check(b, f"c2-small T={T}")
+
+
 @pytest.mark.parametrize("T,H,E", [(256, 544, 72), (301, 2080, 136), (300, 1024, 130)])
 def test_router_tiled_ragged(T, H, E):
     """Router for many tokens: the tiled GEMM with its reduction split into slices (a
