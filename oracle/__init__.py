@@ -7,10 +7,10 @@ it; the GPU library never does, and it shares no code with the GPU library.
 It computes, plainly and slowly, in float64 NumPy, what the pages define:
 
   * router projection and sigmoid/softmax scoring, a per-expert bias used for
-    selection only, top-k, optional renormalisation (mlxcel PR #1044, point 3
-    "Routing is sigmoid, and nothing scales the result"; ferrox-models
-    latent_moe.rs, kimi_latent_moe_forward and its route_top_k_sigmoid_with_bias
-    call);
+    selection only, top-k, optional renormalisation (mlxcel PR #1044, point 3:
+    the routing uses sigmoid scores and applies no routed scaling factor;
+    ferrox-models latent_moe.rs, kimi_latent_moe_forward and its
+    route_top_k_sigmoid_with_bias call);
   * the per-expert SwiGLU MLP with w1 = gate, w3 = up, w2 = down
     (latent_moe.rs, KimiExpertWeights::forward; SwitchGLU in mlx-swift-lm
     PR #364 and mlxcel issue #974), optionally clamped (libmir-metal
@@ -22,9 +22,9 @@ It computes, plainly and slowly, in float64 NumPy, what the pages define:
     Microscaling Formats specification v1.0);
   * the weighted combine, the latent variant (down_proj -> experts in latent
     space -> weighted sum -> RMSNorm -> up_proj, latent_moe.rs module doc) and
-    the shared expert, added at weight 1 or blended through a per-token 2-way
-    softmax coefficient head (mlxcel PR #1044, point 2 "The shared expert is
-    BLENDED, not added").
+    the shared expert, added at weight 1 or mixed with the routed sum through
+    a per-token 2-way softmax coefficient head (mlxcel PR #1044, point 2: the
+    two branches are weighted by that head's coefficients rather than summed).
 
 Readings where the pages are silent (each one is listed with its reason in
 the design notes): selection ties go to the lowest expert index; the K slots
@@ -106,15 +106,20 @@ def e8m0_decode(code) -> np.ndarray:
 
 def dequant_mxfp4(blocks, scales) -> np.ndarray:
     """MXFP4 dequantisation: two E2M1 codes per byte (even element in the low
-    nibble), one E8M0 scale per 32 consecutive elements of a row."""
+    nibble), one E8M0 scale per 32 consecutive elements of a row.  Each code
+    is looked up in the table of its 16 values (e2m1_decode of every code), so
+    a whole expert decodes in one gather."""
     b = np.asarray(blocks, dtype=np.uint8)
-    lo = b & 0xF
-    hi = b >> 4
-    codes = np.stack([lo, hi], axis=-1).reshape(*b.shape[:-1], b.shape[-1] * 2)
-    v = e2m1_decode(codes)
+    codes = np.empty((*b.shape[:-1], b.shape[-1] * 2), dtype=np.uint8)
+    codes[..., 0::2] = b & 0xF
+    codes[..., 1::2] = b >> 4
+    v = E2M1_VALUES[codes]
     sc = e8m0_decode(scales)
     cols = v.shape[-1]
     return (v.reshape(*v.shape[:-1], cols // 32, 32) * sc[..., None]).reshape(v.shape)
+
+
+E2M1_VALUES = e2m1_decode(np.arange(16))
 
 
 # ----------------------------------------------------------------------------
@@ -392,34 +397,60 @@ def block_forward(b: OBlock, routing=None):
 
 
 def block_forward_loop(b: OBlock):
-    """The same block, one token at a time in the pages' order (latent_moe.rs,
-    kimi_latent_moe_forward: route on the full hidden state, project, loop over
-    the chosen experts accumulating w * expert(latent), normalise, project back,
-    add the shared expert; with the blend of mlxcel PR #1044 point 2).  For
-    tiny inputs only."""
+    """The same block written token by token straight from its defining
+    equations, for tiny inputs.  For token t with expert input z_t:
+
+      rank_t(e)  = #{e' : sel[e'] > sel[e]} + #{e' < e : sel[e'] == sel[e]}
+      e chosen  <=> rank_t(e) < K            (the K largest keys, ties to low ids)
+      w_t(e)     = s[e] / sum_{chosen} s     (or s[e] without renormalisation),
+                   times routed_scale; 0 for an expert not chosen
+      y_r[t]     = sum over every expert e of w_t(e) * f_e(z_t), e ascending
+      latent:      y_r[t] = W_up rms_norm(y_r[t])
+      y[t]       = y_r[t] + f_shared(x_t)  or  c0 * y_r[t] + c1 * f_shared(x_t)
+
+    i.e. the sparse mixture as a dense sum masked by the selection (mlxcel PR
+    #1044 points 2 and 3; the latent flow of latent_moe.rs's module doc).  It
+    shares only the per-matrix steps (decoding, one SwiGLU MLP, RMSNorm) with
+    block_forward, not its selection or combine."""
     x = as_f64(b.x)
     T, H = x.shape
+    E = b.router_w.shape[0]
+    W_r = as_f64(b.router_w)
     ys = []
     for t in range(T):
-        xt = x[t:t + 1]
-        r = route(xt, b.router_w, b.scoring, b.K, b.norm_topk, b.routed_scale, b.logit_bias, b.select_bias)
-        zt = xt if b.latent_down is None else apply_linear(b.latent_down, 0, xt)
-        comb = np.zeros((1, zt.shape[1]))
-        for j in range(b.K):
-            e = int(r["idx"][0, j])
-            comb = comb + r["w"][0, j] * mlp_forward(b.experts, e, zt)
+        xt = x[t]
+        logit = np.array([float(np.dot(W_r[e], xt)) for e in range(E)])
+        if b.logit_bias is not None:
+            logit = logit + as_f64(b.logit_bias)
+        if b.scoring == "sigmoid":
+            s = np.array([1.0 / (1.0 + math.exp(-v)) for v in logit])
+        else:
+            ex = np.array([math.exp(v - logit.max()) for v in logit])
+            s = ex / ex.sum()
+        sel = s + (0.0 if b.select_bias is None else as_f64(b.select_bias))
+        rank = [sum(1 for f in range(E) if sel[f] > sel[e] or (sel[f] == sel[e] and f < e)) for e in range(E)]
+        chosen = [rank[e] < b.K for e in range(E)]
+        total = sum(s[e] for e in range(E) if chosen[e])
+        zt = xt[None, :] if b.latent_down is None else apply_linear(b.latent_down, 0, xt[None, :])
+        acc = np.zeros(zt.shape[1])
+        for e in range(E):
+            if not chosen[e]:
+                continue
+            w = (s[e] / total if b.norm_topk else s[e]) * b.routed_scale
+            acc = acc + w * mlp_forward(b.experts, e, zt)[0]
         if b.latent_down is not None:
             if b.latent_norm_w is not None:
-                comb = rms_norm(comb, b.latent_norm_w, b.norm_eps)
-            comb = apply_linear(b.latent_up, 0, comb)
+                acc = acc / math.sqrt(float(np.mean(acc * acc)) + b.norm_eps) * as_f64(b.latent_norm_w)
+            acc = apply_linear(b.latent_up, 0, acc[None, :])[0]
         if b.shared is not None and b.shared_mode != "none":
-            s = mlp_forward(b.shared, 0, xt)
+            sh = mlp_forward(b.shared, 0, xt[None, :])[0]
             if b.shared_mode == "add":
-                comb = comb + s
+                acc = acc + sh
             else:
-                c = coef_head(xt, b.coef_w, b.coef_b)
-                comb = c[:, :1] * comb + c[:, 1:] * s
-        ys.append(comb[0])
+                h = as_f64(b.coef_w) @ xt + as_f64(b.coef_b)
+                c0 = 1.0 / (1.0 + math.exp(h[1] - h[0]))
+                acc = c0 * acc + (1.0 - c0) * sh
+        ys.append(acc)
     return np.stack(ys)
 
 
