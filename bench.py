@@ -7,14 +7,18 @@ One step = one moe_block_forward call (router, top-k, permutation, grouped
 gate/up + SwiGLU, grouped down, combine with the shared expert) over one batch
 of synthetic tokens already resident in HBM.  The default workload is the
 Klear-shaped decode layer (32 tokens, hidden 2048, 256 experts top-8, 4-bit
-affine g64 experts, blended shared expert).  The weights are rotated over
-several copies so that the 256 MB Infinity Cache cannot serve them.
+affine g64 experts, blended shared expert); the default run also measures the
+same layer at prefill (4096 tokens) and reports it under "prefill", the other
+half of the metric.  The weights are rotated over several copies so that the
+256 MB Infinity Cache cannot serve them.
 
-Prints one JSON line: tokens/s for the whole step, the roofline of the dominant
-kernel (the grouped gate/up GEMM, timed live with HIP events on the stream it
-runs on, on every --gu-every'th step of the timed region: the events cost the
-step ~2.5 us), and the float64 CPU oracle timed on the host cores over a bounded
-sample of the same layer.
+Prints one JSON line: tokens/s for the whole step (K steps between two events),
+the per-step distribution (median, p10, p90 of a second run of K steps with an
+event between consecutive steps), the roofline of the dominant kernel (the
+grouped gate/up GEMM, timed live with HIP events on the stream it runs on, on
+every --gu-every'th step of the timed region: the events cost the step ~2.5 us)
+and of the whole step, and the float64 CPU oracle timed on the host cores over
+a bounded sample of the same layer (all cores, then one thread).
 """
 from __future__ import annotations
 
@@ -82,8 +86,14 @@ def work_model(b, hit):
     gu_bytes += T * D * (inter if b.latent_down is not None else act)
     gu_bytes += (T * K * I + (0 if latent_or_f32 else T * Is)) * inter
     gu_flops = 4 * T * K * I * D + (0 if latent_or_f32 else 4 * T * Is * H)
+    # the grouped down launch: hit experts' down planes (+ the shared expert's), its input h,
+    # its output rows o
+    dn_bytes = n * per_dn + (0 if latent_or_f32 else sh_dn)
+    dn_bytes += (T * K * I + (0 if latent_or_f32 else T * Is)) * inter
+    dn_bytes += (T * K + (0 if latent_or_f32 else T)) * D * inter
+    dn_flops = 2 * T * K * I * D + (0 if latent_or_f32 else 2 * T * Is * H)
     return {"step_bytes": step_bytes, "step_flops": step_flops, "gu_bytes": gu_bytes, "gu_flops": gu_flops,
-            "experts_hit": n}
+            "dn_bytes": dn_bytes, "dn_flops": dn_flops, "experts_hit": n}
 
 
 def kernel_source_sha():
@@ -109,27 +119,48 @@ def measured_traffic(workload):
     return d.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(b, workload):
-    """The float64 oracle, untuned, on a bounded sample of the same layer."""
-    import numpy as np
+    """The float64 oracle, untuned, on a bounded sample of the same layer: once with
+    every BLAS thread the host offers, once with one thread."""
     import oracle as O
     import synth
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
         threads = max([i.get("num_threads", 1) for i in blas] or [1])
     except Exception:
-        threads = 1
+        threadpool_limits, threads = None, 1
     ns = min(CPU_SAMPLE_TOKENS[workload], b.T)
     sub = synth.token_subset(b, list(range(ns))).to("cpu")
     ob = O.from_block(sub)
-    t0, c0 = time.perf_counter(), time.process_time()
-    O.block_forward(ob)
-    wall, cpu = time.perf_counter() - t0, time.process_time() - c0
-    return {"value": ns / wall, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {ns} of the {b.T} tokens of the same layer, one float64 forward "
-                      f"(weights decoded per expert); wall {wall:.2f} s, process CPU {cpu:.2f} s",
-            "cpu_seconds": round(cpu, 3), "wall_seconds": round(wall, 3)}
+
+    def timed():
+        t0, c0 = time.perf_counter(), time.process_time()
+        O.block_forward(ob)
+        return time.perf_counter() - t0, time.process_time() - c0
+
+    wall, cpu = timed()
+    out = {"value": ns / wall, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+           "sample": f"first {ns} of the {b.T} tokens of the same layer, one float64 forward "
+                     f"(weights decoded per expert); wall {wall:.2f} s, process CPU {cpu:.2f} s",
+           "cpu_seconds": round(cpu, 3), "wall_seconds": round(wall, 3)}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1, user_api="blas"):
+            w1, c1 = timed()
+        out["one_thread"] = {"value": ns / w1, "unit": "tokens/s", "cores": 1, "wall_seconds": round(w1, 3),
+                             "cpu_seconds": round(c1, 3)}
+    return out
 
 
 def measured_peak(hbm: bool, dev) -> dict:
@@ -168,6 +199,147 @@ def measured_peak(hbm: bool, dev) -> dict:
     return {"value": round(v, 1), "unit": "TFLOP/s", "by": "torch.mm bf16 8192x8192x8192"}
 
 
+def pct(v, q):
+    v = sorted(v)
+    if not v:
+        return None
+    i = min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))
+    return v[i]
+
+
+def measure(wl, steps, warmup, gu_every, copies_arg=0, tokens=0):
+    """Generate the workload's layer on the GPU and time `steps` block forwards."""
+    import torch
+    import synth
+    import sparse_mixture_experts_bias_amd as moe
+    from synth.descs import block_desc
+
+    dev = "cuda:0"
+    spec = synth.FULL_SPECS[wl]
+    if tokens > 0:
+        from dataclasses import replace
+        spec = replace(spec, T=tokens)
+    log(f"workload {wl}: generating the layer on {dev}")
+    b = synth.make_block(spec, dev)
+    moe.lib()
+    desc0 = block_desc(b)
+    y = torch.empty(b.T, b.H, dtype=torch.float32, device=dev)
+    idx = torch.empty(b.T, b.K, dtype=torch.int32, device=dev)
+    w = torch.empty(b.T, b.K, dtype=torch.float32, device=dev)
+    ws = torch.empty(moe.block_ws_bytes(b.x, desc0, with_topk=True) + 256, dtype=torch.uint8, device=dev)
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:]
+    moe.moe_block_forward(b.x, desc0, y, idx, w, ws=ws)
+    torch.cuda.synchronize()
+    hit = sorted(set(idx.flatten().tolist()))
+    wm = work_model(b, hit)
+    # weight copies so that the working set rotates through more than 1 GiB
+    copies = copies_arg
+    if copies <= 0:
+        copies = max(1, min(16, math.ceil((1 << 30) / max(wm["step_bytes"], 1)) + 1))
+    blocks = [b] + [synth.clone_weights(b) for _ in range(copies - 1)]
+    descs = [desc0] + [block_desc(bb) for bb in blocks[1:]]
+    log(f"{wl}: {copies} weight copies, {wm['experts_hit']} experts hit, {wm['step_bytes'] / 1e6:.1f} MB/step")
+
+    stream = torch.cuda.current_stream()
+    step = lambda i: moe.moe_block_forward(b.x, descs[i % copies], y, idx, w, ws=ws, stream=stream)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"{wl}: warmup {warmup} done")
+
+    moe.moe_timing_enable(moe.TIMING_GATEUP)  # creates the event pool outside the timed region
+    moe.moe_timing_enable(0)
+    moe.moe_timing_read()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    every = max(1, gu_every)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        timed = i % every == 0
+        if timed:
+            moe.moe_timing_enable(moe.TIMING_GATEUP)
+        step(i)
+        if timed:
+            moe.moe_timing_enable(0)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    n_gu, gu_ms = moe.moe_timing_read()
+    log(f"{wl}: timed {steps} steps: {total_ms:.3f} ms; gate/up launches {n_gu}, {gu_ms:.3f} ms")
+
+    # per-step distribution: the same steps again, an event between consecutive steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evs[i].record(stream)
+        step(i)
+    evs[steps].record(stream)
+    torch.cuda.synchronize()
+    per_step = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps)]
+
+    # the down launch's average, timed on its own run of steps (outside both timed regions)
+    moe.moe_timing_enable(moe.TIMING_DOWN)
+    for i in range(min(steps, 20)):
+        step(i)
+    moe.moe_timing_enable(0)
+    n_dn, dn_ms = moe.moe_timing_read()
+    return {"b": b, "desc": desc0, "wm": wm, "copies": copies, "total_ms": total_ms, "n_gu": n_gu, "gu_ms": gu_ms,
+            "per_step_us": per_step, "n_dn": n_dn, "dn_ms": dn_ms}
+
+
+def roofline_of(wl, r, hbm_bound, dev, with_peak=True):
+    wm = r["wm"]
+    gu_avg_s = (r["gu_ms"] / max(r["n_gu"], 1)) / 1e3
+    dn_avg_s = (r["dn_ms"] / max(r["n_dn"], 1)) / 1e3
+    if hbm_bound:
+        achieved = wm["gu_bytes"] / gu_avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        dn = wm["dn_bytes"] / dn_avg_s / 1e9
+        roof["down_kernel"] = {"achieved": round(dn, 1), "unit": "GB/s", "frac": round(dn / HBM_PEAK_GBS, 4),
+                               "kernel_avg_us": round(dn_avg_s * 1e6, 2),
+                               "algorithmic_bytes_per_launch": wm["dn_bytes"]}
+    else:
+        achieved = wm["gu_flops"] / gu_avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+        dn = wm["dn_flops"] / dn_avg_s / 1e12
+        roof["down_kernel"] = {"achieved": round(dn, 2), "unit": "TFLOP/s",
+                               "frac": round(dn / MFMA_BF16_PEAK_TFLOPS, 4),
+                               "kernel_avg_us": round(dn_avg_s * 1e6, 2),
+                               "algorithmic_flops_per_launch": wm["dn_flops"]}
+    roof["scope"] = "kernel only: the grouped gate/up GEMM (achieved/frac); down_kernel likewise"
+    if with_peak:
+        mp = measured_peak(hbm_bound, dev)
+        roof["measured_peak"] = mp
+        roof["frac_of_measured"] = round(roof["achieved"] / mp["value"], 4)
+    roof["traffic"] = measured_traffic(wl)
+    roof["kernel"] = "expert_gemm gate/up (grouped, SwiGLU epilogue)"
+    roof["kernel_avg_us"] = round(gu_avg_s * 1e6, 2)
+    roof["algorithmic_bytes_per_launch"] = wm["gu_bytes"]
+    roof["algorithmic_flops_per_launch"] = wm["gu_flops"]
+    return roof
+
+
+def step_stats(r, steps):
+    wm = r["wm"]
+    ms = r["total_ms"] / steps
+    ps = r["per_step_us"]
+    return {
+        "ms_per_step": round(ms, 5),
+        "step_us_median": round(pct(ps, 0.5), 2), "step_us_p10": round(pct(ps, 0.1), 2),
+        "step_us_p90": round(pct(ps, 0.9), 2),
+        "step_hbm_gbs": round(wm["step_bytes"] / (ms / 1e3) / 1e9, 1),
+        "step_frac_of_hbm_peak": round(wm["step_bytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_tflops": round(wm["step_flops"] / (ms / 1e3) / 1e12, 3),
+        "step_frac_of_bf16_mfma_peak": round(wm["step_flops"] / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "step_algorithmic_bytes": wm["step_bytes"], "step_algorithmic_flops": wm["step_flops"],
+        "experts_hit": wm["experts_hit"],
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +352,8 @@ def main():
     ap.add_argument("--gu-every", type=int, default=4,
                     help="time the gate/up launch of every N-th timed step with HIP events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="c2 only: skip the 4096-token prefill record of the same layer")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (the reference kernel that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -200,103 +374,37 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
         return
 
-    import synth
-    import sparse_mixture_experts_bias_amd as moe
-    from synth.descs import block_desc
-
     dev = "cuda:0"
     wl = args.workload
-    spec = synth.FULL_SPECS[wl]
-    if args.tokens > 0:
-        from dataclasses import replace
-        spec = replace(spec, T=args.tokens)
-    log(f"workload {wl}: generating the layer on {dev}")
-    b = synth.make_block(spec, dev)
-    moe.lib()
-    desc0 = block_desc(b)
-    y = torch.empty(b.T, b.H, dtype=torch.float32, device=dev)
-    idx = torch.empty(b.T, b.K, dtype=torch.int32, device=dev)
-    w = torch.empty(b.T, b.K, dtype=torch.float32, device=dev)
-    ws = torch.empty(moe.block_ws_bytes(b.x, desc0, with_topk=True) + 256, dtype=torch.uint8, device=dev)
-    off = (-ws.data_ptr()) % 256
-    ws = ws[off:]
-    moe.moe_block_forward(b.x, desc0, y, idx, w, ws=ws)
-    torch.cuda.synchronize()
-    hit = sorted(set(idx.flatten().tolist()))
-    wm = work_model(b, hit)
-    # weight copies so that the working set rotates through more than 1 GiB
-    copies = args.copies
-    if copies <= 0:
-        touched = wm["step_bytes"]
-        copies = max(1, min(16, math.ceil((1 << 30) / max(touched, 1)) + 1))
-    blocks = [b] + [synth.clone_weights(b) for _ in range(copies - 1)]
-    descs = [desc0] + [block_desc(bb) for bb in blocks[1:]]
-    log(f"{copies} weight copies, {wm['experts_hit']} experts hit, {wm['step_bytes'] / 1e6:.1f} MB/step")
-
-    stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
-        moe.moe_block_forward(b.x, descs[i % copies], y, idx, w, ws=ws, stream=stream)
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} done")
-
-    moe.moe_timing_enable(moe.TIMING_GATEUP)  # creates the event pool outside the timed region
-    moe.moe_timing_enable(0)
-    moe.moe_timing_read()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    every = max(1, args.gu_every)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(args.steps):
-        timed = i % every == 0
-        if timed:
-            moe.moe_timing_enable(moe.TIMING_GATEUP)
-        moe.moe_block_forward(b.x, descs[i % copies], y, idx, w, ws=ws, stream=stream)
-        if timed:
-            moe.moe_timing_enable(0)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    n_gu, gu_ms = moe.moe_timing_read()
-    moe.moe_timing_enable(0)
-    log(f"timed {args.steps} steps: {total_ms:.3f} ms; gate/up launches {n_gu}, {gu_ms:.3f} ms")
-
-    ms_step = total_ms / args.steps
-    tokens_s = b.T * args.steps / (total_ms / 1e3)
-    gu_avg_s = (gu_ms / max(n_gu, 1)) / 1e3
+    r = measure(wl, args.steps, args.warmup, args.gu_every, args.copies, args.tokens)
+    b = r["b"]
     hbm_bound = wl in ("c1", "c2", "c5")
-    if hbm_bound:
-        achieved = wm["gu_bytes"] / gu_avg_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    else:
-        achieved = wm["gu_flops"] / gu_avg_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
-    # the same roof as a plain library kernel reaches it on this machine (outside the timed region)
-    mp = measured_peak(hbm_bound, dev)
-    roof["measured_peak"] = mp
-    roof["frac_of_measured"] = round(roof["achieved"] / mp["value"], 4)
-    roof["traffic"] = measured_traffic(wl)
-    roof["kernel"] = "expert_gemm gate/up (grouped, SwiGLU epilogue)"
-    roof["kernel_avg_us"] = round(gu_avg_s * 1e6, 2)
-    roof["algorithmic_bytes_per_launch"] = wm["gu_bytes"]
-    roof["algorithmic_flops_per_launch"] = wm["gu_flops"]
-
+    roof = roofline_of(wl, r, hbm_bound, dev)
+    st = step_stats(r, args.steps)
+    tokens_s = b.T * args.steps / (r["total_ms"] / 1e3)
     out = {
         "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": st.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if b.x.dtype == torch.bfloat16 else "f32", "data": "synthetic",
         "config": {"workload": f"{wl}: {WORKLOADS[wl]}" + (f" (run on {b.T} tokens)" if args.tokens > 0 else ""),
                    "tokens": b.T, "hidden": b.H, "experts": b.E,
-                   "top_k": b.K, "intermediate": b.I, "weight_copies": copies,
-                   "inter_dtype": {0: "f32", 1: "bf16", 2: "f16"}[desc0.c.inter_dtype], "output": "f32"},
-        "step_hbm_gbs": round(wm["step_bytes"] / (ms_step / 1e3) / 1e9, 1),
-        "step_tflops": round(wm["step_flops"] / (ms_step / 1e3) / 1e12, 3),
-        "step_algorithmic_bytes": wm["step_bytes"], "step_algorithmic_flops": wm["step_flops"],
-        "experts_hit": wm["experts_hit"],
+                   "top_k": b.K, "intermediate": b.I, "weight_copies": r["copies"],
+                   "inter_dtype": {0: "f32", 1: "bf16", 2: "f16"}[r["desc"].c.inter_dtype], "output": "f32"},
+        **st,
         "roofline": roof,
     }
+    del r
+    if wl == "c2" and not args.no_prefill and args.tokens == 0:
+        # the metric's other half: the same layer at 4096-token prefill, its own record
+        torch.cuda.empty_cache()
+        rp = measure("c3", args.steps, args.warmup, args.gu_every)
+        pst = step_stats(rp, args.steps)
+        pre = {"workload": f"c3: {WORKLOADS['c3']}", "tokens_per_s": round(rp["b"].T * args.steps /
+                                                                           (rp["total_ms"] / 1e3), 1),
+               **pst, "roofline": roofline_of("c3", rp, False, dev, with_peak=False)}
+        out["prefill"] = pre
+        del rp
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host")
         out["cpu_baseline"] = cpu_baseline(b, wl)

@@ -137,7 +137,10 @@ typedef struct {
   const float *latent_norm_w;/* optional [D]: RMSNorm of the routed sum before latent_up */
   float norm_eps;            /* > 0 and finite when latent_norm_w != NULL */
   int32_t inter_dtype;       /* storage of z, h, expert outputs: MOE_BF16 or MOE_F16
-                                (MOE_F32 when x is f32) */
+                                (MOE_F32 when x is f32).  MOE_F16 keeps 3 more mantissa
+                                bits but its range ends at 65504: a value beyond it is
+                                stored as +-inf and propagates to y (no saturation, no
+                                error status).  MOE_BF16 has the fp32 range. */
 } moe_block;
 
 /*
@@ -170,7 +173,10 @@ MOE_API moe_status moe_pack_weights(const moe_linear *a, const moe_linear *b, vo
  *            same slot order
  *   logits   optional [T, E] float out: x W_r^T + logit_bias, fp32 (for 256 tokens
  *            or more with BF16 x, the fp32 sum of the partial sums over slices of H,
- *            added in slice order: the same values moe_block_forward selects on)
+ *            added in slice order: the same values moe_block_forward selects on).
+ *            The slices are fixed by (T, H, E) alone, never by the device's compute
+ *            unit count, so the logits (and the selection at near-ties) are the same
+ *            bits on every gfx950 device and partition.
  *   ws       holds the router's partial sums (the query reports its size)
  * Source: mlxcel PR #1044 point 3; latent_moe.rs route_top_k_sigmoid_with_bias.
  */
@@ -215,6 +221,12 @@ MOE_API moe_status moe_experts_forward(const void *z, int32_t z_dtype, int64_t T
  *   x        [T, H] (x_dtype F32 or BF16)
  *   y        [T, H] out, y_dtype F32 or BF16 (F32 when x is F32)
  *   topk_idx, topk_w: optional [T, K] outputs of the routing (may be NULL)
+ * After the call (once the stream has reached it) the workspace begins with the
+ * routing state the experts ran on, int32 arrays at 256-byte aligned offsets, in
+ * this order: counts [E], offsets [E+1], sorted_slot [T*K], slot_pos [T*K] (as
+ * moe_permute defines them; each array starts at the previous one's offset plus
+ * its size rounded up to a multiple of 256 bytes).  The rest of the workspace is
+ * unspecified.
  * Source: all of the above; the blend of mlxcel PR #1044 point 2; the latent flow
  * of latent_moe.rs.
  */

@@ -225,6 +225,87 @@ def block(hidden: int, router_d: Desc, experts: Desc, shared: Optional[Desc] = N
 
 
 # ----------------------------------------------------------------------------
+# argument checks (the C ABI sees pointers only: every size it relies on is
+# checked here, before the first C call)
+# ----------------------------------------------------------------------------
+
+_INT32_LIMIT = 2 ** 31
+
+
+def _bad(msg: str):
+    raise ValueError(msg)
+
+
+def _tensor(t, name: str, shape, dtypes, device=None) -> torch.Tensor:
+    """t must be a contiguous tensor of one of `dtypes` with exactly `shape`
+    (a tuple of ints) on `device` (when given)."""
+    if not isinstance(t, torch.Tensor):
+        _bad(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        _bad(f"{name} has dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if tuple(t.shape) != tuple(shape):
+        _bad(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        _bad(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        _bad(f"{name} is on {t.device}, expected {device} (every tensor of a call lives on one device)")
+    return t
+
+
+def _tokens(x: torch.Tensor, name: str, width: int, what: str) -> int:
+    """Rows of x seen as [tokens, width]: every leading dimension flattens into
+    the token count (the product is exact in Python integers and bounded here,
+    as libmir-metal's ClampedRoutedExperts::forward bounds its checked product)."""
+    if not isinstance(x, torch.Tensor):
+        _bad(f"{name} must be a torch.Tensor, got {type(x).__name__}")
+    if x.dim() < 1:
+        _bad(f"{name} must have at least one dimension ([..., {what}])")
+    if int(x.shape[-1]) != width:
+        _bad(f"{name} has last dimension {int(x.shape[-1])}, expected {what} = {width}")
+    T = 1
+    for d in x.shape[:-1]:
+        T *= int(d)
+    if T * max(width, 1) >= 2 ** 62:
+        _bad(f"{name}: {T} tokens x {width} elements overflows the token product")
+    if not x.is_contiguous():
+        _bad(f"{name} must be contiguous")
+    return T
+
+
+def _gpu(device: torch.device):
+    if device.type != "cuda":
+        _bad(f"tensors are on {device}: libmoe runs on a GPU (HIP) device only")
+
+
+def _slots(T: int, K: int):
+    if T * K >= _INT32_LIMIT:
+        _bad(f"{T} tokens x top_k {K} = {T * K} slots exceeds the int32 slot numbering")
+
+
+def _desc_device(d: "Desc") -> torch.device:
+    """The one device every tensor of a descriptor lives on."""
+    devs = set()
+
+    def walk(obj):
+        if isinstance(obj, torch.Tensor):
+            devs.add(obj.device)
+        elif isinstance(obj, Desc):
+            for k in obj.keep:
+                walk(k)
+        elif isinstance(obj, (list, tuple)):
+            for k in obj:
+                walk(k)
+    walk(d)
+    if len(devs) != 1:
+        _bad(f"descriptor tensors live on {sorted(str(v) for v in devs) or 'no device'}, expected one device")
+    return devs.pop()
+
+
+_ACT = (torch.float32, torch.bfloat16)
+_INTER_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_F16: torch.float16}
+
+
+# ----------------------------------------------------------------------------
 # entry points (same names as the C ABI)
 # ----------------------------------------------------------------------------
 
@@ -236,29 +317,65 @@ def _stream(stream) -> Optional[int]:
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
     nbytes = max(nbytes, 256)
-    if ws is not None and ws.numel() >= nbytes:
-        return ws, ws.numel()
+    if ws is not None:
+        if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or ws.dim() != 1 or ws.device != device:
+            _bad(f"ws must be a 1-D uint8 tensor on {device}")
+        if ws.data_ptr() % 256:
+            _bad("ws must be 256-byte aligned")
+        if ws.numel() >= nbytes:
+            return ws, ws.numel()
     t = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
     off = (-t.data_ptr()) % 256
     return t[off:off + nbytes], nbytes
 
 
+def _router_shape(r: Desc):
+    w = r.keep[0]
+    return int(w.shape[0]), int(w.shape[1]), w.dtype
+
+
 def route_ws_bytes(x: torch.Tensor, r: Desc, with_logits: bool) -> int:
+    E, H, _ = _router_shape(r)
+    T = _tokens(x, "x", H, "hidden")
     n = ctypes.c_size_t(0)
-    _check(lib().moe_route(None, dtype_code(x.dtype), x.shape[0], x.shape[1], ctypes.byref(r.c), None, None,
+    _check(lib().moe_route(None, dtype_code(x.dtype), T, H, ctypes.byref(r.c), None, None,
                            1 if with_logits else None, None, ctypes.byref(n), None))
     return n.value
 
 
 def moe_route(x: torch.Tensor, r: Desc, topk_idx: torch.Tensor, topk_w: torch.Tensor,
               logits: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """x [..., H]; topk_idx int32 / topk_w float32 [..., K] (or [T, K]); logits float32
+    [..., E] (or [T, E]) or None."""
+    E, H, wdt = _router_shape(r)
+    K = int(r.c.top_k)
+    T = _tokens(x, "x", H, "hidden (router weight columns)")
+    if x.dtype != wdt:
+        _bad(f"x has dtype {x.dtype}, the router weight {wdt}")
+    if x.dtype not in _ACT:
+        _bad(f"x has dtype {x.dtype}, expected float32 or bfloat16")
+    _slots(T, K)
+    dev = x.device
+    lead = tuple(x.shape[:-1])
+    for t, name, width, dt in ((topk_idx, "topk_idx", K, torch.int32), (topk_w, "topk_w", K, torch.float32),
+                               (logits, "logits", E, torch.float32)):
+        if t is None:
+            if name == "logits":
+                continue
+            _bad(f"{name} is required")
+        if not isinstance(t, torch.Tensor):
+            _bad(f"{name} must be a torch.Tensor")
+        _tensor(t, name, (*lead, width) if tuple(t.shape[:-1]) == lead else (T, width), (dt,), dev)
+    if _desc_device(r) != dev:
+        _bad(f"the router weights are on {_desc_device(r)}, x on {dev}")
+    _gpu(dev)
     L = lib()
     n = ctypes.c_size_t(0)
-    _check(L.moe_route(_ptr(x), dtype_code(x.dtype), x.shape[0], x.shape[1], ctypes.byref(r.c), _ptr(topk_idx),
+    _check(L.moe_route(_ptr(x), dtype_code(x.dtype), T, H, ctypes.byref(r.c), _ptr(topk_idx),
                        _ptr(topk_w), _ptr(logits), None, ctypes.byref(n), None))
-    w, nb = _workspace(n.value, x.device, ws)
+    w, nb = _workspace(n.value, dev, ws)
     n = ctypes.c_size_t(nb)
-    _check(L.moe_route(_ptr(x), dtype_code(x.dtype), x.shape[0], x.shape[1], ctypes.byref(r.c), _ptr(topk_idx),
+    _check(L.moe_route(_ptr(x), dtype_code(x.dtype), T, H, ctypes.byref(r.c), _ptr(topk_idx),
                        _ptr(topk_w), _ptr(logits), _ptr(w),
                        ctypes.byref(n), _stream(stream)))
     return w
@@ -266,12 +383,26 @@ def moe_route(x: torch.Tensor, r: Desc, topk_idx: torch.Tensor, topk_w: torch.Te
 
 def moe_permute(topk_idx: torch.Tensor, E: int, counts, offsets, sorted_slot, slot_pos,
                 ws: Optional[torch.Tensor] = None, stream=None):
-    L = lib()
+    """topk_idx int32 [T, K]; counts int32 [E]; offsets int32 [E+1]; sorted_slot,
+    slot_pos int32 [T*K]."""
+    if not isinstance(topk_idx, torch.Tensor) or topk_idx.dim() != 2:
+        _bad("topk_idx must be a 2-D tensor [T, K]")
     T, K = int(topk_idx.shape[0]), int(topk_idx.shape[1])
+    E = int(E)
+    _slots(T, K)
+    dev = topk_idx.device
+    i32 = (torch.int32,)
+    _tensor(topk_idx, "topk_idx", (T, K), i32, dev)
+    _tensor(counts, "counts", (E,), i32, dev)
+    _tensor(offsets, "offsets", (E + 1,), i32, dev)
+    _tensor(sorted_slot, "sorted_slot", (T * K,), i32, dev)
+    _tensor(slot_pos, "slot_pos", (T * K,), i32, dev)
+    _gpu(dev)
+    L = lib()
     n = ctypes.c_size_t(0)
-    args = (_ptr(topk_idx), T, K, int(E), _ptr(counts), _ptr(offsets), _ptr(sorted_slot), _ptr(slot_pos))
+    args = (_ptr(topk_idx), T, K, E, _ptr(counts), _ptr(offsets), _ptr(sorted_slot), _ptr(slot_pos))
     _check(L.moe_permute(*args, None, ctypes.byref(n), None))
-    w, nb = _workspace(n.value, topk_idx.device, ws)
+    w, nb = _workspace(n.value, dev, ws)
     n = ctypes.c_size_t(nb)
     _check(L.moe_permute(*args, _ptr(w), ctypes.byref(n), _stream(stream)))
     return w
@@ -280,37 +411,102 @@ def moe_permute(topk_idx: torch.Tensor, E: int, counts, offsets, sorted_slot, sl
 def moe_experts_forward(z: torch.Tensor, experts: Desc, E: int, topk_idx, topk_w, offsets, sorted_slot, slot_pos,
                         y_routed: torch.Tensor, inter_dtype: int = MOE_BF16, ws: Optional[torch.Tensor] = None,
                         stream=None):
+    """z [T, D]; topk_idx int32 / topk_w float32 [T, K]; offsets int32 [E+1];
+    sorted_slot, slot_pos int32 [T*K]; y_routed float32 [T, D]."""
+    D = int(experts.c.gate.cols)
+    if int(E) != int(experts.c.gate.n):
+        _bad(f"E = {E} but the expert stack holds {experts.c.gate.n} experts")
+    if not isinstance(z, torch.Tensor) or z.dim() != 2:
+        _bad("z must be a 2-D tensor [T, D]")
+    T = _tokens(z, "z", D, "expert input width (gate columns)")
+    if z.dtype not in (torch.float32, torch.bfloat16, torch.float16):
+        _bad(f"z has dtype {z.dtype}, expected float32, bfloat16 or float16")
+    if not isinstance(topk_idx, torch.Tensor) or topk_idx.dim() != 2:
+        _bad("topk_idx must be a 2-D tensor [T, K]")
+    K = int(topk_idx.shape[1])
+    _slots(T, K)
+    dev = z.device
+    i32 = (torch.int32,)
+    _tensor(topk_idx, "topk_idx", (T, K), i32, dev)
+    _tensor(topk_w, "topk_w", (T, K), (torch.float32,), dev)
+    _tensor(offsets, "offsets", (int(E) + 1,), i32, dev)
+    _tensor(sorted_slot, "sorted_slot", (T * K,), i32, dev)
+    _tensor(slot_pos, "slot_pos", (T * K,), i32, dev)
+    _tensor(y_routed, "y_routed", (T, D), (torch.float32,), dev)
+    if _desc_device(experts) != dev:
+        _bad(f"the expert weights are on {_desc_device(experts)}, z on {dev}")
+    _gpu(dev)
     L = lib()
-    T, K = int(topk_idx.shape[0]), int(topk_idx.shape[1])
-    args = (_ptr(z), dtype_code(z.dtype), T, int(z.shape[1]), ctypes.byref(experts.c), int(E), K, _ptr(topk_idx),
+    args = (_ptr(z), dtype_code(z.dtype), T, D, ctypes.byref(experts.c), int(E), K, _ptr(topk_idx),
             _ptr(topk_w), _ptr(offsets), _ptr(sorted_slot), _ptr(slot_pos), int(inter_dtype), _ptr(y_routed))
     n = ctypes.c_size_t(0)
     _check(L.moe_experts_forward(*args, None, ctypes.byref(n), None))
-    w, nb = _workspace(n.value, z.device, ws)
+    w, nb = _workspace(n.value, dev, ws)
     n = ctypes.c_size_t(nb)
     _check(L.moe_experts_forward(*args, _ptr(w), ctypes.byref(n), _stream(stream)))
     return w
 
 
 def block_ws_bytes(x: torch.Tensor, b: Desc, with_topk: bool = False) -> int:
+    T = _tokens(x, "x", int(b.c.hidden), "hidden")
     n = ctypes.c_size_t(0)
     dummy = 1 if with_topk else None
-    _check(lib().moe_block_forward(None, dtype_code(x.dtype), x.shape[0], ctypes.byref(b.c), None, MOE_F32, dummy,
+    _check(lib().moe_block_forward(None, dtype_code(x.dtype), T, ctypes.byref(b.c), None, MOE_F32, dummy,
                                    dummy, None, ctypes.byref(n), None))
     return n.value
 
 
+def _check_block_call(x, b: Desc, y, topk_idx, topk_w):
+    H, K = int(b.c.hidden), int(b.c.router.top_k)
+    T = _tokens(x, "x", H, "hidden")
+    if x.dtype not in _ACT:
+        _bad(f"x has dtype {x.dtype}, expected float32 or bfloat16")
+    _slots(T, K)
+    dev = x.device
+    lead = tuple(x.shape[:-1])
+    shape_of = lambda t, w: (*lead, w) if isinstance(t, torch.Tensor) and tuple(t.shape[:-1]) == lead else (T, w)
+    _tensor(y, "y", shape_of(y, H), _ACT, dev)
+    if x.dtype == torch.float32 and y.dtype != torch.float32:
+        _bad("float32 x needs a float32 y")
+    if topk_idx is not None:
+        _tensor(topk_idx, "topk_idx", shape_of(topk_idx, K), (torch.int32,), dev)
+    if topk_w is not None:
+        _tensor(topk_w, "topk_w", shape_of(topk_w, K), (torch.float32,), dev)
+    if _desc_device(b) != dev:
+        _bad(f"the block's weights are on {_desc_device(b)}, x on {dev}")
+    return T, dev
+
+
 def moe_block_forward(x: torch.Tensor, b: Desc, y: torch.Tensor, topk_idx: Optional[torch.Tensor] = None,
                       topk_w: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """x [..., H] (leading dimensions flatten into the token count); y [..., H] or
+    [T, H] float32/bfloat16; topk_idx int32 / topk_w float32 [..., K] or [T, K].
+    Returns the workspace used: after the call it begins with the routing state
+    (see routing_state)."""
+    T, dev = _check_block_call(x, b, y, topk_idx, topk_w)
+    _gpu(dev)
     L = lib()
-    args = (_ptr(x), dtype_code(x.dtype), int(x.shape[0]), ctypes.byref(b.c), _ptr(y), dtype_code(y.dtype),
+    args = (_ptr(x), dtype_code(x.dtype), T, ctypes.byref(b.c), _ptr(y), dtype_code(y.dtype),
             _ptr(topk_idx), _ptr(topk_w))
     n = ctypes.c_size_t(0)
     _check(L.moe_block_forward(*args, None, ctypes.byref(n), None))
-    w, nb = _workspace(n.value, x.device, ws)
+    w, nb = _workspace(n.value, dev, ws)
     n = ctypes.c_size_t(nb)
     _check(L.moe_block_forward(*args, _ptr(w), ctypes.byref(n), _stream(stream)))
     return w
+
+
+def routing_state(ws: torch.Tensor, T: int, K: int, E: int):
+    """Views of the routing state a moe_block_forward call left at the start of its
+    workspace (include/moe.h): counts [E], offsets [E+1], sorted_slot [T*K],
+    slot_pos [T*K], each int32 and 256-byte aligned, in that order."""
+    al = lambda n: (n + 255) // 256 * 256
+    o_counts = 0
+    o_offsets = o_counts + al(4 * E)
+    o_ss = o_offsets + al(4 * (E + 1))
+    o_sp = o_ss + al(4 * T * K)
+    v = lambda off, n: ws[off:off + 4 * n].view(torch.int32)
+    return v(o_counts, E), v(o_offsets, E + 1), v(o_ss, T * K), v(o_sp, T * K)
 
 
 def moe_timing_enable(kind: int):

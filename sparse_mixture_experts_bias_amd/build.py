@@ -7,6 +7,7 @@ Cross-compiles for gfx950 on any machine with ROCm's hipcc; no GPU needed.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -42,13 +43,31 @@ def _compile(src: str, obj: str) -> None:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-8000:]}")
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every source and link libmoe.so next to this file; returns its path."""
+def _key(src: str) -> str:
+    """Hash of a source, every header of csrc/ and the flags (the incremental build's object key)."""
+    h = hashlib.sha256(" ".join(FLAGS).encode())
+    for f in sorted(os.listdir(CSRC)):
+        if f == src or f.endswith(".h"):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:20]
+
+
+def build(verbose: bool = True, incremental: bool = False) -> str:
+    """Compile every source and link libmoe.so next to this file; returns its path.
+    incremental: reuse objects under _build/ whose source, headers and flags are unchanged."""
     with tempfile.TemporaryDirectory(prefix="moe_build_") as tmp:
-        objs = [os.path.join(tmp, s.replace(".hip", ".o")) for s in SOURCES]
-        workers = min(len(SOURCES), max(1, (os.cpu_count() or 2)))
+        if incremental:
+            cache = os.path.join(PKG, "_build")
+            os.makedirs(cache, exist_ok=True)
+            objs = [os.path.join(cache, f"{s[:-4]}-{_key(s)}.o") for s in SOURCES]
+            todo = [(s, o) for s, o in zip(SOURCES, objs) if not os.path.exists(o)]
+        else:
+            objs = [os.path.join(tmp, s.replace(".hip", ".o")) for s in SOURCES]
+            todo = list(zip(SOURCES, objs))
+        workers = min(max(len(todo), 1), max(1, (os.cpu_count() or 2)))
         with cf.ThreadPoolExecutor(workers) as ex:
-            list(ex.map(_compile, SOURCES, objs))
+            list(ex.map(lambda so: _compile(so[0], so[1] + ".part") or os.replace(so[1] + ".part", so[1]), todo))
         out_tmp = LIB + ".tmp"
         cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp]
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -61,5 +80,5 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build(incremental="--incremental" in sys.argv)
     sys.exit(0)

@@ -259,9 +259,13 @@ bool router_tiled(int x_dt, int T, int H, int E) {
   return x_dt == MOE_BF16 && T >= MOE_ROUTER_GEMM_T && E % 8 == 0 && (int64_t)T * H * 2 <= INT32_MAX &&
          (int64_t)E * H * 2 <= INT32_MAX;
 }
+// The slice count is a function of (T, H, E) alone (sized for MI355X's 256 CUs, not read from
+// the device), so the summation order of the logits, and with it the selection at near-ties,
+// is the same on every device and partition.
+constexpr int kRouterSliceCUs = 256;
 int router_slice_len(int T, int H, int E) {
   const int tiles = ((T + 127) / 128) * ((E + 63) / 64);
-  int S = (3 * device_cus() / 2 + tiles - 1) / tiles;
+  int S = (3 * kRouterSliceCUs / 2 + tiles - 1) / tiles;
   S = S < 1 ? 1 : (S > 16 ? 16 : S);
   return (((H + S - 1) / S) + 63) / 64 * 64;
 }
@@ -848,15 +852,16 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   Plan pl;
   const bool blend = b->shared_mode == MOE_SHARED_BLEND;
   const int rs = (T > INT32_MAX) ? 1 : router_slices(x_dtype, (int)T, H, E, true);
+  // the routing state first, at the offsets include/moe.h documents
+  const size_t o_counts = pl.take((size_t)E * 4);
+  const size_t o_offsets = pl.take((size_t)(E + 1) * 4);
+  const size_t o_ss = pl.take((size_t)TK * 4);
+  const size_t o_sp = pl.take((size_t)TK * 4);
   const size_t o_logits = pl.take((size_t)rs * T * E * 4);
   const size_t o_coef = pl.take((size_t)T * 2 * 4);
   const size_t o_clog = pl.take((size_t)rs * T * 2 * 4);
   const size_t o_idx = topk_idx ? 0 : pl.take((size_t)TK * 4);
   const size_t o_w = topk_w ? 0 : pl.take((size_t)TK * 4);
-  const size_t o_counts = pl.take((size_t)E * 4);
-  const size_t o_offsets = pl.take((size_t)(E + 1) * 4);
-  const size_t o_ss = pl.take((size_t)TK * 4);
-  const size_t o_sp = pl.take((size_t)TK * 4);
   const size_t o_chunk = pl.take(perm_ws_bytes(T, E));
   const int ntile = max_tiles(TK, E);
   const int mb = mb_for_routing(TK, E);

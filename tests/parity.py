@@ -32,14 +32,28 @@ def np32(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy()
 
 
-def run_block(b: synth.Block, y_dtype=torch.float32, inter=None, ws=None):
+def run_block(b: synth.Block, y_dtype=torch.float32, inter=None, ws=None, with_state=False):
+    """One moe_block_forward; with_state also returns the routing state the experts
+    ran on (counts, offsets, sorted_slot, slot_pos, read back from the workspace)."""
     dev = b.x.device
     y = torch.empty(b.T, b.H, dtype=y_dtype, device=dev)
     idx = torch.empty(b.T, b.K, dtype=torch.int32, device=dev)
     w = torch.empty(b.T, b.K, dtype=torch.float32, device=dev)
-    moe.moe_block_forward(b.x, block_desc(b, inter), y, idx, w, ws=ws)
+    used = moe.moe_block_forward(b.x, block_desc(b, inter), y, idx, w, ws=ws)
     torch.cuda.synchronize()
+    if with_state:
+        state = tuple(t.cpu().numpy().copy() for t in moe.routing_state(used, b.T, b.K, b.E))
+        return y, idx, w, state
     return y, idx, w
+
+
+def check_permutation(idx: torch.Tensor, E: int, state):
+    """The routing state (counts, offsets, sorted_slot, slot_pos) equals the oracle's
+    permutation of the selection bit for bit."""
+    c, o, s, p = O.permute(idx.cpu().numpy().astype(np.int64), E)
+    names = ("counts", "offsets", "sorted_slot", "slot_pos")
+    for name, got, want in zip(names, state, (c, o, s, p)):
+        assert np.array_equal(got.astype(np.int64), want), f"{name} differs from the oracle's permutation"
 
 
 def run_route(b: synth.Block):

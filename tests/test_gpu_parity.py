@@ -15,7 +15,7 @@ import synth
 import sparse_mixture_experts_bias_amd as moe
 from synth.descs import block_desc, mlp_desc, inter_dtype_for
 
-from parity import check_output, check_routing, np32, run_block, run_route
+from parity import check_output, check_permutation, check_routing, np32, run_block, run_route
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,8 @@ def _gpu():
 
 def _full_check(b: synth.Block, label: str, y_dtype=torch.float32):
     announce(f"{label}: T={b.T} H={b.H} E={b.E} K={b.K} seed={b.seed}")
-    y, idx, w = run_block(b, y_dtype)
+    y, idx, w, state = run_block(b, y_dtype, with_state=True)
+    check_permutation(idx, b.E, state)
     gidx, gw, glog = run_route(b)
     assert torch.equal(gidx, idx), "moe_route and moe_block_forward disagree on the selection"
     assert torch.equal(gw, w)
@@ -89,35 +90,25 @@ def test_block_full_c2_decode():
     _full_check(b, "c2-full")
 
 
-@pytest.mark.parametrize("cfg,nsample", [("c3", 16), ("c4", 16), ("c5", 6)])
-def test_block_full_sampled(cfg, nsample):
-    """Full-size layers in the launch configuration of the benchmark; routing and
-    permutation checked on every token, outputs on a sample of tokens."""
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cfg", ["c3", "c4", "c5"])
+def test_block_full_every_token(cfg):
+    """Full-size layers in the launch configuration of the benchmark: routing, the
+    permutation the experts ran on, and the output of every token against the oracle
+    (the oracle decodes each expert once and applies it to all of its tokens)."""
     spec = synth.FULL_SPECS[cfg]
     b = synth.make_block(spec, DEV)
     announce(f"{cfg}-full: T={b.T} H={b.H} E={b.E} K={b.K} seed={b.seed}")
-    y, idx, w = run_block(b)
+    y, idx, w, state = run_block(b, with_state=True)
+    check_permutation(idx, b.E, state)
     gidx, gw, glog = run_route(b)
     assert torch.equal(gidx, idx) and torch.equal(gw, w)
-    # routing on every token
-    from synth import raw
-    ob_all = O.OBlock(x=raw(b.x), router_w=raw(b.router_w), scoring=b.scoring, K=b.K, norm_topk=b.norm_topk,
-                      routed_scale=b.routed_scale, experts=None, logit_bias=raw(b.logit_bias),
-                      select_bias=raw(b.select_bias))
-    routing, rep = check_routing(ob_all, np32(idx).astype(np.int64), np32(w), np32(glog))
-    print(f"[routing] {cfg}-full {rep}", flush=True)
-    # permutation on every token
-    _check_permute(idx, b.E)
-    # outputs on sampled tokens
-    g = torch.Generator().manual_seed(1234)
-    toks = torch.randperm(b.T, generator=g)[:nsample].sort().values.tolist()
-    sub = synth.token_subset(b, toks)
-    ob = O.from_block(sub)
-    r_sub = {k: (v[toks] if isinstance(v, np.ndarray) and v.ndim >= 1 and v.shape[0] == b.T else v)
-             for k, v in routing.items()}
-    ref = O.block_forward(ob, routing=r_sub)["y"]
-    stats = check_output(np32(y)[toks], ref, False, f"{cfg}-full")
-    print(f"[ok] {cfg}-full sampled {toks}: {stats}", flush=True)
+    ob = O.from_block(b)
+    routing, rep = check_routing(ob, np32(idx).astype(np.int64), np32(w), np32(glog))
+    print(f"[routing] {cfg}-full {rep}; m-tile rows per expert: max {int(state[0].max())}", flush=True)
+    ref = O.block_forward(ob, routing=routing)["y"]
+    stats = check_output(np32(y), ref, False, f"{cfg}-full")
+    print(f"[ok] {cfg}-full, all {b.T} tokens: {stats}", flush=True)
 
 
 def _check_permute(idx: torch.Tensor, E: int):
@@ -309,6 +300,53 @@ def test_swiglu_limit_engages():
     spec = synth.replace(synth.SMALL_SPECS["c5"], swiglu_limit=0.5, seed=77)
     b = synth.make_block(spec, DEV)
     _full_check(b, "clamp 0.5")
+
+
+@pytest.mark.parametrize("T", [1, 37, 64])
+def test_decode_routing_state_bit_exact(T):
+    """T <= 64 routes and permutes in one launch; the counts, offsets, sorted_slot and
+    slot_pos it leaves for the experts equal the oracle's permutation bit for bit."""
+    b = synth.make_block(synth.FULL_SPECS["c2"], DEV, T=T)
+    announce(f"decode routing state c2 T={T}")
+    y, idx, w, state = run_block(b, with_state=True)
+    check_permutation(idx, b.E, state)
+    gidx, gw, glog = run_route(b)
+    assert torch.equal(gidx, idx) and torch.equal(gw, w)
+    check_routing(O.from_block(b), np32(idx).astype(np.int64), np32(w), np32(glog))
+
+
+def test_topk_above_16():
+    """K > 16 takes the wave-per-token selection kernel (one chosen expert per lane)."""
+    spec = synth.replace(synth.SMALL_SPECS["c2"], name="K20", E=64, K=20, T=45, I=128, I_s=128, seed=61)
+    _full_check(synth.make_block(spec, DEV), "K=20 of 64")
+
+
+def test_sigmoid_without_renorm():
+    spec = synth.replace(synth.SMALL_SPECS["c2"], name="sig-norenorm", norm_topk=False, seed=62)
+    b = synth.make_block(spec, DEV)
+    y, idx, w = _full_check(b, "sigmoid, no renorm")[:3]
+    assert not torch.allclose(w.sum(1).cpu(), torch.ones(b.T))
+
+
+@pytest.mark.parametrize("cfg,scale", [("c2", 2.5), ("c4", 0.375)])
+def test_routed_scale(cfg, scale):
+    """routed_scale multiplies the (renormalised) routing weights."""
+    b = synth.make_block(synth.SMALL_SPECS[cfg], DEV)
+    b.routed_scale = scale
+    y, idx, w = _full_check(b, f"{cfg} routed_scale={scale}")[:3]
+    if b.norm_topk:
+        assert torch.allclose(w.sum(1).cpu(), torch.full((b.T,), scale), rtol=1e-5)
+
+
+def test_zero_routed_branch_add():
+    """Add mode with the down weights zeroed: y is the shared expert alone."""
+    b = synth.make_block(synth.SMALL_SPECS["c4"], DEV)
+    b.experts.down.scales = torch.zeros_like(b.experts.down.scales)
+    b.experts.down.qbias = torch.zeros_like(b.experts.down.qbias)
+    y, idx, w, ob, routing = _full_check(b, "zero-routed c4 (add)")
+    out = O.block_forward(ob, routing=routing)
+    assert np.array_equal(out["y_routed"], np.zeros_like(out["y_routed"]))
+    check_output(np32(y), out["shared"], False, "y == shared")
 
 
 # ----------------------------------------------------------------------------
