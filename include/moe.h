@@ -235,6 +235,27 @@ MOE_API moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, 
                              void *ws, size_t *ws_bytes, void *stream);
 
 /*
+ * moe_block_forward_noalloc - moe_block_forward without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and validation as
+ * moe_block_forward; the scratch space is a fixed array of MOE_NOALLOC_SCRATCH_BYTES in
+ * the library's code object, one per GPU, held until the process ends.  The call itself
+ * allocates nothing (no hipMalloc, no hipFree, no allocating library routine).
+ *   - A call whose workspace would exceed MOE_NOALLOC_SCRATCH_BYTES returns
+ *     MOE_ERR_WORKSPACE before launching anything (about 600 tokens of the 2048-hidden,
+ *     256-expert decode layer fit).
+ *   - `stream` must belong to the calling thread's current device (else MOE_ERR_ARG).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap on one GPU (on
+ *     different streams or threads) race and give undefined results.  Calls ordered on
+ *     one stream are safe; each call initialises all the scratch state it reads.
+ *   - The first call on a device looks up the array's device address (once per device).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+MOE_API moe_status moe_block_forward_noalloc(const void *x, int32_t x_dtype, int64_t T, const moe_block *b,
+                                             void *y, int32_t y_dtype, int32_t *topk_idx, float *topk_w,
+                                             void *stream);
+
+/*
  * Live timing of one kernel class with HIP events, for measurement tools.
  *   kind: 0 off; 1 grouped gate/up GEMM; 2 grouped down GEMM; 3 router logits;
  *         4 scores + top-k; 5 permutation; 6 combine; 7 plain GEMMs (latent

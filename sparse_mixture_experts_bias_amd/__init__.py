@@ -27,8 +27,10 @@ FMT_CODES = {"dense": MOE_W_DENSE, "affine4": MOE_W_AFFINE4, "mxfp4": MOE_W_MXFP
 SHARED_CODES = {"none": MOE_SHARED_NONE, "add": MOE_SHARED_ADD, "blend": MOE_SHARED_BLEND}
 SCORING_CODES = {"sigmoid": MOE_SIGMOID, "softmax": MOE_SOFTMAX}
 
-EXPORTS = ("moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward", "moe_pack_weights",
-           "moe_timing_enable", "moe_timing_read", "moe_status_str", "moe_last_error", "moe_abi_version")
+EXPORTS = ("moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward", "moe_block_forward_noalloc",
+           "moe_pack_weights", "moe_timing_enable", "moe_timing_read", "moe_status_str", "moe_last_error",
+           "moe_abi_version")
+NOALLOC_SCRATCH_BYTES = 32 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 
 # kernel classes of moe_timing_enable
 TIMING_GATEUP, TIMING_DOWN, TIMING_ROUTER, TIMING_TOPK, TIMING_PERM, TIMING_COMBINE, TIMING_PLAIN = range(1, 8)
@@ -86,7 +88,9 @@ def lib() -> ctypes.CDLL:
                                           i32, vp, vp, sz, vp]
         L.moe_block_forward.argtypes = [vp, i32, i64, ctypes.POINTER(MoeBlock), vp, i32, vp, vp, vp, sz, vp]
         L.moe_pack_weights.argtypes = [ctypes.POINTER(MoeLinear), ctypes.POINTER(MoeLinear), vp, sz, vp]
-        for f in ("moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward", "moe_pack_weights"):
+        L.moe_block_forward_noalloc.argtypes = [vp, i32, i64, ctypes.POINTER(MoeBlock), vp, i32, vp, vp, vp]
+        for f in ("moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward", "moe_pack_weights",
+                  "moe_block_forward_noalloc"):
             getattr(L, f).restype = ctypes.c_int32
         L.moe_status_str.argtypes = [i32]
         L.moe_status_str.restype = ctypes.c_char_p
@@ -494,6 +498,16 @@ def moe_block_forward(x: torch.Tensor, b: Desc, y: torch.Tensor, topk_idx: Optio
     n = ctypes.c_size_t(nb)
     _check(L.moe_block_forward(*args, _ptr(w), ctypes.byref(n), _stream(stream)))
     return w
+
+
+def moe_block_forward_noalloc(x: torch.Tensor, b: Desc, y: torch.Tensor, topk_idx: Optional[torch.Tensor] = None,
+                              topk_w: Optional[torch.Tensor] = None, stream=None):
+    """moe_block_forward on the library's fixed per-GPU scratch array (no workspace is
+    allocated anywhere); same arguments and checks.  Calls that overlap on one GPU race."""
+    T, dev = _check_block_call(x, b, y, topk_idx, topk_w)
+    _gpu(dev)
+    _check(lib().moe_block_forward_noalloc(_ptr(x), dtype_code(x.dtype), T, ctypes.byref(b.c), _ptr(y),
+                                           dtype_code(y.dtype), _ptr(topk_idx), _ptr(topk_w), _stream(stream)))
 
 
 def routing_state(ws: torch.Tensor, T: int, K: int, E: int):

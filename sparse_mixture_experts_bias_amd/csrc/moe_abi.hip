@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "moe_kernels.h"
@@ -560,6 +561,32 @@ moe_status combine(int odt, int ydt, const void *o, int64_t ldo, const int32_t *
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------------------
+// scratch memory of moe_block_forward_noalloc: one array per GPU, in the code object, held
+// until the process ends.  Host code never uses the array's name as an address (on the host
+// it is only a stand-in for the symbol): the device address of each GPU's copy is looked up
+// once, with that GPU current, and kept here.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// the device address of `scratch` on device dev (the calling thread's current device)
+moe_status scratch_on(int dev, void **out) {
+  CHECK(dev >= 0 && dev < kMaxDevices, MOE_ERR_DEVICE, "device %d outside 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    HIPCHK(hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch)));
+    CHECK(ptr != nullptr, MOE_ERR_DEVICE, "hipGetSymbolAddress returned NULL for the scratch array");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -1008,6 +1035,28 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   }
   TRY(run_plain(inter, b->latent_up, nullptr, 0.f, false, y_dtype, yn, D, Ti, y, H, resid, H, s));
   return MOE_OK;
+}
+
+moe_status moe_block_forward_noalloc(const void *x, int32_t x_dtype, int64_t T, const moe_block *b, void *y,
+                                     int32_t y_dtype, int32_t *topk_idx, float *topk_w, void *stream) {
+  g_err[0] = 0;
+  // the workspace this call needs (validates every argument; launches nothing)
+  size_t need = 0;
+  TRY(moe_block_forward(x, x_dtype, T, b, y, y_dtype, topk_idx, topk_w, nullptr, &need, nullptr));
+  CHECK(need <= (size_t)MOE_NOALLOC_SCRATCH_BYTES, MOE_ERR_WORKSPACE,
+        "moe_block_forward_noalloc: %lld tokens need %zu bytes of scratch, above its fixed %u bytes "
+        "(use moe_block_forward with a workspace)", (long long)T, need, (unsigned)MOE_NOALLOC_SCRATCH_BYTES);
+  if (T == 0) return MOE_OK;
+  CHECK(x && y, MOE_ERR_ARG, "x and y must be non-NULL");
+  int dev = -1, sdev = -1;
+  HIPCHK(hipGetDevice(&dev));
+  HIPCHK(hipStreamGetDevice((hipStream_t)stream, &sdev));
+  CHECK(sdev == dev, MOE_ERR_ARG, "the stream belongs to device %d, the calling thread's current device is %d",
+        sdev, dev);
+  void *ws = nullptr;
+  TRY(scratch_on(dev, &ws));
+  size_t have = MOE_NOALLOC_SCRATCH_BYTES;
+  return moe_block_forward(x, x_dtype, T, b, y, y_dtype, topk_idx, topk_w, ws, &have, stream);
 }
 
 }  // extern "C"

@@ -30,7 +30,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     names = header_functions()
     assert set(names) == {"moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward", "moe_pack_weights",
-                          "moe_status_str",
+                          "moe_block_forward_noalloc", "moe_status_str",
                           "moe_last_error", "moe_abi_version", "moe_timing_enable", "moe_timing_read"}
     L = moe.lib()
     for n in names:
@@ -290,3 +290,22 @@ def test_pack_rejects_bad_arguments(layers):
     assert L.moe_pack_weights(ctypes.byref(g.c), None, base, ctypes.byref(n), None) == moe.MOE_ERR_WORKSPACE
     n = ctypes.c_size_t(need)
     assert L.moe_pack_weights(ctypes.byref(g.c), None, base + 8, ctypes.byref(n), None) == moe.MOE_ERR_ARG
+
+
+def test_noalloc_rejects_more_than_its_scratch(layers):
+    """moe_block_forward_noalloc: a call whose workspace would exceed the fixed scratch
+    array fails with MOE_ERR_WORKSPACE before any HIP call (no pointers needed); a
+    call that fits passes that check (and then needs its tensors: MOE_ERR_ARG)."""
+    L = moe.lib()
+    b = layers["c2"]
+    d = bdesc(b)
+    for T, want in ((1 << 16, moe.MOE_ERR_WORKSPACE), (b.T, moe.MOE_ERR_ARG)):
+        need = ctypes.c_size_t(0)
+        assert L.moe_block_forward(None, moe.MOE_BF16, T, ctypes.byref(d.c), None, moe.MOE_F32, None, None, None,
+                                   ctypes.byref(need), None) == moe.MOE_OK
+        assert (need.value > moe.NOALLOC_SCRATCH_BYTES) == (want == moe.MOE_ERR_WORKSPACE)
+        st = L.moe_block_forward_noalloc(None, moe.MOE_BF16, T, ctypes.byref(d.c), None, moe.MOE_F32, None, None,
+                                         None)
+        assert st == want, L.moe_last_error()
+        if want == moe.MOE_ERR_WORKSPACE:
+            assert "scratch" in L.moe_last_error().decode()
