@@ -229,8 +229,13 @@ def measure(wl, steps, warmup, gu_every, copies_arg=0, tokens=0):
     ws = torch.empty(moe.block_ws_bytes(b.x, desc0, with_topk=True) + 256, dtype=torch.uint8, device=dev)
     off = (-ws.data_ptr()) % 256
     ws = ws[off:]
+    # which launch carries the experts: the one-launch decode path or the grouped gate/up GEMM
+    moe.moe_timing_enable(moe.TIMING_FUSED)
     moe.moe_block_forward(b.x, desc0, y, idx, w, ws=ws)
+    moe.moe_timing_enable(0)
     torch.cuda.synchronize()
+    fused = moe.moe_timing_read()[0] > 0
+    kind = moe.TIMING_FUSED if fused else moe.TIMING_GATEUP
     hit = sorted(set(idx.flatten().tolist()))
     wm = work_model(b, hit)
     # weight copies so that the working set rotates through more than 1 GiB
@@ -248,7 +253,7 @@ def measure(wl, steps, warmup, gu_every, copies_arg=0, tokens=0):
     torch.cuda.synchronize()
     log(f"{wl}: warmup {warmup} done")
 
-    moe.moe_timing_enable(moe.TIMING_GATEUP)  # creates the event pool outside the timed region
+    moe.moe_timing_enable(kind)  # creates the event pool outside the timed region
     moe.moe_timing_enable(0)
     moe.moe_timing_read()
     t0 = torch.cuda.Event(enable_timing=True)
@@ -259,7 +264,7 @@ def measure(wl, steps, warmup, gu_every, copies_arg=0, tokens=0):
     for i in range(steps):
         timed = i % every == 0
         if timed:
-            moe.moe_timing_enable(moe.TIMING_GATEUP)
+            moe.moe_timing_enable(kind)
         step(i)
         if timed:
             moe.moe_timing_enable(0)
@@ -267,7 +272,8 @@ def measure(wl, steps, warmup, gu_every, copies_arg=0, tokens=0):
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     n_gu, gu_ms = moe.moe_timing_read()
-    log(f"{wl}: timed {steps} steps: {total_ms:.3f} ms; gate/up launches {n_gu}, {gu_ms:.3f} ms")
+    log(f"{wl}: timed {steps} steps: {total_ms:.3f} ms; {'fused' if fused else 'gate/up'} launches {n_gu}, "
+        f"{gu_ms:.3f} ms")
 
     # per-step distribution: the same steps again, an event between consecutive steps
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
@@ -280,18 +286,39 @@ def measure(wl, steps, warmup, gu_every, copies_arg=0, tokens=0):
     per_step = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps)]
 
     # the down launch's average, timed on its own run of steps (outside both timed regions)
-    moe.moe_timing_enable(moe.TIMING_DOWN)
-    for i in range(min(steps, 20)):
-        step(i)
-    moe.moe_timing_enable(0)
-    n_dn, dn_ms = moe.moe_timing_read()
+    n_dn, dn_ms = 0, 0.0
+    if not fused:
+        moe.moe_timing_enable(moe.TIMING_DOWN)
+        for i in range(min(steps, 20)):
+            step(i)
+        moe.moe_timing_enable(0)
+        n_dn, dn_ms = moe.moe_timing_read()
     return {"b": b, "desc": desc0, "wm": wm, "copies": copies, "total_ms": total_ms, "n_gu": n_gu, "gu_ms": gu_ms,
-            "per_step_us": per_step, "n_dn": n_dn, "dn_ms": dn_ms}
+            "per_step_us": per_step, "n_dn": n_dn, "dn_ms": dn_ms, "fused": fused}
 
 
 def roofline_of(wl, r, hbm_bound, dev, with_peak=True):
     wm = r["wm"]
     gu_avg_s = (r["gu_ms"] / max(r["n_gu"], 1)) / 1e3
+    if r["fused"]:
+        # one launch: gate/up + SwiGLU and down; its algorithmic bytes are both GEMMs' (the h
+        # rows it hands from one to the other count once as written and once as read)
+        fb = wm["gu_bytes"] + wm["dn_bytes"]
+        achieved = fb / gu_avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "scope": "kernel only: the one-launch decode experts (gate/up + SwiGLU and down, routed and "
+                         "shared)"}
+        if with_peak:
+            mp = measured_peak(True, dev)
+            roof["measured_peak"] = mp
+            roof["frac_of_measured"] = round(roof["achieved"] / mp["value"], 4)
+        roof["traffic"] = measured_traffic(wl)
+        roof["kernel"] = "decode_fused (gate/up + down)"
+        roof["kernel_avg_us"] = round(gu_avg_s * 1e6, 2)
+        roof["algorithmic_bytes_per_launch"] = fb
+        roof["algorithmic_flops_per_launch"] = wm["gu_flops"] + wm["dn_flops"]
+        return roof
     dn_avg_s = (r["dn_ms"] / max(r["n_dn"], 1)) / 1e3
     if hbm_bound:
         achieved = wm["gu_bytes"] / gu_avg_s / 1e9
@@ -354,6 +381,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="c2 only: skip the 4096-token prefill record of the same layer")
+    ap.add_argument("--separate-decode-launches", action="store_true",
+                    help="run decode-sized batches with separate gate/up, down and combine launches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (the reference kernel that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -376,6 +405,9 @@ def main():
 
     dev = "cuda:0"
     wl = args.workload
+    if args.separate_decode_launches:
+        import sparse_mixture_experts_bias_amd as moe
+        moe.moe_set_decode_fusion(False)
     r = measure(wl, args.steps, args.warmup, args.gu_every, args.copies, args.tokens)
     b = r["b"]
     hbm_bound = wl in ("c1", "c2", "c5")

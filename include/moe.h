@@ -224,9 +224,12 @@ MOE_API moe_status moe_experts_forward(const void *z, int32_t z_dtype, int64_t T
  * After the call (once the stream has reached it) the workspace begins with the
  * routing state the experts ran on, int32 arrays at 256-byte aligned offsets, in
  * this order: counts [E], offsets [E+1], sorted_slot [T*K], slot_pos [T*K] (as
- * moe_permute defines them; each array starts at the previous one's offset plus
- * its size rounded up to a multiple of 256 bytes).  The rest of the workspace is
- * unspecified.
+ * moe_permute defines them), then status [1]; each array starts at the previous
+ * one's offset plus its size rounded up to a multiple of 256 bytes.  status is 0,
+ * or 1 if a bounded wait between workgroups of the one-launch decode path (see
+ * moe_set_decode_fusion) gave up, in which case that call's outputs are invalid
+ * (a wait gives up only if the device could not hold the launch's workgroups at
+ * once).  The rest of the workspace is unspecified.
  * Source: all of the above; the blend of mlxcel PR #1044 point 2; the latent flow
  * of latent_moe.rs.
  */
@@ -256,10 +259,25 @@ MOE_API moe_status moe_block_forward_noalloc(const void *x, int32_t x_dtype, int
                                              void *stream);
 
 /*
+ * moe_set_decode_fusion - choose how moe_block_forward runs the experts of a decode-sized
+ * batch (at most 64 tokens, top_k <= 16, bf16 activations and intermediates, 4-bit routed
+ * experts, a shared expert of the same format or none, no latent projection):
+ *   enabled = 1 (default): gate/up and the down projection of every slot (and of the shared
+ *                expert) in one launch, then the weighted combine (4 launches per block);
+ *   enabled = 0: separate gate/up, down and combine launches (5 in all).
+ * Both give the same bits: the same arithmetic in the same order (unlike the pages'
+ * fused MoE decode kernel, whose output was not byte-identical to the unfused path;
+ * this switch mirrors theirs: mlxcel PR #1044, "Validation", MLXCEL_FUSED_MOE).
+ * Process-wide, not thread-safe; enabled must be 0 or 1 (else MOE_ERR_ARG).
+ */
+MOE_API moe_status moe_set_decode_fusion(int32_t enabled);
+
+/*
  * Live timing of one kernel class with HIP events, for measurement tools.
  *   kind: 0 off; 1 grouped gate/up GEMM; 2 grouped down GEMM; 3 router logits;
  *         4 scores + top-k; 5 permutation; 6 combine; 7 plain GEMMs (latent
- *         projections, a shared expert run outside the grouped launches).
+ *         projections, a shared expert run outside the grouped launches); 8 the
+ *         one-launch decode experts (gate/up + down).
  * While a kind is on, every launch of that class is bracketed by hipEventRecord on
  * the stream it is launched on (a pool of 8192 event pairs, created on the first
  * call with kind != 0; launches past a full pool are not timed).  moe_timing_read

@@ -28,12 +28,13 @@ SHARED_CODES = {"none": MOE_SHARED_NONE, "add": MOE_SHARED_ADD, "blend": MOE_SHA
 SCORING_CODES = {"sigmoid": MOE_SIGMOID, "softmax": MOE_SOFTMAX}
 
 EXPORTS = ("moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward", "moe_block_forward_noalloc",
-           "moe_pack_weights", "moe_timing_enable", "moe_timing_read", "moe_status_str", "moe_last_error",
-           "moe_abi_version")
+           "moe_pack_weights", "moe_set_decode_fusion", "moe_timing_enable", "moe_timing_read", "moe_status_str",
+           "moe_last_error", "moe_abi_version")
 NOALLOC_SCRATCH_BYTES = 32 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 
 # kernel classes of moe_timing_enable
-TIMING_GATEUP, TIMING_DOWN, TIMING_ROUTER, TIMING_TOPK, TIMING_PERM, TIMING_COMBINE, TIMING_PLAIN = range(1, 8)
+TIMING_GATEUP, TIMING_DOWN, TIMING_ROUTER, TIMING_TOPK, TIMING_PERM, TIMING_COMBINE, TIMING_PLAIN, TIMING_FUSED = \
+    range(1, 9)
 
 
 class MoeError(RuntimeError):
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_set_decode_fusion.argtypes = [i32]
+        L.moe_set_decode_fusion.restype = ctypes.c_int32
         L.moe_timing_enable.argtypes = [i32]
         L.moe_timing_enable.restype = ctypes.c_int32
         L.moe_timing_read.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]
@@ -521,6 +524,18 @@ def routing_state(ws: torch.Tensor, T: int, K: int, E: int):
     o_sp = o_ss + al(4 * T * K)
     v = lambda off, n: ws[off:off + 4 * n].view(torch.int32)
     return v(o_counts, E), v(o_offsets, E + 1), v(o_ss, T * K), v(o_sp, T * K)
+
+
+def call_status(ws: torch.Tensor, T: int, K: int, E: int) -> torch.Tensor:
+    """The status word after the routing state (0: every bounded wait completed)."""
+    al = lambda n: (n + 255) // 256 * 256
+    off = al(4 * E) + al(4 * (E + 1)) + 2 * al(4 * T * K)
+    return ws[off:off + 4].view(torch.int32)
+
+
+def moe_set_decode_fusion(enabled: bool):
+    """One launch for the experts of a decode-sized batch (default) or separate launches."""
+    _check(lib().moe_set_decode_fusion(1 if enabled else 0))
 
 
 def moe_timing_enable(kind: int):

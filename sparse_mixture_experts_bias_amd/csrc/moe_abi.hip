@@ -216,10 +216,14 @@ WMat wmat(const moe_linear &L, bool gateup = false) {
 
 int wf_of(const moe_linear &L) { return L.fmt == MOE_W_DENSE ? WF_DENSE : (L.fmt == MOE_W_AFFINE4 ? WF_AFFINE4 : WF_MXFP4); }
 
+// moe_set_decode_fusion: the one-launch decode experts path (on by default)
+int g_decode_fusion = 1;
+
 // ---------------------------------------------------------------------------
 // optional live timing of one kernel class (moe_timing_enable / moe_timing_read)
 // ---------------------------------------------------------------------------
-enum { TK_OFF = 0, TK_GATEUP = 1, TK_DOWN = 2, TK_ROUTER = 3, TK_TOPK = 4, TK_PERM = 5, TK_COMBINE = 6, TK_PLAIN = 7 };
+enum { TK_OFF = 0, TK_GATEUP = 1, TK_DOWN = 2, TK_ROUTER = 3, TK_TOPK = 4, TK_PERM = 5, TK_COMBINE = 6, TK_PLAIN = 7,
+       TK_FUSED = 8 };
 constexpr int kTimingPairs = 8192;
 struct Timing {
   int kind = TK_OFF;
@@ -281,7 +285,7 @@ int router_slices(int x_dt, int T, int H, int E, bool split) {
 // the selection.
 moe_status launch_router(const void *x, int x_dt, int T, int H, const moe_router *r, const void *coef_w,
                          const float *coef_b, float *logits, float *clog, hipStream_t s, int *zero = nullptr,
-                         bool split = false) {
+                         bool split = false, int zero_n = 1) {
   const int E = r->num_experts;
   const int R = E + (coef_w ? 2 : 0);
   Timed tm(TK_ROUTER, s);
@@ -290,16 +294,16 @@ moe_status launch_router(const void *x, int x_dt, int T, int H, const moe_router
     const int S = (H + ks - 1) / ks;
     hipLaunchKernelGGL(router_gemm_bf16, dim3((T + 127) / 128, (R + 63) / 64, S), dim3(256), 0, s,
                        (const uint16_t *)x, (const uint16_t *)r->w, r->logit_bias, logits, T, H, E,
-                       (const uint16_t *)coef_w, coef_b, clog, zero, ks);
+                       (const uint16_t *)coef_w, coef_b, clog, zero, zero_n, ks);
   } else if (x_dt == MOE_BF16) {
     hipLaunchKernelGGL(router_logits_bf16, dim3((T + 15) / 16, (R + 15) / 16), dim3(512), 0, s, (const uint16_t *)x,
                        (const uint16_t *)r->w, r->logit_bias, logits, T, H, E, (const uint16_t *)coef_w, coef_b,
-                       clog, zero);
+                       clog, zero, zero_n);
   } else {
     const int64_t n = (int64_t)T * R;
     hipLaunchKernelGGL(router_logits_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float *)x,
                        (const float *)r->w, r->logit_bias, logits, T, H, E, (const float *)coef_w, coef_b, clog,
-                       zero);
+                       zero, zero_n);
   }
   HIPCHK(hipGetLastError());
   return MOE_OK;
@@ -467,28 +471,36 @@ SegSet segset(AOp A, const moe_linear &w0, const moe_linear *w1, float limit, bo
 
 // routed experts (m-tiles of 16*mb rows from the tile list) + optional segment-1 rows
 // [sh_row0, sh_row0 + sh_rows) (the shared expert) in the same launch
-moe_status run_gemm(int adt, const moe_linear &fmt_of, bool gateup, int odt, int mb, const SegSet &routed,
-                    const SegSet *shared, int sh_row0, int sh_rows, const int4 *tiles, const int *tile_count,
-                    int ntiles_alloc, int TK, int E, void *out, int64_t ldo, const float *resid, int64_t ldr,
-                    hipStream_t s) {
-  const int mt = 16 * mb;
+GemmParams gemm_params(bool gateup, int mb, const SegSet &routed, const SegSet *shared, int sh_row0, int sh_rows,
+                       const int4 *tiles, const int *tile_count, int ntiles_alloc, int E, void *out, int64_t ldo,
+                       const float *resid, int64_t ldr) {
   GemmParams p;
   memset(&p, 0, sizeof p);
   p.seg[0] = routed;
   p.seg[0].nblk = col_blocks(routed, gateup, mb);
   p.seg[1] = shared ? *shared : routed;
   p.seg[1].nblk = shared ? col_blocks(*shared, gateup, mb) : 0;
-  if (!shared) sh_rows = 0;
   p.tiles = tiles;
   p.tile_count = tile_count;
   p.max_tiles = ntiles_alloc;
   p.sh_row0 = sh_row0;
-  p.sh_rows = sh_rows;
+  p.sh_rows = shared ? sh_rows : 0;
   p.E = E;
   p.out = out;
   p.ldo = ldo;
   p.resid = resid;
   p.ldr = ldr;
+  return p;
+}
+
+moe_status run_gemm(int adt, const moe_linear &fmt_of, bool gateup, int odt, int mb, const SegSet &routed,
+                    const SegSet *shared, int sh_row0, int sh_rows, const int4 *tiles, const int *tile_count,
+                    int ntiles_alloc, int TK, int E, void *out, int64_t ldo, const float *resid, int64_t ldr,
+                    hipStream_t s) {
+  const int mt = 16 * mb;
+  const GemmParams p = gemm_params(gateup, mb, routed, shared, sh_row0, sh_rows, tiles, tile_count, ntiles_alloc, E,
+                                   out, ldo, resid, ldr);
+  if (!shared) sh_rows = 0;
   const int units_ub = routed_tiles_ub(TK, E, mt) * p.seg[0].nblk + ((sh_rows + mt - 1) / mt) * p.seg[1].nblk;
   int kmb = kernel_mb(mb, gateup, fmt_of, shared && shared->K > routed.K ? shared->K : routed.K);
   if (kmb == MB_WS && !offsets_fit(p, INT32_MAX)) kmb = 1;
@@ -652,9 +664,16 @@ moe_status moe_pack_weights(const moe_linear *a, const moe_linear *b, void *out,
   return MOE_OK;
 }
 
+moe_status moe_set_decode_fusion(int32_t enabled) {
+  g_err[0] = 0;
+  CHECK(enabled == 0 || enabled == 1, MOE_ERR_ARG, "enabled must be 0 or 1 (got %d)", enabled);
+  g_decode_fusion = enabled;
+  return MOE_OK;
+}
+
 moe_status moe_timing_enable(int32_t kind) {
   g_err[0] = 0;
-  CHECK(kind >= TK_OFF && kind <= TK_PLAIN, MOE_ERR_ARG, "timing kind %d out of range", kind);
+  CHECK(kind >= TK_OFF && kind <= TK_FUSED, MOE_ERR_ARG, "timing kind %d out of range", kind);
   if (kind != TK_OFF && !g_timing.created) {
     for (int i = 0; i < 2 * kTimingPairs; ++i) HIPCHK(hipEventCreate(&g_timing.ev[i]));
     g_timing.created = true;
@@ -879,22 +898,33 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   Plan pl;
   const bool blend = b->shared_mode == MOE_SHARED_BLEND;
   const int rs = (T > INT32_MAX) ? 1 : router_slices(x_dtype, (int)T, H, E, true);
-  // the routing state first, at the offsets include/moe.h documents
+  // the routing state and the status word first, at the offsets include/moe.h documents;
+  // the status word heads the counter block (cleared by the router launch of every call)
+  const int ntile = max_tiles(TK, E);
+  const int mb = mb_for_routing(TK, E);
+  const bool small = T <= MOE_ROUTE_SMALL_T && topk_slots(E, K) > 0;
+  // the one-launch decode experts path: bf16 activations and intermediates, decode-sized
+  // segments, 4-bit routed experts (and a shared expert of the same format, or none)
+  const bool fused = g_decode_fusion && mf && !latent && small && mb == 1 && x_dtype == MOE_BF16 &&
+                     inter == MOE_BF16 && b->experts.gate.fmt != MOE_W_DENSE && (!has_shared || fuse_shared) &&
+                     !router_tiled(x_dtype, (int)T, H, E);
+  const int ns_f = (fused && has_shared) ? (int)((T + 15) / 16) : 0;
+  const int n_tile_cnt = ns_f + ntile;
+  // [0] status, [1] route_decode's counter, then the fused launch's counters (one per 128 bytes)
+  const int n_cnt = fused ? kCntStride * (1 + n_tile_cnt) : 2;
   const size_t o_counts = pl.take((size_t)E * 4);
   const size_t o_offsets = pl.take((size_t)(E + 1) * 4);
   const size_t o_ss = pl.take((size_t)TK * 4);
   const size_t o_sp = pl.take((size_t)TK * 4);
+  const size_t o_cnt = pl.take((size_t)n_cnt * 4);
   const size_t o_logits = pl.take((size_t)rs * T * E * 4);
   const size_t o_coef = pl.take((size_t)T * 2 * 4);
   const size_t o_clog = pl.take((size_t)rs * T * 2 * 4);
   const size_t o_idx = topk_idx ? 0 : pl.take((size_t)TK * 4);
   const size_t o_w = topk_w ? 0 : pl.take((size_t)TK * 4);
   const size_t o_chunk = pl.take(perm_ws_bytes(T, E));
-  const int ntile = max_tiles(TK, E);
-  const int mb = mb_for_routing(TK, E);
   const size_t o_tiles = pl.take((size_t)ntile * 16);
   const size_t o_tc = pl.take(16);
-  const size_t o_done = pl.take(16);
   const size_t o_z = latent ? pl.take((size_t)T * D * isz) : 0;
   const size_t o_h = pl.take((size_t)(TK + Tsh) * ldh * isz);
   const size_t o_o = pl.take((size_t)(TK + Tsh) * D * isz);
@@ -922,12 +952,12 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   void *o = at<char>(ws, o_o);
   const int Ti = (int)T;
 
-  // 1. router + selection (+ blend coefficients)
+  // 1. router + selection (+ blend coefficients); the router launch clears the counters
   float *clog = at<float>(ws, o_clog);
-  const bool small = Ti <= MOE_ROUTE_SMALL_T && topk_slots(E, K) > 0;
-  int *done = at<int>(ws, o_done);
+  int *cnt = at<int>(ws, o_cnt);
+  int *done = cnt + 1;
   TRY(launch_router(x, x_dtype, Ti, H, &b->router, blend ? b->coef_w : nullptr, blend ? b->coef_b : nullptr, logits,
-                    clog, s, small ? done : nullptr, true));
+                    clog, s, cnt, true, n_cnt));
   const TopkArgs ta = topk_args(Ti, &b->router, logits, idx, wts, blend ? clog : nullptr, coef, rs);
   // 2. permutation + tile list (for a few tokens in the same workgroup as the selection)
   if (small) {
@@ -984,6 +1014,39 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
     }
     const int mode = !has_shared ? 0 : (blend ? 3 : 2);
     TRY(combine(MOE_F32, y_dtype, o, D, sp, wts, K, TK, Ti, D, y, H, coef, nullptr, 0.f, mode, s));
+    return MOE_OK;
+  }
+
+  if (fused) {
+    // 3-4. gate/up and down of every slot (and the shared expert) in one persistent launch
+    const SegSet gu = segset(aop(x, H, ss, K, 0, Ti), b->experts.gate, &b->experts.up, b->experts.swiglu_limit, true);
+    SegSet gus, dns;
+    if (has_shared) {
+      gus = segset(aop(x, H, nullptr, 1, TK, Ti), b->shared.gate, &b->shared.up, b->shared.swiglu_limit, true);
+      dns = segset(aop(h, ldh, nullptr, 1, 0, TK + Tsh), b->shared.down, nullptr, 0.f, false);
+    }
+    const SegSet dn = segset(aop(h, ldh, nullptr, 1, 0, TK + Tsh), b->experts.down, nullptr, 0.f, false);
+    FusedParams fp;
+    memset(&fp, 0, sizeof fp);
+    // o: the per-slot outputs in token order (slot t*K + j; the shared expert's rows after)
+    fp.gu = gemm_params(true, 1, gu, has_shared ? &gus : nullptr, TK, Tsh, tiles, tc, ntile, E, h, ldh, nullptr, 0);
+    fp.dn = gemm_params(false, 1, dn, has_shared ? &dns : nullptr, TK, Tsh, tiles, tc, ntile, E, o, D, nullptr, 0);
+    CHECK(offsets_fit(fp.gu, INT32_MAX) && offsets_fit(fp.dn, INT32_MAX), MOE_ERR_SHAPE,
+          "operands of over 2 GiB on the decode path");
+    fp.Dout = D;
+    fp.cnt = cnt + kCntStride;
+    fp.n_tile_cnt = n_tile_cnt;
+    fp.status = cnt;
+    const int tub = routed_tiles_ub(TK, E, 16);
+    const int units_ub = tub * (fp.gu.seg[0].nblk + fp.dn.seg[0].nblk) + ns_f * (fp.gu.seg[1].nblk + fp.dn.seg[1].nblk);
+    {
+      Timed tm(TK_FUSED, s, true);
+      HIPCHK(launch_decode_fused(wf_of(b->experts.gate), b->experts.gate.group_size, DT_BF16, fp, units_ub, s,
+                                 tm.start(), tm.stop()));
+    }
+    // 5. weighted combine + shared add/blend over the token-ordered rows
+    const int mode = !has_shared ? 0 : (blend ? 3 : 2);
+    TRY(combine(inter, y_dtype, o, D, nullptr, wts, K, TK, Ti, H, y, H, coef, nullptr, 0.f, mode, s));
     return MOE_OK;
   }
 

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(CMB_T) void combine_kernel(const CombineArgs a) {
   __shared__ float red[CMB_T / 64];
   const int t = blockIdx.x, tid = threadIdx.x;
   if (tid < a.K) {
-    pos[tid] = a.slot_pos[(int64_t)t * a.K + tid];
+    pos[tid] = a.slot_pos ? a.slot_pos[(int64_t)t * a.K + tid] : t * a.K + tid;
     wt[tid] = a.topk_w[(int64_t)t * a.K + tid];
   }
   __syncthreads();
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(CMB_T) void combine_kernel(const CombineArgs a) {
       } else {
         const float c0 = a.coef[2 * t], c1 = a.coef[2 * t + 1];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = c0 * v[q] + c1 * s[q];
+        for (int q = 0; q < 8; ++q) v[q] = fmaf(c0, v[q], c1 * s[q]);
       }
     }
     store8<YDT>(a.y, (int64_t)t * a.ldy + c, v);

@@ -1,0 +1,490 @@
+// moe_decode.hip - the routed experts of a decode-sized batch in one persistent launch:
+// gate/up + SwiGLU and the down projection of every slot, plus the shared expert
+// (libmir-metal's execute hands the gate/up kernel the routing indices and the clamp limit,
+// and the down kernel the same indices; the weighted combine follows as its own short launch,
+// moe_combine.hip).
+//
+// Work units are those of the loader-wave decode GEMM (moe_gemm_ws.hip): (m-tile of up to
+// 16 rows of one segment, 4 row blocks of the packed stream), 4-bit weights, loader waves
+// streaming records HBM -> LDS, compute waves folding each quantisation group exactly.  The
+// unit sequence of a workgroup runs over the gate/up units first, then the down units, so
+// the down weights stream while gate/up work is still finishing elsewhere, and the two
+// projections pay one ramp and one tail instead of two.  The per-slot outputs o are written
+// in token order (row t*K + j for slot j of token t, row T*K + t for the shared expert), so
+// the combine reads each token's rows contiguously.
+//
+// Hand-over from gate/up to down between workgroups (which sit on different XCDs, each with
+// its own L2): a compute wave stores its h outputs with device-scope cache policy (sc1: the
+// instructions the compiler emits for agent-scope relaxed atomic stores, coherent across the
+// XCDs; pairs of 16-bit values as 32-bit stores), waits until they have completed (vmcnt 0),
+// then increments its m-tile's counter; the loader of a down unit waits until the counter of
+// the unit's m-tile shows every gate/up wave of that m-tile (4 per unit), then loads the h
+// rows with device-scope direct loads.  No L2 write-back or invalidate is needed (an
+// agent-scope release fence per wave and unit, which writes back the whole L2 of the XCD,
+// made the launch several times slower).  Every wait is bounded: a wait that gives up (only
+// possible if the grid were not co-resident) sets the status word and lets the waves run to
+// their end.  The counters are cleared by the router launch that precedes this one.
+#include <hip/hip_ext.h>
+
+#include "moe_ws.h"
+
+namespace {
+
+// A device-scope poll goes to memory (it must not be served by a stale L2 line), so polls are
+// spaced out (~0.25 us: s_sleep 10 is 640 clocks) and every counter has a 128-byte line of its
+// own: polling a shared line back to back loaded one memory channel enough to slow the whole
+// launch several times over.
+constexpr int kSpinLimit = 1 << 19;  // polls of a counter, ~0.15 s in all
+constexpr int kSC1 = 16;             // cache-policy bit of device-scope (sc1) buffer accesses
+
+// waits until *c >= target (device-scope loads of the counter by one lane)
+MOE_DEV bool wait_count(const int *c, int target, int *status, int lane) {
+  for (int it = 0; it < kSpinLimit; ++it) {
+    int v = 0;
+    if (lane == 0) v = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__builtin_amdgcn_readfirstlane(v) >= target) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(10);
+  }
+  if (lane == 0) __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return false;
+}
+
+// the calling wave's stores have completed (device-scope stores: visible to every XCD),
+// then lane 0 adds 1 to *c; returns the value before the add (wave-uniform)
+MOE_DEV int publish(int *c, int lane) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  wait_vmcnt<0>();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  int old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_amdgcn_readfirstlane(old);
+}
+
+}  // namespace
+
+template <int AT, int WF, int GQ, int IT>
+__global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
+  using C = WsCfg<WF, GQ>;
+  constexpr bool AFF = C::AFF;
+  constexpr int MT = 16, KC = C::KC, UE = C::UE, SPU = C::SPU, QE = C::QE, LPU = C::LPU, NU = C::NU;
+  constexpr int RB = C::RB, SW = C::SW, STAGE = C::STAGE, NBUF = C::NBUF, NDMA = C::NDMA;
+  constexpr float MAGIC = AT == DT_BF16 ? 128.0f : 1024.0f;
+  __shared__ __attribute__((aligned(16))) char smem[NBUF * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // ---- the unit list: [gate/up: shared m-tiles, routed m-tiles][down: shared, routed]
+  const int nbg0 = p.gu.seg[0].nblk, nbg1 = p.gu.seg[1].nblk, nbd0 = p.dn.seg[0].nblk, nbd1 = p.dn.seg[1].nblk;
+  const int sh_rows = p.gu.sh_rows, sh_row0 = p.gu.sh_row0, max_tiles = p.gu.max_tiles;
+  const int4 *const tiles = p.gu.tiles;
+  const int *const tcount = p.gu.tile_count;
+  asm volatile("" ::"s"(nbg0), "s"(nbg1), "s"(nbd0), "s"(nbd1), "s"(sh_rows), "s"(sh_row0), "s"(max_tiles),
+               "s"(tiles), "s"(tcount));
+  const int ns = nbg1 > 0 ? (sh_rows + MT - 1) / MT : 0;  // shared m-tiles
+  const int nr = min(load_uniform_int(tcount), max_tiles);  // routed m-tiles
+  const int Ug_s = ns * nbg1, Ug = Ug_s + nr * nbg0;
+  const int Ud_s = ns * nbd1, U = Ug + Ud_s + nr * nbd0;
+  const int G = gridDim.x, g = blockIdx.x;
+  // counters, one per 128-byte line: gate/up waves done per m-tile [ns + max_tiles]
+  int *const tile_cnt = p.cnt;
+
+  struct Unit {
+    bool dn, sh;
+    int e, r0, nr, nb, tile;
+  };
+  auto unit_at = [&](int u) {
+    Unit x;
+    x.dn = u >= Ug;
+    int v = x.dn ? u - Ug : u;
+    const int us = x.dn ? Ud_s : Ug_s;
+    x.sh = v < us;
+    if (x.sh) {
+      const int nb1 = max(x.dn ? nbd1 : nbg1, 1);
+      const int ti = v / nb1;
+      x.nb = v - ti * nb1;
+      x.e = 0;
+      x.r0 = sh_row0 + ti * MT;
+      x.nr = min(MT, sh_rows - ti * MT);
+      x.tile = ti;
+    } else {
+      v -= us;
+      const int nb0 = max(x.dn ? nbd0 : nbg0, 1);
+      const int ti = v / nb0;
+      x.nb = v - ti * nb0;
+      const int4 t = load_uniform_int4(tiles + ti);
+      x.e = t.x;
+      x.r0 = t.y;
+      x.nr = t.z;
+      x.tile = ns + ti;
+    }
+    return x;
+  };
+  // a field of the unit's segment, selected field by field (a selected struct would go to scratch)
+#define SEG(x, f) \
+  ((x).dn ? ((x).sh ? p.dn.seg[1].f : p.dn.seg[0].f) : ((x).sh ? p.gu.seg[1].f : p.gu.seg[0].f))
+  auto nch_of = [&](const Unit &x) { return (SEG(x, K) + KC - 1) / KC; };
+  auto nch_u = [&](int u) {  // the same from the unit index alone (no tile read)
+    const bool dn = u >= Ug;
+    const int v = dn ? u - Ug : u;
+    const bool sh = v < (dn ? Ud_s : Ug_s);
+    const int Kd = dn ? (sh ? p.dn.seg[1].K : p.dn.seg[0].K) : (sh ? p.gu.seg[1].K : p.gu.seg[0].K);
+    return (Kd + KC - 1) / KC;
+  };
+  // gate/up waves that write an m-tile's h rows: 4 per column block of its segment
+  auto tile_target = [&](const Unit &x) { return 4 * (x.sh ? nbg1 : nbg0); };
+
+  if (g >= U) return;
+
+  if (wave >= 4) {
+    // ---------------- loader waves: row block lw's records, activation rows 4 lw .. 4 lw + 3
+    const int lw = wave - 4;
+    __amdgpu_buffer_rsrc_t wrs, ars;
+    uint32_t wvo = 0, svo = 0, avo[2] = {0u, 0u};
+    bool aon[2] = {true, true};
+    int cu = g, cc = 0, cn = 0;
+    Unit cur;
+    bool a_pending = false;  // the current unit's activation rows are not yet addressed
+    auto enter_w = [&](const Unit &x) {
+      cn = nch_of(x);
+      const char *pk = SEG(x, w0.pk);
+      const int64_t pk_mat = SEG(x, w0.pk_mat);
+      const int pk_nblk = SEG(x, w0.pk_nblk), pk_nch = SEG(x, w0.pk_nch);
+      wrs = __builtin_amdgcn_make_buffer_rsrc((void *)(pk + (int64_t)x.e * pk_mat), (short)0, (int)pk_mat,
+                                              0x00020000);
+      const uint32_t rbo = (uint32_t)min(x.nb * 4 + lw, pk_nblk - 1) * (uint32_t)(pk_nch * RB);
+      wvo = rbo + lane * 16;
+      svo = rbo + 4096 + lane * (C::SB == 1024 ? 16 : 4);
+    };
+    // the unit's activation rows: gathered x rows (gate/up), or its h rows once every gate/up
+    // wave of its m-tile has stored them (down)
+    auto enter_a = [&](const Unit &x) {
+      if (x.dn) wait_count(tile_cnt + x.tile * kCntStride, tile_target(x), p.status, lane);
+      const void *a = SEG(x, A.a);
+      const int64_t lda = SEG(x, A.lda), arows = SEG(x, A.rows);
+      ars = __builtin_amdgcn_make_buffer_rsrc((void *)a, (short)0, (int)(arows * lda * 2), 0x00020000);
+      const int32_t *gat = SEG(x, A.gather);
+      const int gdiv = SEG(x, A.gdiv), rsub = SEG(x, A.row_sub);
+      uint32_t ro[4];
+      int gi[4];
+      if (gat) {
+        const int *g0 = gat + x.r0;
+        load_uniform_ints4(g0 + min(4 * lw, x.nr - 1), g0 + min(4 * lw + 1, x.nr - 1), g0 + min(4 * lw + 2, x.nr - 1),
+                           g0 + min(4 * lw + 3, x.nr - 1), gi);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int m = min(4 * lw + k, x.nr - 1);
+        const int arow = gat ? gi[k] / gdiv : x.r0 + m - rsub;
+        ro[k] = (uint32_t)arow * (uint32_t)lda * 2u;
+      }
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        aon[n] = 4 * lw + 2 * n < x.nr;
+        const int r = 4 * lw + 2 * n + (lane >> 5);
+        avo[n] = (lane < 32 ? ro[2 * n] : ro[2 * n + 1]) + (uint32_t)(((lane & 31) ^ (r & 15)) << 4);
+      }
+    };
+    // one stage: the weights first, then (after a down unit's wait) the activation rows
+    auto issue = [&](int b) {
+      char *base = smem + b * STAGE;
+      const int so = cc * RB;
+      char *wl = base + lw * RB;
+      WS_DMA(16, 0, wrs, wl, wvo, so);
+      WS_DMA(16, 1024, wrs, wl, wvo, so);
+      WS_DMA(16, 2048, wrs, wl, wvo, so);
+      WS_DMA(16, 3072, wrs, wl, wvo, so);
+      if constexpr (C::SB == 1024) {
+        WS_DMA(16, 0, wrs, wl + 4096, svo, so);
+      } else {
+        WS_DMA(4, 0, wrs, wl + 4096, svo, so);
+        if constexpr (C::NSD == 2) WS_DMA(4, 256, wrs, wl + 4096, svo, so);
+      }
+      if (a_pending) {
+        enter_a(cur);
+        a_pending = false;
+      }
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        lds_void_t *dst = (lds_void_t *)(base + SW + (2 * lw + n) * 1024);
+        const int so2 = cc * KC * 2;
+        if (cur.dn) {  // h rows written by other workgroups in this launch: device scope
+          if (aon[n])
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, dst, 16, avo[n], so2, 0, kSC1);
+          else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, dst, 4, avo[n], so2, 0, kSC1);
+        } else {
+          if (aon[n])
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, dst, 16, avo[n], so2, 0, 0);
+          else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, dst, 4, avo[n], so2, 0, 0);
+        }
+      }
+    };
+    // past the last unit the cursor stays on the last stage (reloaded into free buffers)
+    auto advance = [&]() {
+      if (cc + 1 < cn) {
+        ++cc;
+      } else if (cu + G < U) {
+        cu += G;
+        cur = unit_at(cu);
+        enter_w(cur);
+        a_pending = true;
+        cc = 0;
+      }
+    };
+    cur = unit_at(g);
+    enter_w(cur);
+    a_pending = true;
+    issue(0);
+    advance();
+    wait_vmcnt<0>();  // stage 0 has landed
+    int s = 0;
+    for (int u = g; u < U; u += G) {
+      const int n = nch_u(u);
+      for (int c = 0; c < n; ++c, ++s) {
+        stage_barrier();  // stage s is handed over; the buffer of stage s - 1 is free
+        issue((s + 1) % NBUF);
+        advance();
+        wait_vmcnt<0>();  // stage s + 1 has landed
+      }
+    }
+    wait_vmcnt<0>();
+    return;
+  }
+  static_assert(NBUF == 2, "one stage in flight");
+  (void)NDMA;
+
+  // ---------------- compute waves: row block `wave` of the unit
+  const int n16 = lane & 15, kq = lane >> 4;
+  const uint32_t msk = in_vgpr(0x000F000Fu);
+  const uint32_t mag = in_vgpr(AT == DT_BF16 ? 0x43004300u : 0x64006400u);
+  const int Dout = p.Dout;
+  int s = 0;
+  for (int u = g; u < U; u += G) {
+    const Unit x = unit_at(u);
+    const bool gu = !x.dn;
+    const int Kd = SEG(x, K), n = nch_of(x), rows = SEG(x, w0.rows);
+    const float limit = SEG(x, limit);
+    const int col0 = gu ? x.nb * 64 + wave * 16 : x.nb * 128 + wave * 32;
+    const bool act = col0 < rows;
+    auto row_of = [&](int t) { return gu ? col0 + (t & 15) : col0 + t; };
+    auto row_ok = [&](int t) { return row_of(t) < rows; };
+    const uint16_t *bp[2] = {(const uint16_t *)SEG(x, w0.bias),
+                             (const uint16_t *)(gu ? SEG(x, w1.bias) : SEG(x, w0.bias))};
+    uint32_t bbits[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = 16 * h + n16;
+      const uint16_t *ba = bp[h] ? bp[h] + (int64_t)x.e * rows + (row_ok(t) ? row_of(t) : 0)
+                                 : (const uint16_t *)p.cnt;
+      bbits[h] = *ba;
+    }
+    // down units: the o row of each of the lane's tokens 4 kq + i (token order: the slot,
+    // whose number the gather list holds, or T*K + t for the shared expert's rows)
+    int orow[4];
+    if (x.dn) {
+      const int32_t *gat = p.gu.seg[0].A.gather;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = min(4 * kq + i, x.nr - 1);
+        orow[i] = x.sh ? x.r0 + m : gat[x.r0 + m];
+      }
+    }
+    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    for (int c = 0; c < n; ++c, ++s) {
+      stage_barrier();
+      if (!act) continue;
+      const char *buf = smem + (s % NBUF) * STAGE;
+      const char *rec = buf + wave * RB;
+      u32x4_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = *(const u32x4_t *)(rec + i * 1024 + lane * 16);
+      uint32_t sw[2][NU];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (AFF) {
+          const char *sp = rec + 4096 + (h * 16 + n16) * NU * 4;
+#pragma unroll
+          for (int q = 0; q < NU; q += 2) {
+            const u32x2_t v2 = *(const u32x2_t *)(sp + q * 4);
+            sw[h][q] = v2[0];
+            sw[h][q + 1] = v2[1];
+          }
+        } else {
+          const u32x2_t v2 = *(const u32x2_t *)(rec + 4096 + (h * 16 + n16) * 8);
+          sw[h][0] = v2[0];
+          sw[h][1] = v2[1];
+        }
+      }
+      const char *arow = buf + SW + n16 * (KC * 2);
+      const int nunits = min(KC, Kd - c * KC) / UE;
+      auto scales = [&](int uu, float (&sc)[2], float (&cc)[2]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if constexpr (AFF) {
+            const uint32_t v = sw[h][uu];
+            sc[h] = __uint_as_float(v << 16);
+            cc[h] = fmaf(-MAGIC, sc[h], __uint_as_float(v & 0xFFFF0000u));
+          } else {
+            sc[h] = e8m0_scale((sw[h][uu >> 1] >> (8 * (2 * (uu & 1) + (kq >> 1)))) & 0xFFu);
+            cc[h] = 0.f;
+          }
+        }
+      };
+      auto word = [&](int uu, int h, int st) {
+        const int q = (uu * 2 + h) * LPU + st;
+        return w[q >> 2][q & 3];
+      };
+      auto afrag = [&](int uu, int st) {
+        const int blk = (uu * UE + kq * QE + 8 * st) >> 3;
+        return *(const u32x4_t *)(arow + ((blk ^ n16) << 4));
+      };
+      struct GS {
+        f32x4_t g0, g1, sx;
+      };
+      auto mfmas = [&](int uu) {
+        constexpr uint32_t ONE2 = (AT == DT_BF16) ? 0x3F803F80u : 0x3C003C00u;
+        const u32x4_t ones = {ONE2, ONE2, ONE2, ONE2};
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        GS r = {z, z, z};
+#pragma unroll
+        for (int st = 0; st < SPU; ++st) {
+          const u32x4_t av = afrag(uu, st);
+          r.g0 = mfma16<AT>(av, magic_pairs(word(uu, 0, st), msk, mag), r.g0);
+          r.g1 = mfma16<AT>(av, magic_pairs(word(uu, 1, st), msk, mag), r.g1);
+          r.sx = mfma16<AT>(av, ones, r.sx);
+        }
+        return r;
+      };
+      auto fold = [&](int uu, const GS &r) {
+        float sc[2], cc[2];
+        scales(uu, sc, cc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[0][i] = fmaf(sc[0], r.g0[i], fmaf(cc[0], r.sx[i], acc[0][i]));
+          acc[1][i] = fmaf(sc[1], r.g1[i], fmaf(cc[1], r.sx[i], acc[1][i]));
+        }
+      };
+      auto mx_group = [&](int uu) {
+        float sc[2], cc[2];
+        scales(uu, sc, cc);
+#pragma unroll
+        for (int st = 0; st < SPU; ++st) {
+          const u32x4_t av = afrag(uu, st);
+          acc[0] = mfma16<AT>(av, cvt_mxfp4<AT>(word(uu, 0, st), sc[0]), acc[0]);
+          acc[1] = mfma16<AT>(av, cvt_mxfp4<AT>(word(uu, 1, st), sc[1]), acc[1]);
+        }
+      };
+#pragma unroll
+      for (int uu = 0; uu < NU; ++uu) {
+        if (uu >= nunits) break;
+        if constexpr (AFF)
+          fold(uu, mfmas(uu));
+        else
+          mx_group(uu);
+      }
+    }
+    // ---- epilogue: acc[h][i] is token 4*kq + i of the m-tile, tile row 16*h + n16
+    float bo[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) bo[h] = bp[h] ? bf16_bits_to_f32(bbits[h]) : 0.f;
+    if (gu) {
+      if (act) {
+        // h = silu(g) * u for token 4 kq + i and output col0 + n16; lanes n16 and n16 + 1
+        // pair their values so each pair goes out as one 32-bit device-scope store
+        uint32_t *hout = (uint32_t *)p.gu.out;
+        const int64_t ldh = p.gu.ldo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 4 * kq + i;
+          float gv = acc[0][i] + bo[0], up = acc[1][i] + bo[1];
+          if (limit > 0.f) {
+            gv = clamp_act(gv, limit);
+            up = clamp_act(up, limit);
+          }
+          uint16_t hb;
+          if constexpr (IT == DT_BF16)
+            hb = __builtin_bit_cast(uint16_t, (__bf16)(silu_f(gv) * up));
+          else
+            hb = __builtin_bit_cast(uint16_t, (_Float16)(silu_f(gv) * up));
+          const uint32_t nb_bits = (uint32_t)__shfl_xor((int)hb, 1, 64) & 0xFFFFu;
+          if (m < x.nr && !(n16 & 1) && row_ok(n16))
+            __hip_atomic_store(hout + (((int64_t)(x.r0 + m) * ldh + row_of(n16)) >> 1), (uint32_t)hb | (nb_bits << 16),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      // every wave of the unit reports, whether or not it had rows to write.  Now, not
+      // deferred: the loaders of this workgroup may already wait for this m-tile's count
+      // before the next stage barrier, which the compute waves reach only after reporting
+      publish(tile_cnt + x.tile * kCntStride, lane);
+    } else {
+      // o in token order; the combine launch that follows reads it (plain stores: the launch
+      // boundary orders them)
+      if (act) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 4 * kq + i;
+          if (m >= x.nr) continue;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int t = 16 * h + n16;
+            if (row_ok(t)) store_act<IT>(p.dn.out, (int64_t)orow[i] * Dout + row_of(t), acc[h][i] + bo[h]);
+          }
+        }
+      }
+    }
+  }
+#undef SEG
+}
+
+// ---------------------------------------------------------------------------
+// host-side dispatch
+// ---------------------------------------------------------------------------
+namespace {
+
+template <int AT, int WF, int GQ, int IT>
+hipError_t fused_launch_t(const FusedParams &p, int units_ub, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  auto kern = decode_fused<AT, WF, GQ, IT>;
+  // persistent: every workgroup must be resident at once (the down units wait for gate/up
+  // units of other workgroups), so the grid is capped at what the device holds
+  static int per_cu[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!per_cu[dev]) {
+    int n = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 512, 0);
+    if (e != hipSuccess) return e;
+    per_cu[dev] = n > 0 ? n : -1;
+  }
+  if (per_cu[dev] < 0) return hipErrorInvalidConfiguration;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return hipErrorInvalidDevice;
+  const int cap = per_cu[dev] * cus;
+  const int grid = units_ub < cap ? units_ub : cap;
+  if (grid <= 0) return hipSuccess;
+  if (e0)
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(512), 0, s, e0, e1, 0, p);
+  else
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(512), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// h and o are stored in the MFMA type of the down projection (bf16 activations: bf16)
+hipError_t launch_decode_fused(int wfmt, int group, int idt, const FusedParams &p, int units_ub, hipStream_t s,
+                               hipEvent_t e0, hipEvent_t e1) {
+  if (idt != DT_BF16) return hipErrorInvalidValue;
+  if (wfmt == WF_MXFP4) return fused_launch_t<DT_BF16, WF_MXFP4, 0, DT_BF16>(p, units_ub, s, e0, e1);
+  if (wfmt == WF_AFFINE4) {
+    if (group == 32) return fused_launch_t<DT_BF16, WF_AFFINE4, 32, DT_BF16>(p, units_ub, s, e0, e1);
+    if (group == 64) return fused_launch_t<DT_BF16, WF_AFFINE4, 64, DT_BF16>(p, units_ub, s, e0, e1);
+    if (group == 128) return fused_launch_t<DT_BF16, WF_AFFINE4, 128, DT_BF16>(p, units_ub, s, e0, e1);
+  }
+  return hipErrorInvalidValue;
+}

@@ -94,6 +94,20 @@ struct GemmParams {
   int64_t ldr;
 };
 
+#define MOE_CNT_STRIDE 32  // ints between the counters of the one-launch decode path (128 bytes)
+constexpr int kCntStride = MOE_CNT_STRIDE;
+
+// gate/up and down of a decode-sized batch in one launch (moe_decode.hip)
+struct FusedParams {
+  GemmParams gu;              // gate/up: seg[0] routed, seg[1] shared; out = h (bf16), ldo = its row stride
+  GemmParams dn;              // down: seg[0] routed, seg[1] shared; out = o in token order (rows t*K + j,
+                              // then T*K + t for the shared expert), ldo = Dout
+  int Dout;
+  int *cnt;                   // [n_tile_cnt] m-tile counters, MOE_CNT_STRIDE ints apart
+  int n_tile_cnt;             // shared m-tiles + routed m-tiles allocated
+  int *status;                // 1 when a bounded wait gave up
+};
+
 struct F32GemmParams {   // f32 activations with DENSE F32 weights (one thread per output)
   const float *a_routed; int64_t lda_r;   // rows gathered through sorted_slot / K
   const float *a_shared; int64_t lda_s;   // rows r - TK
@@ -108,8 +122,8 @@ struct F32GemmParams {   // f32 activations with DENSE F32 weights (one thread p
 };
 
 struct CombineArgs {
-  const void *o; int64_t ldo;        // per-slot expert outputs (sorted rows), ODT
-  const int32_t *slot_pos;
+  const void *o; int64_t ldo;        // per-slot expert outputs (sorted rows, or token order), ODT
+  const int32_t *slot_pos;           // row of slot t*K + j in o; nullptr: o is in token order
   const float *topk_w;
   int K, TK, T, D;
   void *y; int64_t ldy;              // YDT
@@ -119,14 +133,17 @@ struct CombineArgs {
 };
 
 // ---- kernels ----
-// router kernels: zero (optional) is set to 0 by the launch (the counter of route_decode)
+// router kernels: zero[0 .. zero_n) (optional) is cleared by the launch (the status word, the
+// counter of route_decode and the counters of the one-launch decode experts)
 __global__ void router_logits_bf16(const uint16_t *x, const uint16_t *W, const float *lbias, float *logits,
-                                   int T, int H, int E, const uint16_t *cw, const float *cb, float *clog, int *zero);
+                                   int T, int H, int E, const uint16_t *cw, const float *cb, float *clog, int *zero,
+                                   int zero_n);
 __global__ void router_gemm_bf16(const uint16_t *x, const uint16_t *W, const float *lbias, float *logits, int T,
-                                 int H, int E, const uint16_t *cw, const float *cb, float *clog, int *zero, int ks);
+                                 int H, int E, const uint16_t *cw, const float *cb, float *clog, int *zero, int zero_n,
+                                 int ks);
 #define MOE_ROUTER_GEMM_T 256  // tokens from which the router runs as a tiled GEMM
 __global__ void router_logits_f32(const float *x, const float *W, const float *lbias, float *logits, int T,
-                                  int H, int E, const float *cw, const float *cb, float *clog, int *zero);
+                                  int H, int E, const float *cw, const float *cb, float *clog, int *zero, int zero_n);
 __global__ void topk_kernel(TopkArgs a);
 template <int SL> __global__ void topk_half_kernel(TopkArgs a);
 template <int SL>
@@ -153,6 +170,10 @@ int ws_wgs_per_cu(int wfmt, int group);  // resident workgroups per CU (LDS)
 hipError_t launch_expert_gemm_tall(int adt, int wfmt, int group, bool gateup, int odt, const GemmParams &p,
                                    int grid, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 hipError_t launch_f32_gemm(const F32GemmParams &p, int rows, hipStream_t s);
+// units_ub: an upper bound of the launch's units (grid = min(units_ub, resident capacity));
+// idt: storage type of h and o (the activations' type)
+hipError_t launch_decode_fused(int wfmt, int group, int idt, const FusedParams &p, int units_ub, hipStream_t s,
+                               hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 // packed stream of one matrix stack (b: the up stack of a gate/up pair, or nullptr)
 struct PackArgs {
   int wf, gq, n, rows, cols, gateup, dense_f32;

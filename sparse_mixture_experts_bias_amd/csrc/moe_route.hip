@@ -22,8 +22,9 @@ __global__ __launch_bounds__(512) void router_logits_bf16(const uint16_t *__rest
                                                           float *__restrict__ logits, int T, int H, int E,
                                                           const uint16_t *__restrict__ cw,
                                                           const float *__restrict__ cb, float *__restrict__ clog,
-                                                          int *__restrict__ zero) {
-  if (zero && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *zero = 0;
+                                                          int *__restrict__ zero, int zero_n) {
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < zero_n; i += blockDim.x) zero[i] = 0;
   __shared__ float red[8][16][17];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
@@ -83,8 +84,9 @@ __global__ __launch_bounds__(256) void router_gemm_bf16(const uint16_t *__restri
                                                         float *__restrict__ logits, int T, int H, int E,
                                                         const uint16_t *__restrict__ cw,
                                                         const float *__restrict__ cb, float *__restrict__ clog,
-                                                        int *__restrict__ zero, int ks) {
-  if (zero && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *zero = 0;
+                                                        int *__restrict__ zero, int zero_n, int ks) {
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int i = threadIdx.x; i < zero_n; i += blockDim.x) zero[i] = 0;
   constexpr int TM = 128, TN = 64, KC = 64;
   // one LDS variable per stage: reads of one stage then do not wait for direct loads into others
   __shared__ __attribute__((aligned(16))) uint16_t sX0[TM * KC], sX1[TM * KC], sX2[TM * KC];
@@ -233,8 +235,9 @@ __global__ __launch_bounds__(256) void router_gemm_bf16(const uint16_t *__restri
 __global__ void router_logits_f32(const float *__restrict__ x, const float *__restrict__ W,
                                   const float *__restrict__ lbias, float *__restrict__ logits, int T, int H,
                                   int E, const float *__restrict__ cw, const float *__restrict__ cb,
-                                  float *__restrict__ clog, int *__restrict__ zero) {
-  if (zero && blockIdx.x == 0 && threadIdx.x == 0) *zero = 0;
+                                  float *__restrict__ clog, int *__restrict__ zero, int zero_n) {
+  if (zero && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < zero_n; i += blockDim.x) zero[i] = 0;
   const int R = E + (cw ? 2 : 0);
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)T * R) return;

@@ -30,7 +30,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     names = header_functions()
     assert set(names) == {"moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward", "moe_pack_weights",
-                          "moe_block_forward_noalloc", "moe_status_str",
+                          "moe_block_forward_noalloc", "moe_set_decode_fusion", "moe_status_str",
                           "moe_last_error", "moe_abi_version", "moe_timing_enable", "moe_timing_read"}
     L = moe.lib()
     for n in names:
@@ -46,6 +46,8 @@ def test_status_strings_and_version():
     assert L.moe_status_str(99).decode() == "MOE_ERR_UNKNOWN"
     assert moe.abi_version() >> 16 == 2   # 2: moe_linear.packed and moe_pack_weights
     assert L.moe_timing_enable(42) == moe.MOE_ERR_ARG
+    assert L.moe_set_decode_fusion(2) == moe.MOE_ERR_ARG
+    assert L.moe_set_decode_fusion(1) == moe.MOE_OK
     assert L.moe_timing_enable(0) == moe.MOE_OK
     assert moe.moe_timing_read() == (0, 0.0)
 

@@ -350,6 +350,51 @@ def test_zero_routed_branch_add():
 
 
 # ----------------------------------------------------------------------------
+# the one-launch decode experts (gate/up + down + combine) against the separate launches
+# ----------------------------------------------------------------------------
+
+def _decode_specs():
+    c2s = synth.SMALL_SPECS["c2"]
+    return {
+        "c2-full": (synth.FULL_SPECS["c2"], None),
+        "c2-full-T1": (synth.FULL_SPECS["c2"], 1),
+        "c2s-blend": (c2s, None),
+        "c2s-add": (synth.replace(c2s, name="c2s-add", shared_mode="add", seed=71), None),
+        "c2s-none": (synth.replace(c2s, name="c2s-none", shared_mode="none", seed=72), 64),
+        "c2s-g128": (synth.replace(c2s, name="c2s-g128", group=128, I=256, I_s=384, seed=73), 29),
+        "mxfp4-add": (synth.replace(c2s, name="mxfp4", E=48, K=6, H=1024, I=256, I_s=320, expert_fmt=synth.FMT_MXFP4,
+                                    shared_fmt=synth.FMT_MXFP4, group=32, shared_mode="add", swiglu_limit=7.0,
+                                    expert_bias=True, seed=74), 24),
+    }
+
+
+@pytest.mark.parametrize("name", list(_decode_specs()))
+def test_decode_fused_matches_oracle_and_separate_launches(name):
+    """Decode-sized batches run gate/up, down and the combine in one launch by default.
+    The result matches the oracle (C16) and, bit for bit, the separate launches (the same
+    arithmetic in the same order); the status word stays 0 (every wait between
+    workgroups completed)."""
+    spec, T = _decode_specs()[name]
+    b = synth.make_block(spec, DEV, T=T)
+    y, idx, w, ob, routing = _full_check(b, f"fused decode {name}")
+    announce(f"status + separate launches {name}")
+    dev = b.x.device
+    ym = torch.empty(b.T, b.H, dtype=torch.float32, device=dev)
+    ws = moe.moe_block_forward(b.x, block_desc(b), ym)
+    torch.cuda.synchronize()
+    assert int(moe.call_status(ws, b.T, b.K, b.E)[0]) == 0
+    assert torch.equal(ym, y), "the fused path is not deterministic"
+    moe.moe_set_decode_fusion(False)
+    try:
+        yu, iu, wu = run_block(b)
+    finally:
+        moe.moe_set_decode_fusion(True)
+    assert torch.equal(iu, idx) and torch.equal(wu, w)
+    d = (yu - y).abs().max().item()
+    assert torch.equal(yu, y), f"one launch vs separate launches differ: max |diff| {d:.3g}"
+
+
+# ----------------------------------------------------------------------------
 # the packed weight stream: a pure permutation of the stored planes
 # ----------------------------------------------------------------------------
 
