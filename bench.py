@@ -96,25 +96,31 @@ def work_model(b, hit):
             "dn_bytes": dn_bytes, "dn_flops": dn_flops, "experts_hit": n}
 
 
-def kernel_source_sha():
+KERNEL_SOURCES = {
+    "gateup": ("moe_gemm_ws.hip", "moe_gemm.hip", "moe_mfma.h", "moe_kernels.h", "moe_device.h"),
+    "decode_fused": ("moe_decode.hip", "moe_ws.h", "moe_mfma.h", "moe_kernels.h", "moe_device.h"),
+}
+
+
+def kernel_source_sha(kernel="gateup"):
     h = hashlib.sha256()
-    for f in ("moe_gemm_ws.hip", "moe_gemm.hip", "moe_mfma.h", "moe_kernels.h", "moe_device.h"):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "sparse_mixture_experts_bias_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per gate/up launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source."""
-    p = os.path.join(ROOT, "profiles", f"gateup_{workload}_traffic.json")
+def measured_traffic(workload, kernel="gateup"):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(p):
         return None
     try:
         d = json.load(open(p))
     except Exception:
         return None
-    if d.get("kernel_source_sha") != kernel_source_sha():
+    if d.get("kernel_source_sha") != kernel_source_sha(kernel):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -313,7 +319,7 @@ def roofline_of(wl, r, hbm_bound, dev, with_peak=True):
             mp = measured_peak(True, dev)
             roof["measured_peak"] = mp
             roof["frac_of_measured"] = round(roof["achieved"] / mp["value"], 4)
-        roof["traffic"] = measured_traffic(wl)
+        roof["traffic"] = measured_traffic(wl, "decode_fused")
         roof["kernel"] = "decode_fused (gate/up + down)"
         roof["kernel_avg_us"] = round(gu_avg_s * 1e6, 2)
         roof["algorithmic_bytes_per_launch"] = fb
