@@ -910,8 +910,8 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
                      !router_tiled(x_dtype, (int)T, H, E);
   const int ns_f = (fused && has_shared) ? (int)((T + 15) / 16) : 0;
   const int n_tile_cnt = ns_f + ntile;
-  // [0] status, [1] route_decode's counter, then the fused launch's counters (one per 128 bytes)
-  const int n_cnt = fused ? kCntStride * (1 + n_tile_cnt) : 2;
+  // [0] status, [1] route_decode's counter, then the one-launch path's counters (kSelCnt ..)
+  const int n_cnt = fused ? kTileCnt0 + kCntStride * n_tile_cnt : 2;
   const size_t o_counts = pl.take((size_t)E * 4);
   const size_t o_offsets = pl.take((size_t)(E + 1) * 4);
   const size_t o_ss = pl.take((size_t)TK * 4);
@@ -959,8 +959,10 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   TRY(launch_router(x, x_dtype, Ti, H, &b->router, blend ? b->coef_w : nullptr, blend ? b->coef_b : nullptr, logits,
                     clog, s, cnt, true, n_cnt));
   const TopkArgs ta = topk_args(Ti, &b->router, logits, idx, wts, blend ? clog : nullptr, coef, rs);
-  // 2. permutation + tile list (for a few tokens in the same workgroup as the selection)
-  if (small) {
+  // 2. permutation + tile list (for a few tokens in the same workgroup as the selection; on
+  // the one-launch decode path, inside that launch)
+  if (fused) {
+  } else if (small) {
     TRY(launch_route_decode(ta, counts, offsets, ss, sp, mf ? tiles : nullptr, mf ? tc : nullptr, 16 * mb, done, s));
   } else {
     TRY(launch_topk(ta, s));
@@ -1018,7 +1020,8 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   }
 
   if (fused) {
-    // 3-4. gate/up and down of every slot (and the shared expert) in one persistent launch
+    // 2-4. selection, permutation, gate/up and down of every slot (and the shared expert)
+    // in one persistent launch
     const SegSet gu = segset(aop(x, H, ss, K, 0, Ti), b->experts.gate, &b->experts.up, b->experts.swiglu_limit, true);
     SegSet gus, dns;
     if (has_shared) {
@@ -1033,9 +1036,13 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
     fp.dn = gemm_params(false, 1, dn, has_shared ? &dns : nullptr, TK, Tsh, tiles, tc, ntile, E, o, D, nullptr, 0);
     CHECK(offsets_fit(fp.gu, INT32_MAX) && offsets_fit(fp.dn, INT32_MAX), MOE_ERR_SHAPE,
           "operands of over 2 GiB on the decode path");
+    fp.ta = ta;
+    fp.ta.idx = idx;
+    fp.counts = counts;
+    fp.offsets = offsets;
+    fp.slot_pos = sp;
     fp.Dout = D;
-    fp.cnt = cnt + kCntStride;
-    fp.n_tile_cnt = n_tile_cnt;
+    fp.cnt = cnt;
     fp.status = cnt;
     const int tub = routed_tiles_ub(TK, E, 16);
     const int units_ub = tub * (fp.gu.seg[0].nblk + fp.dn.seg[0].nblk) + ns_f * (fp.gu.seg[1].nblk + fp.dn.seg[1].nblk);

@@ -26,6 +26,7 @@
 // their end.  The counters are cleared by the router launch that precedes this one.
 #include <hip/hip_ext.h>
 
+#include "moe_topk.h"
 #include "moe_ws.h"
 
 namespace {
@@ -77,6 +78,53 @@ __global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
+  const int G = gridDim.x, g = blockIdx.x;
+
+  // ---- routing: workgroup g < nsel selects for tokens 16 g .. 16 g + 15 (one half-wave
+  // each); the last of them to finish builds the permutation and the m-tile list and raises
+  // the routing flag; every workgroup waits for the flag.  The selected ids cross to the
+  // permuting workgroup, and the permutation to every workgroup, as device-scope stores that
+  // have completed before the count or the flag that announces them.  (One workgroup
+  // selecting every token in turn, with no hand-over, measured slower: its passes run in
+  // series.)
+  {
+    struct SelSmem {
+      int el[16][16];
+      float esc[16][16];
+      DecodePermSmem<512> perm;
+      int last;
+    };
+    static_assert(sizeof(SelSmem) <= sizeof(smem), "routing scratch fits the stage buffers");
+    SelSmem &ss = *(SelSmem *)smem;
+    const TopkArgs &ta = p.ta;
+    const int nsel = (ta.T + 15) / 16;
+    if (g < nsel) {
+      const int half = tid >> 5, l32 = tid & 31, t = 16 * g + half;
+      if (ta.E <= 128)
+        topk_half<4>(ta, t, l32, ss.el[half], ss.esc[half], nullptr, true);
+      else if (ta.E <= 256)
+        topk_half<8>(ta, t, l32, ss.el[half], ss.esc[half], nullptr, true);
+      else
+        topk_half<16>(ta, t, l32, ss.el[half], ss.esc[half], nullptr, true);
+      wait_vmcnt<0>();  // this thread's id stores have completed
+      __syncthreads();
+      if (tid == 0)
+        ss.last = __hip_atomic_fetch_add(p.cnt + kSelCnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsel - 1;
+      __syncthreads();
+      if (ss.last) {
+        decode_permute<512, true>(ta.idx, ta.T, ta.K, ta.E, p.counts, p.offsets,
+                                  (int32_t *)p.gu.seg[0].A.gather, p.slot_pos, (int4 *)p.gu.tiles,
+                                  (int *)p.gu.tile_count, MT, ss.perm);
+        wait_vmcnt<0>();  // this thread's device-scope stores have completed
+        __syncthreads();
+        if (tid < kFlagCopies)
+          __hip_atomic_store(p.cnt + kFlag0 + tid * kFlagStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (tid == 0) wait_count(p.cnt + kFlag0 + (g % kFlagCopies) * kFlagStride, 1, p.status, 0);
+    __syncthreads();  // (also: the routing scratch is free for the stage buffers)
+  }
+
   // ---- the unit list: [gate/up: shared m-tiles, routed m-tiles][down: shared, routed]
   const int nbg0 = p.gu.seg[0].nblk, nbg1 = p.gu.seg[1].nblk, nbd0 = p.dn.seg[0].nblk, nbd1 = p.dn.seg[1].nblk;
   const int sh_rows = p.gu.sh_rows, sh_row0 = p.gu.sh_row0, max_tiles = p.gu.max_tiles;
@@ -85,12 +133,19 @@ __global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
   asm volatile("" ::"s"(nbg0), "s"(nbg1), "s"(nbd0), "s"(nbd1), "s"(sh_rows), "s"(sh_row0), "s"(max_tiles),
                "s"(tiles), "s"(tcount));
   const int ns = nbg1 > 0 ? (sh_rows + MT - 1) / MT : 0;  // shared m-tiles
-  const int nr = min(load_uniform_int(tcount), max_tiles);  // routed m-tiles
+  // routed m-tiles: written by the permuting workgroup of this launch, read once the flag is
+  // up (a device-scope load; the scalar cache could hold no earlier copy of it)
+  int nr_raw = 0;
+  if (true) {
+    int v = 0;
+    if (lane == 0) v = __hip_atomic_load(tcount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    nr_raw = __builtin_amdgcn_readfirstlane(v);
+  }
+  const int nr = min(nr_raw, max_tiles);
   const int Ug_s = ns * nbg1, Ug = Ug_s + nr * nbg0;
   const int Ud_s = ns * nbd1, U = Ug + Ud_s + nr * nbd0;
-  const int G = gridDim.x, g = blockIdx.x;
   // counters, one per 128-byte line: gate/up waves done per m-tile [ns + max_tiles]
-  int *const tile_cnt = p.cnt;
+  int *const tile_cnt = p.cnt + kTileCnt0;
 
   struct Unit {
     bool dn, sh;

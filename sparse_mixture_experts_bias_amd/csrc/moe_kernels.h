@@ -96,15 +96,23 @@ struct GemmParams {
 
 #define MOE_CNT_STRIDE 32  // ints between the counters of the one-launch decode path (128 bytes)
 constexpr int kCntStride = MOE_CNT_STRIDE;
+// the counter block of the one-launch decode path (ints, cleared by the router launch):
+// [0] status, [1] route_decode's counter, [kSelCnt] selecting workgroups done, the routing
+// flag in kFlagCopies copies kFlagStride apart (4 KB: pollers spread over memory channels),
+// then the m-tile counters from kTileCnt0, kCntStride apart
+constexpr int kSelCnt = 32;
+constexpr int kFlag0 = 64, kFlagStride = 1024, kFlagCopies = 8;
+constexpr int kTileCnt0 = kFlag0 + kFlagCopies * kFlagStride;
 
 // gate/up and down of a decode-sized batch in one launch (moe_decode.hip)
 struct FusedParams {
+  TopkArgs ta;                // selection of every token (its logits from the router launch)
+  int32_t *counts, *offsets, *slot_pos;  // permutation outputs (sorted_slot: gu.seg[0].A.gather)
   GemmParams gu;              // gate/up: seg[0] routed, seg[1] shared; out = h (bf16), ldo = its row stride
   GemmParams dn;              // down: seg[0] routed, seg[1] shared; out = o in token order (rows t*K + j,
                               // then T*K + t for the shared expert), ldo = Dout
   int Dout;
-  int *cnt;                   // [n_tile_cnt] m-tile counters, MOE_CNT_STRIDE ints apart
-  int n_tile_cnt;             // shared m-tiles + routed m-tiles allocated
+  int *cnt;                   // the counter block (see kSelCnt ... kTileCnt0)
   int *status;                // 1 when a bounded wait gave up
 };
 
