@@ -98,7 +98,7 @@ def work_model(b, hit):
 
 KERNEL_SOURCES = {
     "gateup": ("moe_gemm_ws.hip", "moe_gemm.hip", "moe_mfma.h", "moe_kernels.h", "moe_device.h"),
-    "decode_fused": ("moe_decode.hip", "moe_ws.h", "moe_mfma.h", "moe_kernels.h", "moe_device.h"),
+    "decode_fused": ("moe_decode.hip", "moe_ws.h", "moe_topk.h", "moe_mfma.h", "moe_kernels.h", "moe_device.h"),
 }
 
 
@@ -307,20 +307,20 @@ def roofline_of(wl, r, hbm_bound, dev, with_peak=True):
     wm = r["wm"]
     gu_avg_s = (r["gu_ms"] / max(r["n_gu"], 1)) / 1e3
     if r["fused"]:
-        # one launch: gate/up + SwiGLU and down; its algorithmic bytes are both GEMMs' (the h
-        # rows it hands from one to the other count once as written and once as read)
+        # the decode experts launch: gate/up + SwiGLU and down; its algorithmic bytes are both
+        # GEMMs' (the h rows it hands from one to the other count once as written and once as read)
         fb = wm["gu_bytes"] + wm["dn_bytes"]
+        parts = "gate/up + SwiGLU and down of every slot and of the shared expert"
         achieved = fb / gu_avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "scope": "kernel only: the one-launch decode experts (gate/up + SwiGLU and down, routed and "
-                         "shared)"}
+                "scope": f"kernel only: the decode experts launch ({parts})"}
         if with_peak:
             mp = measured_peak(True, dev)
             roof["measured_peak"] = mp
             roof["frac_of_measured"] = round(roof["achieved"] / mp["value"], 4)
         roof["traffic"] = measured_traffic(wl, "decode_fused")
-        roof["kernel"] = "decode_fused (gate/up + down)"
+        roof["kernel"] = "decode_fused (" + parts + ")"
         roof["kernel_avg_us"] = round(gu_avg_s * 1e6, 2)
         roof["algorithmic_bytes_per_launch"] = fb
         roof["algorithmic_flops_per_launch"] = wm["gu_flops"] + wm["dn_flops"]
@@ -388,7 +388,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true",
                     help="c2 only: skip the 4096-token prefill record of the same layer")
     ap.add_argument("--separate-decode-launches", action="store_true",
-                    help="run decode-sized batches with separate gate/up, down and combine launches")
+                    help="run decode-sized batches with separate router, routing, gate/up, down and combine "
+                         "launches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (the reference kernel that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -411,7 +412,8 @@ def main():
 
     dev = "cuda:0"
     wl = args.workload
-    if args.separate_decode_launches:
+    fusion = 0 if args.separate_decode_launches else 1
+    if not fusion:
         import sparse_mixture_experts_bias_amd as moe
         moe.moe_set_decode_fusion(False)
     r = measure(wl, args.steps, args.warmup, args.gu_every, args.copies, args.tokens)
@@ -427,7 +429,8 @@ def main():
         "config": {"workload": f"{wl}: {WORKLOADS[wl]}" + (f" (run on {b.T} tokens)" if args.tokens > 0 else ""),
                    "tokens": b.T, "hidden": b.H, "experts": b.E,
                    "top_k": b.K, "intermediate": b.I, "weight_copies": r["copies"],
-                   "inter_dtype": {0: "f32", 1: "bf16", 2: "f16"}[r["desc"].c.inter_dtype], "output": "f32"},
+                   "inter_dtype": {0: "f32", 1: "bf16", 2: "f16"}[r["desc"].c.inter_dtype], "output": "f32",
+                   "decode_fusion": fusion},
         **st,
         "roofline": roof,
     }

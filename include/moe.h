@@ -259,15 +259,22 @@ MOE_API moe_status moe_block_forward_noalloc(const void *x, int32_t x_dtype, int
                                              void *stream);
 
 /*
- * moe_set_decode_fusion - choose how moe_block_forward runs the experts of a decode-sized
- * batch (at most 64 tokens, top_k <= 16, bf16 activations and intermediates, 4-bit routed
- * experts, a shared expert of the same format or none, no latent projection):
- *   enabled = 1 (default): gate/up and the down projection of every slot (and of the shared
- *                expert) in one launch, then the weighted combine (4 launches per block);
- *   enabled = 0: separate gate/up, down and combine launches (5 in all).
- * Both give the same bits: the same arithmetic in the same order (unlike the pages'
- * fused MoE decode kernel, whose output was not byte-identical to the unfused path;
- * this switch mirrors theirs: mlxcel PR #1044, "Validation", MLXCEL_FUSED_MOE).
+ * moe_set_decode_fusion - choose how moe_block_forward runs a decode-sized batch (at most
+ * 64 tokens, top_k <= 16, at most 256 experts, bf16 activations and intermediates, a router
+ * whose logits take one pass, 4-bit routed experts, a shared expert of the same format or
+ * none, no latent projection):
+ *   enabled = 1 (default): the router, selection and permutation in one launch, gate/up and
+ *                the down projection of every slot (and of the shared expert) in one
+ *                persistent launch, then the weighted combine (3 launches per block);
+ *   enabled = 0: separate router, routing, gate/up, down and combine launches (5 in all).
+ * Both give the same bits: the same arithmetic in the same order (unlike the pages' fused
+ * MoE decode kernel, whose output was not byte-identical to the unfused path; this switch
+ * mirrors theirs: mlxcel PR #1044, "Validation", MLXCEL_FUSED_MOE).
+ * The launches hand work between workgroups through counters that the library keeps in its
+ * code object, one block of 73 KiB for each of up to 16 streams per device (each call leaves
+ * them zero for the next).  A call on a 17th stream of a device, on a stream of another
+ * device than the current one, or on a stream under capture (a graph replayed on another
+ * stream would share the block) takes the separate launches.
  * Process-wide, not thread-safe; enabled must be 0 or 1 (else MOE_ERR_ARG).
  */
 MOE_API moe_status moe_set_decode_fusion(int32_t enabled);

@@ -534,7 +534,8 @@ def call_status(ws: torch.Tensor, T: int, K: int, E: int) -> torch.Tensor:
 
 
 def moe_set_decode_fusion(enabled: bool):
-    """One launch for the experts of a decode-sized batch (default) or separate launches."""
+    """Decode-sized batches: the routing launch and one experts launch (default), or the
+    separate router, routing, gate/up and down launches."""
     _check(lib().moe_set_decode_fusion(1 if enabled else 0))
 
 

@@ -216,7 +216,7 @@ WMat wmat(const moe_linear &L, bool gateup = false) {
 
 int wf_of(const moe_linear &L) { return L.fmt == MOE_W_DENSE ? WF_DENSE : (L.fmt == MOE_W_AFFINE4 ? WF_AFFINE4 : WF_MXFP4); }
 
-// moe_set_decode_fusion: the one-launch decode experts path (on by default)
+// moe_set_decode_fusion: the decode launches (on by default)
 int g_decode_fusion = 1;
 
 // ---------------------------------------------------------------------------
@@ -574,6 +574,54 @@ moe_status combine(int odt, int ydt, const void *o, int64_t ldo, const int32_t *
 }
 
 // ---------------------------------------------------------------------------
+// counters of the decode launches: one block per stream that runs them (up to kCounterSlots
+// streams per device), in the code object: zero when it loads, and each call's routing launch
+// leaves the counters it used zero and clears the ones the experts launch uses.  Calls on one
+// stream are ordered, so no two use a block at the same time.  As with `scratch` below, host
+// code uses only the device address looked up for each GPU.  A graph captured on one stream
+// may be replayed on another, beside calls on the first, so a capturing stream takes the
+// separate launches.
+// ---------------------------------------------------------------------------
+constexpr int kCounterSlots = 16;
+static __device__ __align__(256) int fused_counters[kCounterSlots][kCounterInts];
+
+constexpr int kCounterDevices = 64;
+std::mutex g_counter_mu;
+int *g_counter_ptr[kCounterDevices] = {};
+hipStream_t g_counter_stream[kCounterDevices][kCounterSlots];
+int g_counter_used[kCounterDevices] = {};
+
+// the counter block of stream s (on the calling thread's current device), or nullptr: s is
+// capturing or on another device, or every block already belongs to another stream
+int *counters_for(hipStream_t s) {
+  int dev = -1, sdev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kCounterDevices) return nullptr;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamGetDevice(s, &sdev) != hipSuccess || sdev != dev || hipStreamIsCapturing(s, &cap) != hipSuccess ||
+      cap != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_counter_mu);
+  if (g_counter_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(fused_counters)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_counter_ptr[dev] = (int *)ptr;
+  }
+  int i = 0;
+  while (i < g_counter_used[dev] && g_counter_stream[dev][i] != s) ++i;
+  if (i == g_counter_used[dev]) {
+    if (i == kCounterSlots) return nullptr;
+    g_counter_stream[dev][i] = s;
+    ++g_counter_used[dev];
+  }
+  return g_counter_ptr[dev] + (size_t)i * kCounterInts;
+}
+
+// ---------------------------------------------------------------------------
 // scratch memory of moe_block_forward_noalloc: one array per GPU, in the code object, held
 // until the process ends.  Host code never uses the array's name as an address (on the host
 // it is only a stand-in for the symbol): the device address of each GPU's copy is looked up
@@ -898,25 +946,22 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   Plan pl;
   const bool blend = b->shared_mode == MOE_SHARED_BLEND;
   const int rs = (T > INT32_MAX) ? 1 : router_slices(x_dtype, (int)T, H, E, true);
-  // the routing state and the status word first, at the offsets include/moe.h documents;
-  // the status word heads the counter block (cleared by the router launch of every call)
+  // the routing state and the status word first, at the offsets include/moe.h documents
   const int ntile = max_tiles(TK, E);
   const int mb = mb_for_routing(TK, E);
   const bool small = T <= MOE_ROUTE_SMALL_T && topk_slots(E, K) > 0;
-  // the one-launch decode experts path: bf16 activations and intermediates, decode-sized
-  // segments, 4-bit routed experts (and a shared expert of the same format, or none)
-  const bool fused = g_decode_fusion && mf && !latent && small && mb == 1 && x_dtype == MOE_BF16 &&
-                     inter == MOE_BF16 && b->experts.gate.fmt != MOE_W_DENSE && (!has_shared || fuse_shared) &&
-                     !router_tiled(x_dtype, (int)T, H, E);
-  const int ns_f = (fused && has_shared) ? (int)((T + 15) / 16) : 0;
-  const int n_tile_cnt = ns_f + ntile;
-  // [0] status, [1] route_decode's counter, then the one-launch path's counters (kSelCnt ..)
-  const int n_cnt = fused ? kTileCnt0 + kCntStride * n_tile_cnt : 2;
+  // the one-launch decode path: bf16 activations and intermediates, decode-sized segments,
+  // 4-bit routed experts (and a shared expert of the same format, or none), the router's
+  // logits in one tile pass
+  const int ns_f = has_shared ? (int)((T + 15) / 16) : 0;
+  bool fused = g_decode_fusion && mf && !latent && small && mb == 1 && x_dtype == MOE_BF16 && inter == MOE_BF16 &&
+               b->experts.gate.fmt != MOE_W_DENSE && (!has_shared || fuse_shared) &&
+               !router_tiled(x_dtype, (int)T, H, E) && E <= 256 && ns_f + ntile <= kMaxTileCnt;
   const size_t o_counts = pl.take((size_t)E * 4);
   const size_t o_offsets = pl.take((size_t)(E + 1) * 4);
   const size_t o_ss = pl.take((size_t)TK * 4);
   const size_t o_sp = pl.take((size_t)TK * 4);
-  const size_t o_cnt = pl.take((size_t)n_cnt * 4);
+  const size_t o_st = pl.take(2 * 4);  // [0] status, [1] route_decode's counter
   const size_t o_logits = pl.take((size_t)rs * T * E * 4);
   const size_t o_coef = pl.take((size_t)T * 2 * 4);
   const size_t o_clog = pl.take((size_t)rs * T * 2 * 4);
@@ -952,12 +997,16 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   void *o = at<char>(ws, o_o);
   const int Ti = (int)T;
 
-  // 1. router + selection (+ blend coefficients); the router launch clears the counters
+  // 1. router + selection (+ blend coefficients); the router launch clears the status word
+  // and route_decode's counter (the decode launches have their own router)
   float *clog = at<float>(ws, o_clog);
-  int *cnt = at<int>(ws, o_cnt);
-  int *done = cnt + 1;
-  TRY(launch_router(x, x_dtype, Ti, H, &b->router, blend ? b->coef_w : nullptr, blend ? b->coef_b : nullptr, logits,
-                    clog, s, cnt, true, n_cnt));
+  int *st = at<int>(ws, o_st);
+  int *cnt = fused ? counters_for(s) : nullptr;
+  fused = cnt != nullptr;  // (else separate launches)
+  int *done = st + 1;
+  if (!fused)
+    TRY(launch_router(x, x_dtype, Ti, H, &b->router, blend ? b->coef_w : nullptr, blend ? b->coef_b : nullptr, logits,
+                      clog, s, st, true, 2));
   const TopkArgs ta = topk_args(Ti, &b->router, logits, idx, wts, blend ? clog : nullptr, coef, rs);
   // 2. permutation + tile list (for a few tokens in the same workgroup as the selection; on
   // the one-launch decode path, inside that launch)
@@ -1020,8 +1069,8 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   }
 
   if (fused) {
-    // 2-4. selection, permutation, gate/up and down of every slot (and the shared expert)
-    // in one persistent launch
+    // 1-2. router, selection and permutation in one launch; 3-4. gate/up and down of every
+    // slot (and the shared expert) in one persistent launch
     const SegSet gu = segset(aop(x, H, ss, K, 0, Ti), b->experts.gate, &b->experts.up, b->experts.swiglu_limit, true);
     SegSet gus, dns;
     if (has_shared) {
@@ -1036,16 +1085,26 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
     fp.dn = gemm_params(false, 1, dn, has_shared ? &dns : nullptr, TK, Tsh, tiles, tc, ntile, E, o, D, nullptr, 0);
     CHECK(offsets_fit(fp.gu, INT32_MAX) && offsets_fit(fp.dn, INT32_MAX), MOE_ERR_SHAPE,
           "operands of over 2 GiB on the decode path");
+    fp.x = (const uint16_t *)x;
+    fp.Wr = (const uint16_t *)b->router.w;
+    fp.cw = blend ? (const uint16_t *)b->coef_w : nullptr;
+    fp.lbias = b->router.logit_bias;
+    fp.cb = blend ? b->coef_b : nullptr;
+    fp.H = H;
     fp.ta = ta;
-    fp.ta.idx = idx;
     fp.counts = counts;
     fp.offsets = offsets;
     fp.slot_pos = sp;
     fp.Dout = D;
     fp.cnt = cnt;
-    fp.status = cnt;
+    fp.n_tile_cnt = ns_f + ntile;
+    fp.status = st;
     const int tub = routed_tiles_ub(TK, E, 16);
     const int units_ub = tub * (fp.gu.seg[0].nblk + fp.dn.seg[0].nblk) + ns_f * (fp.gu.seg[1].nblk + fp.dn.seg[1].nblk);
+    {
+      Timed tm(TK_ROUTER, s);
+      HIPCHK(launch_decode_route(fp, s));
+    }
     {
       Timed tm(TK_FUSED, s, true);
       HIPCHK(launch_decode_fused(wf_of(b->experts.gate), b->experts.gate.group_size, DT_BF16, fp, units_ub, s,

@@ -1,29 +1,40 @@
-// moe_decode.hip - the routed experts of a decode-sized batch in one persistent launch:
-// gate/up + SwiGLU and the down projection of every slot, plus the shared expert
+// moe_decode.hip - a decode-sized batch of the block in two launches.
 // (libmir-metal's execute hands the gate/up kernel the routing indices and the clamp limit,
-// and the down kernel the same indices; the weighted combine follows as its own short launch,
-// moe_combine.hip).
+// and the down kernel the same indices with the routing weights, which makes the layer
+// output; mlxcel PR #1044, "Validation", describes a fused MoE kernel for one-token decode.)
 //
-// Work units are those of the loader-wave decode GEMM (moe_gemm_ws.hip): (m-tile of up to
-// 16 rows of one segment, 4 row blocks of the packed stream), 4-bit weights, loader waves
-// streaming records HBM -> LDS, compute waves folding each quantisation group exactly.  The
-// unit sequence of a workgroup runs over the gate/up units first, then the down units, so
-// the down weights stream while gate/up work is still finishing elsewhere, and the two
-// projections pay one ramp and one tail instead of two.  The per-slot outputs o are written
-// in token order (row t*K + j for slot j of token t, row T*K + t for the shared expert), so
-// the combine reads each token's rows contiguously.
+// decode_route (ceil(T/16) * ceil(R/16) workgroups, R = experts + the blend head's 2 rows):
+//   workgroup (tt, rt) computes one 16-token x 16-row tile of the router logits.  For up to
+//   16 tokens the last tile to finish selects for every token (one half-wave each); for
+//   more, tile (tt, rt) selects token 16 tt + rt once its block's tiles are in.  The last
+//   selection to finish builds counts, offsets, sorted_slot, slot_pos and the m-tile list.
+//   The launch also clears the m-tile counters of the experts launch that follows, and the
+//   permuting workgroup clears the launch's own counters.
+// decode_fused (persistent: at most what the device holds at once):
+//   the work units of the loader-wave decode GEMM (moe_gemm_ws.hip: m-tile of up to 16 rows x
+//   4 row blocks of the packed stream; loader waves stream records HBM -> LDS, compute waves
+//   fold each quantisation group exactly), gate/up units first, then down units, so the down
+//   weights stream while gate/up work finishes elsewhere; a down unit waits until every
+//   gate/up wave of its m-tile has stored its h rows.  The per-slot outputs o are written in
+//   token order (row t*K + j, then T*K + t for the shared expert), which the combine launch
+//   reads.  (Combining in this launch, by the wave whose down unit completed a 32-column
+//   block of o, put the combine's loads on the launch's tail and measured slower.)
 //
-// Hand-over from gate/up to down between workgroups (which sit on different XCDs, each with
-// its own L2): a compute wave stores its h outputs with device-scope cache policy (sc1: the
-// instructions the compiler emits for agent-scope relaxed atomic stores, coherent across the
-// XCDs; pairs of 16-bit values as 32-bit stores), waits until they have completed (vmcnt 0),
-// then increments its m-tile's counter; the loader of a down unit waits until the counter of
-// the unit's m-tile shows every gate/up wave of that m-tile (4 per unit), then loads the h
-// rows with device-scope direct loads.  No L2 write-back or invalidate is needed (an
-// agent-scope release fence per wave and unit, which writes back the whole L2 of the XCD,
-// made the launch several times slower).  Every wait is bounded: a wait that gives up (only
-// possible if the grid were not co-resident) sets the status word and lets the waves run to
-// their end.  The counters are cleared by the router launch that precedes this one.
+// (One launch for all of it, with the router tiles and the selection inside the persistent
+// grid and a flag that every workgroup polls, was slower: the routing chain ran while the
+// whole grid polled, and the launch needed a grid-wide count at its end to clear its
+// counters, an atomic from every workgroup on one line.)
+//
+// Hand-overs between workgroups (on different XCDs, each with its own L2) carry their data
+// as device-scope stores (sc1: the instructions the compiler emits for agent-scope relaxed
+// atomic stores, coherent across the XCDs), wait until those have completed (vmcnt 0), then
+// bump a counter; the reader sees the count and reads with device-scope loads.  No L2
+// write-back or invalidate is needed; an agent-scope release fence per wave and unit, which
+// writes back the whole L2 of the XCD, made the launch several times slower.  Counters sit
+// one per 128-byte line and are polled every ~0.25 us (back-to-back polling of one line
+// loaded a memory channel enough to slow the launch threefold).  Every wait is bounded: one
+// that gives up (only possible if the grid were not co-resident) sets the status word and
+// lets the waves run to their end.
 #include <hip/hip_ext.h>
 
 #include "moe_topk.h"
@@ -32,13 +43,12 @@
 namespace {
 
 // A device-scope poll goes to memory (it must not be served by a stale L2 line), so polls are
-// spaced out (~0.25 us: s_sleep 10 is 640 clocks) and every counter has a 128-byte line of its
-// own: polling a shared line back to back loaded one memory channel enough to slow the whole
-// launch several times over.
+// spaced out (~0.25 us: s_sleep 10 is 640 clocks).
 constexpr int kSpinLimit = 1 << 19;  // polls of a counter, ~0.15 s in all
 constexpr int kSC1 = 16;             // cache-policy bit of device-scope (sc1) buffer accesses
 
-// waits until *c >= target (device-scope loads of the counter by one lane)
+// waits until *c >= target (device-scope loads of the counter by the calling lane `lane` of
+// the wave's active lanes; lane 0 when the whole wave calls)
 MOE_DEV bool wait_count(const int *c, int target, int *status, int lane) {
   for (int it = 0; it < kSpinLimit; ++it) {
     int v = 0;
@@ -66,6 +76,81 @@ MOE_DEV int publish(int *c, int lane) {
 
 }  // namespace
 
+// router tiles, selection and permutation (see the top of the file); SL: logits per lane of
+// a half-wave in the selection (E <= 32 SL)
+template <int SL>
+__global__ __launch_bounds__(512) void decode_route(const FusedParams p) {
+  __shared__ float red[8][16][17];
+  __shared__ int el[16][16];
+  __shared__ float esc[16][16];
+  __shared__ int32_t sidx[16 * 16];  // the selected ids of a single token block (K <= 16)
+  __shared__ DecodePermSmem<512> perm;
+  __shared__ int last;
+  const int tid = threadIdx.x, g = blockIdx.x, G = gridDim.x;
+  const TopkArgs &ta = p.ta;
+  const int T = ta.T, E = ta.E;
+  const int nTT = (T + 15) / 16, nRT = (E + (p.cw ? 2 : 0) + 15) / 16;
+  if (g == 0 && tid == 0) *p.status = 0;
+  // the experts launch's m-tile counters
+  for (int i = g * 512 + tid; i < p.n_tile_cnt; i += G * 512) p.cnt[kTileCnt0 + i * kCntStride] = 0;
+  const int tt = g / nRT, rt = g - tt * nRT;
+  // the selection biases, in case this workgroup is the one that selects (loaded now, so
+  // that the selection does not wait for them)
+  const int half = tid >> 5, l32 = tid & 31;
+  float sb[SL];
+  topk_half_sbias<SL>(ta, l32, sb);
+  router_tile_bf16<true>(p.x, p.Wr, p.lbias, (float *)ta.logits, T, p.H, E, p.cw, p.cb, (float *)ta.clog, tt, rt,
+                         red);
+  wait_vmcnt<0>();  // this thread's logit stores have completed
+  __syncthreads();
+  if (nTT == 1) {
+    // a single token block: the last tile to finish selects for every token (one half-wave
+    // each) and permutes, the ids kept in LDS
+    if (tid == 0)
+      last = __hip_atomic_fetch_add(p.cnt + kTileDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == G - 1;
+    __syncthreads();
+    if (!last) return;
+    topk_half<SL, true>(ta, half, l32, el[half], esc[half], sidx, false);
+    __syncthreads();
+    decode_permute<512, false, true>(sidx, T, ta.K, E, p.counts, p.offsets, (int32_t *)p.gu.seg[0].A.gather,
+                                     p.slot_pos, (int4 *)p.gu.tiles, (int *)p.gu.tile_count, 16, perm);
+    if (tid == 0) p.cnt[kTileDone] = 0;  // every other workgroup has counted itself: clear
+    return;
+  }
+  // several token blocks: once every tile of its block is in, tile (tt, rt) selects tokens
+  // 16 tt + rt + nRT h of the block, half-wave h each (spreading the selections over the
+  // block's workgroups keeps each to one short pass, where the selection arithmetic of 16
+  // tokens on one workgroup took ~4 us), and the last workgroup to finish selecting
+  // permutes.  The waits are on tiles of the same small grid, all resident at once.
+  if (tid == 0) __hip_atomic_fetch_add(p.cnt + kTtCnt0 + tt * kCntStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int nbt = min(16, T - 16 * tt);  // tokens of this block
+  if (rt >= nbt) return;                 // no token for this tile
+  const int nh = (nbt - 1 - rt) / nRT + 1;  // its tokens: half-waves 0 .. nh - 1
+  if (tid == 0) wait_count(p.cnt + kTtCnt0 + tt * kCntStride, nRT, p.status, 0);
+  __syncthreads();
+  if ((tid >> 6) < (nh + 1) / 2) {  // waves with a token; a half without one works on a
+                                    // token past the end and stores nothing
+    float lg[SL];
+    float2 cp;
+    const int tq = half < nh ? 16 * tt + rt + nRT * half : T;
+    topk_half_load<SL, true>(ta, tq, l32, lg, cp);
+    topk_half_select<SL>(ta, tq, l32, lg, cp, sb, el[half], esc[half], nullptr, true);
+    wait_vmcnt<0>();  // this thread's id, weight and coefficient stores have completed
+  }
+  __syncthreads();
+  // selecting workgroups: min(nRT, tokens) per block
+  int nsel = 0;
+  for (int b = 0; b < nTT; ++b) nsel += min(nRT, min(16, T - 16 * b));
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(p.cnt + kSelCnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsel - 1;
+  __syncthreads();
+  if (!last) return;
+  decode_permute<512, false>(ta.idx, T, ta.K, E, p.counts, p.offsets, (int32_t *)p.gu.seg[0].A.gather, p.slot_pos,
+                             (int4 *)p.gu.tiles, (int *)p.gu.tile_count, 16, perm);
+  // every workgroup with a token has passed its wait and counted itself: clear
+  for (int i = tid; i <= nTT; i += 512) p.cnt[i == 0 ? kSelCnt : kTtCnt0 + (i - 1) * kCntStride] = 0;
+}
+
 template <int AT, int WF, int GQ, int IT>
 __global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
   using C = WsCfg<WF, GQ>;
@@ -77,71 +162,18 @@ __global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
   const int G = gridDim.x, g = blockIdx.x;
-
-  // ---- routing: workgroup g < nsel selects for tokens 16 g .. 16 g + 15 (one half-wave
-  // each); the last of them to finish builds the permutation and the m-tile list and raises
-  // the routing flag; every workgroup waits for the flag.  The selected ids cross to the
-  // permuting workgroup, and the permutation to every workgroup, as device-scope stores that
-  // have completed before the count or the flag that announces them.  (One workgroup
-  // selecting every token in turn, with no hand-over, measured slower: its passes run in
-  // series.)
-  {
-    struct SelSmem {
-      int el[16][16];
-      float esc[16][16];
-      DecodePermSmem<512> perm;
-      int last;
-    };
-    static_assert(sizeof(SelSmem) <= sizeof(smem), "routing scratch fits the stage buffers");
-    SelSmem &ss = *(SelSmem *)smem;
-    const TopkArgs &ta = p.ta;
-    const int nsel = (ta.T + 15) / 16;
-    if (g < nsel) {
-      const int half = tid >> 5, l32 = tid & 31, t = 16 * g + half;
-      if (ta.E <= 128)
-        topk_half<4>(ta, t, l32, ss.el[half], ss.esc[half], nullptr, true);
-      else if (ta.E <= 256)
-        topk_half<8>(ta, t, l32, ss.el[half], ss.esc[half], nullptr, true);
-      else
-        topk_half<16>(ta, t, l32, ss.el[half], ss.esc[half], nullptr, true);
-      wait_vmcnt<0>();  // this thread's id stores have completed
-      __syncthreads();
-      if (tid == 0)
-        ss.last = __hip_atomic_fetch_add(p.cnt + kSelCnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsel - 1;
-      __syncthreads();
-      if (ss.last) {
-        decode_permute<512, true>(ta.idx, ta.T, ta.K, ta.E, p.counts, p.offsets,
-                                  (int32_t *)p.gu.seg[0].A.gather, p.slot_pos, (int4 *)p.gu.tiles,
-                                  (int *)p.gu.tile_count, MT, ss.perm);
-        wait_vmcnt<0>();  // this thread's device-scope stores have completed
-        __syncthreads();
-        if (tid < kFlagCopies)
-          __hip_atomic_store(p.cnt + kFlag0 + tid * kFlagStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    if (tid == 0) wait_count(p.cnt + kFlag0 + (g % kFlagCopies) * kFlagStride, 1, p.status, 0);
-    __syncthreads();  // (also: the routing scratch is free for the stage buffers)
-  }
 
   // ---- the unit list: [gate/up: shared m-tiles, routed m-tiles][down: shared, routed]
   const int nbg0 = p.gu.seg[0].nblk, nbg1 = p.gu.seg[1].nblk, nbd0 = p.dn.seg[0].nblk, nbd1 = p.dn.seg[1].nblk;
-  const int sh_rows = p.gu.sh_rows, sh_row0 = p.gu.sh_row0, max_tiles = p.gu.max_tiles;
+  const int sh_rows = p.gu.sh_rows, sh_row0 = p.gu.sh_row0, max_tiles = p.gu.max_tiles, n_exp = p.gu.E;
   const int4 *const tiles = p.gu.tiles;
   const int *const tcount = p.gu.tile_count;
   asm volatile("" ::"s"(nbg0), "s"(nbg1), "s"(nbd0), "s"(nbd1), "s"(sh_rows), "s"(sh_row0), "s"(max_tiles),
                "s"(tiles), "s"(tcount));
   const int ns = nbg1 > 0 ? (sh_rows + MT - 1) / MT : 0;  // shared m-tiles
-  // routed m-tiles: written by the permuting workgroup of this launch, read once the flag is
-  // up (a device-scope load; the scalar cache could hold no earlier copy of it)
-  int nr_raw = 0;
-  if (true) {
-    int v = 0;
-    if (lane == 0) v = __hip_atomic_load(tcount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    nr_raw = __builtin_amdgcn_readfirstlane(v);
-  }
-  const int nr = min(nr_raw, max_tiles);
+  // routed m-tiles (written by the routing launch)
+  const int nr = min(max(load_uniform_int(tcount), 0), max_tiles);
   const int Ug_s = ns * nbg1, Ug = Ug_s + nr * nbg0;
   const int Ud_s = ns * nbd1, U = Ug + Ud_s + nr * nbd0;
   // counters, one per 128-byte line: gate/up waves done per m-tile [ns + max_tiles]
@@ -170,10 +202,11 @@ __global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
       const int nb0 = max(x.dn ? nbd0 : nbg0, 1);
       const int ti = v / nb0;
       x.nb = v - ti * nb0;
+      // (clamped into range: whatever the list held, no access leaves its buffer)
       const int4 t = load_uniform_int4(tiles + ti);
-      x.e = t.x;
-      x.r0 = t.y;
-      x.nr = t.z;
+      x.e = min(max(t.x, 0), n_exp - 1);
+      x.r0 = min(max(t.y, 0), sh_row0 - 1);
+      x.nr = min(max(t.z, 1), min(MT, sh_row0 - x.r0));
       x.tile = ns + ti;
     }
     return x;
@@ -346,7 +379,7 @@ __global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = min(4 * kq + i, x.nr - 1);
-        orow[i] = x.sh ? x.r0 + m : gat[x.r0 + m];
+        orow[i] = x.sh ? x.r0 + m : min(max(gat[x.r0 + m], 0), sh_row0 - 1);
       }
     }
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
@@ -530,6 +563,17 @@ hipError_t fused_launch_t(const FusedParams &p, int units_ub, hipStream_t s, hip
 }
 
 }  // namespace
+
+hipError_t launch_decode_route(const FusedParams &p, hipStream_t s) {
+  const int E = p.ta.E;
+  if (p.ta.T <= 0 || p.ta.T > MOE_ROUTE_SMALL_T || E > 256 || p.H % 32 != 0) return hipErrorInvalidValue;
+  const int grid = (p.ta.T + 15) / 16 * ((E + (p.cw ? 2 : 0) + 15) / 16);
+  if (E <= 128)
+    hipLaunchKernelGGL(decode_route<4>, dim3(grid), dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL(decode_route<8>, dim3(grid), dim3(512), 0, s, p);
+  return hipGetLastError();
+}
 
 // h and o are stored in the MFMA type of the down projection (bf16 activations: bf16)
 hipError_t launch_decode_fused(int wfmt, int group, int idt, const FusedParams &p, int units_ub, hipStream_t s,

@@ -97,22 +97,30 @@ struct GemmParams {
 #define MOE_CNT_STRIDE 32  // ints between the counters of the one-launch decode path (128 bytes)
 constexpr int kCntStride = MOE_CNT_STRIDE;
 // the counter block of the one-launch decode path (ints, cleared by the router launch):
-// [0] status, [1] route_decode's counter, [kSelCnt] selecting workgroups done, the routing
-// flag in kFlagCopies copies kFlagStride apart (4 KB: pollers spread over memory channels),
-// then the m-tile counters from kTileCnt0, kCntStride apart
-constexpr int kSelCnt = 32;
-constexpr int kFlag0 = 64, kFlagStride = 1024, kFlagCopies = 8;
-constexpr int kTileCnt0 = kFlag0 + kFlagCopies * kFlagStride;
+// Counter block of the decode launches (kCounterInts ints, every counter at the start of its
+// own 128-byte line; zero when the routing launch starts, and left so): [kTileDone] router
+// tiles done (one token block), [kSelCnt] tokens selected and [kTtCnt0 + kCntStride tt] router
+// tiles of token block tt done (several blocks), all cleared by the routing launch once
+// used, then the experts launch's m-tile counters (gate/up waves done) from kTileCnt0
+// (cleared by the routing launch before it).
+constexpr int kTileDone = 0, kSelCnt = kCntStride, kTtCnt0 = 2 * kCntStride;
+constexpr int kTileCnt0 = kTtCnt0 + (MOE_ROUTE_SMALL_T / 16) * kCntStride;
+constexpr int kMaxTileCnt = 584;  // shared + routed m-tiles
+constexpr int kCounterInts = kTileCnt0 + kMaxTileCnt * kCntStride;
 
-// gate/up and down of a decode-sized batch in one launch (moe_decode.hip)
 struct FusedParams {
-  TopkArgs ta;                // selection of every token (its logits from the router launch)
+  // router: logits [T][E] = x W_r^T (+ logit_bias), blend head logits clog [T][2]
+  const uint16_t *x, *Wr, *cw;  // x [T][H] bf16, W_r [E][H] bf16, blend head [2][H] bf16 or nullptr
+  const float *lbias, *cb;      // logit_bias [E] or nullptr, blend head bias [2]
+  int H;
+  TopkArgs ta;                // selection of every token (ta.logits: the router's output, one slice)
   int32_t *counts, *offsets, *slot_pos;  // permutation outputs (sorted_slot: gu.seg[0].A.gather)
   GemmParams gu;              // gate/up: seg[0] routed, seg[1] shared; out = h (bf16), ldo = its row stride
   GemmParams dn;              // down: seg[0] routed, seg[1] shared; out = o in token order (rows t*K + j,
                               // then T*K + t for the shared expert), ldo = Dout
   int Dout;
-  int *cnt;                   // the counter block (see kSelCnt ... kTileCnt0)
+  int *cnt;                   // the counter block
+  int n_tile_cnt;             // m-tile counters the experts launch uses
   int *status;                // 1 when a bounded wait gave up
 };
 
@@ -180,6 +188,10 @@ hipError_t launch_expert_gemm_tall(int adt, int wfmt, int group, bool gateup, in
 hipError_t launch_f32_gemm(const F32GemmParams &p, int rows, hipStream_t s);
 // units_ub: an upper bound of the launch's units (grid = min(units_ub, resident capacity));
 // idt: storage type of h and o (the activations' type)
+// the routing launch of a decode batch (bf16 x and router, E <= 256): router logits, selection,
+// permutation and m-tile list; clears the experts launch's counters
+hipError_t launch_decode_route(const FusedParams &p, hipStream_t s);
+// the experts launch: grid min(units_ub, what the device holds at once)
 hipError_t launch_decode_fused(int wfmt, int group, int idt, const FusedParams &p, int units_ub, hipStream_t s,
                                hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 // packed stream of one matrix stack (b: the up stack of a gate/up pair, or nullptr)

@@ -26,47 +26,7 @@ __global__ __launch_bounds__(512) void router_logits_bf16(const uint16_t *__rest
   if (zero && blockIdx.x == 0 && blockIdx.y == 0)
     for (int i = threadIdx.x; i < zero_n; i += blockDim.x) zero[i] = 0;
   __shared__ float red[8][16][17];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
-  const int r = lane & 15, kb = lane >> 4;
-  const int trow = min(t0 + r, T - 1), er = e0 + r;
-  const uint16_t *wrow = er < E ? W + (int64_t)er * H
-                                : ((cw && er < E + 2) ? cw + (int64_t)(er - E) * H : W + (int64_t)(E - 1) * H);
-  const u32x4_t *xa = (const u32x4_t *)(x + (int64_t)trow * H + kb * 8);
-  const u32x4_t *wb = (const u32x4_t *)(wrow + kb * 8);
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  const int nsteps = H >> 5;
-  for (int s0 = wave; s0 < nsteps; s0 += 64) {
-    u32x4_t av[8], bv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int st = min(s0 + 8 * i, nsteps - 1);
-      av[i] = xa[st * 4];
-      bv[i] = wb[st * 4];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (s0 + 8 * i < nsteps)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[i]),
-                                                      __builtin_bit_cast(bf16x8_t, bv[i]), acc, 0, 0, 0);
-  }
-  // acc[i] holds row (token) 4*kb+i, column r of the 16x16 tile
-#pragma unroll
-  for (int i = 0; i < 4; ++i) red[wave][4 * kb + i][r] = acc[i];
-  __syncthreads();
-  if (threadIdx.x < 256) {
-    const int m = threadIdx.x >> 4, n = threadIdx.x & 15;
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) v += red[w][m][n];
-    const int t = t0 + m, e = e0 + n;
-    if (t < T) {
-      if (e < E)
-        logits[(int64_t)t * E + e] = v + (lbias ? lbias[e] : 0.f);
-      else if (cw && e < E + 2)
-        clog[2 * t + (e - E)] = v + cb[e - E];
-    }
-  }
+  router_tile_bf16<false>(x, W, lbias, logits, T, H, E, cw, cb, clog, blockIdx.x, blockIdx.y, red);
 }
 
 // router logits for many tokens (bf16): a tiled MFMA GEMM with the reduction split over

@@ -222,22 +222,53 @@ MOE_DEV float half_sum_f32(float v) {
 // token t on one half-wave (both halves of the wave call this together; a half with
 // t >= T computes on a clamped token and stores nothing).  el / esc: 16 ints / floats of
 // LDS private to the half (chosen ids and their unbiased scores, in selection order).
-template <int SL>
-// coherent: the ids are stored at device scope (written through to the point every XCD reads
-// from), for a workgroup on another XCD to read without a cache write-back and invalidate
-MOE_DEV void topk_half(const TopkArgs &a, int t, int l32, int *el, float *esc, int32_t *sidx, bool coherent = false) {
+MOE_DEV float ld_dev(const float *p) {  // a device-scope (sc1) load
+  return __uint_as_float(__hip_atomic_load((const uint32_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+MOE_DEV void st_dev(float *p, float v) {  // a device-scope (sc1) store
+  __hip_atomic_store((uint32_t *)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// the logits of token t (the router's slices summed in order) for this lane's experts
+// l32 + 32 j of a half-wave, and the lane's share of the blend-head logits.  COH_IN: the
+// logits (one slice) and the blend-head logits come from other workgroups of the same launch
+// and are read at device scope.
+template <int SL, bool COH_IN = false>
+MOE_DEV void topk_half_load(const TopkArgs &a, int t, int l32, float (&lg)[SL], float2 &cp) {
   const bool live = t < a.T;
   const float *lrow = a.logits + (int64_t)(live ? t : a.T - 1) * a.E;
-  float lg[SL], sb[SL];
   int ec[SL];
 #pragma unroll
   for (int j = 0; j < SL; ++j) {
     ec[j] = min(l32 + 32 * j, a.E - 1);
-    lg[j] = lrow[ec[j]];
-    sb[j] = a.sbias ? a.sbias[ec[j]] : 0.f;
+    lg[j] = COH_IN ? ld_dev(lrow + ec[j]) : lrow[ec[j]];
   }
-  const float2 cp = clog_part(a, live ? t : a.T - 1, l32);
+  if constexpr (COH_IN) {  // one slice: lane 0 holds the head's two logits
+    const int tc = live ? t : a.T - 1;
+    const bool on = a.clog && l32 == 0;
+    cp = on ? make_float2(ld_dev(a.clog + 2 * tc), ld_dev(a.clog + 2 * tc + 1)) : make_float2(0.f, 0.f);
+  } else {
+    cp = clog_part(a, live ? t : a.T - 1, l32);
+  }
   add_slices<SL>(lg, lrow, ec, a.slices, (int64_t)a.T * a.E);
+}
+
+// the selection bias of this lane's experts (0 without one)
+template <int SL>
+MOE_DEV void topk_half_sbias(const TopkArgs &a, int l32, float (&sb)[SL]) {
+#pragma unroll
+  for (int j = 0; j < SL; ++j) sb[j] = a.sbias ? a.sbias[min(l32 + 32 * j, a.E - 1)] : 0.f;
+}
+
+// scores, selection, weights and blend coefficients of token t from its loaded logits and
+// this lane's selection biases.
+// coherent: the ids, weights and blend coefficients are stored at device scope (written
+// through to the point every XCD reads from), for a workgroup on another XCD to read without
+// a cache write-back and invalidate.
+template <int SL>
+MOE_DEV void topk_half_select(const TopkArgs &a, int t, int l32, const float (&lg)[SL], float2 cp,
+                              const float (&sb)[SL], int *el, float *esc, int32_t *sidx, bool coherent) {
+  const bool live = t < a.T;
   if (a.logits_out && live) {
 #pragma unroll
     for (int j = 0; j < SL; ++j)
@@ -313,11 +344,13 @@ MOE_DEV void topk_half(const TopkArgs &a, int t, int l32, int *el, float *esc, i
     }
     float w = a.norm ? my_s / wsum : my_s;
     w *= a.rscale;
-    if (coherent)
+    if (coherent) {
       __hip_atomic_store(a.idx + (int64_t)t * a.K + rank, my_e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
+      st_dev(a.w + (int64_t)t * a.K + rank, w);
+    } else {
       a.idx[(int64_t)t * a.K + rank] = my_e;
-    a.w[(int64_t)t * a.K + rank] = w;
+      a.w[(int64_t)t * a.K + rank] = w;
+    }
     if (sidx) sidx[t * a.K + rank] = my_e;
   }
   if (a.clog) {
@@ -325,10 +358,25 @@ MOE_DEV void topk_half(const TopkArgs &a, int t, int l32, int *el, float *esc, i
     if (live && l32 == 0) {
       const float m = fmaxf(c0, c1);
       const float x0 = expf(c0 - m), x1 = expf(c1 - m);
-      a.coef[2 * t] = x0 / (x0 + x1);
-      a.coef[2 * t + 1] = x1 / (x0 + x1);
+      if (coherent) {
+        st_dev(a.coef + 2 * t, x0 / (x0 + x1));
+        st_dev(a.coef + 2 * t + 1, x1 / (x0 + x1));
+      } else {
+        a.coef[2 * t] = x0 / (x0 + x1);
+        a.coef[2 * t + 1] = x1 / (x0 + x1);
+      }
     }
   }
+}
+
+// token t on a half-wave (32 lanes, lane l32): topk_half_load then topk_half_select
+template <int SL, bool COH_IN = false>
+MOE_DEV void topk_half(const TopkArgs &a, int t, int l32, int *el, float *esc, int32_t *sidx, bool coherent = false) {
+  float lg[SL], sb[SL];
+  float2 cp;
+  topk_half_load<SL, COH_IN>(a, t, l32, lg, cp);
+  topk_half_sbias<SL>(a, l32, sb);
+  topk_half_select<SL>(a, t, l32, lg, cp, sb, el, esc, sidx, coherent);
 }
 
 }  // namespace
@@ -381,10 +429,21 @@ MOE_DEV void decode_permute(const int32_t *idx, int T, int K, int E, int32_t *__
     else
       return __hip_atomic_load(idx + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  for (int p = tid; p < TK; p += NT) {
-    const int ep = ld_id(p), tp = p / K;
-    atomicAdd(&sm.cnt[ep], 1);
-    atomicOr(&sm.tmask[ep][tp >> 5], 1u << (tp & 31));
+  constexpr int MAXP = (MOE_ROUTE_SMALL_T * 16 + NT - 1) / NT;  // slots per thread (K <= 16)
+  int epv[MAXP];  // the thread's slots' experts, read once
+#pragma unroll
+  for (int q = 0; q < MAXP; ++q) {
+    const int p = tid + q * NT;
+    epv[q] = p < TK ? ld_id(p) : 0;
+  }
+#pragma unroll
+  for (int q = 0; q < MAXP; ++q) {
+    const int p = tid + q * NT;
+    if (p < TK) {
+      const int ep = epv[q], tp = p / K;
+      atomicAdd(&sm.cnt[ep], 1);
+      atomicOr(&sm.tmask[ep][tp >> 5], 1u << (tp & 31));
+    }
   }
   __syncthreads();
   // exclusive scan over experts of (count | tiles << 16), experts EPT tid .. EPT tid + EPT-1
@@ -439,13 +498,88 @@ MOE_DEV void decode_permute(const int32_t *idx, int T, int K, int E, int32_t *__
   }
   __syncthreads();
   // rank of slot p among the slots of its expert: earlier tokens that chose the same expert
-  for (int p = tid; p < TK; p += NT) {
-    const int ep = ld_id(p), tp = p / K;
+#pragma unroll
+  for (int q = 0; q < MAXP; ++q) {
+    const int p = tid + q * NT;
+    if (p >= TK) continue;
+    const int ep = epv[q], tp = p / K;
     int rank = __popc(sm.tmask[ep][tp >> 5] & ((1u << (tp & 31)) - 1u));
     for (int w = 0; w < (tp >> 5); ++w) rank += __popc(sm.tmask[ep][w]);
     const int pos = sm.offs[ep] + rank;
     st(sorted_slot + pos, p);
     slot_pos[p] = pos;
+  }
+}
+
+}  // namespace
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// One tile of the decode router: logits of tokens 16 tt .. 16 tt + 15 for rows 16 rt ..
+// 16 rt + 15 of [W_r; coef head], bf16 x and W_r, MFMA 16x16x32 with the reduction split over
+// the 8 waves of a 512-thread workgroup and summed in a fixed order.  Rows 0..E-1 are the
+// experts (+ logit_bias); with a blend head, rows E and E+1 are its two rows (+ coef_b),
+// written to clog [T][2].  Every wave issues the loads of up to DEPTH of its reduction steps
+// before the first MFMA (the sum runs over the steps in the same order for every DEPTH).  red: 8*16*17 floats of LDS.  COH: the logits are stored at device
+// scope (read by other workgroups of the same launch).
+// ---------------------------------------------------------------------------
+template <bool COH, int DEPTH = 8>
+MOE_DEV void router_tile_bf16(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
+                              const float *__restrict__ lbias, float *__restrict__ logits, int T, int H, int E,
+                              const uint16_t *__restrict__ cw, const float *__restrict__ cb,
+                              float *__restrict__ clog, int tt, int rt, float (*red)[16][17]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = tt * 16, e0 = rt * 16;
+  const int r = lane & 15, kb = lane >> 4;
+  const int trow = min(t0 + r, T - 1), er = e0 + r;
+  const uint16_t *wrow = er < E ? W + (int64_t)er * H
+                                : ((cw && er < E + 2) ? cw + (int64_t)(er - E) * H : W + (int64_t)(E - 1) * H);
+  const u32x4_t *xa = (const u32x4_t *)(x + (int64_t)trow * H + kb * 8);
+  const u32x4_t *wb = (const u32x4_t *)(wrow + kb * 8);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const int nsteps = H >> 5;
+  for (int s0 = wave; s0 < nsteps; s0 += 8 * DEPTH) {
+    u32x4_t av[DEPTH], bv[DEPTH];
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) {
+      const int st = min(s0 + 8 * i, nsteps - 1);
+      av[i] = xa[st * 4];
+      bv[i] = wb[st * 4];
+    }
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i)
+      if (s0 + 8 * i < nsteps)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[i]),
+                                                      __builtin_bit_cast(bf16x8_t, bv[i]), acc, 0, 0, 0);
+  }
+  // acc[i] holds row (token) 4*kb+i, column r of the 16x16 tile
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][4 * kb + i][r] = acc[i];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int m = threadIdx.x >> 4, n = threadIdx.x & 15;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) v += red[w][m][n];
+    const int t = t0 + m, e = e0 + n;
+    if (t < T) {
+      float *dst = nullptr;
+      float val = 0.f;
+      if (e < E) {
+        dst = logits + (int64_t)t * E + e;
+        val = v + (lbias ? lbias[e] : 0.f);
+      } else if (cw && e < E + 2) {
+        dst = clog + 2 * t + (e - E);
+        val = v + cb[e - E];
+      }
+      if (dst) {
+        if constexpr (COH)
+          st_dev(dst, val);
+        else
+          *dst = val;
+      }
+    }
   }
 }
 

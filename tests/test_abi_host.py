@@ -47,6 +47,7 @@ def test_status_strings_and_version():
     assert moe.abi_version() >> 16 == 2   # 2: moe_linear.packed and moe_pack_weights
     assert L.moe_timing_enable(42) == moe.MOE_ERR_ARG
     assert L.moe_set_decode_fusion(2) == moe.MOE_ERR_ARG
+    assert L.moe_set_decode_fusion(-1) == moe.MOE_ERR_ARG
     assert L.moe_set_decode_fusion(1) == moe.MOE_OK
     assert L.moe_timing_enable(0) == moe.MOE_OK
     assert moe.moe_timing_read() == (0, 0.0)

@@ -368,30 +368,56 @@ def _decode_specs():
     }
 
 
+def _run_separate(b, y_dtype=torch.float32):
+    moe.moe_set_decode_fusion(False)
+    try:
+        return run_block(b, y_dtype=y_dtype)
+    finally:
+        moe.moe_set_decode_fusion(True)
+
+
 @pytest.mark.parametrize("name", list(_decode_specs()))
 def test_decode_fused_matches_oracle_and_separate_launches(name):
-    """Decode-sized batches run gate/up, down and the combine in one launch by default.
-    The result matches the oracle (C16) and, bit for bit, the separate launches (the same
-    arithmetic in the same order); the status word stays 0 (every wait between
-    workgroups completed)."""
+    """Decode-sized batches run the router, selection and permutation in one launch and
+    gate/up and down in one persistent launch by default.  The result matches the oracle
+    (C16) and, bit for bit, the separate launches (the same arithmetic in the same order);
+    the status word stays 0 (every wait between workgroups completed), also on a second
+    call (the counters are left zero)."""
     spec, T = _decode_specs()[name]
     b = synth.make_block(spec, DEV, T=T)
     y, idx, w, ob, routing = _full_check(b, f"fused decode {name}")
-    announce(f"status + separate launches {name}")
+    announce(f"status + other modes {name}")
     dev = b.x.device
     ym = torch.empty(b.T, b.H, dtype=torch.float32, device=dev)
     ws = moe.moe_block_forward(b.x, block_desc(b), ym)
     torch.cuda.synchronize()
     assert int(moe.call_status(ws, b.T, b.K, b.E)[0]) == 0
     assert torch.equal(ym, y), "the fused path is not deterministic"
-    moe.moe_set_decode_fusion(False)
-    try:
-        yu, iu, wu = run_block(b)
-    finally:
-        moe.moe_set_decode_fusion(True)
-    assert torch.equal(iu, idx) and torch.equal(wu, w)
+    yu, iu, wu = _run_separate(b)
+    assert torch.equal(iu, idx) and torch.equal(wu, w), "routing differs from the separate launches"
     d = (yu - y).abs().max().item()
-    assert torch.equal(yu, y), f"one launch vs separate launches differ: max |diff| {d:.3g}"
+    assert torch.equal(yu, y), f"decode launches vs separate launches differ: max |diff| {d:.3g}"
+    y1, _, _ = run_block(b, y_dtype=torch.bfloat16)
+    y0, _, _ = _run_separate(b, torch.bfloat16)
+    assert torch.equal(y1, y0), "bf16 output: decode launches vs separate launches differ"
+
+
+def test_decode_fused_call_sequence():
+    """Calls of different sizes and layers in a row on one stream, each bit-identical to the
+    separate launches: every call starts from the counters the one before left."""
+    c2s = synth.SMALL_SPECS["c2"]
+    blocks = [synth.make_block(synth.FULL_SPECS["c2"], DEV),
+              synth.make_block(c2s, DEV, T=5),
+              synth.make_block(synth.replace(c2s, name="c2s-none", shared_mode="none", seed=72), DEV, T=48),
+              synth.make_block(synth.FULL_SPECS["c2"], DEV, T=1)]
+    announce("fused call sequence: expected outputs from the separate launches")
+    want = [_run_separate(b)[0] for b in blocks]
+    for rep in range(2):
+        for i, b in enumerate(blocks):
+            announce(f"fused call sequence rep {rep} block {i} (T={b.T})")
+            y, _, _ = run_block(b)
+            torch.cuda.synchronize()
+            assert torch.equal(y, want[i]), f"rep {rep} block {i}: one launch differs from separate launches"
 
 
 # ----------------------------------------------------------------------------
