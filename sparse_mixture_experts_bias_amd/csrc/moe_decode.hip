@@ -110,7 +110,9 @@ __global__ __launch_bounds__(512) void decode_route(const FusedParams p) {
       last = __hip_atomic_fetch_add(p.cnt + kTileDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == G - 1;
     __syncthreads();
     if (!last) return;
-    topk_half<SL, true>(ta, half, l32, el[half], esc[half], sidx, false);
+    // only the waves with a live token (a dead half-wave of one works on a token past the
+    // end and stores nothing): idle waves would share the SIMDs' issue slots
+    if ((tid >> 6) < (T + 1) / 2) topk_half<SL, true>(ta, half, l32, el[half], esc[half], sidx, false);
     __syncthreads();
     decode_permute<512, false, true>(sidx, T, ta.K, E, p.counts, p.offsets, (int32_t *)p.gu.seg[0].A.gather,
                                      p.slot_pos, (int4 *)p.gu.tiles, (int *)p.gu.tile_count, 16, perm);
