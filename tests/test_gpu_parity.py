@@ -420,6 +420,31 @@ def test_decode_fused_call_sequence():
             assert torch.equal(y, want[i]), f"rep {rep} block {i}: one launch differs from separate launches"
 
 
+def test_block_forward_under_graph_capture():
+    """A decode block captured in a HIP graph (torch.cuda.graph) takes the separate launches
+    (the decode launches keep per-stream counters that a replay elsewhere could share) and
+    every replay, with eager calls of the decode launches between replays, equals the eager
+    result bit for bit."""
+    b = synth.make_block(synth.FULL_SPECS["c2"], DEV)
+    desc = block_desc(b)
+    announce("graph capture: eager reference")
+    y_ref, _, _ = run_block(b)
+    y = torch.empty_like(y_ref)
+    ws = moe.moe_block_forward(b.x, desc, y)          # the workspace, allocated outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_block_forward(b.x, desc, y, ws=ws)
+    for rep in range(3):
+        announce(f"graph capture: replay {rep}")
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"replay {rep} differs from the eager result"
+        y_e, _, _ = run_block(b)                          # eager decode launches between replays
+        assert torch.equal(y_e, y_ref)
+
+
 # ----------------------------------------------------------------------------
 # the packed weight stream: a pure permutation of the stored planes
 # ----------------------------------------------------------------------------
