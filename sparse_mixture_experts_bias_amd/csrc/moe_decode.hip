@@ -1,4 +1,5 @@
-// moe_decode.hip - a decode-sized batch of the block in two launches.
+// moe_decode.hip - the two kernels of a decode-sized batch (the weighted combine follows as
+// a third launch, moe_combine.hip).
 // (libmir-metal's execute hands the gate/up kernel the routing indices and the clamp limit,
 // and the down kernel the same indices with the routing weights, which makes the layer
 // output; mlxcel PR #1044, "Validation", describes a fused MoE kernel for one-token decode.)
@@ -6,8 +7,9 @@
 // decode_route (ceil(T/16) * ceil(R/16) workgroups, R = experts + the blend head's 2 rows):
 //   workgroup (tt, rt) computes one 16-token x 16-row tile of the router logits.  For up to
 //   16 tokens the last tile to finish selects for every token (one half-wave each); for
-//   more, tile (tt, rt) selects token 16 tt + rt once its block's tiles are in.  The last
-//   selection to finish builds counts, offsets, sorted_slot, slot_pos and the m-tile list.
+//   more, tile (tt, rt) selects tokens 16 tt + rt + nRT h of its block once the block's
+//   tiles are in.  The last selection to finish builds counts, offsets, sorted_slot,
+//   slot_pos and the m-tile list.
 //   The launch also clears the m-tile counters of the experts launch that follows, and the
 //   permuting workgroup clears the launch's own counters.
 // decode_fused (persistent: at most what the device holds at once):
