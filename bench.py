@@ -99,6 +99,7 @@ def work_model(b, hit):
 KERNEL_SOURCES = {
     "gateup": ("moe_gemm_ws.hip", "moe_gemm.hip", "moe_mfma.h", "moe_kernels.h", "moe_device.h"),
     "decode_fused": ("moe_decode.hip", "moe_ws.h", "moe_topk.h", "moe_mfma.h", "moe_kernels.h", "moe_device.h"),
+    "gateup_tall": ("moe_gemm_tall.hip", "moe_mfma.h", "moe_kernels.h", "moe_device.h"),
 }
 
 
@@ -348,7 +349,8 @@ def roofline_of(wl, r, hbm_bound, dev, with_peak=True):
         mp = measured_peak(hbm_bound, dev)
         roof["measured_peak"] = mp
         roof["frac_of_measured"] = round(roof["achieved"] / mp["value"], 4)
-    roof["traffic"] = measured_traffic(wl)
+    # (the MFMA-bound workloads run the 128-row prefill kernel, the HBM-bound ones the decode kernels)
+    roof["traffic"] = measured_traffic(wl, "gateup" if hbm_bound else "gateup_tall")
     roof["kernel"] = "expert_gemm gate/up (grouped, SwiGLU epilogue)"
     roof["kernel_avg_us"] = round(gu_avg_s * 1e6, 2)
     roof["algorithmic_bytes_per_launch"] = wm["gu_bytes"]
