@@ -392,6 +392,9 @@ def main():
     ap.add_argument("--separate-decode-launches", action="store_true",
                     help="run decode-sized batches with separate router, routing, gate/up, down and combine "
                          "launches")
+    ap.add_argument("--single-decode-launch", action="store_true",
+                    help="run decode-sized batches of up to 16 tokens in one launch (routing, experts and "
+                         "combine) instead of three")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (the reference kernel that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -414,10 +417,10 @@ def main():
 
     dev = "cuda:0"
     wl = args.workload
-    fusion = 0 if args.separate_decode_launches else 1
-    if not fusion:
+    fusion = 0 if args.separate_decode_launches else (2 if args.single_decode_launch else 1)
+    if fusion != 1:
         import sparse_mixture_experts_bias_amd as moe
-        moe.moe_set_decode_fusion(False)
+        moe.moe_set_decode_fusion(fusion)
     r = measure(wl, args.steps, args.warmup, args.gu_every, args.copies, args.tokens)
     b = r["b"]
     hbm_bound = wl in ("c1", "c2", "c5")

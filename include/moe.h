@@ -266,16 +266,23 @@ MOE_API moe_status moe_block_forward_noalloc(const void *x, int32_t x_dtype, int
  *   enabled = 1 (default): the router, selection and permutation in one launch, gate/up and
  *                the down projection of every slot (and of the shared expert) in one
  *                persistent launch, then the weighted combine (3 launches per block);
+ *   enabled = 2: the same, except that a batch of at most 16 tokens with an f32 or bf16
+ *                output and a hidden size that is a multiple of 32 (at most 8192) runs in one
+ *                launch: router tiles, selection and permutation first, then the experts,
+ *                and each 32-column block of the output combined by the wave that completes
+ *                it (the pages' fused single-token decode kernel, mlxcel PR #1044,
+ *                "Validation"; not faster than the three launches on MI355X);
  *   enabled = 0: separate router, routing, gate/up, down and combine launches (5 in all).
- * Both give the same bits: the same arithmetic in the same order (unlike the pages' fused
+ * All give the same bits: the same arithmetic in the same order (unlike the pages' fused
  * MoE decode kernel, whose output was not byte-identical to the unfused path; this switch
- * mirrors theirs: mlxcel PR #1044, "Validation", MLXCEL_FUSED_MOE).
+ * mirrors theirs: MLXCEL_FUSED_MOE).
  * The launches hand work between workgroups through counters that the library keeps in its
- * code object, one block of 73 KiB for each of up to 16 streams per device (each call leaves
- * them zero for the next).  A call on a 17th stream of a device, on a stream of another
- * device than the current one, or on a stream under capture (a graph replayed on another
- * stream would share the block) takes the separate launches.
- * Process-wide, not thread-safe; enabled must be 0 or 1 (else MOE_ERR_ARG).
+ * code object: three blocks of 110 KiB for each of up to 16 streams per device (one for the
+ * three launches, two that single launches use in turn; each call leaves the next call's
+ * block zero).  A call on a 17th stream of a device, on a stream of another device than the
+ * current one, or on a stream under capture (a graph replayed on another stream would share
+ * the blocks) takes the separate launches.
+ * Process-wide, not thread-safe; enabled must be 0, 1 or 2 (else MOE_ERR_ARG).
  */
 MOE_API moe_status moe_set_decode_fusion(int32_t enabled);
 

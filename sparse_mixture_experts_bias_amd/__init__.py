@@ -533,10 +533,14 @@ def call_status(ws: torch.Tensor, T: int, K: int, E: int) -> torch.Tensor:
     return ws[off:off + 4].view(torch.int32)
 
 
-def moe_set_decode_fusion(enabled: bool):
-    """Decode-sized batches: the routing launch and one experts launch (default), or the
-    separate router, routing, gate/up and down launches."""
-    _check(lib().moe_set_decode_fusion(1 if enabled else 0))
+DECODE_SEPARATE, DECODE_THREE_LAUNCHES, DECODE_SINGLE_LAUNCH = 0, 1, 2
+
+
+def moe_set_decode_fusion(mode):
+    """Decode-sized batches: True / DECODE_THREE_LAUNCHES (default: routing, experts and
+    combine launches), DECODE_SINGLE_LAUNCH (one launch up to 16 tokens, three above), or
+    False / DECODE_SEPARATE (the separate router, routing, gate/up, down and combine launches)."""
+    _check(lib().moe_set_decode_fusion(int(mode)))
 
 
 def moe_timing_enable(kind: int):

@@ -216,7 +216,8 @@ WMat wmat(const moe_linear &L, bool gateup = false) {
 
 int wf_of(const moe_linear &L) { return L.fmt == MOE_W_DENSE ? WF_DENSE : (L.fmt == MOE_W_AFFINE4 ? WF_AFFINE4 : WF_MXFP4); }
 
-// moe_set_decode_fusion: the decode launches (on by default)
+// moe_set_decode_fusion: 1 (default) three launches; 2 one launch up to 16 tokens (three
+// above); 0 the separate launches
 int g_decode_fusion = 1;
 
 // ---------------------------------------------------------------------------
@@ -582,18 +583,22 @@ moe_status combine(int odt, int ydt, const void *o, int64_t ldo, const int32_t *
 // may be replayed on another, beside calls on the first, so a capturing stream takes the
 // separate launches.
 // ---------------------------------------------------------------------------
+// Each slot holds three blocks: [0] the three-launch path's, [1] and [2] the single launch's,
+// used in turn (each call clears the other one for the next call).
 constexpr int kCounterSlots = 16;
-static __device__ __align__(256) int fused_counters[kCounterSlots][kCounterInts];
+static __device__ __align__(256) int fused_counters[kCounterSlots][3][kCounterInts];
 
 constexpr int kCounterDevices = 64;
 std::mutex g_counter_mu;
 int *g_counter_ptr[kCounterDevices] = {};
 hipStream_t g_counter_stream[kCounterDevices][kCounterSlots];
 int g_counter_used[kCounterDevices] = {};
+int g_counter_turn[kCounterDevices][kCounterSlots] = {};  // the single launch's next block (0 or 1)
 
-// the counter block of stream s (on the calling thread's current device), or nullptr: s is
-// capturing or on another device, or every block already belongs to another stream
-int *counters_for(hipStream_t s) {
+// the counter blocks of stream s (on the calling thread's current device), or nullptr: s is
+// capturing or on another device, or every slot already belongs to another stream.  *turn
+// (when given) is the slot's single-launch turn, which the caller flips after a launch.
+int *counters_for(hipStream_t s, int **turn = nullptr) {
   int dev = -1, sdev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kCounterDevices) return nullptr;
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -618,7 +623,8 @@ int *counters_for(hipStream_t s) {
     g_counter_stream[dev][i] = s;
     ++g_counter_used[dev];
   }
-  return g_counter_ptr[dev] + (size_t)i * kCounterInts;
+  if (turn) *turn = &g_counter_turn[dev][i];
+  return g_counter_ptr[dev] + (size_t)i * 3 * kCounterInts;
 }
 
 // ---------------------------------------------------------------------------
@@ -714,7 +720,7 @@ moe_status moe_pack_weights(const moe_linear *a, const moe_linear *b, void *out,
 
 moe_status moe_set_decode_fusion(int32_t enabled) {
   g_err[0] = 0;
-  CHECK(enabled == 0 || enabled == 1, MOE_ERR_ARG, "enabled must be 0 or 1 (got %d)", enabled);
+  CHECK(enabled >= 0 && enabled <= 2, MOE_ERR_ARG, "the decode launch mode must be 0, 1 or 2 (got %d)", enabled);
   g_decode_fusion = enabled;
   return MOE_OK;
 }
@@ -1001,7 +1007,8 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   // and route_decode's counter (the decode launches have their own router)
   float *clog = at<float>(ws, o_clog);
   int *st = at<int>(ws, o_st);
-  int *cnt = fused ? counters_for(s) : nullptr;
+  int *turn = nullptr;
+  int *cnt = fused ? counters_for(s, &turn) : nullptr;
   fused = cnt != nullptr;  // (else separate launches)
   int *done = st + 1;
   if (!fused)
@@ -1101,6 +1108,25 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
     fp.status = st;
     const int tub = routed_tiles_ub(TK, E, 16);
     const int units_ub = tub * (fp.gu.seg[0].nblk + fp.dn.seg[0].nblk) + ns_f * (fp.gu.seg[1].nblk + fp.dn.seg[1].nblk);
+    const int mode = !has_shared ? 0 : (blend ? 3 : 2);
+    if (g_decode_fusion == 2 && T <= 16 && (y_dtype == MOE_F32 || y_dtype == MOE_BF16) && D % 32 == 0 &&
+        D <= 32 * kMaxColCnt) {
+      // up to 16 tokens: everything in one launch, the combine included
+      fp.cnt = cnt + (size_t)(1 + *turn) * kCounterInts;
+      fp.cnt_next = cnt + (size_t)(2 - *turn) * kCounterInts;
+      fp.nr_ub = tub;
+      fp.y = y;
+      fp.ldy = H;
+      fp.ydt = y_dtype == MOE_F32 ? DT_F32 : DT_BF16;
+      fp.mode = mode;
+      {
+        Timed tm(TK_FUSED, s, true);
+        HIPCHK(launch_decode_one(wf_of(b->experts.gate), b->experts.gate.group_size, DT_BF16, fp, units_ub, s,
+                                 tm.start(), tm.stop()));
+      }
+      *turn ^= 1;
+      return MOE_OK;
+    }
     {
       Timed tm(TK_ROUTER, s);
       HIPCHK(launch_decode_route(fp, s));
@@ -1111,7 +1137,6 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
                                  tm.start(), tm.stop()));
     }
     // 5. weighted combine + shared add/blend over the token-ordered rows
-    const int mode = !has_shared ? 0 : (blend ? 3 : 2);
     TRY(combine(inter, y_dtype, o, D, nullptr, wts, K, TK, Ti, H, y, H, coef, nullptr, 0.f, mode, s));
     return MOE_OK;
   }

@@ -22,10 +22,18 @@
 //   reads.  (Combining in this launch, by the wave whose down unit completed a 32-column
 //   block of o, put the combine's loads on the launch's tail and measured slower.)
 //
-// (One launch for all of it, with the router tiles and the selection inside the persistent
-// grid and a flag that every workgroup polls, was slower: the routing chain ran while the
-// whole grid polled, and the launch needed a grid-wide count at its end to clear its
-// counters, an atomic from every workgroup on one line.)
+// The single launch (opt-in, up to 16 tokens: decode_fused with ONE): workgroups g < R/16
+// first compute the router tiles; the last of them selects and permutes, stores the ids,
+// weights, coefficients and m-tile list at device scope and sets a flag kept in 32 lines.
+// The units are ordered [gate/up shared][down shared][gate/up routed][down routed], so the
+// shared expert runs while the routing is computed; workgroup g takes units G-1-g, 2G-1-g,
+// ... (the router workgroups the last ones), and a routed unit waits for the flag.  Each
+// down wave counts its 32 output columns once its o rows are stored, and the wave that
+// completes a column block (the last m-tile to get there) combines those columns for every
+// token, in the combine launch's arithmetic.  Each call clears the other of two counter
+// blocks for the next call, so no grid-wide count is needed at the end.  It gives the three
+// launches' bits and is no faster than them on MI355X (1 and 8 tokens: the same, 16: slower,
+// with two workgroups per CU), so it is not the default.
 //
 // Hand-overs between workgroups (on different XCDs, each with its own L2) carry their data
 // as device-scope stores (sc1: the instructions the compiler emits for agent-scope relaxed
@@ -155,14 +163,17 @@ __global__ __launch_bounds__(512) void decode_route(const FusedParams p) {
   for (int i = tid; i <= nTT; i += 512) p.cnt[i == 0 ? kSelCnt : kTtCnt0 + (i - 1) * kCntStride] = 0;
 }
 
-template <int AT, int WF, int GQ, int IT>
-__global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
+// ONE: the single launch of up to 16 tokens (router tiles, selection and permutation first,
+// the combine at the end; see the top of the file)
+template <int AT, int WF, int GQ, int IT, bool ONE>
+__global__ __launch_bounds__(512, ONE ? 4 : 6) void decode_fused(const FusedParams p) {
   using C = WsCfg<WF, GQ>;
   constexpr bool AFF = C::AFF;
   constexpr int MT = 16, KC = C::KC, UE = C::UE, SPU = C::SPU, QE = C::QE, LPU = C::LPU, NU = C::NU;
   constexpr int RB = C::RB, SW = C::SW, STAGE = C::STAGE, NBUF = C::NBUF, NDMA = C::NDMA;
   constexpr float MAGIC = AT == DT_BF16 ? 128.0f : 1024.0f;
   __shared__ __attribute__((aligned(16))) char smem[NBUF * STAGE];
+  __shared__ int uq[2];  // ONE: the workgroup's next units (-1: none left)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -176,10 +187,12 @@ __global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
   asm volatile("" ::"s"(nbg0), "s"(nbg1), "s"(nbd0), "s"(nbd1), "s"(sh_rows), "s"(sh_row0), "s"(max_tiles),
                "s"(tiles), "s"(tcount));
   const int ns = nbg1 > 0 ? (sh_rows + MT - 1) / MT : 0;  // shared m-tiles
-  // routed m-tiles (written by the routing launch)
-  const int nr = min(max(load_uniform_int(tcount), 0), max_tiles);
-  const int Ug_s = ns * nbg1, Ug = Ug_s + nr * nbg0;
-  const int Ud_s = ns * nbd1, U = Ug + Ud_s + nr * nbd0;
+  // routed m-tiles: written by the routing launch, or (ONE) by this launch's routing, known
+  // once the routing flag is set
+  int nr = ONE ? 0 : min(max(load_uniform_int(tcount), 0), max_tiles);
+  const int Ug_s = ns * nbg1, Ud_s = ns * nbd1;
+  int Ug = Ug_s + nr * nbg0;
+  const int U = Ug + Ud_s + nr * nbd0;  // (not ONE)
   // counters, one per 128-byte line: gate/up waves done per m-tile [ns + max_tiles]
   int *const tile_cnt = p.cnt + kTileCnt0;
 
@@ -187,15 +200,48 @@ __global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
     bool dn, sh;
     int e, r0, nr, nb, tile;
   };
+  // the routed m-tile ti of the list (ONE: written in this launch, read at device scope)
+  auto tile_entry = [&](int ti) {
+    const int4 *tp = tiles + min(max(ti, 0), max_tiles - 1);
+    if constexpr (ONE) {
+      const int *q = (const int *)tp;
+      int4 t;
+      t.x = __builtin_amdgcn_readfirstlane(__hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      t.y = __builtin_amdgcn_readfirstlane(__hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      t.z = __builtin_amdgcn_readfirstlane(__hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      t.w = 0;
+      return t;
+    } else {
+      return load_uniform_int4(tp);
+    }
+  };
+  // unit u: not ONE [gate/up: shared, routed][down: shared, routed]; ONE [gate/up shared]
+  // [down shared][gate/up routed][down routed], so that the shared units come before the
+  // routing is known
   auto unit_at = [&](int u) {
     Unit x;
-    x.dn = u >= Ug;
-    int v = x.dn ? u - Ug : u;
-    const int us = x.dn ? Ud_s : Ug_s;
+    int v, us;
+    if constexpr (ONE) {
+      const int Us = Ug_s + Ud_s;
+      if (u < Us) {
+        x.dn = u >= Ug_s;
+        v = x.dn ? u - Ug_s : u;
+        us = v + 1;  // shared
+      } else {
+        const int w = u - Us, ugr = nr * nbg0;
+        x.dn = w >= ugr;
+        v = x.dn ? w - ugr : w;
+        us = 0;  // routed
+      }
+    } else {
+      x.dn = u >= Ug;
+      v = x.dn ? u - Ug : u;
+      us = x.dn ? Ud_s : Ug_s;
+    }
     x.sh = v < us;
     if (x.sh) {
       const int nb1 = max(x.dn ? nbd1 : nbg1, 1);
-      const int ti = v / nb1;
+      const int ti = min(v / nb1, max(ns - 1, 0));
       x.nb = v - ti * nb1;
       x.e = 0;
       x.r0 = sh_row0 + ti * MT;
@@ -204,10 +250,10 @@ __global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
     } else {
       v -= us;
       const int nb0 = max(x.dn ? nbd0 : nbg0, 1);
-      const int ti = v / nb0;
+      const int ti = min(v / nb0, max_tiles - 1);
       x.nb = v - ti * nb0;
       // (clamped into range: whatever the list held, no access leaves its buffer)
-      const int4 t = load_uniform_int4(tiles + ti);
+      const int4 t = tile_entry(ti);
       x.e = min(max(t.x, 0), n_exp - 1);
       x.r0 = min(max(t.y, 0), sh_row0 - 1);
       x.nr = min(max(t.z, 1), min(MT, sh_row0 - x.r0));
@@ -219,17 +265,95 @@ __global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
 #define SEG(x, f) \
   ((x).dn ? ((x).sh ? p.dn.seg[1].f : p.dn.seg[0].f) : ((x).sh ? p.gu.seg[1].f : p.gu.seg[0].f))
   auto nch_of = [&](const Unit &x) { return (SEG(x, K) + KC - 1) / KC; };
-  auto nch_u = [&](int u) {  // the same from the unit index alone (no tile read)
+  auto nch_u = [&](int u) {  // the same from the unit index alone (no tile read; not ONE)
     const bool dn = u >= Ug;
     const int v = dn ? u - Ug : u;
     const bool sh = v < (dn ? Ud_s : Ug_s);
     const int Kd = dn ? (sh ? p.dn.seg[1].K : p.dn.seg[0].K) : (sh ? p.gu.seg[1].K : p.gu.seg[0].K);
     return (Kd + KC - 1) / KC;
   };
+  // ONE: the routed m-tile count, once the routing flag has been seen (by this wave, or by
+  // loader wave 0 before a barrier this wave has passed)
+  bool have_nr = !ONE;
+  auto learn_nr = [&]() {
+    if (!have_nr) {
+      nr = min(max(__builtin_amdgcn_readfirstlane(
+                       __hip_atomic_load(tcount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)),
+                   0),
+               min(max_tiles, p.nr_ub));
+      Ug = Ug_s + nr * nbg0;
+      have_nr = true;
+    }
+  };
+  // ONE: unit u of this workgroup's sequence if it exists (a routed one waits for the routing)
+  auto unit_if = [&](int u) {
+    const int Us = Ug_s + Ud_s;
+    if (u < Us) return u;
+    if (!have_nr) {
+      wait_count(p.cnt + kFlag0 + (g % kFlagCopies) * kCntStride, 1, p.status, lane);
+      learn_nr();
+    }
+    return u < Us + nr * (nbg0 + nbd0) ? u : -1;
+  };
   // gate/up waves that write an m-tile's h rows: 4 per column block of its segment
   auto tile_target = [&](const Unit &x) { return 4 * (x.sh ? nbg1 : nbg0); };
 
-  if (g >= U) return;
+  int v0 = g;  // the first unit (not ONE: units g, g + G, ...)
+  if constexpr (ONE) {
+    const TopkArgs &ta = p.ta;
+    const int T = ta.T, E = ta.E;
+    const int nRT = (E + (p.cw ? 2 : 0) + 15) / 16;
+    if (g == 0 && tid == 0) __hip_atomic_store(p.status, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the next call's counters start at zero
+    if (g == G - 1) {
+      for (int i = tid; i < 1 + kMaxTileCnt + kMaxColCnt + kFlagCopies; i += 512) {
+        // kTileDone, then the m-tile counters, the column counters and the flag copies (one
+        // contiguous run of lines from kTileCnt0 on)
+        p.cnt_next[i == 0 ? kTileDone : kTileCnt0 + (i - 1) * kCntStride] = 0;
+      }
+    }
+    if (g < nRT) {
+      // router tile (0, g); the last tile to finish selects for every token (one half-wave
+      // each) and permutes; the ids, weights, coefficients and m-tile list are stored at
+      // device scope for the workgroups of this launch, then the routing flag is set.  Its
+      // LDS is the stage buffers', unused until the units start.
+      float (*red)[16][17] = (float (*)[16][17])smem;
+      int (*el)[16] = (int (*)[16])(smem + 8 * 16 * 17 * 4);
+      float (*esc)[16] = (float (*)[16])(smem + 8 * 16 * 17 * 4 + 1024);
+      int32_t *sidx = (int32_t *)(smem + 8 * 16 * 17 * 4 + 2048);
+      DecodePermSmem<512> &perm = *(DecodePermSmem<512> *)(smem + 8 * 16 * 17 * 4 + 3072);
+      static_assert(8 * 16 * 17 * 4 + 3072 + sizeof(DecodePermSmem<512>) <= NBUF * STAGE, "routing LDS");
+      const int half = tid >> 5, l32 = tid & 31;
+      router_tile_bf16<true>(p.x, p.Wr, p.lbias, (float *)ta.logits, T, p.H, E, p.cw, p.cb, (float *)ta.clog, 0, g,
+                             red);
+      wait_vmcnt<0>();  // this thread's logit stores have completed
+      __syncthreads();
+      if (tid == 0)
+        uq[1] = __hip_atomic_fetch_add(p.cnt + kTileDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nRT - 1;
+      __syncthreads();
+      if (uq[1]) {
+        if ((tid >> 6) < (T + 1) / 2) topk_half<8, true>(ta, half, l32, el[half], esc[half], sidx, true);
+        __syncthreads();
+        decode_permute<512, true, true>(sidx, T, ta.K, E, p.counts, p.offsets, (int32_t *)p.gu.seg[0].A.gather,
+                                        p.slot_pos, (int4 *)p.gu.tiles, (int *)p.gu.tile_count, 16, perm);
+        wait_vmcnt<0>();  // this thread's stores have completed
+        __syncthreads();
+        if (tid < kFlagCopies)
+          __hip_atomic_store(p.cnt + kFlag0 + tid * kCntStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();  // the routing LDS is free
+    }
+    // units G-1-g, 2G-1-g, ...: the router workgroups take the last ones
+    if (wave == 4) {
+      const int v = unit_if(G - 1 - g);
+      if (lane == 0) uq[0] = v;
+    }
+    stage_barrier();
+    v0 = __builtin_amdgcn_readfirstlane(uq[0]);
+    if (v0 < 0) return;
+  } else {
+    if (g >= U) return;
+  }
 
   if (wave >= 4) {
     // ---------------- loader waves: row block lw's records, activation rows 4 lw .. 4 lw + 3
@@ -264,8 +388,15 @@ __global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
       int gi[4];
       if (gat) {
         const int *g0 = gat + x.r0;
-        load_uniform_ints4(g0 + min(4 * lw, x.nr - 1), g0 + min(4 * lw + 1, x.nr - 1), g0 + min(4 * lw + 2, x.nr - 1),
-                           g0 + min(4 * lw + 3, x.nr - 1), gi);
+        if (ONE && !x.sh) {  // the gather list of this launch's routing: device scope
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            gi[k] = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(g0 + min(4 * lw + k, x.nr - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        } else {
+          load_uniform_ints4(g0 + min(4 * lw, x.nr - 1), g0 + min(4 * lw + 1, x.nr - 1),
+                             g0 + min(4 * lw + 2, x.nr - 1), g0 + min(4 * lw + 3, x.nr - 1), gi);
+        }
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -316,6 +447,43 @@ __global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
         }
       }
     };
+    if constexpr (ONE) {
+      // the unit sequence G-1-g, + G, ...: loader wave 0 finds the next unit once the
+      // current one's last stage is on its way, and hands it over through LDS.  (A routed
+      // unit is decoded only with the routed m-tile count: loader wave 0 has seen the routing
+      // flag before the barrier that handed the unit over.)
+      if (v0 >= Ug_s + Ud_s) learn_nr();
+      cur = unit_at(v0);
+      cn = nch_of(cur);
+      enter_w(cur);
+      a_pending = true;
+      issue(0);
+      for (int st = 0, k = 0, un = v0;; ++st) {
+        if (cc == cn - 1 && lw == 0) {
+          const int v = unit_if(un + G);
+          if (lane == 0) uq[(k + 1) & 1] = v;
+        }
+        wait_vmcnt<0>();  // stage st has landed
+        stage_barrier();  // stage st is handed over; the buffer of stage st - 1 is free
+        if (cc + 1 < cn) {
+          ++cc;
+        } else {
+          const int v = __builtin_amdgcn_readfirstlane(uq[(k + 1) & 1]);
+          if (v < 0) break;
+          ++k;
+          un = v;
+          if (v >= Ug_s + Ud_s) learn_nr();
+          cur = unit_at(v);
+          cn = nch_of(cur);
+          enter_w(cur);
+          a_pending = true;
+          cc = 0;
+        }
+        issue((st + 1) % NBUF);
+      }
+      wait_vmcnt<0>();
+      return;
+    }
     // past the last unit the cursor stays on the last stage (reloaded into free buffers)
     auto advance = [&]() {
       if (cc + 1 < cn) {
@@ -355,8 +523,61 @@ __global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
   const uint32_t msk = in_vgpr(0x000F000Fu);
   const uint32_t mag = in_vgpr(AT == DT_BF16 ? 0x43004300u : 0x64006400u);
   const int Dout = p.Dout;
+  // ONE: y for columns c0 .. c0 + 31 of every token, from the o rows of this launch (device
+  // scope): the weighted sum over the slots in ascending order, then the shared expert added
+  // or blended, in the combine launch's arithmetic.  Lane: token lane / 4, 8 columns.
+  auto combine_cols = [&](int c0) {
+    const TopkArgs &ta = p.ta;
+    const int T = ta.T, K = ta.K, t = lane >> 2, c = c0 + 8 * (lane & 3);
+    if (t >= T) return;
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+        p.dn.out, (short)0, (int)((int64_t)(T * K + (p.mode >= 2 ? T : 0)) * Dout * 2), 0x00020000);
+    auto row8 = [&](int r, float (&f)[8]) {
+      const u32x4_t v = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ors, (uint32_t)(((int64_t)r * Dout + c) * 2), 0, kSC1));
+      unpack8<DT_BF16>(v, f);
+    };
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < K; ++j) {
+      const float w = __uint_as_float(
+          __hip_atomic_load((const uint32_t *)ta.w + (int64_t)t * K + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      float f[8];
+      row8(t * K + j, f);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = fmaf(w, f[q], v[q]);
+    }
+    if (p.mode >= 2) {
+      float sv[8];
+      row8(T * K + t, sv);
+      if (p.mode == 2) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] += sv[q];
+      } else {
+        const float c0b = __uint_as_float(
+            __hip_atomic_load((const uint32_t *)ta.coef + 2 * t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        const float c1b = __uint_as_float(
+            __hip_atomic_load((const uint32_t *)ta.coef + 2 * t + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = fmaf(c0b, v[q], c1b * sv[q]);
+      }
+    }
+    const int64_t yi = (int64_t)t * p.ldy + c;
+    if (p.ydt == DT_F32) {
+      float *yp = (float *)p.y + yi;
+      *(f32x4_t *)yp = f32x4_t{v[0], v[1], v[2], v[3]};
+      *(f32x4_t *)(yp + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+    } else {
+      u32x4_t wv;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        wv[q] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2 * q]) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2 * q + 1]) << 16);
+      *(u32x4_t *)((uint16_t *)p.y + yi) = wv;
+    }
+  };
   int s = 0;
-  for (int u = g; u < U; u += G) {
+  for (int k = 0, u = v0; ONE ? u >= 0 : u < U; ++k, u = ONE ? __builtin_amdgcn_readfirstlane(uq[k & 1]) : u + G) {
+    if (ONE && u >= Ug_s + Ud_s) learn_nr();
     const Unit x = unit_at(u);
     const bool gu = !x.dn;
     const int Kd = SEG(x, K), n = nch_of(x), rows = SEG(x, w0.rows);
@@ -383,7 +604,10 @@ __global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = min(4 * kq + i, x.nr - 1);
-        orow[i] = x.sh ? x.r0 + m : min(max(gat[x.r0 + m], 0), sh_row0 - 1);
+        const int gs = x.sh ? 0
+                   : (ONE ? __hip_atomic_load(gat + x.r0 + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                          : gat[x.r0 + m]);
+        orow[i] = x.sh ? x.r0 + m : min(max(gs, 0), sh_row0 - 1);
       }
     }
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
@@ -513,6 +737,34 @@ __global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
       // deferred: the loaders of this workgroup may already wait for this m-tile's count
       // before the next stage barrier, which the compute waves reach only after reporting
       publish(tile_cnt + x.tile * kCntStride, lane);
+    } else if constexpr (ONE) {
+      // o in token order at device scope (lanes n16 and n16 + 1 pair their values into one
+      // 32-bit store), then the count of this wave's 32 output columns; the wave that completes
+      // them (the last of the m-tiles) combines those columns for every token
+      uint32_t *o32 = (uint32_t *)p.dn.out;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * kq + i;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int t = 16 * h + n16;
+          const uint16_t hb = __builtin_bit_cast(uint16_t, (__bf16)(acc[h][i] + bo[h]));
+          const uint32_t nb_bits = (uint32_t)__shfl_xor((int)hb, 1, 64) & 0xFFFFu;
+          if (act && m < x.nr && !(n16 & 1) && row_ok(t))
+            __hip_atomic_store(o32 + (((int64_t)orow[i] * Dout + row_of(t)) >> 1), (uint32_t)hb | (nb_bits << 16),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      if (col0 < Dout) {
+        const int cb = col0 / 32;
+        const int old = publish(p.cnt + kColCnt0 + cb * kCntStride, lane);
+        // before the routing is stored no routed down unit has run, so this one is not the
+        // last of its columns (there is at least one routed m-tile)
+        if (!have_nr && __builtin_amdgcn_readfirstlane(__hip_atomic_load(p.cnt + kFlag0 + (g % kFlagCopies) * kCntStride,
+                                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)))
+          learn_nr();
+        if (have_nr && old == ns + nr - 1) combine_cols(col0);
+      }
     } else {
       // o in token order; the combine launch that follows reads it (plain stores: the launch
       // boundary orders them)
@@ -538,12 +790,12 @@ __global__ __launch_bounds__(512, 6) void decode_fused(const FusedParams p) {
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int AT, int WF, int GQ, int IT>
+template <int AT, int WF, int GQ, int IT, bool ONE>
 hipError_t fused_launch_t(const FusedParams &p, int units_ub, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  auto kern = decode_fused<AT, WF, GQ, IT>;
+  auto kern = decode_fused<AT, WF, GQ, IT, ONE>;
   // persistent: every workgroup must be resident at once (the down units wait for gate/up
   // units of other workgroups), so the grid is capped at what the device holds
-  static int per_cu[64] = {0};
+  static int per_cu[64] = {0};  // (per instantiation)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if (!per_cu[dev]) {
@@ -557,7 +809,12 @@ hipError_t fused_launch_t(const FusedParams &p, int units_ub, hipStream_t s, hip
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return hipErrorInvalidDevice;
   const int cap = per_cu[dev] * cus;
-  const int grid = units_ub < cap ? units_ub : cap;
+  int grid = units_ub < cap ? units_ub : cap;
+  if (ONE) {  // at least the router tiles
+    const int nrt = (p.ta.E + (p.cw ? 2 : 0) + 15) / 16;
+    if (nrt > cap) return hipErrorInvalidConfiguration;
+    grid = grid > nrt ? grid : nrt;
+  }
   if (grid <= 0) return hipSuccess;
   if (e0)
     hipExtLaunchKernelGGL(kern, dim3(grid), dim3(512), 0, s, e0, e1, 0, p);
@@ -580,14 +837,31 @@ hipError_t launch_decode_route(const FusedParams &p, hipStream_t s) {
 }
 
 // h and o are stored in the MFMA type of the down projection (bf16 activations: bf16)
-hipError_t launch_decode_fused(int wfmt, int group, int idt, const FusedParams &p, int units_ub, hipStream_t s,
-                               hipEvent_t e0, hipEvent_t e1) {
+template <bool ONE>
+static hipError_t fused_dispatch(int wfmt, int group, int idt, const FusedParams &p, int units_ub, hipStream_t s,
+                                 hipEvent_t e0, hipEvent_t e1) {
   if (idt != DT_BF16) return hipErrorInvalidValue;
-  if (wfmt == WF_MXFP4) return fused_launch_t<DT_BF16, WF_MXFP4, 0, DT_BF16>(p, units_ub, s, e0, e1);
+  if (wfmt == WF_MXFP4) return fused_launch_t<DT_BF16, WF_MXFP4, 0, DT_BF16, ONE>(p, units_ub, s, e0, e1);
   if (wfmt == WF_AFFINE4) {
-    if (group == 32) return fused_launch_t<DT_BF16, WF_AFFINE4, 32, DT_BF16>(p, units_ub, s, e0, e1);
-    if (group == 64) return fused_launch_t<DT_BF16, WF_AFFINE4, 64, DT_BF16>(p, units_ub, s, e0, e1);
-    if (group == 128) return fused_launch_t<DT_BF16, WF_AFFINE4, 128, DT_BF16>(p, units_ub, s, e0, e1);
+    if (group == 32) return fused_launch_t<DT_BF16, WF_AFFINE4, 32, DT_BF16, ONE>(p, units_ub, s, e0, e1);
+    if (group == 64) return fused_launch_t<DT_BF16, WF_AFFINE4, 64, DT_BF16, ONE>(p, units_ub, s, e0, e1);
+    if (group == 128) return fused_launch_t<DT_BF16, WF_AFFINE4, 128, DT_BF16, ONE>(p, units_ub, s, e0, e1);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_fused(int wfmt, int group, int idt, const FusedParams &p, int units_ub, hipStream_t s,
+                               hipEvent_t e0, hipEvent_t e1) {
+  return fused_dispatch<false>(wfmt, group, idt, p, units_ub, s, e0, e1);
+}
+
+// one launch for a batch of up to 16 tokens: router, selection, permutation, gate/up, down and
+// the combine (y of ydt DT_F32 or DT_BF16, hidden a multiple of 32 and at most 32 kMaxColCnt)
+hipError_t launch_decode_one(int wfmt, int group, int idt, const FusedParams &p, int units_ub, hipStream_t s,
+                             hipEvent_t e0, hipEvent_t e1) {
+  if (p.ta.T <= 0 || p.ta.T > 16 || p.ta.E > 256 || p.H % 32 != 0 || p.Dout % 32 != 0 ||
+      p.Dout > 32 * kMaxColCnt || (p.ydt != DT_F32 && p.ydt != DT_BF16) || !(p.mode == 0 || p.mode == 2 || p.mode == 3) ||
+      p.cnt_next == nullptr || p.cnt_next == p.cnt)
+    return hipErrorInvalidValue;
+  return fused_dispatch<true>(wfmt, group, idt, p, units_ub, s, e0, e1);
 }

@@ -103,10 +103,18 @@ constexpr int kCntStride = MOE_CNT_STRIDE;
 // tiles of token block tt done (several blocks), all cleared by the routing launch once
 // used, then the experts launch's m-tile counters (gate/up waves done) from kTileCnt0
 // (cleared by the routing launch before it).
+// The single-launch path (up to 16 tokens) uses two more blocks of the same layout, one per call
+// in turn (each call clears the other for the next): [kTileDone] router tiles done, the m-tile
+// counters from kTileCnt0, from kColCnt0 the down waves done per 32-column block of the
+// output, and from kFlag0 the routing flag (1 once the routing is stored).
 constexpr int kTileDone = 0, kSelCnt = kCntStride, kTtCnt0 = 2 * kCntStride;
 constexpr int kTileCnt0 = kTtCnt0 + (MOE_ROUTE_SMALL_T / 16) * kCntStride;
 constexpr int kMaxTileCnt = 584;  // shared + routed m-tiles
-constexpr int kCounterInts = kTileCnt0 + kMaxTileCnt * kCntStride;
+constexpr int kColCnt0 = kTileCnt0 + kMaxTileCnt * kCntStride;
+constexpr int kMaxColCnt = 256;   // 32-column blocks of the output (hidden <= 8192)
+// the routing flag in kFlagCopies lines (workgroup g polls copy g mod kFlagCopies)
+constexpr int kFlag0 = kColCnt0 + kMaxColCnt * kCntStride, kFlagCopies = 32;
+constexpr int kCounterInts = kFlag0 + kFlagCopies * kCntStride;
 
 struct FusedParams {
   // router: logits [T][E] = x W_r^T (+ logit_bias), blend head logits clog [T][2]
@@ -122,6 +130,12 @@ struct FusedParams {
   int *cnt;                   // the counter block
   int n_tile_cnt;             // m-tile counters the experts launch uses
   int *status;                // 1 when a bounded wait gave up
+  // the single launch (up to 16 tokens) only:
+  int *cnt_next;              // the counter block of the next call, cleared by this one
+  int nr_ub;                  // routed m-tiles at most
+  void *y;                    // the block's output [T][ldy], ydt (DT_F32 or DT_BF16)
+  int ldy, ydt;
+  int mode;                   // 0 routed sum, 2 + shared, 3 blend with the shared expert
 };
 
 struct F32GemmParams {   // f32 activations with DENSE F32 weights (one thread per output)
@@ -192,6 +206,8 @@ hipError_t launch_f32_gemm(const F32GemmParams &p, int rows, hipStream_t s);
 // permutation and m-tile list; clears the experts launch's counters
 hipError_t launch_decode_route(const FusedParams &p, hipStream_t s);
 // the experts launch: grid min(units_ub, what the device holds at once)
+hipError_t launch_decode_one(int wfmt, int group, int idt, const FusedParams &p, int units_ub, hipStream_t s,
+                             hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_decode_fused(int wfmt, int group, int idt, const FusedParams &p, int units_ub, hipStream_t s,
                                hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 // packed stream of one matrix stack (b: the up stack of a gate/up pair, or nullptr)

@@ -46,7 +46,8 @@ def test_status_strings_and_version():
     assert L.moe_status_str(99).decode() == "MOE_ERR_UNKNOWN"
     assert moe.abi_version() >> 16 == 2   # 2: moe_linear.packed and moe_pack_weights
     assert L.moe_timing_enable(42) == moe.MOE_ERR_ARG
-    assert L.moe_set_decode_fusion(2) == moe.MOE_ERR_ARG
+    assert L.moe_set_decode_fusion(3) == moe.MOE_ERR_ARG
+    assert L.moe_set_decode_fusion(2) == moe.MOE_OK
     assert L.moe_set_decode_fusion(-1) == moe.MOE_ERR_ARG
     assert L.moe_set_decode_fusion(1) == moe.MOE_OK
     assert L.moe_timing_enable(0) == moe.MOE_OK

@@ -420,6 +420,60 @@ def test_decode_fused_call_sequence():
             assert torch.equal(y, want[i]), f"rep {rep} block {i}: one launch differs from separate launches"
 
 
+def _run_mode(b, mode, y_dtype=torch.float32, with_state=False):
+    moe.moe_set_decode_fusion(mode)
+    try:
+        return run_block(b, y_dtype=y_dtype, with_state=with_state)
+    finally:
+        moe.moe_set_decode_fusion(moe.DECODE_THREE_LAUNCHES)
+
+
+def _single_specs():
+    c2s = synth.SMALL_SPECS["c2"]
+    d = _decode_specs()
+    return {
+        "c2-full-T1": (synth.FULL_SPECS["c2"], 1),
+        "c2-full-T8": (synth.FULL_SPECS["c2"], 8),
+        "c2-full-T16": (synth.FULL_SPECS["c2"], 16),
+        "c2s-blend-T7": (c2s, 7),
+        "c2s-add-T5": (d["c2s-add"][0], 5),
+        "c2s-none-T3": (d["c2s-none"][0], 3),
+        "c2s-g128-T9": (d["c2s-g128"][0], 9),
+        "mxfp4-add-T4": (d["mxfp4-add"][0], 4),
+    }
+
+
+@pytest.mark.parametrize("name", list(_single_specs()))
+def test_decode_single_launch(name):
+    """The opt-in single launch (up to 16 tokens: router tiles, selection, permutation,
+    gate/up, down and the combine of each 32-column block by the wave that completes it)
+    matches the oracle (C16), gives the three launches' and the separate launches' bits for
+    f32 and bf16 outputs, leaves the oracle's permutation in the workspace and a zero status
+    word, and stays bit-identical on a second call (the counter blocks alternate)."""
+    spec, T = _single_specs()[name]
+    b = synth.make_block(spec, DEV, T=T)
+    announce(f"single launch {name}: expected outputs")
+    y3, i3, w3 = _run_mode(b, moe.DECODE_THREE_LAUNCHES)
+    y0, _, _ = _run_mode(b, moe.DECODE_SEPARATE)
+    assert torch.equal(y3, y0)
+    yb3, _, _ = _run_mode(b, moe.DECODE_THREE_LAUNCHES, y_dtype=torch.bfloat16)
+    moe.moe_set_decode_fusion(moe.DECODE_SINGLE_LAUNCH)
+    try:
+        y1, i1, w1 = _full_check(b, f"single launch {name}")[:3]
+        assert torch.equal(i1, i3) and torch.equal(w1, w3), "routing differs from the three launches"
+        d = (y1 - y3).abs().max().item()
+        assert torch.equal(y1, y3), f"single launch vs three launches differ: max |diff| {d:.3g}"
+        ym = torch.empty(b.T, b.H, dtype=torch.float32, device=b.x.device)
+        ws = moe.moe_block_forward(b.x, block_desc(b), ym)
+        torch.cuda.synchronize()
+        assert int(moe.call_status(ws, b.T, b.K, b.E)[0]) == 0
+        assert torch.equal(ym, y1), "second call differs"
+        yb1, _, _ = run_block(b, y_dtype=torch.bfloat16)
+        assert torch.equal(yb1, yb3), "bf16 output: single launch vs three launches differ"
+    finally:
+        moe.moe_set_decode_fusion(moe.DECODE_THREE_LAUNCHES)
+
+
 def test_block_forward_under_graph_capture():
     """A decode block captured in a HIP graph (torch.cuda.graph) takes the separate launches
     (the decode launches keep per-stream counters that a replay elsewhere could share) and
