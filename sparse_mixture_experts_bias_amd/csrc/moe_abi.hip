@@ -367,8 +367,12 @@ moe_status launch_route_decode(const TopkArgs &a, int32_t *counts, int32_t *offs
 
 size_t perm_ws_bytes(int64_t T, int E) { return T <= 256 ? 0 : (size_t)((T + 255) / 256) * E * 4; }
 
+// done / status: a counter that is zero when the launch starts and the status word (the
+// block's router launch clears both): then more than 256 tokens take the single-launch
+// permutation (up to kPermFusedChunks chunks of 256 tokens), else count, scan and scatter
 moe_status launch_permute(const int32_t *idx, int T, int K, int E, int32_t *counts, int32_t *offsets, int32_t *ss,
-                          int32_t *sp, int32_t *chunk_ws, int4 *tiles, int *tile_count, int mt, hipStream_t s) {
+                          int32_t *sp, int32_t *chunk_ws, int4 *tiles, int *tile_count, int mt, hipStream_t s,
+                          int *done = nullptr, int *status = nullptr) {
   Timed tm(TK_PERM, s);
   if (T <= 256) {
     hipLaunchKernelGGL(perm_small, dim3(1), dim3(256), 0, s, idx, T, K, E, counts, offsets, ss, sp, tiles, tile_count,
@@ -377,6 +381,12 @@ moe_status launch_permute(const int32_t *idx, int T, int K, int E, int32_t *coun
     return MOE_OK;
   }
   const int nch = (T + 255) / 256;
+  if (done && status && nch <= kPermFusedChunks) {
+    hipLaunchKernelGGL(perm_fused, dim3(nch), dim3(256), 0, s, idx, T, K, E, chunk_ws, counts, offsets, ss, sp, tiles,
+                       tile_count, mt, done, status);
+    HIPCHK(hipGetLastError());
+    return MOE_OK;
+  }
   hipLaunchKernelGGL(perm_count, dim3(nch), dim3(256), 0, s, idx, T, K, E, chunk_ws);
   HIPCHK(hipGetLastError());
   hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, s, chunk_ws, nch, E, T * K, counts, offsets, tiles,
@@ -1023,7 +1033,7 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   } else {
     TRY(launch_topk(ta, s));
     TRY(launch_permute(idx, Ti, K, E, counts, offsets, ss, sp, at<int32_t>(ws, o_chunk), mf ? tiles : nullptr,
-                       mf ? tc : nullptr, 16 * mb, s));
+                       mf ? tc : nullptr, 16 * mb, s, done, st));
   }
 
   if (!mf) {

@@ -187,6 +187,10 @@ __global__ void perm_scatter(const int32_t *idx, int T, int K, int E, const int3
 __global__ void perm_small(const int32_t *idx, int T, int K, int E, int32_t *counts, int32_t *offsets,
                            int32_t *sorted_slot, int32_t *slot_pos, int4 *tiles, int *tile_count, int mt);
 __global__ void build_tiles(const int32_t *offsets, int E, int4 *tiles, int *tile_count, int mt);
+constexpr int kPermFusedChunks = 256;  // chunks of 256 tokens of the single-launch permutation
+__global__ void perm_fused(const int32_t *idx, int T, int K, int E, int32_t *chunk_counts, int32_t *counts,
+                           int32_t *offsets, int32_t *sorted_slot, int32_t *slot_pos, int4 *tiles, int *tile_count,
+                           int mt, int *done, int *status);
 
 // host-side launchers (moe_gemm.hip, moe_combine.hip)
 hipError_t launch_expert_gemm(int adt, int wfmt, int group, bool gateup, int odt, int mb, const GemmParams &p,

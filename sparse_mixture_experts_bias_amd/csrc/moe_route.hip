@@ -409,6 +409,34 @@ __global__ __launch_bounds__(1024) void perm_scan(int32_t *__restrict__ chunk_co
   }
 }
 
+// each slot of the chunk's tokens (mask: bit t of word t / 32 of its expert's row set for every
+// token t of the chunk that chose that expert) placed at base[e] + its rank among them
+static __device__ void chunk_scatter(const int32_t *__restrict__ idx, int T, int K, int chunk, const int *base,
+                                     const uint32_t (*mask)[8], int32_t *__restrict__ sorted_slot,
+                                     int32_t *__restrict__ slot_pos) {
+  const int tid = threadIdx.x;
+  const int t = chunk * 256 + tid;
+  if (t >= T) return;
+  const int wd = tid >> 5;
+  const uint32_t below = (1u << (tid & 31)) - 1u;
+  for (int j0 = 0; j0 < K; j0 += kIdBatch) {
+    int ids[kIdBatch];
+    load_ids(idx, t, K, j0, ids);
+#pragma unroll
+    for (int j = 0; j < kIdBatch; ++j) {
+      if (j0 + j < K) {
+        const int e = ids[j];
+        int rank = __popc(mask[e][wd] & below);
+        for (int w = 0; w < wd; ++w) rank += __popc(mask[e][w]);
+        const int pos = base[e] + rank;
+        const int p = t * K + j0 + j;
+        sorted_slot[pos] = p;
+        slot_pos[p] = pos;
+      }
+    }
+  }
+}
+
 // rank of each (token, slot) among the chunk's tokens that chose the same expert
 static __device__ void scatter_chunk(const int32_t *__restrict__ idx, int T, int K, int E, int chunk,
                                      const int *base /* [E], absolute position of the chunk's first slot of e */,
@@ -428,26 +456,7 @@ static __device__ void scatter_chunk(const int32_t *__restrict__ idx, int T, int
     }
   }
   __syncthreads();
-  if (t < T) {
-    const int wd = tid >> 5;
-    const uint32_t below = (1u << (tid & 31)) - 1u;
-    for (int j0 = 0; j0 < K; j0 += kIdBatch) {
-      int ids[kIdBatch];
-      load_ids(idx, t, K, j0, ids);
-#pragma unroll
-      for (int j = 0; j < kIdBatch; ++j) {
-        if (j0 + j < K) {
-          const int e = ids[j];
-          int rank = __popc(mask[e][wd] & below);
-          for (int w = 0; w < wd; ++w) rank += __popc(mask[e][w]);
-          const int pos = base[e] + rank;
-          const int p = t * K + j0 + j;
-          sorted_slot[pos] = p;
-          slot_pos[p] = pos;
-        }
-      }
-    }
-  }
+  chunk_scatter(idx, T, K, chunk, base, mask, sorted_slot, slot_pos);
 }
 
 __global__ __launch_bounds__(256) void perm_scatter(const int32_t *__restrict__ idx, int T, int K, int E,
@@ -458,6 +467,115 @@ __global__ __launch_bounds__(256) void perm_scatter(const int32_t *__restrict__ 
   __shared__ int base[MOE_MAX_EXPERTS];
   for (int e = threadIdx.x; e < E; e += 256) base[e] = chunk_base[(int64_t)blockIdx.x * E + e];
   scatter_chunk(idx, T, K, E, blockIdx.x, base, mask, sorted_slot, slot_pos);
+}
+
+// More than 256 tokens, at most kPermFusedChunks chunks of 256: count, scan and scatter in one
+// launch of a workgroup per chunk (all resident at once).  Each counts its slots per expert
+// and keeps the per-expert token masks in LDS, stores its counts at device scope, waits until
+// its stores have completed and counts itself on *done (zero when the launch starts); once
+// every chunk is in, each reads all the counts (device scope), sums them per expert, scans
+// the totals into the offsets, adds the counts of the chunks before its own, and places its
+// slots; workgroup 0 also writes counts, offsets and the m-tile list.  The same arithmetic and
+// the same positions as perm_count + perm_scan + perm_scatter.  The wait is bounded: if it
+// gives up (only possible when the chunks are not all resident) *status is set.
+__global__ __launch_bounds__(256) void perm_fused(const int32_t *__restrict__ idx, int T, int K, int E,
+                                                  int32_t *__restrict__ chunk_counts, int32_t *__restrict__ counts,
+                                                  int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_slot,
+                                                  int32_t *__restrict__ slot_pos, int4 *tiles, int *tile_count,
+                                                  int mt, int *done, int *status) {
+  __shared__ uint32_t mask[MOE_MAX_EXPERTS][8];
+  __shared__ int offs[MOE_MAX_EXPERTS + 1];
+  __shared__ int base[MOE_MAX_EXPERTS];
+  __shared__ int tmp[16];
+  __shared__ int cls[16];
+  const int tid = threadIdx.x, c = blockIdx.x, nch = gridDim.x;
+  const int t = c * 256 + tid;
+  for (int i = tid; i < E * 8; i += 256) mask[i >> 3][i & 7] = 0u;
+  for (int e = tid; e < E; e += 256) offs[e] = 0;
+  __syncthreads();
+  constexpr int KC = 2 * kIdBatch;  // ids kept in registers for the scatter (top_k <= 16)
+  int idc[KC];
+  if (t < T) {
+    for (int j0 = 0; j0 < K; j0 += kIdBatch) {
+      int ids[kIdBatch];
+      load_ids(idx, t, K, j0, ids);
+#pragma unroll
+      for (int j = 0; j < kIdBatch; ++j) {
+        if (j0 + j < K) {
+          atomicAdd(&offs[ids[j]], 1);
+          atomicOr(&mask[ids[j]][tid >> 5], 1u << (tid & 31));
+        }
+        if (j0 == 0) idc[j] = ids[j];
+        if (j0 == kIdBatch) idc[kIdBatch + j] = ids[j];
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256)
+    __hip_atomic_store(chunk_counts + (int64_t)c * E + e, offs[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_vmcnt<0>();  // this thread's count stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int it = 0;
+    for (; it < (1 << 19); ++it) {
+      if (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= nch) break;
+      __builtin_amdgcn_s_sleep(4);
+    }
+    if (it == (1 << 19)) __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  // per expert: the total over every chunk and the part of the chunks before this one
+  constexpr int B = 16;
+  for (int e = tid; e < E; e += 256) {
+    int run = 0, pre = 0;
+    for (int c0 = 0; c0 < nch; c0 += B) {
+      int v[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j)
+        v[j] = __hip_atomic_load(chunk_counts + (int64_t)min(c0 + j, nch - 1) * E + e, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        if (c0 + j == c) pre = run;
+        run += c0 + j < nch ? v[j] : 0;
+      }
+    }
+    offs[e] = run;
+    base[e] = pre;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(offs, E, tmp);
+  if (tid == 0) offs[E] = total;
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) base[e] += offs[e];
+  if (c == 0) {
+    for (int e = tid; e <= E; e += 256) {
+      offsets[e] = offs[e];
+      if (e < E) counts[e] = offs[e + 1] - offs[e];
+    }
+    if (tiles) emit_tiles(offs, E, mt, tiles, tile_count, cls);
+  }
+  __syncthreads();
+  if (K > KC) {
+    chunk_scatter(idx, T, K, c, base, mask, sorted_slot, slot_pos);
+    return;
+  }
+  if (t >= T) return;
+  const int wd = tid >> 5;
+  const uint32_t below = (1u << (tid & 31)) - 1u;
+#pragma unroll
+  for (int j = 0; j < KC; ++j) {
+    if (j < K) {
+      const int e = idc[j];
+      int rank = __popc(mask[e][wd] & below);
+      for (int w = 0; w < wd; ++w) rank += __popc(mask[e][w]);
+      const int pos = base[e] + rank;
+      const int p = t * K + j;
+      sorted_slot[pos] = p;
+      slot_pos[p] = pos;
+    }
+  }
 }
 
 // T <= 256: the whole permutation (and the tile list) in one workgroup (blockDim >= 256).
