@@ -272,26 +272,33 @@ __global__ __launch_bounds__(512, ONE ? 4 : 6) void decode_fused(const FusedPara
     const int Kd = dn ? (sh ? p.dn.seg[1].K : p.dn.seg[0].K) : (sh ? p.gu.seg[1].K : p.gu.seg[0].K);
     return (Kd + KC - 1) / KC;
   };
-  // ONE: the routed m-tile count, once the routing flag has been seen (by this wave, or by
-  // loader wave 0 before a barrier this wave has passed)
+  // ONE: the routing flag (this workgroup's copy) holds 1 + the routed m-tile count once the
+  // routing is stored
+  const int *const flag = p.cnt + kFlag0 + (g % kFlagCopies) * kCntStride;
   bool have_nr = !ONE;
+  auto set_nr = [&](int f) {
+    nr = min(max(f - 1, 0), min(max_tiles, p.nr_ub));
+    Ug = Ug_s + nr * nbg0;
+    have_nr = true;
+  };
+  // the count, once the flag has been seen set (by this wave, or by loader wave 0 before a
+  // barrier this wave has passed)
   auto learn_nr = [&]() {
-    if (!have_nr) {
-      nr = min(max(__builtin_amdgcn_readfirstlane(
-                       __hip_atomic_load(tcount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)),
-                   0),
-               min(max_tiles, p.nr_ub));
-      Ug = Ug_s + nr * nbg0;
-      have_nr = true;
-    }
+    if (!have_nr) set_nr(__builtin_amdgcn_readfirstlane(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
   };
   // ONE: unit u of this workgroup's sequence if it exists (a routed one waits for the routing)
   auto unit_if = [&](int u) {
     const int Us = Ug_s + Ud_s;
     if (u < Us) return u;
     if (!have_nr) {
-      wait_count(p.cnt + kFlag0 + (g % kFlagCopies) * kCntStride, 1, p.status, lane);
-      learn_nr();
+      int f = 0;
+      for (int it = 0; it < kSpinLimit; ++it) {
+        f = __builtin_amdgcn_readfirstlane(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (f > 0) break;
+        __builtin_amdgcn_s_sleep(10);
+      }
+      if (f <= 0 && lane == 0) __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      set_nr(f);
     }
     return u < Us + nr * (nbg0 + nbd0) ? u : -1;
   };
@@ -334,12 +341,13 @@ __global__ __launch_bounds__(512, ONE ? 4 : 6) void decode_fused(const FusedPara
       if (uq[1]) {
         if ((tid >> 6) < (T + 1) / 2) topk_half<8, true>(ta, half, l32, el[half], esc[half], sidx, true);
         __syncthreads();
-        decode_permute<512, true, true>(sidx, T, ta.K, E, p.counts, p.offsets, (int32_t *)p.gu.seg[0].A.gather,
-                                        p.slot_pos, (int4 *)p.gu.tiles, (int *)p.gu.tile_count, 16, perm);
+        const int ntl = decode_permute<512, true, true>(sidx, T, ta.K, E, p.counts, p.offsets,
+                                                        (int32_t *)p.gu.seg[0].A.gather, p.slot_pos,
+                                                        (int4 *)p.gu.tiles, (int *)p.gu.tile_count, 16, perm);
         wait_vmcnt<0>();  // this thread's stores have completed
         __syncthreads();
         if (tid < kFlagCopies)
-          __hip_atomic_store(p.cnt + kFlag0 + tid * kCntStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(p.cnt + kFlag0 + tid * kCntStride, 1 + ntl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __syncthreads();  // the routing LDS is free
     }
@@ -760,9 +768,10 @@ __global__ __launch_bounds__(512, ONE ? 4 : 6) void decode_fused(const FusedPara
         const int old = publish(p.cnt + kColCnt0 + cb * kCntStride, lane);
         // before the routing is stored no routed down unit has run, so this one is not the
         // last of its columns (there is at least one routed m-tile)
-        if (!have_nr && __builtin_amdgcn_readfirstlane(__hip_atomic_load(p.cnt + kFlag0 + (g % kFlagCopies) * kCntStride,
-                                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)))
-          learn_nr();
+        if (!have_nr) {
+          const int f = __builtin_amdgcn_readfirstlane(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          if (f > 0) set_nr(f);
+        }
         if (have_nr && old == ns + nr - 1) combine_cols(col0);
       }
     } else {

@@ -399,9 +399,10 @@ struct DecodePermSmem {
   int wtot[NT / 64];
 };
 
-// IDX_LDS: idx is the workgroup's own copy in LDS (else global memory, read at device scope)
+// IDX_LDS: idx is the workgroup's own copy in LDS (else global memory, read at device scope).
+// Returns the number of m-tiles (in every thread).
 template <int NT, bool COH, bool IDX_LDS = false>
-MOE_DEV void decode_permute(const int32_t *idx, int T, int K, int E, int32_t *__restrict__ counts,
+MOE_DEV int decode_permute(const int32_t *idx, int T, int K, int E, int32_t *__restrict__ counts,
                             int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_slot,
                             int32_t *__restrict__ slot_pos, int4 *tiles, int *tile_count, int mt,
                             DecodePermSmem<NT> &sm) {
@@ -509,6 +510,7 @@ MOE_DEV void decode_permute(const int32_t *idx, int T, int K, int E, int32_t *__
     st(sorted_slot + pos, p);
     slot_pos[p] = pos;
   }
+  return total >> 16;
 }
 
 }  // namespace
