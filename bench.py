@@ -214,7 +214,7 @@ def pct(v, q):
     return v[i]
 
 
-def measure(wl, steps, warmup, gu_every, copies_arg=0, tokens=0):
+def measure(wl, steps, warmup, gu_every, copies_arg=0, tokens=0, inter=None, scaled=False):
     """Generate the workload's layer on the GPU and time `steps` block forwards."""
     import torch
     import synth
@@ -229,7 +229,7 @@ def measure(wl, steps, warmup, gu_every, copies_arg=0, tokens=0):
     log(f"workload {wl}: generating the layer on {dev}")
     b = synth.make_block(spec, dev)
     moe.lib()
-    desc0 = block_desc(b)
+    desc0 = block_desc(b, inter, scaled)
     y = torch.empty(b.T, b.H, dtype=torch.float32, device=dev)
     idx = torch.empty(b.T, b.K, dtype=torch.int32, device=dev)
     w = torch.empty(b.T, b.K, dtype=torch.float32, device=dev)
@@ -250,7 +250,7 @@ def measure(wl, steps, warmup, gu_every, copies_arg=0, tokens=0):
     if copies <= 0:
         copies = max(1, min(16, math.ceil((1 << 30) / max(wm["step_bytes"], 1)) + 1))
     blocks = [b] + [synth.clone_weights(b) for _ in range(copies - 1)]
-    descs = [desc0] + [block_desc(bb) for bb in blocks[1:]]
+    descs = [desc0] + [block_desc(bb, inter, scaled) for bb in blocks[1:]]
     log(f"{wl}: {copies} weight copies, {wm['experts_hit']} experts hit, {wm['step_bytes'] / 1e6:.1f} MB/step")
 
     stream = torch.cuda.current_stream()
@@ -395,6 +395,10 @@ def main():
     ap.add_argument("--single-decode-launch", action="store_true",
                     help="run decode-sized batches of up to 16 tokens in one launch (routing, experts and "
                          "combine) instead of three")
+    ap.add_argument("--inter", choices=("auto", "bf16", "f16"), default="auto",
+                    help="storage of the intermediates (auto: the layer's default)")
+    ap.add_argument("--scaled-mfma", action="store_true",
+                    help="MXFP4 experts (c5): run the routed GEMMs on the block-scaled FP4 x FP8 MFMA")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (the reference kernel that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -421,7 +425,9 @@ def main():
     if fusion != 1:
         import sparse_mixture_experts_bias_amd as moe
         moe.moe_set_decode_fusion(fusion)
-    r = measure(wl, args.steps, args.warmup, args.gu_every, args.copies, args.tokens)
+    import sparse_mixture_experts_bias_amd as moe
+    inter = {"auto": None, "bf16": moe.MOE_BF16, "f16": moe.MOE_F16}[args.inter]
+    r = measure(wl, args.steps, args.warmup, args.gu_every, args.copies, args.tokens, inter, args.scaled_mfma)
     b = r["b"]
     hbm_bound = wl in ("c1", "c2", "c5")
     roof = roofline_of(wl, r, hbm_bound, dev)
@@ -435,7 +441,7 @@ def main():
                    "tokens": b.T, "hidden": b.H, "experts": b.E,
                    "top_k": b.K, "intermediate": b.I, "weight_copies": r["copies"],
                    "inter_dtype": {0: "f32", 1: "bf16", 2: "f16"}[r["desc"].c.inter_dtype], "output": "f32",
-                   "decode_fusion": fusion},
+                   "decode_fusion": fusion, "scaled_mfma": bool(args.scaled_mfma)},
         **st,
         "roofline": roof,
     }
@@ -443,10 +449,11 @@ def main():
     if wl == "c2" and not args.no_prefill and args.tokens == 0:
         # the metric's other half: the same layer at 4096-token prefill, its own record
         torch.cuda.empty_cache()
-        rp = measure("c3", args.steps, args.warmup, args.gu_every)
+        rp = measure("c3", args.steps, args.warmup, args.gu_every, inter=inter)
         pst = step_stats(rp, args.steps)
         pre = {"workload": f"c3: {WORKLOADS['c3']}", "tokens_per_s": round(rp["b"].T * args.steps /
                                                                            (rp["total_ms"] / 1e3), 1),
+               "inter_dtype": {0: "f32", 1: "bf16", 2: "f16"}[rp["desc"].c.inter_dtype],
                **pst, "roofline": roofline_of("c3", rp, False, dev, with_peak=False)}
         out["prefill"] = pre
         del rp

@@ -88,6 +88,13 @@ typedef enum { MOE_SHARED_NONE = 0, MOE_SHARED_ADD = 1, MOE_SHARED_BLEND = 2 } m
  *           stream of the pair, set on `gate`; `up.packed` is not read).  Required by
  *           every BF16/F16-activation GEMM; there w, scales and qbias are not read
  *           (they describe the source of the stream).  Unused on the F32 path.
+ *   packed_scaled (optional, MXFP4 only): the stream moe_pack_weights_scaled wrote.  When
+ *           the routed experts' gate and down stacks both carry one, prefill-sized
+ *           batches of the latent layer (f16 intermediates, expert widths in whole blocks
+ *           of 128) run those GEMMs on gfx950's block-scaled FP4 x FP8 MFMA: the weights
+ *           as stored (codes and E8M0 scales), the activations split into two FP8 terms
+ *           with E8M0 block scales of 32 (about 8 significant bits, more than bf16).
+ *           NULL, or any other batch: the 16-bit MFMA path.  256-byte aligned.
  * "qbias" (the affine offset of each group) and "bias" (the linear layer's output
  * bias) are different things on purpose.
  */
@@ -102,6 +109,7 @@ typedef struct {
   const void *qbias;
   const void *bias;
   const void *packed;
+  const void *packed_scaled;
 } moe_linear;
 
 /* SwiGLU expert stack: h = silu(gate z) * (up z) with gate/up [n, I, D], down [n, D, I].
@@ -163,6 +171,21 @@ typedef struct {
  */
 MOE_API moe_status moe_pack_weights(const moe_linear *a, const moe_linear *b, void *out, size_t *out_bytes,
                                     void *stream);
+
+/*
+ * moe_pack_weights_scaled - the stream of MXFP4 weights for the block-scaled MFMA (once,
+ * at load time; see moe_linear.packed_scaled).  Arguments, sizes (the same as
+ * moe_pack_weights for the stack) and errors as moe_pack_weights; `a` must be MXFP4
+ * (else MOE_ERR_UNSUPPORTED).  Each record (32 tile rows x 256 elements) holds, for each
+ * of its two 128-element stages and two 16-row halves, 1 KB in the FP4 operand order of
+ * the 16x16x128 MFMA (lane l: the 16 stored bytes of row l%16 at elements 32*(l/16)..+32),
+ * then one word per lane whose byte 2*stage + half is the E8M0 scale of those elements.
+ * A permutation of the stored codes and scales: nothing is converted.
+ * Source: libmir-metal ExpertLayout::Native (the MXFP4 gate/up and down kernels read the
+ * weights as stored); the layout is gfx950's MFMA operand order.
+ */
+MOE_API moe_status moe_pack_weights_scaled(const moe_linear *a, const moe_linear *b, void *out, size_t *out_bytes,
+                                           void *stream);
 
 /*
  * moe_route - router projection, scoring, selection and weights.
@@ -307,7 +330,7 @@ MOE_API const char *moe_status_str(int32_t status);
 /* Text of the last validation failure on the calling thread ("" if none). */
 MOE_API const char *moe_last_error(void);
 
-/* ABI version: (major << 16) | minor. */
+/* ABI version: (major << 16) | minor.  Major 3: moe_linear.packed_scaled. */
 MOE_API int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

@@ -28,7 +28,7 @@ SHARED_CODES = {"none": MOE_SHARED_NONE, "add": MOE_SHARED_ADD, "blend": MOE_SHA
 SCORING_CODES = {"sigmoid": MOE_SIGMOID, "softmax": MOE_SOFTMAX}
 
 EXPORTS = ("moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward", "moe_block_forward_noalloc",
-           "moe_pack_weights", "moe_set_decode_fusion", "moe_timing_enable", "moe_timing_read", "moe_status_str",
+           "moe_pack_weights", "moe_pack_weights_scaled", "moe_set_decode_fusion", "moe_timing_enable", "moe_timing_read", "moe_status_str",
            "moe_last_error", "moe_abi_version")
 NOALLOC_SCRATCH_BYTES = 32 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 
@@ -51,7 +51,8 @@ class MoeLinear(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("dense_dtype", ctypes.c_int32), ("n", ctypes.c_int32),
                 ("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("bits", ctypes.c_int32), ("w", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("qbias", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("packed", ctypes.c_void_p)]
+                ("qbias", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("packed", ctypes.c_void_p),
+                ("packed_scaled", ctypes.c_void_p)]
 
 
 class MoeMLP(ctypes.Structure):
@@ -89,8 +90,10 @@ def lib() -> ctypes.CDLL:
                                           i32, vp, vp, sz, vp]
         L.moe_block_forward.argtypes = [vp, i32, i64, ctypes.POINTER(MoeBlock), vp, i32, vp, vp, vp, sz, vp]
         L.moe_pack_weights.argtypes = [ctypes.POINTER(MoeLinear), ctypes.POINTER(MoeLinear), vp, sz, vp]
+        L.moe_pack_weights_scaled.argtypes = [ctypes.POINTER(MoeLinear), ctypes.POINTER(MoeLinear), vp, sz, vp]
         L.moe_block_forward_noalloc.argtypes = [vp, i32, i64, ctypes.POINTER(MoeBlock), vp, i32, vp, vp, vp]
         for f in ("moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward", "moe_pack_weights",
+                  "moe_pack_weights_scaled",
                   "moe_block_forward_noalloc"):
             getattr(L, f).restype = ctypes.c_int32
         L.moe_status_str.argtypes = [i32]
@@ -171,40 +174,51 @@ def _on_gpu(d: Desc) -> bool:
     return d.keep[0] is not None and d.keep[0].is_cuda
 
 
-def packed_bytes(a: Desc, b: Optional[Desc] = None) -> int:
-    """Size of the packed stream moe_pack_weights writes for a (gate/up pair: a, b)."""
+def packed_bytes(a: Desc, b: Optional[Desc] = None, scaled: bool = False) -> int:
+    """Size of the packed stream moe_pack_weights (scaled: moe_pack_weights_scaled) writes
+    for a (gate/up pair: a, b)."""
     n = ctypes.c_size_t(0)
-    _check(lib().moe_pack_weights(ctypes.byref(a.c), ctypes.byref(b.c) if b is not None else None, None,
-                                  ctypes.byref(n), None))
+    fn = lib().moe_pack_weights_scaled if scaled else lib().moe_pack_weights
+    _check(fn(ctypes.byref(a.c), ctypes.byref(b.c) if b is not None else None, None, ctypes.byref(n), None))
     return n.value
 
 
-def moe_pack_weights(a: Desc, b: Optional[Desc] = None, stream=None) -> torch.Tensor:
+def moe_pack_weights(a: Desc, b: Optional[Desc] = None, stream=None, scaled: bool = False) -> torch.Tensor:
     """The packed stream of stack a (or of the gate/up pair a, b) in a new 256-byte
-    aligned device buffer; the descriptor is not modified."""
-    nbytes = packed_bytes(a, b)
+    aligned device buffer; the descriptor is not modified.  scaled: the stream of the
+    block-scaled MFMA (moe_pack_weights_scaled, MXFP4 only)."""
+    nbytes = packed_bytes(a, b, scaled)
     dev = a.keep[0].device
     buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
     off = (-buf.data_ptr()) % 256
     out = buf[off:off + nbytes]
     n = ctypes.c_size_t(nbytes)
-    _check(lib().moe_pack_weights(ctypes.byref(a.c), ctypes.byref(b.c) if b is not None else None, out.data_ptr(),
-                                  ctypes.byref(n), _stream(stream)))
+    fn = lib().moe_pack_weights_scaled if scaled else lib().moe_pack_weights
+    _check(fn(ctypes.byref(a.c), ctypes.byref(b.c) if b is not None else None, out.data_ptr(), ctypes.byref(n),
+              _stream(stream)))
     return out
 
 
-def attach_packed(d: Desc, b: Optional[Desc] = None):
-    """Pack d (the gate/up pair d, b) and point d.packed at the stream (kept alive by d)."""
-    t = moe_pack_weights(d, b)
-    d.c.packed = t.data_ptr()
+def attach_packed(d: Desc, b: Optional[Desc] = None, scaled: bool = False):
+    """Pack d (the gate/up pair d, b) and point d.packed (scaled: d.packed_scaled) at the
+    stream (kept alive by d)."""
+    t = moe_pack_weights(d, b, scaled=scaled)
+    if scaled:
+        d.c.packed_scaled = t.data_ptr()
+    else:
+        d.c.packed = t.data_ptr()
     d.keep.append(t)
 
 
-def mlp(gate: Desc, up: Desc, down: Desc, swiglu_limit: float = 0.0) -> Desc:
-    """SwiGLU stack; on the GPU the gate/up pair and the down stack are packed here."""
+def mlp(gate: Desc, up: Desc, down: Desc, swiglu_limit: float = 0.0, scaled: bool = False) -> Desc:
+    """SwiGLU stack; on the GPU the gate/up pair and the down stack are packed here.
+    scaled (MXFP4): also the streams of the block-scaled MFMA (moe_linear.packed_scaled)."""
     if _on_gpu(gate) and _packable(gate):
         attach_packed(gate, up)
         attach_packed(down)
+        if scaled and gate.c.fmt == MOE_W_MXFP4:
+            attach_packed(gate, up, scaled=True)
+            attach_packed(down, scaled=True)
     return Desc(MoeMLP(gate.c, up.c, down.c, float(swiglu_limit)), [gate, up, down])
 
 

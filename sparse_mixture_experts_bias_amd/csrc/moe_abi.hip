@@ -70,6 +70,10 @@ moe_status check_linear(const moe_linear *L, const char *name, int n, int rows, 
     CHECK(aligned(L->packed, 256), MOE_ERR_ARG, "%s: packed stream not 256-byte aligned", name);
   }
   CHECK(L->bias == nullptr || aligned(L->bias, 4), MOE_ERR_ARG, "%s: bias pointer misaligned", name);
+  CHECK(L->packed_scaled == nullptr || L->fmt == MOE_W_MXFP4, MOE_ERR_ARG,
+        "%s: packed_scaled is for MXFP4 weights only", name);
+  CHECK(L->packed_scaled == nullptr || aligned(L->packed_scaled, 256), MOE_ERR_ARG,
+        "%s: packed_scaled stream not 256-byte aligned", name);
   switch (L->fmt) {
     case MOE_W_DENSE:
       CHECK(L->dense_dtype == MOE_F32 || L->dense_dtype == MOE_BF16, MOE_ERR_ARG, "%s: dense dtype %d not F32/BF16",
@@ -425,7 +429,7 @@ int col_blocks(const SegSet &sg, bool gateup, int mb) {
 }
 
 hipError_t launch_gemm_kernel(int adt, const moe_linear &fmt_of, bool gateup, int odt, int kmb, const GemmParams &p,
-                              int units_ub, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                              int units_ub, hipStream_t s, hipEvent_t e0, hipEvent_t e1, bool scaled = false) {
   const int adt_k = adt == MOE_BF16 ? DT_BF16 : DT_F16;
   const int odt_k = odt == MOE_F32 ? DT_F32 : (odt == MOE_BF16 ? DT_BF16 : DT_F16);
   if (kmb == MB_WS)
@@ -433,7 +437,7 @@ hipError_t launch_gemm_kernel(int adt, const moe_linear &fmt_of, bool gateup, in
                                  gemm_grid(units_ub, kmb, ws_wgs_per_cu(wf_of(fmt_of), fmt_of.group_size)), s, e0,
                                  e1);
   if (kmb == MB_TALL)
-    return launch_expert_gemm_tall(adt_k, wf_of(fmt_of), fmt_of.group_size, gateup, odt_k, p,
+    return launch_expert_gemm_tall(adt_k, scaled ? WF_MXS : wf_of(fmt_of), fmt_of.group_size, gateup, odt_k, p,
                                    gemm_grid(units_ub, kmb), s, e0, e1);
   return launch_expert_gemm(adt_k, wf_of(fmt_of), fmt_of.group_size, gateup, odt_k, kmb, p, gemm_grid(units_ub, kmb),
                             s, e0, e1);
@@ -457,6 +461,8 @@ AOp aop(const void *a, int64_t lda, const int32_t *gather, int gdiv, int row_sub
   o.gdiv = gdiv;
   o.row_sub = row_sub;
   o.rows = rows;
+  o.as = nullptr;
+  o.ldas = 0;
   return o;
 }
 
@@ -504,10 +510,12 @@ GemmParams gemm_params(bool gateup, int mb, const SegSet &routed, const SegSet *
   return p;
 }
 
+// scaled: the prefill kernel on the block-scaled MFMA (routed.A: split FP8 activations with
+// their scale pairs; routed.w0.pk: the moe_pack_weights_scaled stream)
 moe_status run_gemm(int adt, const moe_linear &fmt_of, bool gateup, int odt, int mb, const SegSet &routed,
                     const SegSet *shared, int sh_row0, int sh_rows, const int4 *tiles, const int *tile_count,
                     int ntiles_alloc, int TK, int E, void *out, int64_t ldo, const float *resid, int64_t ldr,
-                    hipStream_t s) {
+                    hipStream_t s, bool scaled = false) {
   const int mt = 16 * mb;
   const GemmParams p = gemm_params(gateup, mb, routed, shared, sh_row0, sh_rows, tiles, tile_count, ntiles_alloc, E,
                                    out, ldo, resid, ldr);
@@ -517,7 +525,8 @@ moe_status run_gemm(int adt, const moe_linear &fmt_of, bool gateup, int odt, int
   if (kmb == MB_WS && !offsets_fit(p, INT32_MAX)) kmb = 1;
   CHECK(kmb != MB_TALL || tall_offsets_fit(p), MOE_ERR_SHAPE, "activation operand of over 4 GiB");
   Timed tm(gateup ? TK_GATEUP : TK_DOWN, s, true);
-  HIPCHK(launch_gemm_kernel(adt, fmt_of, gateup, odt, kmb, p, units_ub, s, tm.start(), tm.stop()));
+  CHECK(!scaled || kmb == MB_TALL, MOE_ERR_UNSUPPORTED, "the block-scaled MFMA runs on the prefill kernel only");
+  HIPCHK(launch_gemm_kernel(adt, fmt_of, gateup, odt, kmb, p, units_ub, s, tm.start(), tm.stop(), scaled));
   return MOE_OK;
 }
 
@@ -685,10 +694,10 @@ const char *moe_status_str(int32_t st) {
 
 const char *moe_last_error(void) { return g_err; }
 
-int32_t moe_abi_version(void) { return (2 << 16) | 0; }
+int32_t moe_abi_version(void) { return (3 << 16) | 0; }
 
-moe_status moe_pack_weights(const moe_linear *a, const moe_linear *b, void *out, size_t *out_bytes, void *stream) {
-  g_err[0] = 0;
+static moe_status pack_stream(const moe_linear *a, const moe_linear *b, void *out, size_t *out_bytes, void *stream,
+                              bool scaled) {
   CHECK(out_bytes != nullptr, MOE_ERR_ARG, "out_bytes is NULL");
   CHECK(a != nullptr, MOE_ERR_ARG, "weight descriptor is NULL");
   CHECK(a->fmt == MOE_W_AFFINE4 || a->fmt == MOE_W_MXFP4 || (a->fmt == MOE_W_DENSE && a->dense_dtype == MOE_BF16),
@@ -708,7 +717,7 @@ moe_status moe_pack_weights(const moe_linear *a, const moe_linear *b, void *out,
   CHECK(*out_bytes >= need, MOE_ERR_WORKSPACE, "packed buffer %zu bytes, need %zu", *out_bytes, need);
   CHECK(aligned(out, 256), MOE_ERR_ARG, "packed buffer not 256-byte aligned");
   PackArgs pa;
-  pa.wf = wf_of(*a);
+  pa.wf = scaled ? WF_MXS : wf_of(*a);
   pa.gq = a->fmt == MOE_W_AFFINE4 ? a->group_size : (a->fmt == MOE_W_MXFP4 ? 32 : 0);
   pa.n = a->n;
   pa.rows = a->rows;
@@ -726,6 +735,19 @@ moe_status moe_pack_weights(const moe_linear *a, const moe_linear *b, void *out,
   pa.nch = m.pk_nch;
   HIPCHK(launch_pack(pa, (hipStream_t)stream));
   return MOE_OK;
+}
+
+moe_status moe_pack_weights(const moe_linear *a, const moe_linear *b, void *out, size_t *out_bytes, void *stream) {
+  g_err[0] = 0;
+  return pack_stream(a, b, out, out_bytes, stream, false);
+}
+
+moe_status moe_pack_weights_scaled(const moe_linear *a, const moe_linear *b, void *out, size_t *out_bytes,
+                                   void *stream) {
+  g_err[0] = 0;
+  CHECK(a != nullptr, MOE_ERR_ARG, "weight descriptor is NULL");
+  CHECK(a->fmt == MOE_W_MXFP4, MOE_ERR_UNSUPPORTED, "the block-scaled stream needs MXFP4 weights (fmt %d)", a->fmt);
+  return pack_stream(a, b, out, out_bytes, stream, true);
 }
 
 moe_status moe_set_decode_fusion(int32_t enabled) {
@@ -992,6 +1014,14 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   const size_t o_yn = latent ? pl.take((size_t)T * D * isz) : 0;
   const size_t o_hs = (latent && has_shared) ? pl.take((size_t)T * Is * isz) : 0;
   const size_t o_s = (latent && has_shared) ? pl.take((size_t)T * H * 4) : 0;
+  // the routed experts of the latent layer on the block-scaled MFMA: both stacks carry the
+  // scaled stream, prefill-sized segments, f16 intermediates, widths in whole 128-blocks
+  const bool mxs = latent && b->experts.gate.packed_scaled != nullptr && b->experts.down.packed_scaled != nullptr &&
+                   inter == MOE_F16 && mb == MB_TALL && D % 128 == 0 && I % 128 == 0;
+  const size_t o_zhl = mxs ? pl.take((size_t)T * D * 2) : 0;
+  const size_t o_zs = mxs ? pl.take((size_t)T * (D / 32) * 2) : 0;
+  const size_t o_hhl = mxs ? pl.take((size_t)TK * I * 2) : 0;
+  const size_t o_hsc = mxs ? pl.take((size_t)TK * (I / 32) * 2) : 0;
   bool query;
   TRY(check_ws(ws, ws_bytes, pl.off, &query));
   if (query || T == 0) return MOE_OK;
@@ -1180,12 +1210,33 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   void *z = at<char>(ws, o_z);
   void *yn = at<char>(ws, o_yn);
   TRY(run_plain(x_dtype, b->latent_down, nullptr, 0.f, false, inter, x, H, Ti, z, D, nullptr, 0, s));
-  SegSet gu = segset(aop(z, D, ss, K, 0, Ti), b->experts.gate, &b->experts.up, b->experts.swiglu_limit, true);
-  TRY(run_gemm(inter, b->experts.gate, true, inter, mb, gu, nullptr, 0, 0, tiles, tc, ntile, TK, E, h, ldh, nullptr,
-               0, s));
-  SegSet dn = segset(aop(h, ldh, nullptr, 1, 0, TK), b->experts.down, nullptr, 0.f, false);
-  TRY(run_gemm(inter, b->experts.down, false, inter, mb, dn, nullptr, 0, 0, tiles, tc, ntile, TK, E, o, D, nullptr, 0,
-               s));
+  if (mxs) {
+    // z and h split into FP8 pairs with E8M0 block scales; the MXFP4 weights go to the MFMA as
+    // stored (libmir-metal ExpertLayout::Native)
+    void *zhl = at<char>(ws, o_zhl), *hhl = at<char>(ws, o_hhl);
+    uint16_t *zs = at<uint16_t>(ws, o_zs), *hsc = at<uint16_t>(ws, o_hsc);
+    HIPCHK(launch_split_fp8(z, D, Ti, D, zhl, zs, s));
+    SegSet gu = segset(aop(zhl, D, ss, K, 0, Ti), b->experts.gate, &b->experts.up, b->experts.swiglu_limit, true);
+    gu.A.as = zs;
+    gu.A.ldas = D / 32;
+    gu.w0.pk = (const char *)b->experts.gate.packed_scaled;
+    TRY(run_gemm(inter, b->experts.gate, true, inter, mb, gu, nullptr, 0, 0, tiles, tc, ntile, TK, E, h, ldh, nullptr,
+                 0, s, true));
+    HIPCHK(launch_split_fp8(h, ldh, TK, I, hhl, hsc, s));
+    SegSet dn = segset(aop(hhl, I, nullptr, 1, 0, TK), b->experts.down, nullptr, 0.f, false);
+    dn.A.as = hsc;
+    dn.A.ldas = I / 32;
+    dn.w0.pk = (const char *)b->experts.down.packed_scaled;
+    TRY(run_gemm(inter, b->experts.down, false, inter, mb, dn, nullptr, 0, 0, tiles, tc, ntile, TK, E, o, D, nullptr,
+                 0, s, true));
+  } else {
+    SegSet gu = segset(aop(z, D, ss, K, 0, Ti), b->experts.gate, &b->experts.up, b->experts.swiglu_limit, true);
+    TRY(run_gemm(inter, b->experts.gate, true, inter, mb, gu, nullptr, 0, 0, tiles, tc, ntile, TK, E, h, ldh, nullptr,
+                 0, s));
+    SegSet dn = segset(aop(h, ldh, nullptr, 1, 0, TK), b->experts.down, nullptr, 0.f, false);
+    TRY(run_gemm(inter, b->experts.down, false, inter, mb, dn, nullptr, 0, 0, tiles, tc, ntile, TK, E, o, D, nullptr,
+                 0, s));
+  }
   TRY(combine(inter, inter, o, D, sp, wts, K, TK, Ti, D, yn, D, nullptr, b->latent_norm_w, b->norm_eps,
               b->latent_norm_w ? 1 : 0, s));
   const float *resid = nullptr;

@@ -153,3 +153,104 @@ hipError_t launch_combine(int odt, int ydt, const CombineArgs &a, hipStream_t s)
 #undef C
   return hipErrorInvalidValue;
 }
+
+// ---------------------------------------------------------------------------
+// split_fp8: f16 activations -> the FP8 operand pair of the block-scaled MFMA.
+// Per row and block of 32 elements: hi = e4m3(v / 2^Eh) with the smallest Eh that keeps the
+// block's largest magnitude within e4m3's 448, then the remainder r = v - hi * 2^Eh (exact in
+// fp32) as lo = e4m3(r / 2^El) with El chosen the same way from r.  hi * 2^Eh + lo * 2^El keeps
+// about 8 significant bits of every element (more than bf16's), and each of the two products
+// with the weights carries its own E8M0 block scale, so the pair costs two MFMAs where the
+// weights need no conversion at all.
+// Output: hl [rows][cols / 128][256 bytes]: per 128 elements the 128 hi codes, then the 128 lo
+// codes (the row stride is cols * 2 bytes, that of the f16 input rows); hs [rows][cols / 32]:
+// Eh + 127 | (El + 127) << 8.  cols % 128 == 0.
+// ---------------------------------------------------------------------------
+static __device__ __forceinline__ int e8m0_for(float amax) {
+  if (!(amax > 0.f)) return 127;  // an all-zero block (and NaN: out of contract)
+  int x;
+  const float m = frexpf(amax, &x);  // amax = m 2^x, m in [0.5, 1); 448 = 0.875 2^9
+  const int E = m <= 0.875f ? x - 9 : x - 8;
+  return min(max(E + 127, 1), 254);
+}
+
+// 2^(127 - e) for e in 1..254
+static __device__ __forceinline__ float inv_pow2(int e) { return __uint_as_float((uint32_t)(254 - e) << 23); }
+static __device__ __forceinline__ float pow2(int e) { return __uint_as_float((uint32_t)e << 23); }
+
+// OCP E4M3 (bias 7, 3 mantissa bits, no infinities, largest finite 448), written out from the
+// format: y with |y| <= 448 rounded to nearest even; returns the code and the rounded value.
+// Below 2^-6 the codes are the subnormals q 2^-9 (q = 0..8, 8 being the smallest normal).
+static __device__ __forceinline__ uint32_t e4m3_rne(float y, float &yr) {
+  const uint32_t sgn = __float_as_uint(y) >> 31 << 7;
+  const float a = fabsf(y);
+  uint32_t code;
+  float r;
+  if (a < 0.015625f) {
+    const float q = rintf(a * 512.0f);  // 0..8, ties to even
+    code = (uint32_t)q;
+    r = q * (1.0f / 512.0f);
+  } else {
+    uint32_t bits = __float_as_uint(a);
+    bits += 0x7FFFFu + ((bits >> 20) & 1u);  // round the mantissa to 3 bits, ties to even
+    bits &= 0xFFF00000u;
+    r = __uint_as_float(bits);
+    code = ((((bits >> 23) - 120u) << 3) | ((bits >> 20) & 7u));
+  }
+  yr = sgn ? -r : r;
+  return code | sgn;
+}
+
+__global__ __launch_bounds__(256) void split_fp8_kernel(const uint16_t *in, int64_t ldi, int rows, int cols,
+                                                        uint8_t *hl, uint16_t *hs) {
+  const int nb = cols / 32;
+  const int64_t total = (int64_t)rows * nb;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(i / nb), b = (int)(i % nb);
+    const f16x8_t *src = (const f16x8_t *)(in + (int64_t)r * ldi + 32 * b);
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f16x8_t h = src[q];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[8 * q + j] = (float)h[j];
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(v[k]));
+    const int eh = e8m0_for(amax);
+    const float ih = inv_pow2(eh), ph = pow2(eh);
+    uint32_t hw[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u}, lw[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    float ramax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      float yr;
+      hw[k / 4] |= e4m3_rne(v[k] * ih, yr) << (8 * (k % 4));
+      v[k] -= yr * ph;  // exact: both terms carry at most 11 significant bits at nearby scales
+      ramax = fmaxf(ramax, fabsf(v[k]));
+    }
+    const int el = e8m0_for(ramax);
+    const float il = inv_pow2(el);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      float yr;
+      lw[k / 4] |= e4m3_rne(v[k] * il, yr) << (8 * (k % 4));
+    }
+    uint8_t *dst = hl + (int64_t)r * cols * 2 + (b >> 2) * 256 + (b & 3) * 32;
+    *(u32x4_t *)dst = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+    *(u32x4_t *)(dst + 16) = u32x4_t{hw[4], hw[5], hw[6], hw[7]};
+    *(u32x4_t *)(dst + 128) = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+    *(u32x4_t *)(dst + 144) = u32x4_t{lw[4], lw[5], lw[6], lw[7]};
+    hs[(int64_t)r * nb + b] = (uint16_t)(eh | (el << 8));
+  }
+}
+
+hipError_t launch_split_fp8(const void *in, int64_t ldi, int rows, int cols, void *hl, uint16_t *hs, hipStream_t s) {
+  const int64_t total = (int64_t)rows * (cols / 32);
+  if (total <= 0) return hipSuccess;
+  const int64_t want = (total + 255) / 256;
+  const int grid = (int)(want < 16384 ? want : 16384);
+  hipLaunchKernelGGL(split_fp8_kernel, dim3(grid), dim3(256), 0, s, (const uint16_t *)in, ldi, rows, cols,
+                     (uint8_t *)hl, hs);
+  return hipGetLastError();
+}

@@ -18,7 +18,8 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 // storage type tags
 enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 // weight format tags
-enum { WF_DENSE = 0, WF_AFFINE4 = 1, WF_MXFP4 = 2 };
+// WF_MXS: MXFP4 in the stream of the block-scaled FP4 x FP8 MFMA (moe_pack_weights_scaled)
+enum { WF_DENSE = 0, WF_AFFINE4 = 1, WF_MXFP4 = 2, WF_MXS = 3 };
 
 MOE_DEV float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 MOE_DEV float f16_bits_to_f32(uint32_t b) {

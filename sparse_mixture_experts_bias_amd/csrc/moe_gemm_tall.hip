@@ -42,7 +42,7 @@ __device__ u32x4_t g_zero_block = {0u, 0u, 0u, 0u};
 // stages in registers; loads run D = NBUF - 1 stages ahead of the MFMAs.
 template <int WF, int GQ>
 struct TallCfg {
-  static constexpr bool AFF = WF == WF_AFFINE4, MX = WF == WF_MXFP4, DENSE = WF == WF_DENSE;
+  static constexpr bool AFF = WF == WF_AFFINE4, MX = WF == WF_MXFP4, DENSE = WF == WF_DENSE, MXS = WF == WF_MXS;
   static constexpr int NW = 8;                           // waves per workgroup
   static constexpr int MT = 128;                         // rows per m-tile
   static constexpr int KC = pk_kc(WF);                   // reduction elements per packed record
@@ -58,9 +58,10 @@ struct TallCfg {
   static constexpr int RPI = 1024 / ROWB;                // rows per direct load
   static constexpr int NU = pk_nu(WF, GQ);               // units per record
   static constexpr int NUS = NU / SPR;                   // units per stage
-  static constexpr int NSW = AFF ? 2 * NUS : (MX ? 2 : 0);  // scale words per lane per stage
-  static constexpr int NSL = NSW ? 2 : 0;                // scale loads per stage (one per half)
-  static constexpr int LPS = NI + PPS + NSL;             // vector-memory loads per stage per lane
+  static constexpr int NSW = AFF ? 2 * NUS : (MX ? 2 : (MXS ? 1 : 0));  // scale words per lane per stage
+  static constexpr int NSL = NSW ? (MXS ? 1 : 2) : 0;    // scale loads per stage (one per half; MXS: one)
+  static constexpr int NAS = MXS ? 1 : 0;                // activation-scale direct loads per stage
+  static constexpr int LPS = NI + NAS + PPS + NSL;       // vector-memory loads per stage per lane
   static_assert(NI * NW * 1024 == ABUF && RPI * ROWB == 1024, "stage = whole 1 KB loads");
   static_assert(NW * (MT / NW) == MT && (MT / NW) == NI * RPI, "each wave stages 16 rows");
   static_assert(NUS * SPR == NU, "whole units per stage");
@@ -79,6 +80,7 @@ MOE_DEV int row_swizzle(int r) {
 // every read of it would then wait for all direct loads in flight)
 struct StageBufs {
   char *b[4];
+  char *s[4];  // WF_MXS: the activations' scale pairs of each stage (8 waves x 256 bytes)
 };
 
 // four adjacent outputs (nv of them valid): one 8- or 16-byte store when aligned
@@ -109,6 +111,8 @@ struct TallUnit {
   float limit;
   const char *Ab;
   int64_t lda, arows;
+  const uint16_t *As;       // WF_MXS: activation scale pairs and their row stride (elements)
+  int64_t ldas;
   const int32_t *gat;
   int gdiv, rsub;
   int rows;                 // weight rows (output columns, GATEUP: per half)
@@ -131,6 +135,8 @@ MOE_DEV TallUnit tall_unit_of(const GemmParams &p, bool sh, int4 tile, int nb) {
   t.Ab = (const char *)SF(A.a);
   t.lda = SF(A.lda);
   t.arows = SF(A.rows);
+  t.As = SF(A.as);
+  t.ldas = SF(A.ldas);
   t.gat = SF(A.gather);
   t.gdiv = SF(A.gdiv);
   t.rsub = SF(A.row_sub);
@@ -169,10 +175,12 @@ struct TallSlot {
 template <int WF, int GQ, bool GATEUP>
 struct TallLoader {
   using C = TallCfg<WF, GQ>;
-  static constexpr int NI = C::NI, PPS = C::PPS, NU = C::NU, NUS = C::NUS, SPR = C::SPR, KS = C::KS;
+  static constexpr int NI = C::NI, PPS = C::PPS, NU = C::NU, NUS = C::NUS, SPR = C::SPR, KS = C::KS, NAS = C::NAS;
   static constexpr int RB = pk_record_bytes(WF, GQ);
   __amdgpu_buffer_rsrc_t arsrc;
   uint32_t aoff[NI];
+  __amdgpu_buffer_rsrc_t srsrc;  // WF_MXS: the activation scale pairs
+  uint32_t soff;
   int ablk[NI];
   const char *wbase;
   int wave_u, lane, n16, Kd, nst;
@@ -200,12 +208,25 @@ struct TallLoader {
       aoff[n] = aon ? (uint32_t)sRow[rr] + (uint32_t)(ablk[n] * 16) : 0xF0000000u;
     }
     arsrc = __builtin_amdgcn_make_buffer_rsrc((void *)u.Ab, (short)0, (int)(uint32_t)(u.arows * u.lda * 2), 0x00020000);
+    if constexpr (C::MXS) {
+      // lanes 0..31 stage the 8 bytes (4 blocks x (Eh, El)) of the wave's 16 rows for the
+      // stage, two lanes a row; lanes 32..63 read past the range (zeros, no traffic)
+      const int rr = 16 * wave + ((lane & 31) >> 1);
+      const uint32_t arow = (uint32_t)sRow[rr] / (uint32_t)(u.lda * 2);
+      soff = (aon && lane < 32) ? arow * (uint32_t)(u.ldas * 2) + (uint32_t)(lane & 1) * 4u : 0xF0000000u;
+      srsrc = __builtin_amdgcn_make_buffer_rsrc((void *)u.As, (short)0, (int)(uint32_t)(u.arows * u.ldas * 2), 0x00020000);
+    }
     wbase = u.pk + (int64_t)u.e * u.pk_mat + (int64_t)min(u.nb * C::NW + wave, u.pk_nblk - 1) * u.pk_nch * RB;
   }
   // direct load n (0 .. NI-1) of stage c's activations into LDS stage buffer dst
   __device__ __forceinline__ void load_a1(int c, char *buf, int n) const {
     char *dst = buf + wave_u * (NI * 1024) + n * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void_t *)dst, 16, aoff[n], c * KS * 2, 0, 0);
+  }
+  // the scale pairs of stage c's activations into scale buffer dst (WF_MXS)
+  __device__ __forceinline__ void load_as(int c, char *buf) const {
+    char *dst = buf + wave_u * 256;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, (lds_void_t *)dst, 4, soff, c * 8, 0, 0);
   }
   // load k (0 .. PPS + NSL - 1) of stage c's weights into ring slot ch: the weight pieces,
   // then one scale load per tile half.  The slot's old values are "used" right before the
@@ -217,6 +238,9 @@ struct TallLoader {
     if (k < PPS) {
       asm volatile("" : "+v"(ch.w[k]));
       ch.w[k] = *(const u32x4_t *)(rec + (half * PPS + k) * 1024 + lane * 16);
+    } else if constexpr (C::MXS) {
+      asm volatile("" : "+v"(ch.s[0]));
+      ch.s[0] = *(const uint32_t *)(rec + 4096 + lane * 4);
     } else if constexpr (C::AFF) {
       const int h = k - PPS;
 #pragma unroll
@@ -239,19 +263,24 @@ struct TallLoader {
       ch.s[h] = *(const uint32_t *)(rec + 4096 + (h * 16 + n16) * 8 + half * 4);
     }
   }
-  // load k (0 .. LPS-1) of stage c: activations first, then the weights
-  __device__ __forceinline__ void load_k(int c, char *buf, TallSlot<WF, GQ> &ch, int k) const {
+  // load k (0 .. LPS-1) of stage c into stage buffer bi: activations (and their scales)
+  // first, then the weights
+  __device__ __forceinline__ void load_k(int c, const StageBufs &sA, int bi, TallSlot<WF, GQ> &ch, int k) const {
     if (k < NI)
-      load_a1(c, buf, k);
+      load_a1(c, sA.b[bi], k);
+    else if (k < NI + NAS)
+      load_as(c, sA.s[bi]);
     else
-      load_w1(c, ch, k - NI);
+      load_w1(c, ch, k - NI - NAS);
   }
   // the activations of the unit's first D stages (repeats of its last stage if it has fewer)
   __device__ __forceinline__ void load_first_a(const StageBufs &sA) const {
 #pragma unroll
-    for (int j = 0; j < C::D; ++j)
+    for (int j = 0; j < C::D; ++j) {
 #pragma unroll
       for (int n = 0; n < NI; ++n) load_a1(min(j, nst - 1), sA.b[j], n);
+      if constexpr (C::MXS) load_as(min(j, nst - 1), sA.s[j]);
+    }
   }
   // ... and their weights
   __device__ __forceinline__ void load_first_w(TallSlot<WF, GQ> (&ring)[C::NBUF]) const {
@@ -336,6 +365,10 @@ MOE_DEV void tall_unit(const GemmParams &p, const TallUnit &u, const int64_t *sR
   const int lx = (kq * (QE / 8)) ^ row_swizzle<BPR>(n16);
   // one MFMA step t = uu*SPU + s of a stage: the B fragments of both halves ...
   auto deq_step = [&](const Ch &ch, int t, u32x4_t (&b)[2]) {
+    if constexpr (C::MXS) {  // the block-scaled MFMA takes the stored codes as they are
+      b[0] = b[1] = u32x4_t{0u, 0u, 0u, 0u};
+      return;
+    }
     const int uu = t / SPU, s = t % SPU;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -370,7 +403,72 @@ MOE_DEV void tall_unit(const GemmParams &p, const TallUnit &u, const int64_t *sR
   constexpr int VPM = (VPS + 2 * NMB - 1) / (2 * NMB);     // ... per MFMA
   // (b0: step 0's B fragments, dequantised before the stage barrier, while the wave waits for
   // the others)
+  // WF_MXS: a stage is one step of the block-scaled 16x16x128 MFMA.  Per row block: the
+  // FP8 operand pair of the 16 tokens (hi: 16-byte blocks kq and 4 + kq of the staged row,
+  // lo: 8 + kq and 12 + kq -- the operand's two 16-element halves, K = 16 kq .. and
+  // 64 + 16 kq ..), the pair's E8M0 scales (Eh | El << 8) of the lane's block kq, then four
+  // MFMAs: each weight half (FP4 codes as stored, E8M0 byte 2 * (c % 2) + h of the slot's
+  // scale word) times hi and lo, accumulated in fp32.
+  auto compute_mxs = [&](int c, int buf, const Ch &ch, bool issue, int cl, int bufl, Ch &chl) {
+    constexpr int LPT = (LPS + NMB - 1) / NMB;
+    const char *sAb = sA.b[buf];
+    const char *sSb = sA.s[buf] + n16 * 8 + kq * 2;
+    typedef int v8i_t __attribute__((ext_vector_type(8)));
+    v8i_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      w[h] = v8i_t{(int)ch.w[h][0], (int)ch.w[h][1], (int)ch.w[h][2], (int)ch.w[h][3], 0, 0, 0, 0};
+    const int sa = (int)ch.s[0];
+    // row block mb's operands: read one block ahead of its MFMAs, nothing moved across blocks
+    struct Ops {
+      v8i_t hi, lo;
+      int sb;
+    };
+    auto read_ops = [&](int mb) {
+      const char *rp = sAb + (16 * mb + n16) * ROWB;
+      const int sw = row_swizzle<BPR>(16 * mb + n16);
+      const u32x4_t h0 = *(const u32x4_t *)(rp + ((kq ^ sw) << 4));
+      const u32x4_t h1 = *(const u32x4_t *)(rp + (((4 + kq) ^ sw) << 4));
+      const u32x4_t l0 = *(const u32x4_t *)(rp + (((8 + kq) ^ sw) << 4));
+      const u32x4_t l1 = *(const u32x4_t *)(rp + (((12 + kq) ^ sw) << 4));
+      Ops o;
+      o.sb = (int)*(const uint16_t *)(sSb + mb * 256);
+      o.hi = v8i_t{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+      o.lo = v8i_t{(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+      return o;
+    };
+    Ops cur = read_ops(0);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      if (issue) {
+#pragma unroll
+        for (int k = mb * LPT; k < (mb + 1) * LPT && k < LPS; ++k) ld.load_k(cl, sA, bufl, chl, k);
+      }
+      Ops nxt = cur;
+      if (mb + 1 < NMB) nxt = read_ops(mb + 1);
+      if (c & 1) {
+        acc[mb][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w[0], cur.hi, acc[mb][0], 4, 0, 2, sa, 0, cur.sb);
+        acc[mb][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w[1], cur.hi, acc[mb][1], 4, 0, 3, sa, 0, cur.sb);
+        acc[mb][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w[0], cur.lo, acc[mb][0], 4, 0, 2, sa, 1, cur.sb);
+        acc[mb][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w[1], cur.lo, acc[mb][1], 4, 0, 3, sa, 1, cur.sb);
+      } else {
+        acc[mb][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w[0], cur.hi, acc[mb][0], 4, 0, 0, sa, 0, cur.sb);
+        acc[mb][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w[1], cur.hi, acc[mb][1], 4, 0, 1, sa, 0, cur.sb);
+        acc[mb][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w[0], cur.lo, acc[mb][0], 4, 0, 0, sa, 1, cur.sb);
+        acc[mb][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w[1], cur.lo, acc[mb][1], 4, 0, 1, sa, 1, cur.sb);
+      }
+      // (the MFMAs are pure: without a use here they would sink to the epilogue, and every
+      // stage's operands would stay live until then)
+      asm volatile("" : "+v"(acc[mb][0]), "+v"(acc[mb][1]));
+      __builtin_amdgcn_sched_barrier(0);
+      cur = nxt;
+    }
+  };
   auto compute = [&](int c, int buf, const Ch &ch, const u32x4_t (&b0)[2], bool issue, int cl, int bufl, Ch &chl) {
+    if constexpr (C::MXS) {
+      compute_mxs(c, buf, ch, issue, cl, bufl, chl);
+      return;
+    }
     constexpr int NS = NUS * SPU;
     constexpr int LPT = (LPS + NS - 1) / NS;               // loads issued per step
     const char *sAb = sA.b[buf] + n16 * ROWB;
@@ -386,7 +484,7 @@ MOE_DEV void tall_unit(const GemmParams &p, const TallUnit &u, const int64_t *sR
       }
       if (issue) {
 #pragma unroll
-        for (int k = t * LPT; k < (t + 1) * LPT && k < LPS; ++k) ld.load_k(cl, sA.b[bufl], chl, k);
+        for (int k = t * LPT; k < (t + 1) * LPT && k < LPS; ++k) ld.load_k(cl, sA, bufl, chl, k);
       }
       if (t + 1 < NS) deq_step(ch, t + 1, bN);
       const char *apn = sAb + ((((t + 1) / SPU * (UE / 8) + (t + 1) % SPU) ^ lx) << 4);
@@ -552,7 +650,12 @@ __global__ __launch_bounds__(512, 2) void expert_gemm_tall(const GemmParams p) {
   __shared__ __attribute__((aligned(1024))) char sA1[C::ABUF];
   __shared__ __attribute__((aligned(1024))) char sA2[C::ABUF];
   __shared__ __attribute__((aligned(1024))) char sA3[C::NBUF > 3 ? C::ABUF : 16];
-  const StageBufs sA = {{sA0, sA1, sA2, sA3}};
+  constexpr int SSB = C::MXS ? C::NW * 256 : 16;  // scale pairs of one stage (WF_MXS)
+  __shared__ __attribute__((aligned(256))) char sS0[SSB];
+  __shared__ __attribute__((aligned(256))) char sS1[SSB];
+  __shared__ __attribute__((aligned(256))) char sS2[SSB];
+  __shared__ __attribute__((aligned(256))) char sS3[SSB];
+  const StageBufs sA = {{sA0, sA1, sA2, sA3}, {sS0, sS1, sS2, sS3}};
   __shared__ int64_t sRow[2][C::MT];
 
   // units: segment 1 (shared expert / plain rows) first, then the routed m-tiles
@@ -654,6 +757,16 @@ template <int AT>
 static hipError_t launch_w(int wfmt, int group, bool gateup, int odt, const GemmParams &p, int grid, hipStream_t s,
                            hipEvent_t e0, hipEvent_t e1) {
   if (wfmt == WF_DENSE) return launch_o<AT, WF_DENSE, 0>(gateup, odt, p, grid, s, e0, e1);
+  if (wfmt == WF_MXS) {  // split FP8 activations (their f16 source type names the kernel)
+    if constexpr (AT == DT_F16) {
+      if (odt == DT_F16) {
+        if (gateup) launch_t<AT, WF_MXS, 0, true, DT_F16>(p, grid, s, e0, e1);
+        else launch_t<AT, WF_MXS, 0, false, DT_F16>(p, grid, s, e0, e1);
+        return hipGetLastError();
+      }
+    }
+    return hipErrorInvalidValue;
+  }
   if (wfmt == WF_MXFP4) return launch_o<AT, WF_MXFP4, 0>(gateup, odt, p, grid, s, e0, e1);
   if (wfmt == WF_AFFINE4) {
     if (group == 32) return launch_o<AT, WF_AFFINE4, 32>(gateup, odt, p, grid, s, e0, e1);

@@ -32,14 +32,21 @@ struct TopkArgs {
 // chunk's scales: AFFINE4 [half][lane%16][unit] words (scale | qbias << 16), MXFP4
 // [half][lane%16][8] E8M0 bytes.  AFFINE4 weight words keep their 8 codes in pair order:
 // element 2j at bits 4j..4j+3, element 2j+1 at bits 16+4j..19+4j.
+// WF_MXS (MXFP4 for the block-scaled 16x16x128 FP4 x FP8 MFMA): the record's 256 elements are
+// two stages of 128; piece i = 2*stage + half holds, at lane l, the 16 stored bytes (32 codes,
+// low nibble first) of tile row 16*half + l%16 at elements 128*stage + 32*(l/16) .. +32 -- the
+// MFMA's FP4 operand order -- and the 256 scale bytes are one word per lane, byte 2*stage + half
+// the E8M0 scale of those 32 elements.
 __host__ __device__ constexpr int pk_kc(int wf) { return wf == WF_DENSE ? 64 : 256; }
-__host__ __device__ constexpr int pk_ue(int wf, int gq) { return wf == WF_AFFINE4 ? gq : (wf == WF_MXFP4 ? 64 : 32); }
+__host__ __device__ constexpr int pk_ue(int wf, int gq) {
+  return wf == WF_AFFINE4 ? gq : (wf == WF_MXFP4 ? 64 : (wf == WF_MXS ? 128 : 32));
+}
 __host__ __device__ constexpr int pk_lb(int wf, int gq) {  // weight bytes per lane, unit and half
   return wf == WF_DENSE ? 2 * (pk_ue(wf, gq) / 4) : pk_ue(wf, gq) / 8;
 }
 __host__ __device__ constexpr int pk_nu(int wf, int gq) { return pk_kc(wf) / pk_ue(wf, gq); }
 __host__ __device__ constexpr int pk_scale_bytes(int wf, int gq) {
-  return wf == WF_AFFINE4 ? 32 * pk_nu(wf, gq) * 4 : (wf == WF_MXFP4 ? 32 * 8 : 0);
+  return wf == WF_AFFINE4 ? 32 * pk_nu(wf, gq) * 4 : (wf == WF_MXFP4 || wf == WF_MXS ? 32 * 8 : 0);
 }
 __host__ __device__ constexpr int pk_record_bytes(int wf, int gq) { return 4096 + pk_scale_bytes(wf, gq); }
 
@@ -69,6 +76,8 @@ struct AOp {
   int gdiv;
   int row_sub;
   int64_t rows;         // rows of a (bounds of the byte offsets the tall kernel uses)
+  const uint16_t *as;   // WF_MXS: the split activations' scale pairs [rows][ldas] (see split_fp8)
+  int64_t ldas;
 };
 
 struct SegSet {
@@ -223,4 +232,5 @@ struct PackArgs {
   int nblk, nch;
 };
 hipError_t launch_pack(const PackArgs &a, hipStream_t s);
+hipError_t launch_split_fp8(const void *in, int64_t ldi, int rows, int cols, void *hl, uint16_t *hs, hipStream_t s);
 hipError_t launch_combine(int odt, int ydt, const CombineArgs &a, hipStream_t s);

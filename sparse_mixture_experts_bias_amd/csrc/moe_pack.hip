@@ -40,7 +40,35 @@ __global__ __launch_bounds__(256) void pack_kernel(const PackArgs a) {
       return a.gateup ? 16 * b + n16 : 32 * b + 16 * h + n16;
     };
     uint32_t v = 0u;
-    if (o < 1024) {  // weights: piece i = o / 256, lane = (o / 4) % 64, word j = o % 4
+    if (a.wf == WF_MXS) {
+      // piece i = 2 * stage + half: lane l's 16 stored bytes of tile row (half, l % 16) at
+      // elements kc + 128 * stage + 32 * (l / 16); the scale word of lane l: byte 2 * stage +
+      // half is the E8M0 scale of those 32 elements
+      const int lane = o < 1024 ? (o >> 2) & 63 : o - 1024, n16 = lane & 15, kq = lane >> 4;
+      const int NB = a.cols / 32;
+      if (o < 1024) {
+        const int i = o >> 8, st = i >> 1, h = i & 1;
+        bool upper;
+        const int row = src_row(h, n16, upper);
+        const int e0 = kc + 128 * st + 32 * kq;
+        if (row < a.rows && e0 < a.cols) {
+          const uint32_t *w = (const uint32_t *)(upper ? a.b_w : a.a_w);
+          v = w[((int64_t)m * a.rows + row) * wpr + e0 / 8 + (o & 3)];
+        }
+      } else {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int st = bb >> 1, h = bb & 1;
+          bool upper;
+          const int row = src_row(h, n16, upper);
+          const int g = kc / 32 + 4 * st + kq;
+          if (row < a.rows && g < NB) {
+            const uint8_t *sc = (const uint8_t *)(upper ? a.b_s : a.a_s);
+            v |= (uint32_t)sc[((int64_t)m * a.rows + row) * NB + g] << (8 * bb);
+          }
+        }
+      }
+    } else if (o < 1024) {  // weights: piece i = o / 256, lane = (o / 4) % 64, word j = o % 4
       const int i = o >> 8, lane = (o >> 2) & 63, j = o & 3;
       const int q = 4 * i + j;
       const int uu = q / (2 * lpu), h = (q / lpu) & 1, wi = q % lpu;

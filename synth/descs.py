@@ -10,8 +10,8 @@ def linear_desc(l: Linear) -> "moe.Desc":
     return moe.linear(l.fmt, l.w, l.scales, l.qbias, l.bias, l.group_size)
 
 
-def mlp_desc(m: MLP) -> "moe.Desc":
-    return moe.mlp(linear_desc(m.gate), linear_desc(m.up), linear_desc(m.down), m.swiglu_limit)
+def mlp_desc(m: MLP, scaled: bool = False) -> "moe.Desc":
+    return moe.mlp(linear_desc(m.gate), linear_desc(m.up), linear_desc(m.down), m.swiglu_limit, scaled=scaled)
 
 
 def router_desc(b: Block) -> "moe.Desc":
@@ -26,11 +26,12 @@ def inter_dtype_for(b: Block) -> int:
     return moe.MOE_F16 if b.latent_down is not None else moe.MOE_BF16
 
 
-def block_desc(b: Block, inter_dtype: int = None) -> "moe.Desc":
+def block_desc(b: Block, inter_dtype: int = None, scaled: bool = False) -> "moe.Desc":
+    """scaled: MXFP4 routed experts also get the block-scaled MFMA's streams."""
     if inter_dtype is None:
         inter_dtype = inter_dtype_for(b)
     return moe.block(
-        b.H, router_desc(b), mlp_desc(b.experts),
+        b.H, router_desc(b), mlp_desc(b.experts, scaled),
         shared=None if b.shared is None else mlp_desc(b.shared), shared_mode=b.shared_mode,
         coef_w=b.coef_w, coef_b=b.coef_b,
         latent_down=None if b.latent_down is None else linear_desc(b.latent_down),

@@ -30,6 +30,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     names = header_functions()
     assert set(names) == {"moe_route", "moe_permute", "moe_experts_forward", "moe_block_forward", "moe_pack_weights",
+                          "moe_pack_weights_scaled",
                           "moe_block_forward_noalloc", "moe_set_decode_fusion", "moe_status_str",
                           "moe_last_error", "moe_abi_version", "moe_timing_enable", "moe_timing_read"}
     L = moe.lib()
@@ -44,7 +45,7 @@ def test_status_strings_and_version():
                                  "MOE_ERR_DEVICE", "MOE_ERR_UNSUPPORTED"]):
         assert L.moe_status_str(code).decode() == name
     assert L.moe_status_str(99).decode() == "MOE_ERR_UNKNOWN"
-    assert moe.abi_version() >> 16 == 2   # 2: moe_linear.packed and moe_pack_weights
+    assert moe.abi_version() >> 16 == 3   # 3: moe_linear.packed_scaled and moe_pack_weights_scaled
     assert L.moe_timing_enable(42) == moe.MOE_ERR_ARG
     assert L.moe_set_decode_fusion(3) == moe.MOE_ERR_ARG
     assert L.moe_set_decode_fusion(2) == moe.MOE_OK
@@ -56,7 +57,8 @@ def test_status_strings_and_version():
 
 def test_struct_layouts_match_c():
     """ctypes mirrors of the C structs have the C sizes (x86-64 SysV alignment)."""
-    assert ctypes.sizeof(moe.MoeLinear) == 7 * 4 + 4 + 5 * 8
+    assert ctypes.sizeof(moe.MoeLinear) == 7 * 4 + 4 + 6 * 8
+    assert moe.MoeLinear.packed_scaled.offset == 7 * 4 + 4 + 5 * 8
     assert ctypes.sizeof(moe.MoeMLP) == 3 * ctypes.sizeof(moe.MoeLinear) + 8
     assert ctypes.sizeof(moe.MoeRouter) == 5 * 4 + 4 + 3 * 8
 
@@ -136,6 +138,8 @@ HOSTILE = [
     ("c2", "experts.gate.fmt", 9, moe.MOE_ERR_ARG),
     ("c2", "experts.gate.packed", None, moe.MOE_ERR_ARG),          # the GEMM reads only the packed stream
     ("c2", "experts.down.packed", "misaligned", moe.MOE_ERR_ARG),
+    ("c2", "experts.gate.packed_scaled", 1 << 20, moe.MOE_ERR_ARG),  # the scaled stream is MXFP4-only
+    ("c5", "experts.down.packed_scaled", (1 << 20) + 64, moe.MOE_ERR_ARG),  # not 256-byte aligned
     ("c2", "experts.up.fmt", moe.MOE_W_MXFP4, moe.MOE_ERR_QUANT),  # up checked on its own first (group 64)
     ("c5", "latent_down.packed", None, moe.MOE_ERR_ARG),
     ("c2", "experts.swiglu_limit", float("inf"), moe.MOE_ERR_ARG),
@@ -271,6 +275,11 @@ def test_pack_sizes_follow_the_documented_layout(layers):
     assert _pack_query(g5, u5) == (moe.MOE_OK, b5.E * ceil(b5.I, 16) * ceil(b5.D, 256) * (4096 + 32 * 8))
     ld = linear_desc(b5.latent_down)
     assert _pack_query(ld) == (moe.MOE_OK, ceil(b5.D, 32) * ceil(b5.H, 64) * 4096)
+    # the block-scaled MFMA's stream: the same records (1 KB pieces and 256 scale bytes)
+    n = ctypes.c_size_t(0)
+    assert moe.lib().moe_pack_weights_scaled(ctypes.byref(g5.c), ctypes.byref(u5.c), None, ctypes.byref(n),
+                                             None) == moe.MOE_OK
+    assert n.value == b5.E * ceil(b5.I, 16) * ceil(b5.D, 256) * (4096 + 256)
 
 
 def test_pack_rejects_bad_arguments(layers):
@@ -294,6 +303,10 @@ def test_pack_rejects_bad_arguments(layers):
     assert L.moe_pack_weights(ctypes.byref(g.c), None, base, ctypes.byref(n), None) == moe.MOE_ERR_WORKSPACE
     n = ctypes.c_size_t(need)
     assert L.moe_pack_weights(ctypes.byref(g.c), None, base + 8, ctypes.byref(n), None) == moe.MOE_ERR_ARG
+    # the scaled stream exists for MXFP4 weights only
+    n = ctypes.c_size_t(0)
+    assert L.moe_pack_weights_scaled(ctypes.byref(g.c), None, None, ctypes.byref(n), None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_weights_scaled(None, None, None, ctypes.byref(n), None) == moe.MOE_ERR_ARG
 
 
 def test_noalloc_rejects_more_than_its_scratch(layers):

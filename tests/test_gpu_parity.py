@@ -604,3 +604,121 @@ def test_packed_stream_is_the_documented_permutation(cfg, which):
     have = got.cpu().numpy().view(np.uint32)
     assert have.shape == want.shape
     assert np.array_equal(have, want)
+
+
+def _expect_packed_scaled(lins, gateup: bool):
+    """The block-scaled MFMA's stream rebuilt in numpy from include/moe.h: per matrix, per
+    32-row block, per 256-element record: piece i = 2*stage + half holds at lane l the 16
+    stored bytes of tile row (half, l % 16) at elements 128*stage + 32*(l // 16) .. +32, then
+    one word per lane whose byte 2*stage + half is the E8M0 scale of those elements; zero
+    past the rows and columns."""
+    a = lins[0]
+    n, R, K = a.n, a.rows, a.cols
+    nblk = -(-R // 16) if gateup else -(-R // 32)
+    nch = -(-K // 256)
+    words = [l.w.cpu().contiguous().numpy().view(np.uint32).reshape(n, R, -1) for l in lins]
+    e8 = [l.scales.cpu().contiguous().numpy().view(np.uint8).reshape(n, R, K // 32) for l in lins]
+    wpr = words[0].shape[2]
+    out = np.zeros((n, nblk, nch, 1024 + 64), dtype=np.uint32)
+    lane = np.arange(64)
+    n16, kq = lane % 16, lane // 16
+    for st in range(2):
+        for h in range(2):
+            src, sc = (words[h], e8[h]) if gateup else (words[0], e8[0])
+            for bk in range(nblk):
+                row = (16 * bk + n16) if gateup else (32 * bk + 16 * h + n16)
+                for c in range(nch):
+                    e0 = c * 256 + 128 * st + 32 * kq
+                    ok = (row < R) & (e0 < K)
+                    r_ = np.minimum(row, R - 1)
+                    for j in range(4):
+                        word = np.minimum(e0 // 8 + j, wpr - 1)
+                        out[:, bk, c, (2 * st + h) * 256 + lane * 4 + j] = np.where(ok[None, :], src[:, r_, word], 0)
+                    g = np.minimum(e0 // 32, K // 32 - 1)
+                    byte = np.where(ok[None, :], sc[:, r_, g], 0).astype(np.uint32)
+                    out[:, bk, c, 1024 + lane] |= byte << (8 * (2 * st + h))
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("which", ["gateup", "down"])
+def test_packed_scaled_stream_is_the_documented_permutation(which):
+    from synth.descs import linear_desc
+    announce(f"scaled packed layout c5 {which}")
+    b = synth.make_block(synth.SMALL_SPECS["c5"], "cuda:0")
+    if which == "gateup":
+        lins, gu = [b.experts.gate, b.experts.up], True
+        got = moe.moe_pack_weights(linear_desc(lins[0]), linear_desc(lins[1]), scaled=True)
+    else:
+        lins, gu = [b.experts.down], False
+        got = moe.moe_pack_weights(linear_desc(lins[0]), scaled=True)
+    torch.cuda.synchronize()
+    want = _expect_packed_scaled(lins, gu)
+    have = got.cpu().numpy().view(np.uint32)
+    assert have.shape == want.shape
+    assert np.array_equal(have, want)
+
+
+def _scaled_check(b, label, engaged=True):
+    """The latent layer with its routed experts on the block-scaled FP4 x FP8 MFMA: routing
+    bit-exact as everywhere, outputs against the oracle within the bf16 tolerance."""
+    announce(f"{label}: T={b.T} H={b.H} E={b.E} K={b.K} seed={b.seed} (block-scaled MFMA)")
+    dev = b.x.device
+    y = torch.empty(b.T, b.H, dtype=torch.float32, device=dev)
+    idx = torch.empty(b.T, b.K, dtype=torch.int32, device=dev)
+    w = torch.empty(b.T, b.K, dtype=torch.float32, device=dev)
+    used = moe.moe_block_forward(b.x, block_desc(b, scaled=True), y, idx, w)
+    torch.cuda.synchronize()
+    state = tuple(t.cpu().numpy().copy() for t in moe.routing_state(used, b.T, b.K, b.E))
+    check_permutation(idx, b.E, state)
+    y16, idx16, w16 = run_block(b)
+    assert torch.equal(idx, idx16) and torch.equal(w, w16), "the selection must not depend on the GEMM path"
+    # the two GEMM paths round differently: equal bits mean the scaled path did not run
+    assert torch.equal(y, y16) != engaged, "block-scaled path engaged" if not engaged else "block-scaled path not taken"
+    ob = O.from_block(b)
+    gidx, gw, glog = run_route(b)
+    routing, rep = check_routing(ob, np32(idx).astype(np.int64), np32(w), np32(glog))
+    ref = O.block_forward(ob, routing=routing)["y"]
+    stats = check_output(np32(y), ref, False, label)
+    stats16 = check_output(np32(y16), ref, False, label + " (16-bit path)")
+    print(f"[ok] {label}: scaled {stats}; 16-bit {stats16}", flush=True)
+    return y
+
+
+_SCALED_SPECS = {
+    # several m-tiles per expert and column blocks; widths of 4 and 2 stages per record
+    "c5-scaled-a": dict(T=256, D=512, I=256, E=48),
+    # ragged m-tiles, an odd number of 128-element stages (3) in both reductions, top-6
+    "c5-scaled-b": dict(T=301, D=384, I=384, E=24, K=6, seed=16),
+}
+
+
+@pytest.mark.parametrize("name", list(_SCALED_SPECS))
+def test_block_scaled_mfma_small(name):
+    from dataclasses import replace
+    b = synth.make_block(replace(synth.SMALL_SPECS["c5"], name=name, **_SCALED_SPECS[name]), DEV)
+    _scaled_check(b, name)
+
+
+@pytest.mark.timeout(600)
+def test_block_scaled_mfma_full_every_token():
+    """The c5 layer at full size on the block-scaled MFMA: every token against the oracle."""
+    b = synth.make_block(synth.FULL_SPECS["c5"], DEV)
+    _scaled_check(b, "c5-full scaled")
+
+
+def test_block_scaled_mfma_deterministic_and_fallbacks():
+    """Two calls give the same bits; a decode-sized batch, and a layer whose latent width is
+    not a whole number of 128-blocks, keep the 16-bit path with the scaled streams attached."""
+    from dataclasses import replace
+    b = synth.make_block(replace(synth.SMALL_SPECS["c5"], name="c5-scaled-a", **_SCALED_SPECS["c5-scaled-a"]), DEV)
+    d = block_desc(b, scaled=True)
+    outs = []
+    for _ in range(2):
+        y = torch.empty(b.T, b.H, dtype=torch.float32, device=DEV)
+        moe.moe_block_forward(b.x, d, y)
+        outs.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    bs = synth.make_block(replace(synth.SMALL_SPECS["c5"], **_SCALED_SPECS["c5-scaled-a"]), DEV, T=3)
+    _scaled_check(bs, "c5-scaled-a T=3 (16-bit path)", engaged=False)
+    _scaled_check(synth.make_block(synth.SMALL_SPECS["c5"], DEV), "c5-small D=448 (16-bit path)", engaged=False)
