@@ -25,6 +25,11 @@
 //   AFFINE4  w = scale*(1024+q) + (qbias - 1024*scale), q exact in f16 as 1024+q
 //   MXFP4    the scaled FP4 conversion (exact)
 //   DENSE    bf16 as is (rounded to f16 for f16 activations)
+//   WF_MXS   none: MXFP4 codes and E8M0 scales go to the block-scaled 16x16x128 FP4 x FP8
+//            MFMA as stored (moe_pack_weights_scaled stream), against activations split
+//            into two e4m3 terms with E8M0 block scales (split_fp8_kernel); a stage is one
+//            MFMA step, and the activations' scale pairs travel in a small LDS ring of
+//            their own (one more direct load per stage)
 // Reduction elements past the matrix width are zero in the packed stream and the matching
 // activation blocks are read from a zero block, so tails need no special arithmetic.
 #include <hip/hip_ext.h>
