@@ -184,6 +184,10 @@ static __device__ __forceinline__ float pow2(int e) { return __uint_as_float((ui
 static __device__ __forceinline__ uint32_t e4m3_rne(float y, float &yr) {
   const uint32_t sgn = __float_as_uint(y) >> 31 << 7;
   const float a = fabsf(y);
+  if (!(a <= 448.0f)) {  // NaN (nothing larger reaches here): the e4m3 NaN code, so it propagates
+    yr = y;
+    return 0x7Fu | sgn;
+  }
   uint32_t code;
   float r;
   if (a < 0.015625f) {

@@ -722,3 +722,29 @@ def test_block_scaled_mfma_deterministic_and_fallbacks():
     bs = synth.make_block(replace(synth.SMALL_SPECS["c5"], **_SCALED_SPECS["c5-scaled-a"]), DEV, T=3)
     _scaled_check(bs, "c5-scaled-a T=3 (16-bit path)", engaged=False)
     _scaled_check(synth.make_block(synth.SMALL_SPECS["c5"], DEV), "c5-small D=448 (16-bit path)", engaged=False)
+
+
+def test_block_scaled_mfma_scale_extremes():
+    """E8M0 scale bytes 255 (NaN) and 0 in the routed gate weights on the block-scaled MFMA
+    path: the NaN reaches the same output rows as on the 16-bit path and in the oracle (the
+    split keeps a NaN activation NaN); the other rows match the oracle."""
+    from dataclasses import replace
+    b = synth.make_block(replace(synth.SMALL_SPECS["c5"], name="c5-scaled-a", **_SCALED_SPECS["c5-scaled-a"]), DEV)
+    announce("MXFP4 scale bytes 0 and 255 on the block-scaled MFMA, c5-scaled-a")
+    idx, w, _ = run_route(b)
+    e_nan, e_tiny = int(idx[0, 0]), int(idx[0, 1])
+    sc = b.experts.gate.scales.clone()
+    sc[e_nan, 3, 0] = 255
+    sc[e_tiny] = 0
+    b.experts.gate.scales = sc
+    ys = torch.empty(b.T, b.H, dtype=torch.float32, device=DEV)
+    moe.moe_block_forward(b.x, block_desc(b, scaled=True), ys)
+    y16, _, _ = run_block(b)
+    torch.cuda.synchronize()
+    ob = O.from_block(b)
+    with np.errstate(invalid="ignore"):
+        ref = O.block_forward(ob)["y"]
+    got, got16 = np32(ys), np32(y16)
+    nan_ref, nan_got, nan16 = np.isnan(ref).any(axis=1), np.isnan(got).any(axis=1), np.isnan(got16).any(axis=1)
+    assert nan_ref[0] and (nan_got == nan_ref).all() and (nan16 == nan_ref).all(), "NaN rows differ"
+    check_output(got[~nan_ref], ref[~nan_ref], False, "scaled-mfma-scale-extremes")
