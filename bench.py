@@ -404,7 +404,7 @@ def main():
                          "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build runs the block on a "
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the library runs the block on a "
               f"single MI355X; there is no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
 
