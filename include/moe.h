@@ -88,10 +88,12 @@ typedef enum { MOE_SHARED_NONE = 0, MOE_SHARED_ADD = 1, MOE_SHARED_BLEND = 2 } m
  *           stream of the pair, set on `gate`; `up.packed` is not read).  Required by
  *           every BF16/F16-activation GEMM; there w, scales and qbias are not read
  *           (they describe the source of the stream).  Unused on the F32 path.
- *   packed_scaled (optional, MXFP4 only): the stream moe_pack_weights_scaled wrote.  When
- *           the routed experts' gate and down stacks both carry one, prefill-sized
- *           batches of the latent layer (f16 intermediates, expert widths in whole blocks
- *           of 128) run those GEMMs on gfx950's block-scaled FP4 x FP8 MFMA: the weights
+ *   packed_scaled (optional, MXFP4 only): the stream moe_pack_weights_scaled wrote (for
+ *           gate/up: the pair's stream, set on `gate`).  When the routed experts' gate and
+ *           down stacks both carry one, moe_block_forward runs prefill-sized batches of the
+ *           latent layer (f16 intermediates, expert widths in whole blocks of 128) on
+ *           gfx950's block-scaled FP4 x FP8 MFMA (moe_experts_forward keeps the 16-bit
+ *           path): the weights
  *           as stored (codes and E8M0 scales), the activations split into two FP8 terms
  *           with E8M0 block scales of 32 (about 8 significant bits, more than bf16).
  *           NULL, or any other batch: the 16-bit MFMA path.  256-byte aligned.
