@@ -58,11 +58,17 @@ __global__ __launch_bounds__(CMB_T) void combine_kernel(const CombineArgs a) {
   __shared__ float wt[MOE_MAX_TOPK];
   __shared__ float red[CMB_T / 64];
   const int t = blockIdx.x, tid = threadIdx.x;
-  if (tid < a.K) {
-    pos[tid] = a.slot_pos ? a.slot_pos[(int64_t)t * a.K + tid] : t * a.K + tid;
-    wt[tid] = a.topk_w[(int64_t)t * a.K + tid];
+  // token-ordered rows (no slot_pos: row t*K + j): the row loads need nothing from memory
+  // first, and the weights come through the scalar cache beside them; otherwise the slot
+  // positions and weights go through LDS before the row loads
+  const bool direct = a.slot_pos == nullptr;
+  if (!direct) {
+    if (tid < a.K) {
+      pos[tid] = a.slot_pos[(int64_t)t * a.K + tid];
+      wt[tid] = a.topk_w[(int64_t)t * a.K + tid];
+    }
+    __syncthreads();
   }
-  __syncthreads();
   const int ncb = (a.D + CMB_COLS - 1) / CMB_COLS;
   float keep[CMB_MAXIT][8];
   float ss = 0.f;
@@ -80,11 +86,14 @@ __global__ __launch_bounds__(CMB_T) void combine_kernel(const CombineArgs a) {
     for (int j0 = 0; j0 < a.K; j0 += CMB_JB) {
       float f[CMB_JB][8];
 #pragma unroll
-      for (int jj = 0; jj < CMB_JB; ++jj) load8<ODT>(a.o, (int64_t)pos[min(j0 + jj, a.K - 1)] * a.ldo + c, f[jj]);
+      for (int jj = 0; jj < CMB_JB; ++jj) {
+        const int j = min(j0 + jj, a.K - 1);
+        load8<ODT>(a.o, (direct ? (int64_t)t * a.K + j : (int64_t)pos[j]) * a.ldo + c, f[jj]);
+      }
 #pragma unroll
       for (int jj = 0; jj < CMB_JB; ++jj) {
         if (j0 + jj < a.K) {
-          const float w = wt[j0 + jj];
+          const float w = direct ? a.topk_w[(int64_t)t * a.K + j0 + jj] : wt[j0 + jj];
 #pragma unroll
           for (int q = 0; q < 8; ++q) v[q] = fmaf(w, f[jj][q], v[q]);
         }
