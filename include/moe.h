@@ -150,7 +150,10 @@ typedef struct {
                                 (MOE_F32 when x is f32).  MOE_F16 keeps 3 more mantissa
                                 bits but its range ends at 65504: a value beyond it is
                                 stored as +-inf and propagates to y (no saturation, no
-                                error status).  MOE_BF16 has the fp32 range. */
+                                error status).  With MOE_F16 a prefill-sized batch of a
+                                bf16 layer also reads x as f16 and dequantises 4-bit
+                                weights to f16 (11 bits instead of 8), so x is bound by
+                                the same range there.  MOE_BF16 has the fp32 range. */
 } moe_block;
 
 /*

@@ -1022,6 +1022,10 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
   const size_t o_zs = mxs ? pl.take((size_t)T * (D / 32) * 2) : 0;
   const size_t o_hhl = mxs ? pl.take((size_t)TK * I * 2) : 0;
   const size_t o_hsc = mxs ? pl.take((size_t)TK * (I / 32) * 2) : 0;
+  // f16 intermediates on the prefill kernel: the gate/up launch reads an f16 copy of x, so
+  // that its MFMAs and the dequantisation run in f16 (packed half-precision arithmetic)
+  const bool x16 = !latent && mf && x_dtype == MOE_BF16 && inter == MOE_F16 && mb == MB_TALL;
+  const size_t o_x16 = x16 ? pl.take((size_t)T * H * 2) : 0;
   bool query;
   TRY(check_ws(ws, ws_bytes, pl.off, &query));
   if (query || T == 0) return MOE_OK;
@@ -1183,13 +1187,20 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int64_t T, const mo
 
   if (!latent) {
     // 3. gate/up (+ SwiGLU) for every slot, shared rows appended
-    SegSet gu = segset(aop(x, H, ss, K, 0, Ti), b->experts.gate, &b->experts.up, b->experts.swiglu_limit, true);
+    const void *xa = x;
+    int xdt = x_dtype;
+    if (x16) {
+      xa = at<char>(ws, o_x16);
+      xdt = MOE_F16;
+      HIPCHK(launch_bf16_to_f16(x, (void *)xa, T * H, s));
+    }
+    SegSet gu = segset(aop(xa, H, ss, K, 0, Ti), b->experts.gate, &b->experts.up, b->experts.swiglu_limit, true);
     SegSet gus;
-    if (has_shared) gus = segset(aop(x, H, nullptr, 1, TK, Ti), b->shared.gate, &b->shared.up, b->shared.swiglu_limit, true);
-    TRY(run_gemm(x_dtype, b->experts.gate, true, inter, mb, gu, fuse_shared ? &gus : nullptr, TK, Tsh, tiles, tc,
+    if (has_shared) gus = segset(aop(xa, H, nullptr, 1, TK, Ti), b->shared.gate, &b->shared.up, b->shared.swiglu_limit, true);
+    TRY(run_gemm(xdt, b->experts.gate, true, inter, mb, gu, fuse_shared ? &gus : nullptr, TK, Tsh, tiles, tc,
                  ntile, TK, E, h, ldh, nullptr, 0, s));
     if (has_shared && !fuse_shared)
-      TRY(run_plain(x_dtype, b->shared.gate, &b->shared.up, b->shared.swiglu_limit, true, inter, x, H, Ti,
+      TRY(run_plain(xdt, b->shared.gate, &b->shared.up, b->shared.swiglu_limit, true, inter, xa, H, Ti,
                     (char *)h + (size_t)TK * ldh * isz, ldh, nullptr, 0, s));
     // 4. down
     SegSet dn = segset(aop(h, ldh, nullptr, 1, 0, TK + Tsh), b->experts.down, nullptr, 0.f, false);

@@ -267,3 +267,26 @@ hipError_t launch_split_fp8(const void *in, int64_t ldi, int rows, int cols, voi
                      (uint8_t *)hl, hs);
   return hipGetLastError();
 }
+
+// bf16 -> f16, 8 elements per thread (n a multiple of 8; both 16-byte aligned): the f16 copy of
+// the block input that the prefill GEMMs read when the intermediates are f16.  Exact for
+// magnitudes in f16's normal range (a bf16 mantissa fits in f16's); below it the f16
+// subnormals round, above 65504 the result is inf.
+__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint32_t *in, uint32_t *out, int64_t n8) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+    const bf16x8_t v = *(const bf16x8_t *)(in + 4 * i);
+    f16x8_t r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (_Float16)(float)v[j];
+    *(f16x8_t *)(out + 4 * i) = r;
+  }
+}
+
+hipError_t launch_bf16_to_f16(const void *in, void *out, int64_t n, hipStream_t s) {
+  const int64_t n8 = n / 8;
+  if (n8 <= 0) return hipSuccess;
+  const int64_t want = (n8 + 255) / 256;
+  const int grid = (int)(want < 8192 ? want : 8192);
+  hipLaunchKernelGGL(bf16_to_f16_kernel, dim3(grid), dim3(256), 0, s, (const uint32_t *)in, (uint32_t *)out, n8);
+  return hipGetLastError();
+}

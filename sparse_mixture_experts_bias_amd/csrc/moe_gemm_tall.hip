@@ -22,7 +22,8 @@
 //     current MFMAs).
 //
 // Dequantisation (per weight, fp32 then one rounding to the MFMA's 16-bit type):
-//   AFFINE4  w = scale*(1024+q) + (qbias - 1024*scale), q exact in f16 as 1024+q
+//   AFFINE4  w = scale*(1024+q) + (qbias - 1024*scale), q exact in f16 as 1024+q (f16
+//            activations: packed half-precision q = (1024+q) - 1024, then scale*q + qbias)
 //   MXFP4    the scaled FP4 conversion (exact)
 //   DENSE    bf16 as is (rounded to f16 for f16 activations)
 //   WF_MXS   none: MXFP4 codes and E8M0 scales go to the block-scaled 16x16x128 FP4 x FP8
@@ -381,7 +382,10 @@ MOE_DEV void tall_unit(const GemmParams &p, const TallUnit &u, const int64_t *sR
       if constexpr (AFF) {
         const uint32_t v = ch.s[h * NUS + uu];
         const float sc = __uint_as_float(v << 16), qb = __uint_as_float(v & 0xFFFF0000u);
-        b[h] = deq_affine<AT>(ch.w[q >> 2][q & 3], m0, m1, g0, g1, sc, fmaf(-1024.0f, sc, qb), fmaf(-64.0f, sc, qb));
+        if constexpr (AT == DT_F16)
+          b[h] = deq_affine_h16(ch.w[q >> 2][q & 3], m0, m1, g0, g1, h16_pair(sc), h16_pair(qb));
+        else
+          b[h] = deq_affine<AT>(ch.w[q >> 2][q & 3], m0, m1, g0, g1, sc, fmaf(-1024.0f, sc, qb), fmaf(-64.0f, sc, qb));
       } else if constexpr (MX) {
         const float sc = e8m0_scale((ch.s[h] >> (8 * (2 * uu + (kq >> 1)))) & 0xFFu);
         b[h] = cvt_mxfp4<AT>(ch.w[q >> 2][q & 3], sc);
@@ -404,7 +408,7 @@ MOE_DEV void tall_unit(const GemmParams &p, const TallUnit &u, const int64_t *sR
   // steps, LPS/NS per step: issued all at once they stall every wave on the address path.
   // The wave priority falls with the step, so that the wave of a SIMD pair that is behind
   // issues first and the pair reaches the stage barrier together.
-  constexpr int VPS = AFF ? 40 : 12;                       // VALU of one step's dequantisation
+  constexpr int VPS = AFF ? (AT == DT_F16 ? 28 : 40) : 12;  // VALU of one step's dequantisation
   constexpr int VPM = (VPS + 2 * NMB - 1) / (2 * NMB);     // ... per MFMA
   // (b0: step 0's B fragments, dequantised before the stage barrier, while the wave waits for
   // the others)

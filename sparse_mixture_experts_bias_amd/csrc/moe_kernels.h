@@ -232,5 +232,6 @@ struct PackArgs {
   int nblk, nch;
 };
 hipError_t launch_pack(const PackArgs &a, hipStream_t s);
+hipError_t launch_bf16_to_f16(const void *in, void *out, int64_t n, hipStream_t s);
 hipError_t launch_split_fp8(const void *in, int64_t ldi, int rows, int cols, void *hl, uint16_t *hs, hipStream_t s);
 hipError_t launch_combine(int odt, int ydt, const CombineArgs &a, hipStream_t s);

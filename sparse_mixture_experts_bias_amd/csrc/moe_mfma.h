@@ -81,6 +81,32 @@ MOE_DEV u32x4_t deq_affine(uint32_t w, uint32_t m0, uint32_t m1, uint32_t g0, ui
   return r;
 }
 
+// The f16 form of deq_affine in packed half-precision arithmetic: the magic words hold the
+// exact pairs (1024 + q, 1024 + q') or (64 + q, 64 + q'); one packed add takes the magic off
+// (exact: q and the result are small integers) and one packed FMA gives sc*q + qbias rounded
+// once to f16 -- the same single rounding as the fp32 form, with half the instructions.
+// s2 = (sc, sc) and qb2 = (qbias, qbias) in f16: bf16 values convert to f16 exactly inside
+// f16's normal range (a bf16 mantissa fits in f16's).
+MOE_DEV u32x4_t deq_affine_h16(uint32_t w, uint32_t m0, uint32_t m1, uint32_t g0, uint32_t g1, f16x2_t s2,
+                               f16x2_t qb2) {
+  const uint32_t w8 = w >> 8;
+  const uint32_t m[4] = {(w & m0) | g0, (w & m1) | g1, (w8 & m0) | g0, (w8 & m1) | g1};
+  const f16x2_t o0 = {(_Float16)-1024.0f, (_Float16)-1024.0f}, o1 = {(_Float16)-64.0f, (_Float16)-64.0f};
+  u32x4_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f16x2_t q = __builtin_bit_cast(f16x2_t, m[j]) + ((j & 1) ? o1 : o0);
+    r[j] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, qb2));
+  }
+  return r;
+}
+
+// (v, v) in f16
+MOE_DEV f16x2_t h16_pair(float v) {
+  const f16x2_t r = {(_Float16)v, (_Float16)v};  // one v_cvt_pk_f16_f32
+  return r;
+}
+
 // 8 E2M1 codes (two per byte, low nibble first) times a power-of-two scale
 template <int AT>
 MOE_DEV u32x4_t cvt_mxfp4(uint32_t w, float scale) {

@@ -20,10 +20,12 @@ def router_desc(b: Block) -> "moe.Desc":
 
 def inter_dtype_for(b: Block) -> int:
     """f32 layers keep f32 intermediates; the latent layer keeps fp16 ones (its
-    unit-scale outputs need them to stay inside the error budget); the others bf16."""
+    unit-scale outputs need them to stay inside the error budget), and so do prefill-sized
+    batches (more than 64 tokens), whose GEMMs then also dequantise and multiply in f16;
+    decode-sized batches of the other layers keep bf16 (the decode launches take bf16)."""
     if b.x.dtype.is_floating_point and b.x.element_size() == 4:
         return moe.MOE_F32
-    return moe.MOE_F16 if b.latent_down is not None else moe.MOE_BF16
+    return moe.MOE_F16 if (b.latent_down is not None or b.T > 64) else moe.MOE_BF16
 
 
 def block_desc(b: Block, inter_dtype: int = None, scaled: bool = False) -> "moe.Desc":

@@ -91,15 +91,16 @@ def test_block_full_c2_decode():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("cfg", ["c3", "c4", "c5"])
-def test_block_full_every_token(cfg):
+@pytest.mark.parametrize("cfg,inter", [("c3", None), ("c4", None), ("c5", None), ("c3", "bf16"), ("c4", "bf16")])
+def test_block_full_every_token(cfg, inter):
     """Full-size layers in the launch configuration of the benchmark: routing, the
     permutation the experts ran on, and the output of every token against the oracle
-    (the oracle decodes each expert once and applies it to all of its tokens)."""
+    (the oracle decodes each expert once and applies it to all of its tokens).  "bf16":
+    the layer with bf16 intermediates instead of its default."""
     spec = synth.FULL_SPECS[cfg]
     b = synth.make_block(spec, DEV)
-    announce(f"{cfg}-full: T={b.T} H={b.H} E={b.E} K={b.K} seed={b.seed}")
-    y, idx, w, state = run_block(b, with_state=True)
+    announce(f"{cfg}-full inter={inter}: T={b.T} H={b.H} E={b.E} K={b.K} seed={b.seed}")
+    y, idx, w, state = run_block(b, inter=moe.MOE_BF16 if inter == "bf16" else None, with_state=True)
     check_permutation(idx, b.E, state)
     gidx, gw, glog = run_route(b)
     assert torch.equal(gidx, idx) and torch.equal(gw, w)
