@@ -52,11 +52,12 @@ constexpr int CMB_COLS = 8 * CMB_T;
 constexpr int CMB_MAXIT = 4;    // rms-norm mode keeps up to 4*2048 columns in registers
 constexpr int CMB_JB = 8;       // slot rows loaded together
 
-template <int ODT, int YDT>
-__global__ __launch_bounds__(CMB_T) void combine_kernel(const CombineArgs a) {
+template <int ODT, int YDT, int NT>
+__global__ __launch_bounds__(NT) void combine_kernel(const CombineArgs a) {
+  constexpr int CMB_COLS = 8 * NT;  // columns per block pass
   __shared__ int pos[MOE_MAX_TOPK];
   __shared__ float wt[MOE_MAX_TOPK];
-  __shared__ float red[CMB_T / 64];
+  __shared__ float red[NT / 64];
   const int t = blockIdx.x, tid = threadIdx.x;
   // token-ordered rows (no slot_pos: row t*K + j): the row loads need nothing from memory
   // first, and the weights come through the scalar cache beside them; otherwise the slot
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(CMB_T) void combine_kernel(const CombineArgs a) {
   __syncthreads();
   float tot = 0.f;
 #pragma unroll
-  for (int w = 0; w < CMB_T / 64; ++w) tot += red[w];
+  for (int w = 0; w < NT / 64; ++w) tot += red[w];
   const float inv = 1.0f / sqrtf(tot / (float)a.D + a.eps);
 #pragma unroll
   for (int it = 0; it < CMB_MAXIT; ++it) {
@@ -139,11 +140,18 @@ __global__ __launch_bounds__(CMB_T) void combine_kernel(const CombineArgs a) {
   }
 }
 
+// a few tokens (decode): 64-thread blocks over 512 columns each, so that the rows spread over
+// four times the CUs; otherwise (and for the rms norm, which needs a whole row per block) 256
 template <int ODT, int YDT>
 static hipError_t launch_c(const CombineArgs &a, hipStream_t s) {
-  const int ncb = (a.D + CMB_COLS - 1) / CMB_COLS;
-  const int gy = (a.mode == 1) ? 1 : ncb;
-  hipLaunchKernelGGL((combine_kernel<ODT, YDT>), dim3(a.T, gy), dim3(CMB_T), 0, s, a);
+  if (a.mode != 1 && a.T <= 64) {
+    const int ncb = (a.D + 8 * 64 - 1) / (8 * 64);
+    hipLaunchKernelGGL((combine_kernel<ODT, YDT, 64>), dim3(a.T, ncb), dim3(64), 0, s, a);
+  } else {
+    const int ncb = (a.D + CMB_COLS - 1) / CMB_COLS;
+    const int gy = (a.mode == 1) ? 1 : ncb;
+    hipLaunchKernelGGL((combine_kernel<ODT, YDT, CMB_T>), dim3(a.T, gy), dim3(CMB_T), 0, s, a);
+  }
   return hipGetLastError();
 }
 
