@@ -112,6 +112,26 @@ def test_block_full_every_token(cfg, inter):
     print(f"[ok] {cfg}-full, all {b.T} tokens: {stats}", flush=True)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cfg", ["c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("seed", [101, 102, 103])
+def test_block_full_other_seeds(cfg, seed):
+    """The full-size layers drawn from three more seeds (a robustness check of the parity:
+    skew, near-ties and segment sizes change with the draw): routing, permutation and every
+    token's output against the oracle."""
+    b = synth.make_block(synth.FULL_SPECS[cfg], DEV, seed=seed)
+    announce(f"{cfg}-full seed {seed}: T={b.T} H={b.H} E={b.E} K={b.K}")
+    y, idx, w, state = run_block(b, with_state=True)
+    check_permutation(idx, b.E, state)
+    gidx, gw, glog = run_route(b)
+    assert torch.equal(gidx, idx) and torch.equal(gw, w)
+    ob = O.from_block(b)
+    routing, rep = check_routing(ob, np32(idx).astype(np.int64), np32(w), np32(glog))
+    ref = O.block_forward(ob, routing=routing)["y"]
+    stats = check_output(np32(y), ref, False, f"{cfg}-full seed {seed}")
+    print(f"[ok] {cfg}-full seed {seed}: {stats} {rep}", flush=True)
+
+
 def _check_permute(idx: torch.Tensor, E: int):
     T, K = idx.shape
     counts = torch.empty(E, dtype=torch.int32, device=DEV)
